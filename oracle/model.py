@@ -1,0 +1,201 @@
+"""Oracle of KV injection and of the block-diffusion draft (test infrastructure only).
+
+Dimensions come from any object ``cfg`` with the attributes hidden,
+n_layers, n_q_heads, n_kv_heads, head_dim, intermediate, vocab, n_fuse,
+target_hidden, rope_base, rms_eps, mask_token_id and dtype ('bf16'/'fp32').
+Weights come as a dict of numpy arrays holding the exact stored values:
+
+    w_fc [H, F*Ht]; w_kv [L*2*n_kv*d, H] (per layer: n_kv*d K rows, then
+    n_kv*d V rows); embed [V, H]; final_norm [H]; lm_head [V, H];
+    per-layer lists attn_norm [H], w_q [n_q*d, H], w_o [H, n_q*d],
+    mlp_norm [H], w_gate [I, H], w_up [I, H], w_down [H, I].
+
+A linear layer y = W x uses W as [out, in].  The KV pool of one sequence is
+a pair (K, V) of float64 arrays [L, T, n_kv, d] in logical token order.
+
+What the pages fix, and the readings taken where they are silent:
+
+* Fusion ([Note] 三大核心创新 §1 and 整体架构): hidden states taken from several
+  target layers are fused into compact context features.  Reading: the F
+  hidden vectors are concatenated in layer order and mapped by one linear
+  projection f = W_fc x, no bias, no norm.
+* Injection ([Note] 三大核心创新 §2; [Deep] 2.2): the context features enter
+  each draft layer's K/V projection and the result is cached and reused, so
+  the draft sees the context only through this cache, with no extra context
+  tokens.  "Immediate Materialization" ([Note]) projects at injection time so
+  only K/V are kept, and layer-batched projections compute every layer's
+  K/V in one product.  Reading: the draft layer's own K/V weights (rows of
+  w_kv) project f; K gets rotary embedding at the token's absolute position.
+* Block diffusion ([Deep] 2.3; [Note] 三大核心创新 §3): a block of B positions
+  starts all [MASK]; one forward predicts every position at once; a few
+  denoising rounds fix the tokens progressively.  Reading: step s of S
+  commits the floor(sB/S)-floor((s-1)B/S) still-open positions whose
+  prediction is most confident (confidence = log-probability of the chosen
+  token, ties to the lower position); later steps re-embed the committed
+  tokens and leave them unchanged.  Every block query sees all context keys
+  and all B block keys (bidirectional inside the block).
+* Draft layer: RMSNorm, grouped-query attention (head n uses kv head
+  n // (n_q/n_kv)), residual, RMSNorm, SwiGLU MLP, residual; final RMSNorm,
+  LM head.  The mask token is id V-1 and argmax runs over the whole vocab.
+"""
+import numpy as np
+
+from .numerics import F64, bf16_round, rope, rmsnorm, silu, logsumexp
+from .philox import gumbel_noise
+
+
+def _store(cfg, x):
+    """Round to the storage type of the KV pool / LM-head input."""
+    return bf16_round(x) if cfg.dtype == "bf16" else np.asarray(x, F64)
+
+
+def _lin(x, w):
+    """y = x W^T with W [out, in]; float64 matmul."""
+    return np.asarray(x, F64) @ np.asarray(w, F64).T
+
+
+def inject(cfg, W, x, pos):
+    """Context features -> per-layer K/V for the KV pool.
+
+    x: [n, F*Ht] target hidden states (concatenated layers), pos: [n]
+    absolute positions.  Returns K, V as float64 [L, n, n_kv, d], rounded to
+    the pool's storage type.
+    """
+    L, nkv, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
+    f = _lin(x, W["w_fc"])                       # fused context features [n, H]
+    kv = _lin(f, W["w_kv"])                      # all layers at once [n, L*2*nkv*d]
+    kv = kv.reshape(-1, L, 2, nkv, d)
+    pos = np.asarray(pos)
+    K = rope(kv[:, :, 0], pos[:, None, None], cfg.rope_base)
+    V = kv[:, :, 1]
+    return _store(cfg, K.transpose(1, 0, 2, 3)), _store(cfg, V.transpose(1, 0, 2, 3))
+
+
+def attention_group(q, keys, vals, scale, return_probs=False):
+    """Softmax attention of queries q [R, d] over keys/vals [T, d]."""
+    s = (np.asarray(q, F64) @ np.asarray(keys, F64).T) * scale
+    s = s - s.max(axis=-1, keepdims=True)
+    p = np.exp(s)
+    p = p / p.sum(axis=-1, keepdims=True)
+    o = p @ np.asarray(vals, F64)
+    return (o, p) if return_probs else o
+
+
+def forward_hidden(cfg, W, pools, ctx_len, tau):
+    """One draft forward.  tau: [bt, B] token ids.  Returns the LM-head input
+    y [bt, B, H] (final RMSNorm, rounded to the LM-head storage type)."""
+    H, L = cfg.hidden, cfg.n_layers
+    nq, nkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
+    g = nq // nkv
+    tau = np.asarray(tau)
+    bt, B = tau.shape
+    ctx_len = np.asarray(ctx_len, dtype=np.int64)
+    pos = ctx_len[:, None] + np.arange(B)[None, :]            # [bt, B]
+    h = np.asarray(W["embed"], F64)[tau]                       # [bt, B, H]
+    scale = 1.0 / np.sqrt(d)
+    nkvd = nkv * d
+    for l in range(L):
+        u = rmsnorm(h, W["attn_norm"][l], cfg.rms_eps)
+        q = _lin(u, W["w_q"][l]).reshape(bt, B, nq, d)
+        q = rope(q, pos[:, :, None], cfg.rope_base)
+        kvw = W["w_kv"][l * 2 * nkvd:(l + 1) * 2 * nkvd]
+        kv = _lin(u, kvw)
+        k = rope(kv[..., :nkvd].reshape(bt, B, nkv, d), pos[:, :, None], cfg.rope_base)
+        v = kv[..., nkvd:].reshape(bt, B, nkv, d)
+        o = np.empty((bt, B, nq, d), F64)
+        for b in range(bt):
+            Kc, Vc = pools[b]
+            T = int(ctx_len[b])
+            for m in range(nkv):
+                keys = np.concatenate([Kc[l, :T, m], k[b, :, m]], axis=0)
+                vals = np.concatenate([Vc[l, :T, m], v[b, :, m]], axis=0)
+                qm = q[b, :, m * g:(m + 1) * g].reshape(B * g, d)
+                o[b, :, m * g:(m + 1) * g] = attention_group(qm, keys, vals, scale).reshape(B, g, d)
+        h = h + _lin(o.reshape(bt, B, nq * d), W["w_o"][l])
+        u = rmsnorm(h, W["mlp_norm"][l], cfg.rms_eps)
+        a = silu(_lin(u, W["w_gate"][l])) * _lin(u, W["w_up"][l])
+        h = h + _lin(a, W["w_down"][l])
+    y = rmsnorm(h, W["final_norm"], cfg.rms_eps)
+    return _store(cfg, y)
+
+
+def lm_head_logits(cfg, W, y, chunk=16384):
+    """z = W_lm y for rows y [R, H] -> [R, V], computed over vocab chunks."""
+    y = np.asarray(y, F64)
+    V = cfg.vocab
+    z = np.empty((y.shape[0], V), F64)
+    for v0 in range(0, V, chunk):
+        z[:, v0:v0 + chunk] = y @ np.asarray(W["lm_head"][v0:v0 + chunk], F64).T
+    return z
+
+
+def commit_counts(B, S):
+    """Positions committed at each of the S steps: floor(sB/S)-floor((s-1)B/S)."""
+    return [(s * B) // S - ((s - 1) * B) // S for s in range(1, S + 1)]
+
+
+def _top2_gap(x):
+    if x.shape[-1] < 2:
+        return np.full(x.shape[:-1], np.inf)
+    part = np.partition(x, -2, axis=-1)
+    return part[..., -1] - part[..., -2]
+
+
+def draft_block(cfg, W, pools, ctx_len, block_size, n_steps, temperature=0.0, seed=0,
+                want_logits=True):
+    """Denoise one [MASK] block per sequence in n_steps forwards.
+
+    Returns a dict with
+      tokens [bt, B]            committed tokens,
+      logits [bt, B, V]         each position's logits at its commit step (if want_logits),
+      conf [bt, S, B]           confidence of every still-open position at each step (nan otherwise),
+      cand [bt, S, B]           candidate token of every open position at each step (-1 otherwise),
+      committed_at [bt, B]      step index (0-based) at which each position was committed,
+      gap [bt, S, B]            top-1 minus top-2 of the score the candidate maximises
+                                (logits at T=0, logits/T + Gumbel at T>0),
+      boundary_gap [bt, S]      confidence gap between the last committed and the first
+                                left-open position (inf when nothing is left open).
+    """
+    B, S, V = block_size, n_steps, cfg.vocab
+    bt = len(ctx_len)
+    tau = np.full((bt, B), cfg.mask_token_id, dtype=np.int64)
+    committed = np.zeros((bt, B), dtype=bool)
+    committed_at = np.full((bt, B), -1, dtype=np.int64)
+    conf = np.full((bt, S, B), np.nan)
+    cand = np.full((bt, S, B), -1, dtype=np.int64)
+    gap = np.full((bt, S, B), np.nan)
+    boundary = np.full((bt, S), np.inf)
+    logits = np.zeros((bt, B, V), F64) if want_logits else None
+    ks = commit_counts(B, S)
+    for s in range(S):
+        y = forward_hidden(cfg, W, pools, ctx_len, tau)
+        rows = [(b, i) for b in range(bt) for i in range(B) if not committed[b, i]]
+        z = lm_head_logits(cfg, W, np.stack([y[b, i] for b, i in rows]))
+        for r, (b, i) in enumerate(rows):
+            zr = z[r]
+            if temperature > 0:
+                zt = zr / temperature
+                score = zt + gumbel_noise(seed, b, s, i, V)
+                c = int(np.argmax(score))           # first maximum = lowest index
+                conf[b, s, i] = zt[c] - logsumexp(zt)
+            else:
+                score = zr
+                c = int(np.argmax(score))
+                conf[b, s, i] = zr[c] - logsumexp(zr)
+            cand[b, s, i] = c
+            gap[b, s, i] = _top2_gap(score)
+            if want_logits:
+                logits[b, i] = zr
+        for b in range(bt):
+            open_i = np.nonzero(~committed[b])[0]
+            # most confident first; equal confidence -> lower position first
+            order = open_i[np.lexsort((open_i, -conf[b, s, open_i]))]
+            k = ks[s] if s < S - 1 else len(order)
+            take = order[:k]
+            if k < len(order):
+                boundary[b, s] = conf[b, s, order[k - 1]] - conf[b, s, order[k]] if k > 0 else np.inf
+            tau[b, take] = cand[b, s, take]
+            committed[b, take] = True
+            committed_at[b, take] = s
+    return dict(tokens=tau, logits=logits, conf=conf, cand=cand, committed_at=committed_at,
+                gap=gap, boundary_gap=boundary)
