@@ -1,0 +1,485 @@
+// libdflash C ABI: argument checks, workspace layout and the launch sequence
+// of KV injection, the block-diffusion draft and block verification.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <vector>
+
+#include "dflash.h"
+#include "kernels.h"
+
+using namespace dflash;
+
+namespace {
+
+// ---------------------------------------------------------------- timing hooks
+struct Prof {
+  int cls = DFLASH_PROF_NONE;
+  std::vector<hipEvent_t> pool;  // reusable events
+  std::vector<std::pair<hipEvent_t, hipEvent_t>> recorded;
+  hipEvent_t open = nullptr;
+  size_t used = 0;
+} g_prof;
+
+hipEvent_t prof_event() {
+  if (g_prof.used == g_prof.pool.size()) {
+    hipEvent_t e;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    g_prof.pool.push_back(e);
+  }
+  return g_prof.pool[g_prof.used++];
+}
+
+void prof_mark(int cls, int phase, hipStream_t s) {
+  if (g_prof.cls == DFLASH_PROF_NONE || g_prof.cls != cls) return;
+  hipEvent_t e = prof_event();
+  if (!e) return;
+  if (hipEventRecord(e, s) != hipSuccess) return;
+  if (phase == 0) {
+    g_prof.open = e;
+  } else if (g_prof.open) {
+    g_prof.recorded.emplace_back(g_prof.open, e);
+    g_prof.open = nullptr;
+  }
+}
+
+void prof_attn(int phase, hipStream_t s) { prof_mark(DFLASH_PROF_ATTN, phase, s); }
+
+hipError_t gemm(int cls, const GemmArgs& g, hipStream_t s) {
+  prof_mark(cls, 0, s);
+  hipError_t e = launch_gemm(g, s);
+  prof_mark(cls, 1, s);
+  return e;
+}
+
+// ---------------------------------------------------------------- checks
+bool ptr_ok(const void* p) { return p != nullptr; }
+
+dflash_status check_cfg(const dflash_config* c) {
+  if (!c) return DFLASH_EINVAL;
+  if (c->dtype != DFLASH_F32 && c->dtype != DFLASH_BF16) return DFLASH_EDTYPE;
+  if (c->hidden <= 0 || c->n_layers <= 0 || c->n_q_heads <= 0 || c->n_kv_heads <= 0 || c->intermediate <= 0 ||
+      c->vocab < 2 || c->n_fuse <= 0 || c->target_hidden <= 0)
+    return DFLASH_ESHAPE;
+  if (c->head_dim != 64 && c->head_dim != 128) return DFLASH_ESHAPE;
+  if (c->n_q_heads % c->n_kv_heads) return DFLASH_ESHAPE;
+  if (c->hidden % 64 || c->intermediate % 64 || (c->n_fuse * c->target_hidden) % 64) return DFLASH_ESHAPE;
+  if (c->page_size != 16) return DFLASH_ESHAPE;
+  if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab) return DFLASH_EINVAL;
+  if (!(c->rope_base > 0.f) || !(c->rms_eps >= 0.f)) return DFLASH_EINVAL;
+  return DFLASH_OK;
+}
+
+dflash_status check_weights(const dflash_config* c, const dflash_weights* w, bool draft) {
+  if (!w) return DFLASH_EINVAL;
+  if (!ptr_ok(w->w_fc) || !ptr_ok(w->w_kv)) return DFLASH_EINVAL;
+  if (!draft) return DFLASH_OK;
+  if (!ptr_ok(w->embed) || !ptr_ok(w->final_norm) || !ptr_ok(w->lm_head)) return DFLASH_EINVAL;
+  const void* const* arrs[7] = {(const void* const*)w->attn_norm, w->w_q, w->w_o, (const void* const*)w->mlp_norm,
+                                w->w_gate, w->w_up, w->w_down};
+  for (auto a : arrs) {
+    if (!a) return DFLASH_EINVAL;
+    for (int l = 0; l < c->n_layers; ++l)
+      if (!a[l]) return DFLASH_EINVAL;
+  }
+  return DFLASH_OK;
+}
+
+// ---------------------------------------------------------------- workspace
+struct Carve {
+  size_t off = 0;
+  size_t take(size_t bytes) {
+    const size_t o = off;
+    off += (bytes + 255) & ~(size_t)255;
+    return o;
+  }
+};
+
+void attn_split(int bt, int nkv, int nqg, int ctx_cap, int& ns, int& pps) {
+  const int pages = (ctx_cap + 15) / 16;
+  if (pages <= 0) {
+    ns = 0;
+    pps = 2;
+    return;
+  }
+  const int pairs = std::max(1, bt * nkv * nqg);
+  const int want = (2048 + pairs - 1) / pairs;
+  const int max_ns = (pages + 1) / 2;
+  ns = std::max(1, std::min(want, max_ns));
+  pps = (pages + ns - 1) / ns;
+  pps = (pps + 1) & ~1;
+  ns = (pages + pps - 1) / pps;
+}
+
+int n_qgroups(const dflash_config* c, int B) { return ((c->n_q_heads / c->n_kv_heads) * B + 63) / 64; }
+
+struct DraftWS {
+  size_t h, u_hi, u_lo, qkv, o_hi, o_lo, act_hi, act_lo, y, row_map, part_f, part_i, att_o, att_lse, cs, tau,
+      committed, cand, conf, total;
+  int ns, pps, ntiles;
+};
+
+DraftWS draft_layout(const dflash_config* c, int bt, int B, int ctx_cap) {
+  DraftWS w{};
+  const size_t M = (size_t)bt * B;
+  const size_t H = c->hidden, I = c->intermediate, d = c->head_dim, nq = c->n_q_heads, nkv = c->n_kv_heads;
+  const size_t el = c->dtype == DFLASH_BF16 ? 2 : 4;  // one plane of an activation operand
+  attn_split(bt, (int)nkv, n_qgroups(c, B), ctx_cap, w.ns, w.pps);
+  w.ntiles = (c->vocab + gemm_bn(c->dtype) - 1) / gemm_bn(c->dtype);
+  Carve k;
+  w.h = k.take(M * H * 4);
+  w.u_hi = k.take(M * H * el);
+  w.u_lo = k.take(M * H * el);
+  w.qkv = k.take(M * (nq + 2 * nkv) * d * 4);
+  w.o_hi = k.take(M * nq * d * el);
+  w.o_lo = k.take(M * nq * d * el);
+  w.act_hi = k.take(M * I * el);
+  w.act_lo = k.take(M * I * el);
+  w.y = k.take(M * H * 4);
+  w.row_map = k.take(M * 4);
+  w.part_f = k.take(M * w.ntiles * 16);
+  w.part_i = k.take(M * w.ntiles * 4);
+  w.att_o = k.take((size_t)(w.ns + 1) * M * nq * d * 4);
+  w.att_lse = k.take((size_t)(w.ns + 1) * M * nq * 4);
+  w.cs = k.take(M * (d / 2) * 8);
+  w.tau = k.take(M * 4);
+  w.committed = k.take(M * 4);
+  w.cand = k.take(M * 4);
+  w.conf = k.take(M * 4);
+  w.total = k.off;
+  return w;
+}
+
+struct InjectWS {
+  size_t f_hi, f_lo, cs, total;
+};
+
+InjectWS inject_layout(const dflash_config* c, int chunk) {
+  InjectWS w{};
+  const size_t el = c->dtype == DFLASH_BF16 ? 2 : 4;
+  Carve k;
+  w.f_hi = k.take((size_t)chunk * c->hidden * el);
+  w.f_lo = k.take((size_t)chunk * c->hidden * el);
+  w.cs = k.take((size_t)chunk * (c->head_dim / 2) * 8);
+  w.total = k.off;
+  return w;
+}
+
+// Injection chunk the workspace holds (rows of one fused-feature pass).
+int inject_chunk_capacity(const dflash_config* c, size_t ws_bytes) {
+  const size_t el = c->dtype == DFLASH_BF16 ? 2 : 4;
+  const size_t per = 2 * c->hidden * el + (c->head_dim / 2) * 8;
+  size_t n = ws_bytes / (per + 1);
+  while (n > 0 && inject_layout(c, (int)std::min<size_t>(n, 1 << 30)).total > ws_bytes) n -= std::max<size_t>(1, n / 64);
+  return (int)std::min<size_t>(n, 1 << 30);
+}
+
+char* at(void* ws, size_t off) { return (char*)ws + off; }
+
+ActOut act_out(const dflash_config* c, void* hi, void* lo, int ld) {
+  ActOut o;
+  o.p0 = hi;
+  o.p1 = lo;
+  o.ld = ld;
+  o.mode = c->dtype == DFLASH_BF16 ? ACT_HILO : ACT_F32;
+  return o;
+}
+ActIn act_in(const ActOut& o) { return ActIn{o.p0, o.p1, o.ld, o.mode}; }
+
+#define HIP_TRY(x)                              \
+  do {                                          \
+    if ((x) != hipSuccess) return DFLASH_EHIP;  \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* dflash_status_string(dflash_status s) {
+  switch (s) {
+    case DFLASH_OK: return "ok";
+    case DFLASH_EINVAL: return "invalid argument";
+    case DFLASH_ESHAPE: return "unsupported or inconsistent shape";
+    case DFLASH_EDTYPE: return "unknown dtype";
+    case DFLASH_ECAPACITY: return "capacity exceeded";
+    case DFLASH_EWORKSPACE: return "workspace missing, misaligned or too small";
+    case DFLASH_EHIP: return "HIP error";
+  }
+  return "unknown status";
+}
+
+size_t dflash_workspace_size(const dflash_config* cfg, int32_t max_batch, int32_t block_size,
+                             int32_t max_inject_tokens, int32_t max_ctx_len) {
+  if (check_cfg(cfg) != DFLASH_OK || max_batch < 0 || block_size < 1 || block_size > 16 || max_inject_tokens < 0 ||
+      max_ctx_len < 0)
+    return 0;
+  size_t need = 256;
+  for (int bt = 1; bt <= max_batch; ++bt) need = std::max(need, draft_layout(cfg, bt, block_size, max_ctx_len).total);
+  if (max_inject_tokens > 0) need = std::max(need, inject_layout(cfg, max_inject_tokens).total);
+  return need;
+}
+
+dflash_status dflash_inject_kv(const dflash_config* cfg, const dflash_weights* w, const void* target_hidden,
+                               const int32_t* tok_seq, const int32_t* tok_pos, int32_t n_tok, void* kv_pool,
+                               int32_t n_pages, const int32_t* block_table, int32_t n_seqs, int32_t max_pages,
+                               void* workspace, size_t ws_bytes, hipStream_t stream) {
+  dflash_status st = check_cfg(cfg);
+  if (st != DFLASH_OK) return st;
+  if ((st = check_weights(cfg, w, false)) != DFLASH_OK) return st;
+  if (n_tok < 0 || n_pages < 0 || n_seqs < 0 || max_pages < 0) return DFLASH_EINVAL;
+  if (n_tok == 0) return DFLASH_OK;
+  if (!target_hidden || !tok_seq || !tok_pos || !kv_pool || !block_table) return DFLASH_EINVAL;
+  if (!workspace || ((uintptr_t)workspace & 255)) return DFLASH_EWORKSPACE;
+  const int chunk = inject_chunk_capacity(cfg, ws_bytes);
+  if (chunk < 1) return DFLASH_EWORKSPACE;
+  const InjectWS L = inject_layout(cfg, chunk);
+  const int bf = cfg->dtype == DFLASH_BF16;
+  const size_t el = bf ? 2 : 4;
+  const int H = cfg->hidden, FH = cfg->n_fuse * cfg->target_hidden;
+  const int d = cfg->head_dim, nkv = cfg->n_kv_heads;
+  for (int t0 = 0; t0 < n_tok; t0 += chunk) {
+    const int n = std::min(chunk, n_tok - t0);
+    HIP_TRY(launch_rope_table_tokens(tok_pos + t0, n, d, (double)cfg->rope_base, (float2*)at(workspace, L.cs),
+                                     stream));
+    GemmArgs g{};
+    g.wdtype = bf;
+    g.a = ActIn{(const char*)target_hidden + (size_t)t0 * FH * el, nullptr, FH, bf ? ACT_BF16 : ACT_F32};
+    g.b = BRowsArgs{w->w_fc, nullptr, FH, 0, 0};
+    g.M = n;
+    g.N = H;
+    g.K = FH;
+    g.kind = EPI_STORE;
+    const ActOut f = act_out(cfg, at(workspace, L.f_hi), at(workspace, L.f_lo), H);
+    g.e.out = f;
+    HIP_TRY(gemm(DFLASH_PROF_INJECT_FC, g, stream));
+
+    GemmArgs k{};
+    k.wdtype = bf;
+    k.a = act_in(f);
+    k.b = BRowsArgs{w->w_kv, nullptr, H, 0, 0};
+    k.M = n;
+    k.N = cfg->n_layers * 2 * nkv * d;
+    k.K = H;
+    k.kind = EPI_KVSCATTER;
+    k.e.pool = kv_pool;
+    k.e.tok_seq = tok_seq + t0;
+    k.e.tok_pos = tok_pos + t0;
+    k.e.block_table = block_table;
+    k.e.n_seqs = n_seqs;
+    k.e.max_pages = max_pages;
+    k.e.n_pages = n_pages;
+    k.e.rope_cs = (const float2*)at(workspace, L.cs);
+    k.e.n_layers = cfg->n_layers;
+    k.e.n_kv = nkv;
+    k.e.head_dim = d;
+    HIP_TRY(gemm(DFLASH_PROF_INJECT_KV, k, stream));
+  }
+  return DFLASH_OK;
+}
+
+dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, const void* kv_pool,
+                                 int32_t n_pages, const int32_t* block_table, int32_t max_pages,
+                                 const int32_t* ctx_len, int32_t max_ctx_len, int32_t batch, int32_t block_size,
+                                 int32_t n_steps, float temperature, uint64_t seed, int32_t* out_tokens,
+                                 float* out_logits, float* out_conf, void* workspace, size_t ws_bytes,
+                                 hipStream_t stream) {
+  dflash_status st = check_cfg(cfg);
+  if (st != DFLASH_OK) return st;
+  if ((st = check_weights(cfg, w, true)) != DFLASH_OK) return st;
+  if (batch < 0 || n_pages < 0 || max_pages < 0 || max_ctx_len < 0) return DFLASH_EINVAL;
+  if (block_size < 1 || block_size > 16) return DFLASH_ECAPACITY;
+  if (n_steps < 1 || n_steps > block_size) return DFLASH_EINVAL;
+  if (!(temperature >= 0.f)) return DFLASH_EINVAL;
+  if (batch == 0) return DFLASH_OK;
+  if (!ctx_len || !out_tokens || !block_table || (!kv_pool && max_ctx_len > 0)) return DFLASH_EINVAL;
+  if (!workspace || ((uintptr_t)workspace & 255)) return DFLASH_EWORKSPACE;
+  const int ctx_cap = std::min<long long>(max_ctx_len, (long long)max_pages * 16);
+  const DraftWS L = draft_layout(cfg, batch, block_size, ctx_cap);
+  if (L.total > ws_bytes) return DFLASH_EWORKSPACE;
+
+  const int bf = cfg->dtype == DFLASH_BF16;
+  const int B = block_size, M = batch * B, S = n_steps;
+  const int H = cfg->hidden, I = cfg->intermediate, d = cfg->head_dim, nq = cfg->n_q_heads, nkv = cfg->n_kv_heads;
+  const int Nqkv = (nq + 2 * nkv) * d;
+  float* h = (float*)at(workspace, L.h);
+  const ActOut u = act_out(cfg, at(workspace, L.u_hi), at(workspace, L.u_lo), H);
+  const ActOut o = act_out(cfg, at(workspace, L.o_hi), at(workspace, L.o_lo), nq * d);
+  const ActOut act = act_out(cfg, at(workspace, L.act_hi), at(workspace, L.act_lo), I);
+  ActOut y;
+  y.p0 = at(workspace, L.y);
+  y.p1 = nullptr;
+  y.ld = H;
+  y.mode = bf ? ACT_BF16 : ACT_F32;
+  float* qkv = (float*)at(workspace, L.qkv);
+  int* row_map = (int*)at(workspace, L.row_map);
+  int* tau = (int*)at(workspace, L.tau);
+  int* committed = (int*)at(workspace, L.committed);
+  int* cand = (int*)at(workspace, L.cand);
+  float* conf = (float*)at(workspace, L.conf);
+  float2* cs = (float2*)at(workspace, L.cs);
+
+  AttnParams ap{};
+  ap.pool = kv_pool;
+  ap.n_pages = n_pages;
+  ap.block_table = block_table;
+  ap.max_pages = max_pages;
+  ap.ctx_len = ctx_len;
+  ap.ctx_cap = ctx_cap;
+  ap.qkv = qkv;
+  ap.cs = cs;
+  ap.batch = batch;
+  ap.B = B;
+  ap.nq = nq;
+  ap.nkv = nkv;
+  ap.d = d;
+  ap.n_layers = cfg->n_layers;
+  ap.scale = 1.0f / sqrtf((float)d);
+  ap.n_splits = L.ns;
+  ap.pps = L.pps;
+  ap.part_o = (float*)at(workspace, L.att_o);
+  ap.part_lse = (float*)at(workspace, L.att_lse);
+
+  HIP_TRY(launch_rope_table_block(ctx_len, ctx_cap, batch, B, d, (double)cfg->rope_base, cs, stream));
+  HIP_TRY(launch_block_init(tau, committed, M, cfg->mask_token_id, stream));
+
+  int done = 0;
+  for (int s = 0; s < S; ++s) {
+    const int k_s = ((s + 1) * B) / S - (s * B) / S;
+    const int n_open = B - done;
+    const int last = s == S - 1;
+    HIP_TRY(launch_embed(tau, w->embed, bf, cfg->vocab, h, M, H, stream));
+    for (int l = 0; l < cfg->n_layers; ++l) {
+      HIP_TRY(launch_rmsnorm(h, w->attn_norm[l], u, M, H, cfg->rms_eps, nullptr, B, 0, nullptr, stream));
+      GemmArgs g{};
+      g.wdtype = bf;
+      g.a = act_in(u);
+      g.b = BRowsArgs{w->w_q[l], (const char*)w->w_kv + (size_t)l * 2 * nkv * d * H * (bf ? 2 : 4), H, nq * d, 1};
+      g.M = M;
+      g.N = Nqkv;
+      g.K = H;
+      g.kind = EPI_STORE;
+      g.e.out = ActOut{qkv, nullptr, Nqkv, ACT_F32};
+      HIP_TRY(gemm(DFLASH_PROF_GEMM_QKV, g, stream));
+
+      ap.layer = l;
+      HIP_TRY(launch_attention(ap, bf, stream, g_prof.cls == DFLASH_PROF_ATTN ? prof_attn : nullptr));
+      HIP_TRY(launch_attn_combine(ap, o, stream));
+
+      GemmArgs go{};
+      go.wdtype = bf;
+      go.a = act_in(o);
+      go.b = BRowsArgs{w->w_o[l], nullptr, nq * d, 0, 0};
+      go.M = M;
+      go.N = H;
+      go.K = nq * d;
+      go.kind = EPI_ADD;
+      go.e.resid = h;
+      go.e.ldr = H;
+      HIP_TRY(gemm(DFLASH_PROF_GEMM_O, go, stream));
+
+      HIP_TRY(launch_rmsnorm(h, w->mlp_norm[l], u, M, H, cfg->rms_eps, nullptr, B, 0, nullptr, stream));
+      GemmArgs gu{};
+      gu.wdtype = bf;
+      gu.a = act_in(u);
+      gu.b = BRowsArgs{w->w_gate[l], w->w_up[l], H, 0, 2};
+      gu.M = M;
+      gu.N = 2 * I;
+      gu.K = H;
+      gu.kind = EPI_SWIGLU;
+      gu.e.out = act;
+      HIP_TRY(gemm(DFLASH_PROF_GEMM_GATEUP, gu, stream));
+
+      GemmArgs gd{};
+      gd.wdtype = bf;
+      gd.a = act_in(act);
+      gd.b = BRowsArgs{w->w_down[l], nullptr, I, 0, 0};
+      gd.M = M;
+      gd.N = H;
+      gd.K = I;
+      gd.kind = EPI_ADD;
+      gd.e.resid = h;
+      gd.e.ldr = H;
+      HIP_TRY(gemm(DFLASH_PROF_GEMM_DOWN, gd, stream));
+    }
+    const int Ms = batch * n_open;
+    HIP_TRY(launch_rmsnorm(h, w->final_norm, y, Ms, H, cfg->rms_eps, committed, B, n_open, row_map, stream));
+    GemmArgs gl{};
+    gl.wdtype = bf;
+    gl.a = ActIn{y.p0, nullptr, H, y.mode};
+    gl.b = BRowsArgs{w->lm_head, nullptr, H, 0, 0};
+    gl.M = Ms;
+    gl.N = cfg->vocab;
+    gl.K = H;
+    gl.kind = EPI_LMHEAD;
+    gl.e.part_f = (float4*)at(workspace, L.part_f);
+    gl.e.part_i = (int*)at(workspace, L.part_i);
+    gl.e.ntiles = L.ntiles;
+    gl.e.row_map = row_map;
+    gl.e.logits = out_logits;
+    gl.e.block = B;
+    gl.e.temperature = temperature;
+    gl.e.seed_lo = (uint32_t)(seed & 0xffffffffu);
+    gl.e.seed_hi = (uint32_t)(seed >> 32);
+    gl.e.step = s;
+    HIP_TRY(gemm(DFLASH_PROF_LMHEAD, gl, stream));
+    HIP_TRY(launch_lm_combine(gl.e.part_f, gl.e.part_i, L.ntiles, Ms, row_map, cand, conf, stream));
+    HIP_TRY(launch_commit(cand, conf, tau, committed, out_conf, out_tokens, batch, B, S, s, k_s, last, stream));
+    done += k_s;
+  }
+  return DFLASH_OK;
+}
+
+size_t dflash_verify_workspace_size(int32_t batch, int32_t block_size, int32_t vocab) {
+  if (batch < 0 || block_size < 1 || block_size > 16 || vocab < 1) return 0;
+  return verify_ws_bytes(batch, block_size, vocab);
+}
+
+dflash_status dflash_verify_block(int32_t batch, int32_t block_size, int32_t vocab, const float* target_logits,
+                                  const int32_t* draft_tokens, float temperature, const float* draft_logits,
+                                  const float* uniforms, int32_t* accept_len, int32_t* out_tokens,
+                                  void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (batch < 0 || vocab < 1) return DFLASH_EINVAL;
+  if (block_size < 1 || block_size > 16) return DFLASH_ECAPACITY;
+  if (!(temperature >= 0.f)) return DFLASH_EINVAL;
+  if (batch == 0) return DFLASH_OK;
+  if (!target_logits || !draft_tokens || !accept_len || !out_tokens) return DFLASH_EINVAL;
+  if (temperature > 0.f && (!draft_logits || !uniforms)) return DFLASH_EINVAL;
+  if (!workspace || ((uintptr_t)workspace & 255)) return DFLASH_EWORKSPACE;
+  if (ws_bytes < verify_ws_bytes(batch, block_size, vocab)) return DFLASH_EWORKSPACE;
+  hipError_t e;
+  prof_mark(DFLASH_PROF_VERIFY, 0, stream);
+  if (temperature > 0.f)
+    e = launch_verify_sampled(batch, block_size, vocab, target_logits, draft_logits, draft_tokens, uniforms,
+                              temperature, accept_len, out_tokens, workspace, stream);
+  else
+    e = launch_verify_greedy(batch, block_size, vocab, target_logits, draft_tokens, accept_len, out_tokens,
+                             workspace, stream);
+  prof_mark(DFLASH_PROF_VERIFY, 1, stream);
+  return e == hipSuccess ? DFLASH_OK : DFLASH_EHIP;
+}
+
+dflash_status dflash_prof_select(int32_t kernel_class) {
+  if (kernel_class < DFLASH_PROF_NONE || kernel_class > DFLASH_PROF_VERIFY) return DFLASH_EINVAL;
+  g_prof.cls = kernel_class;
+  return DFLASH_OK;
+}
+
+dflash_status dflash_prof_collect(float* total_ms, int32_t* n_launches) {
+  if (!total_ms || !n_launches) return DFLASH_EINVAL;
+  double tot = 0.0;
+  for (auto& pr : g_prof.recorded) {
+    if (hipEventSynchronize(pr.second) != hipSuccess) return DFLASH_EHIP;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, pr.first, pr.second) != hipSuccess) return DFLASH_EHIP;
+    tot += ms;
+  }
+  *total_ms = (float)tot;
+  *n_launches = (int32_t)g_prof.recorded.size();
+  g_prof.recorded.clear();
+  g_prof.open = nullptr;
+  g_prof.used = 0;
+  return DFLASH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,219 @@
+// Small kernels of the draft step: rotary tables, block init, embedding
+// gather, RMSNorm (with the gather of still-open rows before the LM head),
+// the LM-head row combine and the denoise commit.
+#include "kernels.h"
+
+namespace dflash {
+
+// Rotary table cs[row][j] = (cos, sin)(pos * base^(-2j/d)) for j < d/2.  The
+// angle reaches ~3e4 rad at long contexts, so it is formed and reduced in
+// double precision; only the final cos/sin are rounded to float.
+__device__ __forceinline__ float2 rope_cs(int pos, int j, int d, double base) {
+  const double w = pow(base, -2.0 * (double)j / (double)d);
+  double sn, c;
+  sincos((double)pos * w, &sn, &c);
+  return make_float2((float)c, (float)sn);
+}
+
+__global__ void rope_block_kernel(const int* ctx_len, int ctx_cap, int batch, int B, int d, double base,
+                                  float2* cs) {
+  const int hd = d / 2;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= batch * B * hd) return;
+  const int row = idx / hd, j = idx - row * hd;
+  const int b = row / B, i = row - b * B;
+  int c = ctx_len[b];
+  c = c < 0 ? 0 : (c > ctx_cap ? ctx_cap : c);
+  cs[idx] = rope_cs(c + i, j, d, base);
+}
+
+__global__ void rope_tokens_kernel(const int* tok_pos, int n, int d, double base, float2* cs) {
+  const int hd = d / 2;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n * hd) return;
+  const int row = idx / hd, j = idx - row * hd;
+  cs[idx] = rope_cs(tok_pos[row], j, d, base);
+}
+
+__global__ void block_init_kernel(int* tau, int* committed, int M, int mask_id) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < M) {
+    tau[i] = mask_id;
+    committed[i] = 0;
+  }
+}
+
+template <typename T>
+__global__ void embed_kernel(const int* tau, const T* embed, int vocab, float* h, int H) {
+  const int row = blockIdx.x;
+  int t = tau[row];
+  t = t < 0 ? 0 : (t >= vocab ? vocab - 1 : t);
+  for (int c = threadIdx.x; c < H; c += blockDim.x) h[(size_t)row * H + c] = ld_f(embed, (size_t)t * H + c);
+}
+
+// One workgroup per output row.  With committed != null the output rows are
+// the still-open positions of each sequence in position order (n_open per
+// sequence) and row_map receives b*B + i for each.
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, const float* gain, ActOut out, int H,
+                                                      float eps, const int* committed, int B, int n_open,
+                                                      int* row_map) {
+  __shared__ double red[4];
+  __shared__ int src_s;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  if (tid == 0) {
+    int src = r;
+    if (committed) {
+      const int b = r / n_open, jj = r - b * n_open;
+      int seen = 0;
+      src = b * B;
+      for (int i = 0; i < B; ++i) {
+        if (!committed[b * B + i]) {
+          if (seen == jj) { src = b * B + i; break; }
+          ++seen;
+        }
+      }
+      row_map[r] = src;
+    }
+    src_s = src;
+  }
+  __syncthreads();
+  const float* x = h + (size_t)src_s * H;
+  double ss = 0.0;
+  for (int c = tid; c < H; c += 256) {
+    const double v = x[c];
+    ss += v * v;
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, kWave);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  const double tot = red[0] + red[1] + red[2] + red[3];
+  const float rs = (float)(1.0 / sqrt(tot / (double)H + (double)eps));
+  for (int c = tid * 4; c < H; c += 1024) {
+    const float4 v = *(const float4*)(x + c);
+    const float4 gg = *(const float4*)(gain + c);
+    act_store4(out, r, c, make_float4(v.x * rs * gg.x, v.y * rs * gg.y, v.z * rs * gg.z, v.w * rs * gg.w));
+  }
+}
+
+// Row combine of the LM-head tile partials, in tile order (one wave per row).
+__global__ __launch_bounds__(64) void lm_combine_kernel(const float4* part_f, const int* part_i, int ntiles,
+                                                        const int* row_map, int* cand, float* conf) {
+  const int r = blockIdx.x, lane = threadIdx.x;
+  float pmax = -INFINITY, zmax = -INFINITY, zsum = 0.f, zc = -INFINITY;
+  int idx = -1;
+  for (int t = lane; t < ntiles; t += 64) {
+    const float4 f = part_f[(size_t)r * ntiles + t];
+    const int ii = part_i[(size_t)r * ntiles + t];
+    if (ii >= 0 && (idx < 0 || f.x > pmax)) { pmax = f.x; idx = ii; zc = f.w; }
+    const float M = fmaxf(zmax, f.y);
+    float s = 0.f;
+    if (zsum > 0.f) s += zsum * expf(zmax - M);
+    if (f.z > 0.f) s += f.z * expf(f.y - M);
+    zmax = M;
+    zsum = s;
+  }
+  // lanes hold strided tile sets; argmax ties resolve to the smallest index
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float qp = __shfl_xor(pmax, o, kWave), qz = __shfl_xor(zmax, o, kWave);
+    const float qs = __shfl_xor(zsum, o, kWave), qc = __shfl_xor(zc, o, kWave);
+    const int qi = __shfl_xor(idx, o, kWave);
+    if (qi >= 0 && (idx < 0 || qp > pmax || (qp == pmax && qi < idx))) { pmax = qp; idx = qi; zc = qc; }
+    const float M = fmaxf(zmax, qz);
+    float s = 0.f;
+    if (zsum > 0.f) s += zsum * expf(zmax - M);
+    if (qs > 0.f) s += qs * expf(qz - M);
+    zmax = M;
+    zsum = s;
+  }
+  if (lane == 0) {
+    const int dst = row_map[r];
+    cand[dst] = idx;
+    conf[dst] = zc - (zmax + logf(zsum));
+  }
+}
+
+// Denoise commit for one sequence (one wave, lane = block position): the
+// k_step most confident open positions (ties to the lower position) take
+// their candidate; at the last step every open position does.
+__global__ __launch_bounds__(64) void commit_kernel(const int* cand, const float* conf, int* tau, int* committed,
+                                                    float* out_conf, int* out_tokens, int B, int S, int step,
+                                                    int k_step, int last) {
+  __shared__ float cs[16];
+  __shared__ int open[16];
+  const int b = blockIdx.x, i = threadIdx.x;
+  const int row = b * B + i;
+  if (i < B) {
+    open[i] = !committed[row];
+    cs[i] = conf[row];
+  }
+  __syncthreads();
+  if (i < B) {
+    if (out_conf) out_conf[((size_t)b * S + step) * B + i] = open[i] ? cs[i] : __int_as_float(0x7fc00000);
+    if (open[i]) {
+      int rank = 0;
+      for (int k = 0; k < B; ++k)
+        if (open[k] && (cs[k] > cs[i] || (cs[k] == cs[i] && k < i))) ++rank;
+      if (last || rank < k_step) {
+        tau[row] = cand[row];
+        committed[row] = 1;
+      }
+    }
+  }
+  __syncthreads();
+  if (last && out_tokens && i < B) out_tokens[row] = tau[row];
+}
+
+hipError_t launch_rope_table_block(const int* ctx_len, int ctx_cap, int batch, int B, int d, double base,
+                                   float2* cs, hipStream_t s) {
+  const int n = batch * B * (d / 2);
+  hipLaunchKernelGGL(rope_block_kernel, dim3((n + 255) / 256), dim3(256), 0, s, ctx_len, ctx_cap, batch, B, d,
+                     base, cs);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_table_tokens(const int* tok_pos, int n, int d, double base, float2* cs, hipStream_t s) {
+  const int t = n * (d / 2);
+  if (t <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_tokens_kernel, dim3((t + 255) / 256), dim3(256), 0, s, tok_pos, n, d, base, cs);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_init(int* tau, int* committed, int M, int mask_id, hipStream_t s) {
+  hipLaunchKernelGGL(block_init_kernel, dim3((M + 255) / 256), dim3(256), 0, s, tau, committed, M, mask_id);
+  return hipGetLastError();
+}
+
+hipError_t launch_embed(const int* tau, const void* embed, int wdtype, int vocab, float* h, int M, int H,
+                        hipStream_t s) {
+  if (wdtype)
+    hipLaunchKernelGGL(embed_kernel<bf16_t>, dim3(M), dim3(256), 0, s, tau, (const bf16_t*)embed, vocab, h, H);
+  else
+    hipLaunchKernelGGL(embed_kernel<float>, dim3(M), dim3(256), 0, s, tau, (const float*)embed, vocab, h, H);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(const float* h, const float* gain, ActOut out, int M, int H, float eps,
+                          const int* committed, int B, int n_open, int* row_map, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(256), 0, s, h, gain, out, H, eps, committed, B, n_open,
+                     row_map);
+  return hipGetLastError();
+}
+
+hipError_t launch_lm_combine(const float4* part_f, const int* part_i, int ntiles, int rows, const int* row_map,
+                             int* cand, float* conf, hipStream_t s) {
+  if (rows <= 0) return hipSuccess;
+  hipLaunchKernelGGL(lm_combine_kernel, dim3(rows), dim3(64), 0, s, part_f, part_i, ntiles, row_map, cand, conf);
+  return hipGetLastError();
+}
+
+hipError_t launch_commit(const int* cand, const float* conf, int* tau, int* committed, float* out_conf,
+                         int* out_tokens, int batch, int B, int S, int step, int k_step, int last, hipStream_t s) {
+  hipLaunchKernelGGL(commit_kernel, dim3(batch), dim3(64), 0, s, cand, conf, tau, committed, out_conf, out_tokens,
+                     B, S, step, k_step, last);
+  return hipGetLastError();
+}
+
+}  // namespace dflash

@@ -1,0 +1,106 @@
+// Internal launch interface between the C-ABI host layer and the kernels.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace dflash {
+
+// GEMM: C[M, N] = A[M, K] * W[N, K]^T, fp32 accumulation, fused epilogue.
+enum EpiKind : int { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2, EPI_LMHEAD = 3, EPI_KVSCATTER = 4 };
+
+// Rows of W.  mode 0: row n of b0.  mode 1: rows [0, split) of b0 then b1.
+// mode 2 (SwiGLU): each tile of BN columns holds BN/2 rows of b0 (gate) then
+// the same BN/2 rows of b1 (up).
+struct BRowsArgs {
+  const void* b0;
+  const void* b1;
+  int ldb;
+  int split;
+  int mode;
+};
+
+struct EpiParams {
+  // EPI_STORE / EPI_SWIGLU: destination
+  ActOut out;
+  // EPI_ADD: resid[row * ldr + col] += value
+  float* resid;
+  int ldr;
+  // EPI_LMHEAD: per (row, column tile) partials, optional logits
+  float4* part_f;        // (pmax, zmax, zsum, zc)
+  int* part_i;           // argmax index
+  int ntiles;
+  const int* row_map;    // compact row -> b*B + i
+  float* logits;         // [bt*B, V] or null
+  int block;             // B
+  float temperature;
+  uint32_t seed_lo, seed_hi;
+  int step;
+  // EPI_KVSCATTER: write K (rotated) / V into the paged pool
+  void* pool;
+  const int* tok_seq;
+  const int* tok_pos;
+  const int* block_table;
+  int n_seqs, max_pages, n_pages;
+  const float2* rope_cs;  // [M, d/2]
+  int n_layers, n_kv, head_dim;
+};
+
+struct GemmArgs {
+  int wdtype;            // 0 f32 weights (A f32), 1 bf16 weights (A hi/lo or bf16)
+  ActIn a;
+  BRowsArgs b;
+  int M, N, K;
+  int kind;
+  EpiParams e;
+};
+
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
+int gemm_bn(int wdtype);       // column tile width (LM-head partial count = ceil(N / bn))
+
+// Attention of the block queries over paged context KV plus in-block keys.
+struct AttnParams {
+  const void* pool;
+  int n_pages;
+  const int* block_table;
+  int max_pages;
+  const int* ctx_len;
+  int ctx_cap;            // clamp of ctx_len
+  const float* qkv;       // [M, (nq + 2 nkv) d] fp32, not yet rotated
+  const float2* cs;       // rope table [M, d/2]
+  int batch, B, nq, nkv, d, n_layers, layer;
+  float scale;
+  int n_splits, pps;      // context splits and pages per split (pps even)
+  float* part_o;          // [(n_splits + 1), M*nq, d]
+  float* part_lse;        // [(n_splits + 1), M*nq]
+};
+hipError_t launch_attention(const AttnParams& p, int wdtype, hipStream_t s, void (*mark)(int, hipStream_t));
+hipError_t launch_attn_combine(const AttnParams& p, ActOut out, hipStream_t s);
+
+// Elementwise and bookkeeping kernels.
+hipError_t launch_rope_table_block(const int* ctx_len, int ctx_cap, int batch, int B, int d,
+                                   double base, float2* cs, hipStream_t s);
+hipError_t launch_rope_table_tokens(const int* tok_pos, int n, int d, double base, float2* cs,
+                                    hipStream_t s);
+hipError_t launch_block_init(int* tau, int* committed, int M, int mask_id, hipStream_t s);
+hipError_t launch_embed(const int* tau, const void* embed, int wdtype, int vocab, float* h, int M,
+                        int H, hipStream_t s);
+hipError_t launch_rmsnorm(const float* h, const float* gain, ActOut out, int M, int H, float eps,
+                          const int* committed, int B, int n_open, int* row_map, hipStream_t s);
+hipError_t launch_lm_combine(const float4* part_f, const int* part_i, int ntiles, int rows,
+                             const int* row_map, int* cand, float* conf, hipStream_t s);
+hipError_t launch_commit(const int* cand, const float* conf, int* tau, int* committed,
+                         float* out_conf, int* out_tokens, int batch, int B, int S, int step,
+                         int k_step, int last, hipStream_t s);
+
+// Verification.
+int verify_chunks(int vocab);
+hipError_t launch_verify_greedy(int batch, int B, int V, const float* zt, const int* draft,
+                                int* accept_len, int* out_tokens, void* ws, hipStream_t s);
+hipError_t launch_verify_sampled(int batch, int B, int V, const float* zt, const float* zd,
+                                 const int* draft, const float* uniforms, float T,
+                                 int* accept_len, int* out_tokens, void* ws, hipStream_t s);
+size_t verify_ws_bytes(int batch, int B, int V);
+
+}  // namespace dflash

@@ -1,0 +1,125 @@
+"""The C-ABI library loads, exports every entry point include/dflash.h declares,
+and rejects invalid arguments on the host before touching the GPU (CPU only:
+every call here returns from argument checks, none launches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_diffusion_drafter_injection_amd import binding as B
+from block_diffusion_drafter_injection_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dflash.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dflash_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(B.LIB_PATH):
+        from block_diffusion_drafter_injection_amd import build
+        build.build()
+    return B.lib()
+
+
+def test_every_declared_symbol_is_exported(L):
+    names = declared_functions()
+    assert len(names) >= 8
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(B.EXPORTS)
+
+
+def test_status_strings(L):
+    for code in range(0, -7, -1):
+        assert B.dflash_status_string(code) != "unknown status"
+
+
+def _cfg(**kw):
+    c = B.make_config(synth.small_dims())
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_workspace_size_rejects_bad_configs(L):
+    assert B.dflash_workspace_size(_cfg(), 4, 8, 64, 512) > 0
+    assert B.dflash_workspace_size(_cfg(head_dim=96), 4, 8, 64, 512) == 0
+    assert B.dflash_workspace_size(_cfg(n_kv_heads=3), 4, 8, 64, 512) == 0
+    assert B.dflash_workspace_size(_cfg(page_size=32), 4, 8, 64, 512) == 0
+    assert B.dflash_workspace_size(_cfg(dtype=7), 4, 8, 64, 512) == 0
+    assert B.dflash_workspace_size(_cfg(), 4, 17, 64, 512) == 0
+    assert B.dflash_workspace_size(_cfg(hidden=500), 4, 8, 64, 512) == 0
+
+
+def test_workspace_grows_with_batch_and_context(L):
+    c = B.make_config(synth.QWEN3_8B_SHAPE)
+    a = B.dflash_workspace_size(c, 1, 16, 0, 4096)
+    b = B.dflash_workspace_size(c, 32, 16, 0, 4096)
+    assert b > a > 0
+    assert B.dflash_workspace_size(c, 32, 16, 8192, 0) >= B.dflash_workspace_size(c, 32, 16, 1024, 0)
+
+
+def _weights_stub(n_layers):
+    arr = (ctypes.c_void_p * n_layers)(*([8] * n_layers))
+    pp = ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p))
+    w = B.dflash_weights(8, 8, 8, 8, 8, pp, pp, pp, pp, pp, pp, pp)
+    return w, arr
+
+
+def _draft(L, cfg, w, **kw):
+    args = dict(pool=8, n_pages=4, table=8, max_pages=4, ctx=8, max_ctx=16, batch=2, B=8, S=2, T=0.0,
+                tok=8, ws=256, ws_bytes=1 << 40)
+    args.update(kw)
+    return L.dflash_draft_block(ctypes.byref(cfg), ctypes.byref(w), args["pool"], args["n_pages"], args["table"],
+                                args["max_pages"], args["ctx"], args["max_ctx"], args["batch"], args["B"],
+                                args["S"], args["T"], 0, args["tok"], None, None, args["ws"], args["ws_bytes"],
+                                None)
+
+
+def test_draft_argument_errors_return_before_launch(L):
+    cfg = _cfg()
+    w, keep = _weights_stub(cfg.n_layers)
+    assert _draft(L, cfg, w, B=17) == -4
+    assert _draft(L, cfg, w, B=0) == -4
+    assert _draft(L, cfg, w, S=9) == -1
+    assert _draft(L, cfg, w, S=0) == -1
+    assert _draft(L, cfg, w, T=-1.0) == -1
+    assert _draft(L, cfg, w, T=float("nan")) == -1
+    assert _draft(L, cfg, w, tok=None) == -1
+    assert _draft(L, cfg, w, ws=None) == -5
+    assert _draft(L, cfg, w, ws=300) == -5                      # not 256-byte aligned
+    assert _draft(L, cfg, w, ws_bytes=1024) == -5               # too small
+    assert _draft(L, _cfg(dtype=5), w) == -3
+    assert _draft(L, _cfg(mask_token_id=-1), w) == -1
+    assert _draft(L, cfg, w, batch=0) == 0                      # nothing to do
+    w2, keep2 = _weights_stub(cfg.n_layers)
+    keep2[1] = None
+    assert _draft(L, cfg, w2) == -1                             # a missing per-layer weight
+
+
+def test_verify_and_inject_argument_errors(L):
+    f = L.dflash_verify_block
+    assert f(2, 17, 100, 8, 8, 0.0, None, None, 8, 8, 256, 1 << 30, None) == -4
+    assert f(2, 8, 100, 8, 8, 1.0, None, None, 8, 8, 256, 1 << 30, None) == -1   # T > 0 needs draft logits
+    assert f(2, 8, 100, None, 8, 0.0, None, None, 8, 8, 256, 1 << 30, None) == -1
+    assert f(2, 8, 100, 8, 8, 0.0, None, None, 8, 8, 256, 8, None) == -5
+    assert f(0, 8, 100, None, None, 0.0, None, None, None, None, None, 0, None) == 0
+    cfg = _cfg()
+    w, keep = _weights_stub(cfg.n_layers)
+    g = L.dflash_inject_kv
+    assert g(ctypes.byref(cfg), ctypes.byref(w), 8, 8, 8, -1, 8, 4, 8, 1, 4, 256, 1 << 30, None) == -1
+    assert g(ctypes.byref(cfg), ctypes.byref(w), 8, 8, 8, 0, 8, 4, 8, 1, 4, 256, 1 << 30, None) == 0
+    assert g(ctypes.byref(cfg), ctypes.byref(w), None, 8, 8, 5, 8, 4, 8, 1, 4, 256, 1 << 30, None) == -1
+    assert g(ctypes.byref(cfg), ctypes.byref(w), 8, 8, 8, 5, 8, 4, 8, 1, 4, 256, 16, None) == -5
+
+
+def test_profiler_select_validates_class(L):
+    assert L.dflash_prof_select(99) == -1
+    assert L.dflash_prof_select(0) == 0
