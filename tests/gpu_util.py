@@ -101,21 +101,34 @@ def bf16_ulp(x):
     return np.ldexp(1.0, (e - 7).astype(np.int64))
 
 
-def compare_pool_entries(got, ref, dtype):
-    """bf16: equal, or one ulp apart in at most 1% of entries.  fp32: 1e-5 of the max."""
+def compare_pool_entries(got, ref, dtype, label=""):
+    """Pool entries against the oracle's.
+
+    bf16: equal, except where the fp32 value before storage lay within the
+    GPU's accumulation error of a rounding boundary; those entries may differ
+    by one bf16 ulp, or, for entries near zero (where one ulp is smaller than
+    that error), by at most 2^-14 of the tensor's largest magnitude.  At most
+    1% of entries may differ.  fp32: |diff| <= 1e-5 of the largest magnitude.
+    """
     got, ref = np.asarray(got), np.asarray(ref)
     assert got.shape == ref.shape
-    assert np.all(np.isfinite(got))
+    assert np.all(np.isfinite(got)), f"{label}: non-finite pool entries"
+    scale = max(float(np.max(np.abs(ref))), 1e-30)
     if dtype == "bf16":
         diff = got != ref
-        frac = diff.mean()
+        frac = float(diff.mean())
+        worst_abs = float(np.max(np.abs(got - ref))) / scale
+        print(f"  pool {label}: {frac:.4%} entries differ, max |diff| = {worst_abs:.2e} of max |ref|")
         if diff.any():
+            d = np.abs(got[diff] - ref[diff])
             ulp = bf16_ulp(np.maximum(np.abs(got[diff]), np.abs(ref[diff])))
-            assert np.all(np.abs(got[diff] - ref[diff]) <= ulp * 1.0000001), "pool entry off by more than 1 ulp"
-        assert frac <= 0.01, f"{frac:.4%} of pool entries differ"
+            ok = (d <= ulp * 1.0000001) | (d <= scale * 2.0 ** -14)
+            assert np.all(ok), f"{label}: {int((~ok).sum())} entries beyond one ulp / near-zero floor"
+        assert frac <= 0.01, f"{label}: {frac:.4%} of pool entries differ"
         return frac
-    err = np.max(np.abs(got - ref)) / max(np.max(np.abs(ref)), 1e-30)
-    assert err <= 1e-5, f"pool rel err {err}"
+    err = float(np.max(np.abs(got - ref))) / scale
+    print(f"  pool {label}: max |diff| = {err:.2e} of max |ref|")
+    assert err <= 1e-5, f"{label}: pool rel err {err}"
     return err
 
 

@@ -46,8 +46,8 @@ def test_inject_matches_oracle(name, ctx, chunk):
             continue
         Ko, Vo = oracle.inject(dims, Wn, x[off:off + c], np.arange(c))
         K, V = unpack_pool(dims, pool, n_pages, table, b, c)
-        compare_pool_entries(K, Ko, dims.dtype)
-        compare_pool_entries(V, Vo, dims.dtype)
+        compare_pool_entries(K, Ko, dims.dtype, f"K b={b}")
+        compare_pool_entries(V, Vo, dims.dtype, f"V b={b}")
         off += c
 
 
