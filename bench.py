@@ -1,0 +1,285 @@
+"""Benchmark of the block-diffusion drafter step on one MI355X.
+
+One step = the whole hot path over one batch: inject the a+1 newly accepted
+tokens of every sequence into the paged KV pool, draft a block (two denoise
+forwards), verify it greedily against target logits.  Inputs are seeded
+synthetic tensors resident in HBM; the target logits of each step are made
+from a pre-drawn N(0,1) base by forcing each block position to agree with
+the draft token with the workload's match probability (this stands in for
+the target model, which is outside the path, and is excluded from the timed
+intervals by HIP events).
+
+Prints one JSON line (see --help for options).
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16 = 2.5e15      # dense bf16 MFMA, FLOP/s
+PEAK_FP32 = 157.3e12
+PEAK_HBM = 8.0e12       # B/s
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="qwen3_8b_shape_b16_bs32")
+    ap.add_argument("--roofline-kernel", default="auto",
+                    help="kernel class timed for the roofline object (auto: the one with the largest time)")
+    ap.add_argument("--cpu-baseline", type=int, default=1, help="time the fp64 oracle on a bounded sample")
+    ap.add_argument("--seed", type=int, default=0)
+    return ap.parse_args()
+
+
+def work_per_class(dims, bt, B, S, ctx, n_new):
+    """Algorithmic work of each kernel class over one step: dict cls -> (amount, unit, bound, launches).
+
+    GEMMs: 2*M*N*K flops (the second MFMA of a hi/lo operand is not counted).
+    Attention: K and V bytes of every context token read once per layer per forward.
+    """
+    H, L, I, V = dims.hidden, dims.n_layers, dims.intermediate, dims.vocab
+    nq, nkv, d = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    M = bt * B
+    el = 2 if dims.dtype == "bf16" else 4
+    out = {}
+    out["gemm_qkv"] = (2.0 * M * (nq + 2 * nkv) * d * H * L * S, "flop", L * S)
+    out["gemm_o"] = (2.0 * M * H * nq * d * L * S, "flop", L * S)
+    out["gemm_gateup"] = (2.0 * M * 2 * I * H * L * S, "flop", L * S)
+    out["gemm_down"] = (2.0 * M * H * I * L * S, "flop", L * S)
+    opens, done = [], 0
+    for s in range(S):
+        opens.append(B - done)
+        done += (s + 1) * B // S - s * B // S
+    out["lmhead"] = (sum(2.0 * bt * o * V * H for o in opens), "flop", S)
+    out["attn"] = (float(sum(ctx)) * nkv * d * 2 * el * L * S, "byte", L * S)
+    out["inject_fc"] = (2.0 * n_new * H * dims.n_fuse * dims.target_hidden, "flop", 1)
+    out["inject_kv"] = (2.0 * n_new * L * 2 * nkv * d * H, "flop", 1)
+    out["verify"] = (float(bt) * (B + 1) * V * 4, "byte", 1)
+    return out
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; multi-GPU runs are not part of it "
+                                   "(the draft step shards by sequence with no exchange)", "n_gpus": a.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from block_diffusion_drafter_injection_amd import binding as Bn
+    from block_diffusion_drafter_injection_amd import synth
+
+    wl = synth.WORKLOADS[a.workload]
+    dims = wl.dims
+    bt, B, S = wl.batch, wl.block_size, wl.n_steps
+    dev = "cuda"
+    torch.manual_seed(a.seed)
+    t_setup = time.time()
+    W = synth.make_weights(dims, wl.seed, dev)
+    cfg, w = Bn.make_config(dims), Bn.Weights(W)
+    ctx0 = synth.context_lengths(wl).numpy().astype(np.int64)
+    grow = (a.steps + a.warmup + 12) * (B + 1)
+    max_ctx = int(ctx0.max()) + grow
+    pages_per = (max_ctx + 15) // 16
+    n_pages = bt * pages_per
+    table = torch.arange(n_pages, dtype=torch.int32, device=dev).view(bt, pages_per)
+    pool = torch.zeros(Bn.pool_elems(dims, n_pages), dtype=dims.torch_dtype, device=dev)
+    max_inject = 8192
+    ws_bytes = Bn.dflash_workspace_size(cfg, bt, B, max_inject, max_ctx)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    vws_bytes = Bn.dflash_verify_workspace_size(bt, B, dims.vocab)
+    vws = torch.empty(vws_bytes, dtype=torch.uint8, device=dev)
+
+    # one-shot injection of the initial contexts (setup, untimed)
+    for b in range(bt):
+        c = int(ctx0[b])
+        hid = synth.make_hiddens(dims, c, wl.seed * 1000 + b, dev)
+        seq = torch.full((c,), b, dtype=torch.int32, device=dev)
+        pos = torch.arange(c, dtype=torch.int32, device=dev)
+        Bn.dflash_inject_kv(cfg, w, hid, seq, pos, c, pool, n_pages, table, bt, pages_per, ws, ws_bytes)
+        del hid
+    torch.cuda.synchronize()
+
+    new_hid = synth.make_hiddens(dims, bt * (B + 1), wl.seed + 77, dev)
+    g = torch.Generator(device=dev).manual_seed(3000 + wl.seed)
+    z0 = torch.randn(bt, B + 1, dims.vocab, generator=g, device=dev, dtype=torch.float32)
+    zmax = z0[:, :B].amax(-1) + 1.0
+    zmin = z0[:, :B].amin(-1) - 1.0
+    ctx = ctx0.copy()
+    ctx_dev = torch.tensor(ctx, dtype=torch.int32, device=dev)
+    tok = torch.empty(bt, B, dtype=torch.int32, device=dev)
+    acc = torch.empty(bt, dtype=torch.int32, device=dev)
+    outt = torch.empty(bt, B + 1, dtype=torch.int32, device=dev)
+    pin_seq = torch.empty(bt * (B + 1), dtype=torch.int32, pin_memory=True)
+    pin_pos = torch.empty(bt * (B + 1), dtype=torch.int32, pin_memory=True)
+    dev_seq = torch.empty(bt * (B + 1), dtype=torch.int32, device=dev)
+    dev_pos = torch.empty(bt * (B + 1), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    last_acc = np.zeros(bt, dtype=np.int64)     # before the first step nothing is pending
+    first = True
+    setup_s = time.time() - t_setup
+
+    def step(ev):
+        nonlocal first, ctx
+        # tokens accepted by the previous step: a+1 per sequence at positions ctx .. ctx+a
+        if first:
+            n_new = 0
+        else:
+            seqs = np.concatenate([np.full(int(x) + 1, b) for b, x in enumerate(last_acc)])
+            poss = np.concatenate([np.arange(ctx[b], ctx[b] + int(x) + 1) for b, x in enumerate(last_acc)])
+            n_new = len(seqs)
+            pin_seq[:n_new] = torch.from_numpy(seqs.astype(np.int32))
+            pin_pos[:n_new] = torch.from_numpy(poss.astype(np.int32))
+            dev_seq[:n_new].copy_(pin_seq[:n_new], non_blocking=True)
+            dev_pos[:n_new].copy_(pin_pos[:n_new], non_blocking=True)
+            ctx = ctx + last_acc + 1
+            ctx_dev.copy_(torch.from_numpy(ctx.astype(np.int32)), non_blocking=True)
+        ev[0].record(stream)
+        if n_new:
+            Bn.dflash_inject_kv(cfg, w, new_hid, dev_seq, dev_pos, n_new, pool, n_pages, table, bt, pages_per, ws,
+                                ws_bytes)
+        Bn.dflash_draft_block(cfg, w, pool, n_pages, table, pages_per, ctx_dev, max_ctx, bt, B, S, 0.0, 0, tok,
+                              None, None, ws, ws_bytes)
+        ev[1].record(stream)
+        # target logits for this block (stand-in for the target model; not timed)
+        coin = torch.rand(bt, B, generator=g, device=dev) < wl.p_match
+        val = torch.where(coin, zmax, zmin)
+        idx = tok.long().unsqueeze(-1)
+        keep = z0[:, :B].gather(-1, idx)
+        z0[:, :B].scatter_(-1, idx, val.unsqueeze(-1))
+        ev[2].record(stream)
+        Bn.dflash_verify_block(bt, B, dims.vocab, z0, tok, 0.0, None, None, acc, outt, vws, vws_bytes)
+        ev[3].record(stream)
+        z0[:, :B].scatter_(-1, idx, keep)
+        first = False
+        return n_new
+
+    def run(n, sel=None):
+        nonlocal last_acc
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(n)]
+        dl = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        accs, news = [], []
+        for i in range(n):
+            news.append(step(evs[i]))
+            a_np = acc.cpu().numpy().astype(np.int64)      # the scheduler needs the acceptance
+            last_acc = a_np
+            accs.append(a_np)
+        torch.cuda.synchronize()
+        hot = [evs[i][0].elapsed_time(evs[i][1]) + evs[i][2].elapsed_time(evs[i][3]) for i in range(n)]
+        return hot, accs, news
+
+    # warmup
+    run(a.warmup)
+    # pick the roofline kernel
+    cls = a.roofline_kernel
+    if cls == "auto":
+        best, cls = -1.0, "attn"
+        for c in ["attn", "gemm_gateup", "lmhead", "gemm_down", "gemm_qkv", "gemm_o"]:
+            Bn.dflash_prof_select(c)
+            run(1)
+            ms, n = Bn.dflash_prof_collect()
+            if ms > best:
+                best, cls = ms, c
+        Bn.dflash_prof_select("none")
+
+    # draft-only latency (separate, a few calls on the current state)
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    d0.record(stream)
+    nd = 5
+    for _ in range(nd):
+        Bn.dflash_draft_block(cfg, w, pool, n_pages, table, pages_per, ctx_dev, max_ctx, bt, B, S, 0.0, 0, tok, None,
+                              None, ws, ws_bytes)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    draft_ms = d0.elapsed_time(d1) / nd
+
+    # timed region
+    Bn.dflash_prof_select(cls)
+    ctx_before = ctx.copy()
+    torch.cuda.synchronize()
+    t0 = time.time()
+    hot, accs, news = run(a.steps)
+    torch.cuda.synchronize()
+    wall = time.time() - t0
+    kms, kn = Bn.dflash_prof_collect()
+    Bn.dflash_prof_select("none")
+
+    ms_step = float(np.mean(hot))
+    accepted = float(np.mean([np.sum(x + 1) for x in accs]))
+    value = accepted / (ms_step / 1e3)
+    n_new_mean = float(np.mean(news))
+    work = work_per_class(dims, bt, B, S, (ctx_before + ctx) / 2.0, n_new_mean)
+    amount, unit, launches_per_step = work[cls]
+    bound = "hbm" if unit == "byte" else "mfma"
+    peak = PEAK_HBM if unit == "byte" else (PEAK_BF16 if dims.dtype == "bf16" else PEAK_FP32)
+    achieved = amount * a.steps / (kms / 1e3) if kms > 0 else 0.0
+    roof = {"kernel": cls, "bound": bound,
+            "achieved": round(achieved / (1e9 if unit == "byte" else 1e12), 2),
+            "peak": round(peak / (1e9 if unit == "byte" else 1e12), 1),
+            "unit": "GB/s" if unit == "byte" else "TFLOP/s",
+            "frac": round(achieved / peak, 4), "traffic": None,
+            "launches": kn, "avg_launch_us": round(kms * 1e3 / max(kn, 1), 2)}
+
+    res = {
+        "metric": "accepted tok/s of the drafter step (inject a+1, 2-step block draft, greedy verify)",
+        "value": round(value, 1), "unit": "tok/s", "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if dims.dtype == "bf16" else "f32", "data": "synthetic (seeded random-init weights, "
+        "N(0,1) target hiddens, forced-match target logits)",
+        "config": {"workload": wl.name, "batch": bt, "block": B, "denoise_steps": S, "hidden": dims.hidden,
+                   "layers": dims.n_layers, "vocab": dims.vocab, "ctx_start": int(ctx0.mean()),
+                   "p_match": wl.p_match},
+        "draft_ms": round(draft_ms, 4),
+        "drafted_tok_s": round(bt * B / (draft_ms / 1e3), 1),
+        "mean_accept_plus_bonus": round(accepted / bt, 3),
+        "wall_ms_per_step": round(wall * 1e3 / a.steps, 3),
+        "roofline": roof,
+    }
+    if a.cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(dims, W, wl, B, S, int(ctx_before[0]))
+    res["setup_s"] = round(setup_s, 1)
+    print(json.dumps(res))
+
+
+def cpu_baseline(dims, W, wl, B, S, ctx):
+    """The fp64 oracle, as it stands, on one sequence of the workload: inject 4
+    new tokens, draft one block, verify it.  Throughput = accepted tokens / time."""
+    import numpy as np
+    import torch
+    import oracle
+    from block_diffusion_drafter_injection_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    Wn = {k: ([t.float().cpu().numpy() for t in v] if isinstance(v, list) else v.float().cpu().numpy())
+          for k, v in W.items()}
+    K, V = synth.make_pool_values(dims, ctx, 99, "cpu")
+    K, V = K.double().numpy(), V.double().numpy()
+    x = synth.make_hiddens(dims, 4, 98, "cpu").double().numpy()
+    t0 = time.time()
+    Kn, Vn = oracle.inject(dims, Wn, x, np.arange(ctx, ctx + 4))
+    K = np.concatenate([K, Kn], axis=1)
+    V = np.concatenate([V, Vn], axis=1)
+    r = oracle.draft_block(dims, Wn, [(K, V)], [ctx + 4], B, S, want_logits=False)
+    tok = torch.from_numpy(r["tokens"].astype(np.int32))
+    zt = synth.make_greedy_target_logits(tok, dims.vocab, wl.p_match, seed=5).numpy()
+    acc, _ = oracle.verify_greedy(zt, r["tokens"])
+    dt = time.time() - t0
+    return {"value": round(float(acc[0] + 1) / dt, 4), "unit": "tok/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"1 of {wl.batch} sequences, one step (inject 4 tokens, {S}-step block-{B} draft at "
+                      f"ctx {ctx}, greedy verify), {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -11,7 +11,7 @@ import os
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libdflash.so")
+LIB_PATH = os.environ.get("DFLASH_LIB") or os.path.join(_PKG, "libdflash.so")
 
 DFLASH_F32, DFLASH_BF16 = 0, 1
 PROF = dict(none=0, attn=1, gemm_qkv=2, gemm_o=3, gemm_gateup=4, gemm_down=5, lmhead=6, inject_fc=7,

@@ -32,14 +32,14 @@ def compile_flags():
             "-Wno-unused-result"]
 
 
-def build(jobs=5, verbose=False):
+def build(jobs=5, verbose=False, defines=(), out=None, objdir=None):
     cc = hipcc()
-    objdir = os.path.join(PKG, "_build")
+    objdir = objdir or os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
 
     def one(src):
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *compile_flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *compile_flags(), *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr[-6000:]}")
@@ -51,13 +51,14 @@ def build(jobs=5, verbose=False):
 
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         objs = list(ex.map(one, SOURCES))
-    tmp = LIB + ".tmp"
+    lib = out or LIB
+    tmp = lib + ".tmp"
     cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr[-6000:]}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -106,7 +106,8 @@ void attn_split(int bt, int nkv, int nqg, int ctx_cap, int& ns, int& pps) {
   const int pairs = std::max(1, bt * nkv * nqg);
   const int want = (2048 + pairs - 1) / pairs;
   const int max_ns = (pages + 1) / 2;
-  ns = std::max(1, std::min(want, max_ns));
+  const int min_ns = (pages + 511) / 512;   // the context kernel stages at most 512 page ids
+  ns = std::max(min_ns, std::max(1, std::min(want, max_ns)));
   pps = (pages + ns - 1) / ns;
   pps = (pps + 1) & ~1;
   ns = (pages + pps - 1) / pps;
@@ -116,7 +117,7 @@ int n_qgroups(const dflash_config* c, int B) { return ((c->n_q_heads / c->n_kv_h
 
 struct DraftWS {
   size_t h, u_hi, u_lo, qkv, o_hi, o_lo, act_hi, act_lo, y, row_map, part_f, part_i, att_o, att_lse, cs, tau,
-      committed, cand, conf, total;
+      committed, cand, conf, gemm_part, total;
   int ns, pps, ntiles;
 };
 
@@ -147,13 +148,35 @@ DraftWS draft_layout(const dflash_config* c, int bt, int B, int ctx_cap) {
   w.committed = k.take(M * 4);
   w.cand = k.take(M * 4);
   w.conf = k.take(M * 4);
+  {
+    const int wd = c->dtype == DFLASH_BF16;
+    const int am = wd ? ACT_HILO : ACT_F32;
+    const int Mi = (int)M, Hi = (int)H, Ii = (int)I, Nq = (int)(nq * d), Nqkv = (int)((nq + 2 * nkv) * d);
+    size_t pb = 0;
+    pb = std::max(pb, gemm_partial_bytes(gemm_plan(wd, am, Mi, Nqkv, Hi, EPI_STORE, false), Mi, Nqkv));
+    pb = std::max(pb, gemm_partial_bytes(gemm_plan(wd, am, Mi, Hi, Nq, EPI_ADD, false), Mi, Hi));
+    pb = std::max(pb, gemm_partial_bytes(gemm_plan(wd, am, Mi, 2 * Ii, Hi, EPI_SWIGLU, false), Mi, 2 * Ii));
+    pb = std::max(pb, gemm_partial_bytes(gemm_plan(wd, am, Mi, Hi, Ii, EPI_ADD, false), Mi, Hi));
+    w.gemm_part = k.take(pb);
+  }
   w.total = k.off;
   return w;
 }
 
 struct InjectWS {
-  size_t f_hi, f_lo, cs, total;
+  size_t f_hi, f_lo, cs, gemm_part, total;
 };
+
+// Split-K partial bytes per injected token (the fc and KV GEMMs run one after
+// the other and share the region).
+size_t inject_part_per_token(const dflash_config* c) {
+  const int wd = c->dtype == DFLASH_BF16;
+  const int H = c->hidden, FH = c->n_fuse * c->target_hidden;
+  const int Nkv = c->n_layers * 2 * c->n_kv_heads * c->head_dim;
+  const GemmPlan pf = gemm_plan(wd, wd ? ACT_BF16 : ACT_F32, 1, H, FH, EPI_STORE, true);
+  const GemmPlan pk = gemm_plan(wd, wd ? ACT_HILO : ACT_F32, 1, Nkv, H, EPI_KVSCATTER, true);
+  return std::max(gemm_partial_bytes(pf, 1, H), gemm_partial_bytes(pk, 1, Nkv));
+}
 
 InjectWS inject_layout(const dflash_config* c, int chunk) {
   InjectWS w{};
@@ -162,6 +185,7 @@ InjectWS inject_layout(const dflash_config* c, int chunk) {
   w.f_hi = k.take((size_t)chunk * c->hidden * el);
   w.f_lo = k.take((size_t)chunk * c->hidden * el);
   w.cs = k.take((size_t)chunk * (c->head_dim / 2) * 8);
+  w.gemm_part = k.take((size_t)chunk * inject_part_per_token(c));
   w.total = k.off;
   return w;
 }
@@ -169,7 +193,7 @@ InjectWS inject_layout(const dflash_config* c, int chunk) {
 // Injection chunk the workspace holds (rows of one fused-feature pass).
 int inject_chunk_capacity(const dflash_config* c, size_t ws_bytes) {
   const size_t el = c->dtype == DFLASH_BF16 ? 2 : 4;
-  const size_t per = 2 * c->hidden * el + (c->head_dim / 2) * 8;
+  const size_t per = 2 * c->hidden * el + (c->head_dim / 2) * 8 + inject_part_per_token(c);
   size_t n = ws_bytes / (per + 1);
   while (n > 0 && inject_layout(c, (int)std::min<size_t>(n, 1 << 30)).total > ws_bytes) n -= std::max<size_t>(1, n / 64);
   return (int)std::min<size_t>(n, 1 << 30);
@@ -250,6 +274,8 @@ dflash_status dflash_inject_kv(const dflash_config* cfg, const dflash_weights* w
     g.N = H;
     g.K = FH;
     g.kind = EPI_STORE;
+    g.fixed_split = true;
+    g.part = (float*)at(workspace, L.gemm_part);
     const ActOut f = act_out(cfg, at(workspace, L.f_hi), at(workspace, L.f_lo), H);
     g.e.out = f;
     HIP_TRY(gemm(DFLASH_PROF_INJECT_FC, g, stream));
@@ -262,6 +288,8 @@ dflash_status dflash_inject_kv(const dflash_config* cfg, const dflash_weights* w
     k.N = cfg->n_layers * 2 * nkv * d;
     k.K = H;
     k.kind = EPI_KVSCATTER;
+    k.fixed_split = true;
+    k.part = (float*)at(workspace, L.gemm_part);
     k.e.pool = kv_pool;
     k.e.tok_seq = tok_seq + t0;
     k.e.tok_pos = tok_pos + t0;
@@ -318,6 +346,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
   int* cand = (int*)at(workspace, L.cand);
   float* conf = (float*)at(workspace, L.conf);
   float2* cs = (float2*)at(workspace, L.cs);
+  float* gpart = (float*)at(workspace, L.gemm_part);
 
   AttnParams ap{};
   ap.pool = kv_pool;
@@ -357,6 +386,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
       g.b = BRowsArgs{w->w_q[l], (const char*)w->w_kv + (size_t)l * 2 * nkv * d * H * (bf ? 2 : 4), H, nq * d, 1};
       g.M = M;
       g.N = Nqkv;
+      g.part = gpart;
       g.K = H;
       g.kind = EPI_STORE;
       g.e.out = ActOut{qkv, nullptr, Nqkv, ACT_F32};
@@ -372,6 +402,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
       go.b = BRowsArgs{w->w_o[l], nullptr, nq * d, 0, 0};
       go.M = M;
       go.N = H;
+      go.part = gpart;
       go.K = nq * d;
       go.kind = EPI_ADD;
       go.e.resid = h;
@@ -385,6 +416,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
       gu.b = BRowsArgs{w->w_gate[l], w->w_up[l], H, 0, 2};
       gu.M = M;
       gu.N = 2 * I;
+      gu.part = gpart;
       gu.K = H;
       gu.kind = EPI_SWIGLU;
       gu.e.out = act;
@@ -396,6 +428,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
       gd.b = BRowsArgs{w->w_down[l], nullptr, I, 0, 0};
       gd.M = M;
       gd.N = H;
+      gd.part = gpart;
       gd.K = I;
       gd.kind = EPI_ADD;
       gd.e.resid = h;

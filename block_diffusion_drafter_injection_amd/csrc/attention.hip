@@ -36,22 +36,31 @@ __device__ __forceinline__ float rope_elem(const float* v, const float2* cs, int
 }
 
 // ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
+constexpr int kMaxPPS = 512;   // pages per context split (bounded by the host)
+
+template <int D, int NW>
+__global__ __launch_bounds__(NW * 64) void attn_ctx_mfma_kernel(AttnParams p) {
+  constexpr int NT = NW * 64;
   constexpr int KK = D / 32;         // 32-wide k-steps of QK^T
   constexpr int NN = D / 16;         // 16-row tiles of O^T
   constexpr int LDK = D + 8, LDV = 32 + 8;
+  constexpr int KPC = 32 * D / 8;    // 16-byte pieces of a 32-token K tile
+  constexpr int VPC = 4 * D;         // 16-byte pieces of the two V pages
+  constexpr int KP = (KPC + NT - 1) / NT, VP = (VPC + NT - 1) / NT;
   __shared__ __attribute__((aligned(16))) bf16_t Ks[32 * LDK];
   __shared__ __attribute__((aligned(16))) bf16_t Vt[D * LDV];
+  __shared__ int ptab[kMaxPPS];
 
   const int g = p.nq / p.nkv, R = g * p.B;
   const int nqg = (R + 63) / 64;
   const int split = blockIdx.x / nqg, qg = blockIdx.x - split * nqg;
   const int m = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6, nthr = blockDim.x;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int ctx = clamp_ctx(p, b);
   const int npages = (ctx + 15) >> 4;
   const int pg0 = split * p.pps, pg1 = min(pg0 + p.pps, npages);
+
+  for (int i = tid; i < pg1 - pg0; i += NT) ptab[i] = phys_page(p, b, pg0 + i);
 
   const int r = qg * 64 + wid * 16 + (lane & 15);
   const bool rvalid = r < R;
@@ -72,7 +81,7 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
         const float x = rvalid ? rope_elem(qv, cs, dd, D) : 0.f;
         split_hilo(x, hv[e], lv[e]);
       }
-      uint4 hu, lu;
+      u32x4 hu, lu;
       hu.x = hv[0] | ((uint32_t)hv[1] << 16); hu.y = hv[2] | ((uint32_t)hv[3] << 16);
       hu.z = hv[4] | ((uint32_t)hv[5] << 16); hu.w = hv[6] | ((uint32_t)hv[7] << 16);
       lu.x = lv[0] | ((uint32_t)lv[1] << 16); lu.y = lv[2] | ((uint32_t)lv[3] << 16);
@@ -81,6 +90,7 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
       ql[kk] = as_bf16x8(lu);
     }
   }
+  __syncthreads();   // ptab ready
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 ot[NN];
@@ -88,47 +98,67 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
   for (int nn = 0; nn < NN; ++nn) ot[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const size_t chunk = 16 * D;
-  const bf16_t* pool = (const bf16_t*)p.pool;
-  const uint4 z4 = make_uint4(0, 0, 0, 0);
+  const size_t kv_stride = (size_t)p.nkv * chunk;                   // K region -> V region of one layer
+  const size_t page_stride = (size_t)p.n_layers * 2 * kv_stride;
+  const bf16_t* base = (const bf16_t*)p.pool + (size_t)p.layer * 2 * kv_stride + (size_t)m * chunk;
+  u32x4 rk[KP], rv[VP];
+  const u32x4 z4 = {0u, 0u, 0u, 0u};
 
+  // Global -> registers for the 32-token tile starting at page pg (two pages).
+#define DFLASH_ATT_LOAD(pg)                                                                    \
+  do {                                                                                         \
+    _Pragma("unroll") for (int q = 0; q < KP; ++q) {                                           \
+      const int c = tid + q * NT;                                                              \
+      const int tok = c / (D / 8), part = c - tok * (D / 8);                                   \
+      const int pp = (pg) + (tok >> 4), slot = tok & 15;                                       \
+      u32x4 v = z4;                                                                            \
+      if (c < KPC && pp < pg1 && pp * 16 + slot < ctx) {                                       \
+        const int ph = ptab[pp - pg0];                                                         \
+        if (ph >= 0) v = *(const u32x4*)(base + (size_t)ph * page_stride + slot * D + part * 8); \
+      }                                                                                        \
+      rk[q] = v;                                                                               \
+    }                                                                                          \
+    _Pragma("unroll") for (int q = 0; q < VP; ++q) {                                           \
+      const int c = tid + q * NT;                                                              \
+      const int t = c / (2 * D), rem = c - t * 2 * D, dd = rem >> 1, half = rem & 1;           \
+      const int pp = (pg) + t;                                                                 \
+      u32x4 v = z4;                                                                            \
+      if (c < VPC && pp < pg1) {                                                               \
+        const int ph = ptab[pp - pg0];                                                         \
+        if (ph >= 0) {                                                                         \
+          v = *(const u32x4*)(base + kv_stride + (size_t)ph * page_stride + dd * 16 + half * 8); \
+          const int valid = ctx - (pp * 16 + half * 8);                                        \
+          if (valid < 8) {                                                                     \
+            _Pragma("unroll") for (int e = 0; e < 8; ++e)                                      \
+              if (e >= valid) v[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;                \
+          }                                                                                    \
+        }                                                                                      \
+      }                                                                                        \
+      rv[q] = v;                                                                               \
+    }                                                                                          \
+  } while (0)
+
+  if (pg0 < pg1) DFLASH_ATT_LOAD(pg0);
   for (int pg = pg0; pg < pg1; pg += 2) {
-    __syncthreads();
-    // K: 32 tokens x D, 16-byte pieces
-    for (int c = tid; c < 32 * D / 8; c += nthr) {
-      const int tok = c / (D / 8), part = c - tok * (D / 8);
-      const int pp = pg + (tok >> 4), slot = tok & 15;
-      uint4 v = z4;
-      if (pp < pg1 && pp * 16 + slot < ctx) {
-        const int ph = phys_page(p, b, pp);
-        if (ph >= 0)
-          v = *(const uint4*)(pool + (((size_t)ph * p.n_layers + p.layer) * 2 * p.nkv + m) * chunk +
-                              slot * D + part * 8);
-      }
-      *(uint4*)(Ks + tok * LDK + part * 8) = v;
-    }
-    // V: per page D rows of 16 slots, 8 slots per piece
-    for (int c = tid; c < 4 * D; c += nthr) {
-      const int t = c / (2 * D), rem = c - t * 2 * D, dd = rem >> 1, half = rem & 1;
-      const int pp = pg + t;
-      uint4 v = z4;
-      if (pp < pg1) {
-        const int ph = phys_page(p, b, pp);
-        if (ph >= 0) {
-          v = *(const uint4*)(pool + ((((size_t)ph * p.n_layers + p.layer) * 2 + 1) * p.nkv + m) * chunk +
-                              dd * 16 + half * 8);
-          const int valid = ctx - (pp * 16 + half * 8);  // slots of this piece below ctx
-          if (valid < 8) {
-            uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    __syncthreads();   // the previous tile has been consumed
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              if (e >= valid) w[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;
-            v = make_uint4(w[0], w[1], w[2], w[3]);
-          }
-        }
+    for (int q = 0; q < KP; ++q) {
+      const int c = tid + q * NT;
+      if (c < KPC) {
+        const int tok = c / (D / 8), part = c - tok * (D / 8);
+        *(u32x4*)(Ks + tok * LDK + part * 8) = rk[q];
       }
-      *(uint4*)(Vt + dd * LDV + t * 16 + half * 8) = v;
+    }
+#pragma unroll
+    for (int q = 0; q < VP; ++q) {
+      const int c = tid + q * NT;
+      if (c < VPC) {
+        const int t = c / (2 * D), rem = c - t * 2 * D, dd = rem >> 1, half = rem & 1;
+        *(u32x4*)(Vt + dd * LDV + t * 16 + half * 8) = rv[q];
+      }
     }
     __syncthreads();
+    if (pg + 2 < pg1) DFLASH_ATT_LOAD(pg + 2);   // next tile in flight during this one
 
     f32x4 st[2];
 #pragma unroll
@@ -136,7 +166,7 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
       st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const bf16x8 a = as_bf16x8(*(const uint4*)(Ks + (16 * t + (lane & 15)) * LDK + 32 * kk + 8 * (lane >> 4)));
+        const bf16x8 a = as_bf16x8(*(const u32x4*)(Ks + (16 * t + (lane & 15)) * LDK + 32 * kk + 8 * (lane >> 4)));
         st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[kk], st[t], 0, 0, 0);
         st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[kk], st[t], 0, 0, 0);
       }
@@ -168,7 +198,7 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
     }
     l_run = l_run * alpha + ps;
     m_run = m_new;
-    uint4 hu, lu;
+    u32x4 hu, lu;
     hu.x = ph[0] | ((uint32_t)ph[1] << 16); hu.y = ph[2] | ((uint32_t)ph[3] << 16);
     hu.z = ph[4] | ((uint32_t)ph[5] << 16); hu.w = ph[6] | ((uint32_t)ph[7] << 16);
     lu.x = pl[0] | ((uint32_t)pl[1] << 16); lu.y = pl[2] | ((uint32_t)pl[3] << 16);
@@ -178,12 +208,14 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
     for (int nn = 0; nn < NN; ++nn) {
       ot[nn] *= alpha;
       const bf16_t* vr = Vt + (16 * nn + (lane & 15)) * LDV + 4 * (lane >> 4);
-      uint2 lo2 = *(const uint2*)vr, hi2 = *(const uint2*)(vr + 16);
-      const bf16x8 va = as_bf16x8(make_uint4(lo2.x, lo2.y, hi2.x, hi2.y));
+      const u32x2 lo2 = *(const u32x2*)vr, hi2 = *(const u32x2*)(vr + 16);
+      const u32x4 vv = {lo2.x, lo2.y, hi2.x, hi2.y};
+      const bf16x8 va = as_bf16x8(vv);
       ot[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbh, ot[nn], 0, 0, 0);
       ot[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbl, ot[nn], 0, 0, 0);
     }
   }
+#undef DFLASH_ATT_LOAD
 
   float l_tot = l_run;
   l_tot += __shfl_xor(l_tot, 16, kWave);
@@ -231,7 +263,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
     }
   }
   float m_run = -INFINITY, l_run = 0.f;
-  auto consume = [&](float sdot, const float* vvals) {
+  auto consume = [&](float sdot, const float* vvals) {  // vvals may point to LDS
     // vvals: this lane's DQ value entries
     const float sc = sdot * p.scale;
     const float m_new = fmaxf(m_run, sc);
@@ -267,20 +299,23 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
       }
     }
   } else {
-    for (int jb = 0; jb < p.B; ++jb) {
+    // the B block keys (rotated) and values of kv head m, staged once
+    __shared__ float kb[16 * D], vb[16 * D];
+    for (int c = tid; c < p.B * D; c += 256) {
+      const int jb = c / D, e = c - jb * D;
       const int krow = b * p.B + jb;
       const float* kv = p.qkv + (size_t)krow * ldq + p.nq * D + m * D;
-      const float* vv0 = p.qkv + (size_t)krow * ldq + (p.nq + p.nkv) * D + m * D;
-      const float2* cs = p.cs + (size_t)krow * (D / 2);
+      kb[c] = rope_elem(kv, p.cs + (size_t)krow * (D / 2), e, D);
+      vb[c] = p.qkv[(size_t)krow * ldq + (p.nq + p.nkv) * D + m * D + e];
+    }
+    __syncthreads();
+    for (int jb = 0; jb < p.B; ++jb) {
       float sd = 0.f;
 #pragma unroll
-      for (int e = 0; e < DQ; ++e) sd += q[e] * rope_elem(kv, cs, q4 * DQ + e, D);
+      for (int e = 0; e < DQ; ++e) sd += q[e] * kb[jb * D + q4 * DQ + e];
       sd += __shfl_xor(sd, 1, kWave);
       sd += __shfl_xor(sd, 2, kWave);
-      float vv[DQ];
-#pragma unroll
-      for (int e = 0; e < DQ; ++e) vv[e] = vv0[q4 * DQ + e];
-      consume(sd, vv);
+      consume(sd, vb + jb * D + q4 * DQ);
     }
   }
   if (!rvalid) return;
@@ -329,10 +364,15 @@ hipError_t launch_attention(const AttnParams& p, int wdtype, hipStream_t s, void
   if (mark) mark(0, s);
   if (wdtype == 1) {
     const int waves = min(4, (R + 15) / 16);
-    if (p.d == 128)
-      hipLaunchKernelGGL(attn_ctx_mfma_kernel<128>, gctx, dim3(64 * waves), 0, s, p);
-    else
-      hipLaunchKernelGGL(attn_ctx_mfma_kernel<64>, gctx, dim3(64 * waves), 0, s, p);
+#define DFLASH_ATT_GO(DD, NWV) hipLaunchKernelGGL((attn_ctx_mfma_kernel<DD, NWV>), gctx, dim3(64 * NWV), 0, s, p)
+    if (p.d == 128) {
+      if (waves == 4) DFLASH_ATT_GO(128, 4); else if (waves == 3) DFLASH_ATT_GO(128, 3);
+      else if (waves == 2) DFLASH_ATT_GO(128, 2); else DFLASH_ATT_GO(128, 1);
+    } else {
+      if (waves == 4) DFLASH_ATT_GO(64, 4); else if (waves == 3) DFLASH_ATT_GO(64, 3);
+      else if (waves == 2) DFLASH_ATT_GO(64, 2); else DFLASH_ATT_GO(64, 1);
+    }
+#undef DFLASH_ATT_GO
   } else {
     if (p.d == 128)
       hipLaunchKernelGGL((attn_valu_kernel<float, 128, true>), gctx, dim3(256), 0, s, p);

@@ -8,6 +8,8 @@ namespace dflash {
 typedef uint16_t bf16_t;
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // 16-byte register payload
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
@@ -27,6 +29,7 @@ __device__ __forceinline__ void split_hilo(float x, bf16_t& hi, bf16_t& lo) {
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
 // Where an activation producer writes its result, in the form its consumer reads.
 enum ActMode : int { ACT_F32 = 0, ACT_HILO = 1, ACT_BF16 = 2 };

@@ -10,6 +10,8 @@
 // whole tile rows: plain/hi-lo stores, residual add, SwiGLU (gate and up
 // halves of the same tile), the LM-head argmax / log-sum-exp partials, and
 // the KV-injection scatter (rotary on K pairs (j, j+d/2), then the page slot).
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace dflash {
@@ -102,62 +104,64 @@ __device__ __forceinline__ void run_epilogue(const float* Cs, int ldc, int m0, i
       }
     }
     constexpr int TPR = NT / BM;      // threads per row
-    constexpr int CPT = BN / TPR;     // columns per thread
-    static_assert(NT % BM == 0 && BN % TPR == 0, "tile split");
+    constexpr int GRP = 128;          // columns per partial
+    constexpr int CPT = GRP / TPR;    // columns per thread within a group
+    static_assert(NT % BM == 0 && GRP % TPR == 0 && BN % GRP == 0, "tile split");
     const int r = tid / TPR, q = tid - r * TPR;
     const int row = m0 + r;
     const bool rv = row < M;
     const float T = e.temperature;
     const bool samp = T > 0.f;
-    const float invT = samp ? 1.f / T : 1.f;
     int bi = 0, bb = 0;
     if (rv) {
       const int rm = e.row_map[row];
       bb = rm / e.block;
       bi = rm - bb * e.block;
     }
-    LMPart P;
-    P.pmax = -INFINITY; P.zmax = -INFINITY; P.zsum = 0.f; P.zc = -INFINITY; P.idx = -1;
-    const int c0 = q * CPT;
-    if (rv) {
-      for (int c = 0; c < CPT; c += 4) {
-        const int v0 = n0 + c0 + c;
-        uint4 w = make_uint4(0, 0, 0, 0);
-        if (samp && v0 < N)
-          w = philox4x32_10(make_uint4((uint32_t)(v0 >> 2), (uint32_t)bi, (uint32_t)e.step, (uint32_t)bb),
-                            e.seed_lo, e.seed_hi);
-        const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll 1
+    for (int gq = 0; gq < BN / GRP; ++gq) {
+      LMPart P;
+      P.pmax = -INFINITY; P.zmax = -INFINITY; P.zsum = 0.f; P.zc = -INFINITY; P.idx = -1;
+      const int c0 = gq * GRP + q * CPT;
+      if (rv) {
+        for (int c = 0; c < CPT; c += 4) {
+          const int v0 = n0 + c0 + c;
+          uint4 w = make_uint4(0, 0, 0, 0);
+          if (samp && v0 < N)
+            w = philox4x32_10(make_uint4((uint32_t)(v0 >> 2), (uint32_t)bi, (uint32_t)e.step, (uint32_t)bb),
+                              e.seed_lo, e.seed_hi);
+          const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int v = v0 + k;
-          if (v >= N) break;
-          const float zt = samp ? Cs[r * ldc + c0 + c + k] / T : Cs[r * ldc + c0 + c + k];
-          const float sc = samp ? zt + gumbel_from_word(ww[k]) : zt;
-          if (sc > P.pmax || P.idx < 0) { P.pmax = sc; P.idx = v; P.zc = zt; }
-          P.zmax = fmaxf(P.zmax, zt);
+          for (int k = 0; k < 4; ++k) {
+            const int v = v0 + k;
+            if (v >= N) break;
+            const float zt = samp ? Cs[r * ldc + c0 + c + k] / T : Cs[r * ldc + c0 + c + k];
+            const float sc = samp ? zt + gumbel_from_word(ww[k]) : zt;
+            if (sc > P.pmax || P.idx < 0) { P.pmax = sc; P.idx = v; P.zc = zt; }
+            P.zmax = fmaxf(P.zmax, zt);
+          }
+        }
+        for (int c = 0; c < CPT; ++c) {
+          if (n0 + c0 + c >= N) break;
+          const float zt = samp ? Cs[r * ldc + c0 + c] / T : Cs[r * ldc + c0 + c];
+          P.zsum += expf(zt - P.zmax);
         }
       }
-      for (int c = 0; c < CPT; ++c) {
-        if (n0 + c0 + c >= N) break;
-        const float zt = samp ? Cs[r * ldc + c0 + c] / T : Cs[r * ldc + c0 + c];
-        P.zsum += expf(zt - P.zmax);
-      }
-    }
-    (void)invT;
 #pragma unroll
-    for (int o = 1; o < TPR; o <<= 1) {
-      LMPart Q;
-      Q.pmax = __shfl_xor(P.pmax, o, kWave);
-      Q.zmax = __shfl_xor(P.zmax, o, kWave);
-      Q.zsum = __shfl_xor(P.zsum, o, kWave);
-      Q.zc = __shfl_xor(P.zc, o, kWave);
-      Q.idx = __shfl_xor(P.idx, o, kWave);
-      P = (q & o) ? lm_merge(Q, P) : lm_merge(P, Q);
-    }
-    if (rv && q == 0) {
-      const size_t pi = (size_t)row * e.ntiles + n0 / BN;
-      e.part_f[pi] = make_float4(P.pmax, P.zmax, P.zsum, P.zc);
-      e.part_i[pi] = P.idx;
+      for (int o = 1; o < TPR; o <<= 1) {
+        LMPart Q;
+        Q.pmax = __shfl_xor(P.pmax, o, kWave);
+        Q.zmax = __shfl_xor(P.zmax, o, kWave);
+        Q.zsum = __shfl_xor(P.zsum, o, kWave);
+        Q.zc = __shfl_xor(P.zc, o, kWave);
+        Q.idx = __shfl_xor(P.idx, o, kWave);
+        P = (q & o) ? lm_merge(Q, P) : lm_merge(P, Q);
+      }
+      if (rv && q == 0 && n0 + gq * GRP < N) {
+        const size_t pi = (size_t)row * e.ntiles + (n0 + gq * GRP) / GRP;
+        e.part_f[pi] = make_float4(P.pmax, P.zmax, P.zsum, P.zc);
+        e.part_i[pi] = P.idx;
+      }
     }
   } else if constexpr (KIND == EPI_KVSCATTER) {
     const int d = e.head_dim, hd = d / 2, nkv = e.n_kv;
@@ -215,63 +219,88 @@ __device__ __forceinline__ bool tile_of(int ntm, int total, int& tm, int& tn) {
 }
 
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int WM, int WN, bool HILO, int KIND>
-__global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_mfma_kernel(
-    ActIn a, BRows<bf16_t> b, int M, int N, int K, EpiParams e) {
-  constexpr int BK = 64, LDK = BK + 8;
-  constexpr int NWN = BN / WN, NT = (BM / WM) * NWN * 64;
-  constexpr int TM = WM / 16, TN = WN / 16;
-  constexpr int NP = HILO ? 2 : 1;
-  constexpr int APER = BM * BK / 8 / NT, BPER = BN * BK / 8 / NT;
+// MFMA GEMM.  NP = 2: A is a (hi, lo) bf16 pair, two MFMAs per product.
+// STAGES = 2 double-buffers LDS (one barrier per K-tile), 1 uses one buffer.
+// ksplit > 1: this workgroup covers one contiguous range of K-tiles and
+// writes its raw fp32 tile to part[ks][M][N]; splitk_reduce_kernel then sums
+// the ranges in fixed order and runs the epilogue (deterministic, and the
+// same for every M).
+template <int BM, int BN, int WM, int WN, int NP, int STAGES>
+struct MfmaCfg {
+  static constexpr int BK = 64, LDK = BK + 8;
+  static constexpr int NWN = BN / WN, NT = (BM / WM) * NWN * 64;
+  static constexpr int TM = WM / 16, TN = WN / 16;
+  static constexpr int APER = BM * BK / 8 / NT, BPER = BN * BK / 8 / NT;
+  static constexpr int LDC = BN + 4;
+  static constexpr int STAGE_ELEMS = (NP * BM + BN) * LDK;
+  static constexpr int STAGE_BYTES = STAGES * STAGE_ELEMS * 2;
+  static constexpr int EPI_BYTES = BM * LDC * 4;
+  static constexpr int SMEM = STAGE_BYTES > EPI_BYTES ? STAGE_BYTES : EPI_BYTES;
+  // waves per SIMD to keep resident: two workgroups per CU when LDS allows it
+  static constexpr int MINW = SMEM <= 80 * 1024 ? 2 : 1;
   static_assert(APER * NT == BM * BK / 8 && BPER * NT == BN * BK / 8, "load split");
-  constexpr int LDC = BN + 4;
-  constexpr int STAGE = (NP * BM + BN) * LDK * 2;
-  constexpr int EPI = BM * LDC * 4;
-  constexpr int SMEM = STAGE > EPI ? STAGE : EPI;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
-  bf16_t* As = (bf16_t*)smem;
-  bf16_t* Bs = As + NP * BM * LDK;
+};
+
+template <int BM, int BN, int WM, int WN, int NP, int STAGES, int KIND>
+__global__ __launch_bounds__((MfmaCfg<BM, BN, WM, WN, NP, STAGES>::NT), (MfmaCfg<BM, BN, WM, WN, NP, STAGES>::MINW)) void gemm_mfma_kernel(
+    ActIn a, BRows<bf16_t> b, int M, int N, int K, int ksplit, float* part, EpiParams e) {
+  using C = MfmaCfg<BM, BN, WM, WN, NP, STAGES>;
+  constexpr int BK = C::BK, LDK = C::LDK, NT = C::NT, TM = C::TM, TN = C::TN;
+  constexpr int APER = C::APER, BPER = C::BPER, NWN = C::NWN;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
 
   const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
-  int tm, tn;
-  if (!tile_of(ntm, ntm * ntn, tm, tn)) return;
+  int t;
+  {
+    const int per = gridDim.x / 8, L = blockIdx.x;
+    t = (per > 0) ? (L & 7) * per + (L >> 3) : L;
+    if (t >= ntm * ntn * ksplit) return;
+  }
+  const int tm = t % ntm, tn = (t / ntm) % ntn, ks = t / (ntm * ntn);
   const int m0 = tm * BM, n0 = tn * BN;
+  const int nkt = K / BK;
+  const int kt0 = (int)((long long)ks * nkt / ksplit), kt1 = (int)((long long)(ks + 1) * nkt / ksplit);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid / NWN, wn = wid - (wid / NWN) * NWN;
 
-  const bf16_t* ap[2] = {(const bf16_t*)a.p0, (const bf16_t*)a.p1};
-  uint4 ra[NP][APER], rb[BPER];
-  const uint4 z4 = make_uint4(0, 0, 0, 0);
+  // Per-thread load slots are fixed for the whole K loop.  Rows past M (or
+  // columns past N) are clamped to the last valid one: they only feed output
+  // rows / columns that are never stored, so every load is unconditional.
+  const bf16_t* a_src[NP][APER];
+  const bf16_t* b_src[BPER];
+  int lds_a[APER], lds_b[BPER];
+#pragma unroll
+  for (int j = 0; j < APER; ++j) {
+    const int c = tid + j * NT, r = c >> 3, kc = (c & 7) * 8;
+    const int row = min(m0 + r, M - 1);
+    a_src[0][j] = (const bf16_t*)a.p0 + (size_t)row * a.ld + kc;
+    if constexpr (NP == 2) a_src[NP - 1][j] = (const bf16_t*)a.p1 + (size_t)row * a.ld + kc;
+    lds_a[j] = r * LDK + kc;
+  }
+#pragma unroll
+  for (int j = 0; j < BPER; ++j) {
+    const int c = tid + j * NT, r = c >> 3, kc = (c & 7) * 8;
+    b_src[j] = b.row(min(n0 + r, N - 1), BN) + kc;
+    lds_b[j] = r * LDK + kc;
+  }
+  u32x4 ra[NP][APER], rb[BPER];
 
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int j = 0; j < APER; ++j) {
-      const int c = tid + j * NT, r = c >> 3, kc = (c & 7) * 8;
-      const int row = m0 + r;
-#pragma unroll
-      for (int p = 0; p < NP; ++p)
-        ra[p][j] = row < M ? *(const uint4*)(ap[p] + (size_t)row * a.ld + k0 + kc) : z4;
-    }
-#pragma unroll
-    for (int j = 0; j < BPER; ++j) {
-      const int c = tid + j * NT, r = c >> 3, kc = (c & 7) * 8;
-      const int n = n0 + r;
-      rb[j] = n < N ? *(const uint4*)(b.row(n, BN) + k0 + kc) : z4;
-    }
-  };
-  auto sstore = [&]() {
-#pragma unroll
-    for (int j = 0; j < APER; ++j) {
-      const int c = tid + j * NT, r = c >> 3, kc = (c & 7) * 8;
-#pragma unroll
-      for (int p = 0; p < NP; ++p) *(uint4*)(As + (p * BM + r) * LDK + kc) = ra[p][j];
-    }
-#pragma unroll
-    for (int j = 0; j < BPER; ++j) {
-      const int c = tid + j * NT, r = c >> 3, kc = (c & 7) * 8;
-      *(uint4*)(Bs + r * LDK + kc) = rb[j];
-    }
-  };
+#define DFLASH_GLOAD(kt)                                                                            \
+  do {                                                                                              \
+    const int k0_ = (kt) * BK;                                                                      \
+    _Pragma("unroll") for (int j = 0; j < APER; ++j) {                                              \
+      _Pragma("unroll") for (int p = 0; p < NP; ++p) ra[p][j] = *(const u32x4*)(a_src[p][j] + k0_); \
+    }                                                                                               \
+    _Pragma("unroll") for (int j = 0; j < BPER; ++j) rb[j] = *(const u32x4*)(b_src[j] + k0_);       \
+  } while (0)
+#define DFLASH_SSTORE(buf)                                                                          \
+  do {                                                                                              \
+    bf16_t* st_ = (bf16_t*)smem + (buf) * C::STAGE_ELEMS;                                          \
+    _Pragma("unroll") for (int j = 0; j < APER; ++j) {                                              \
+      _Pragma("unroll") for (int p = 0; p < NP; ++p) *(u32x4*)(st_ + p * BM * LDK + lds_a[j]) = ra[p][j]; \
+    }                                                                                               \
+    _Pragma("unroll") for (int j = 0; j < BPER; ++j) *(u32x4*)(st_ + NP * BM * LDK + lds_b[j]) = rb[j]; \
+  } while (0)
 
   f32x4 acc[TM][TN];
 #pragma unroll
@@ -279,24 +308,19 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_mfma_kernel(
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nk = K / BK;
-  gload(0);
-  sstore();
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload((kt + 1) * BK);
+  auto compute = [&](const bf16_t* As, const bf16_t* Bs) __attribute__((always_inline)) {
 #pragma unroll
-    for (int ks = 0; ks < BK / 32; ++ks) {
-      const int kof = ks * 32 + 8 * (lane >> 4);
+    for (int kq = 0; kq < BK / 32; ++kq) {
+      const int kof = kq * 32 + 8 * (lane >> 4);
       bf16x8 af[NP][TM], bfr[TN];
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int p = 0; p < NP; ++p)
-          af[p][i] = as_bf16x8(*(const uint4*)(As + (p * BM + wm * WM + 16 * i + (lane & 15)) * LDK + kof));
+          af[p][i] = as_bf16x8(*(const u32x4*)(As + (p * BM + wm * TM * 16 + 16 * i + (lane & 15)) * LDK + kof));
 #pragma unroll
       for (int j = 0; j < TN; ++j)
-        bfr[j] = as_bf16x8(*(const uint4*)(Bs + (wn * WN + 16 * j + (lane & 15)) * LDK + kof));
+        bfr[j] = as_bf16x8(*(const u32x4*)(Bs + (wn * TN * 16 + 16 * j + (lane & 15)) * LDK + kof));
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -305,12 +329,34 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_mfma_kernel(
           for (int p = 0; p < NP; ++p)
             acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[p][i], bfr[j], acc[i][j], 0, 0, 0);
     }
+  };
+
+  if (kt0 < kt1) {
+    DFLASH_GLOAD(kt0);
+    DFLASH_SSTORE(0);
     __syncthreads();
-    if (kt + 1 < nk) {
-      sstore();
+  }
+  for (int kt = kt0; kt < kt1; ++kt) {
+    const bool more = kt + 1 < kt1;
+    if (more) DFLASH_GLOAD(kt + 1);
+    if constexpr (STAGES == 2) {
+      const int cur = (kt - kt0) & 1;
+      const bf16_t* st = (const bf16_t*)smem + cur * C::STAGE_ELEMS;
+      compute(st, st + NP * BM * LDK);
+      if (more) DFLASH_SSTORE(cur ^ 1);
       __syncthreads();
+    } else {
+      const bf16_t* st = (const bf16_t*)smem;
+      compute(st, st + NP * BM * LDK);
+      __syncthreads();
+      if (more) {
+        DFLASH_SSTORE(0);
+        __syncthreads();
+      }
     }
   }
+#undef DFLASH_GLOAD
+#undef DFLASH_SSTORE
 
   float* Cs = (float*)smem;
 #pragma unroll
@@ -319,9 +365,191 @@ __global__ __launch_bounds__((BM / WM) * (BN / WN) * 64) void gemm_mfma_kernel(
     for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        Cs[(wm * WM + 16 * i + 4 * (lane >> 4) + q) * LDC + wn * WN + 16 * j + (lane & 15)] = acc[i][j][q];
+        Cs[(wm * TM * 16 + 16 * i + 4 * (lane >> 4) + q) * C::LDC + wn * TN * 16 + 16 * j + (lane & 15)] = acc[i][j][q];
   __syncthreads();
-  run_epilogue<KIND, BM, BN, NT, bf16_t>(Cs, LDC, m0, n0, M, N, e);
+  if (ksplit > 1) {
+    float* dst = part + (size_t)ks * M * N;
+    constexpr int C4 = BN / 4;
+    for (int idx = tid; idx < BM * C4; idx += NT) {
+      const int r = idx / C4, c = (idx - r * C4) * 4;
+      if (m0 + r < M && n0 + c < N)
+        *(float4*)(dst + (size_t)(m0 + r) * N + n0 + c) = *(const float4*)(Cs + r * C::LDC + c);
+    }
+    return;
+  }
+  run_epilogue<KIND, BM, BN, NT, bf16_t>(Cs, C::LDC, m0, n0, M, N, e);
+}
+
+// MFMA GEMM with direct global->LDS loads (gfx950 global_load_lds_dwordx4):
+// 128x128x32 tiles, four 64x64 waves, three LDS stages, one barrier per
+// K-tile and no staging registers.  Each 16-byte load instruction of a wave
+// fills 1 KiB of LDS lane-linearly (lane i -> base + 16 i), so the LDS tile is
+// row-major with 64-byte rows; the 16-byte chunk c of row r is stored at
+// chunk c ^ ((r >> 1) & 3), which keeps the MFMA operand reads of eight
+// consecutive lanes (eight rows, same chunk) on distinct banks.
+template <int NP>
+struct DmaCfg {
+  static constexpr int BM = 128, BN = 128, BK = 32, NT = 256, STAGES = 3;
+  static constexpr int ROWS = NP * BM + BN;          // LDS rows per stage (64 B each)
+  static constexpr int STAGE_BYTES = ROWS * 64;
+  static constexpr int BLOCKS = STAGE_BYTES / 1024;   // 1 KiB load instructions per stage
+  static constexpr int LPT = BLOCKS / 4;              // per wave (and per thread)
+  static constexpr int LDC = BN + 4;
+  static constexpr int SMEM_PIPE = STAGES * STAGE_BYTES;
+  static constexpr int SMEM_EPI = BM * LDC * 4;
+  static constexpr int SMEM = SMEM_PIPE > SMEM_EPI ? SMEM_PIPE : SMEM_EPI;
+  static_assert(BLOCKS % 4 == 0, "blocks per wave");
+};
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Workgroup barrier without the memory fence of __syncthreads(): the fence
+// would also wait for the next tile's loads still in flight.  LDS data of the
+// current tile is covered by each wave's own vmcnt wait before the barrier;
+// LDS reads of the previous tile completed before their MFMAs issued.
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int NP, int KIND>
+__global__ __launch_bounds__(256, 2) void gemm_dma_kernel(ActIn a, BRows<bf16_t> b, int M, int N, int K, int ksplit,
+                                                           float* part, EpiParams e) {
+  using C = DmaCfg<NP>;
+  constexpr int BM = C::BM, BN = C::BN, BK = C::BK, LPT = C::LPT;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::SMEM];
+
+  const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
+  int t;
+  {
+    const int per = gridDim.x / 8, L = blockIdx.x;
+    t = (per > 0) ? (L & 7) * per + (L >> 3) : L;
+    if (t >= ntm * ntn * ksplit) return;
+  }
+  const int tm = t % ntm, tn = (t / ntm) % ntn, ks = t / (ntm * ntn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nkt = K / BK;
+  const int kt0 = (int)((long long)ks * nkt / ksplit), kt1 = (int)((long long)(ks + 1) * nkt / ksplit);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid >> 1, wn = wid & 1;
+
+  // source row pointers of this lane's LPT load blocks (fixed over K)
+  const bf16_t* src[LPT];
+#pragma unroll
+  for (int q = 0; q < LPT; ++q) {
+    const int blk = wid * LPT + q;
+    const int row = blk * 16 + (lane >> 2);
+    const int pc = lane & 3, lc = pc ^ ((row >> 1) & 3);
+    const bf16_t* base;
+    if (row < NP * BM) {
+      const int p = row / BM, r = row - p * BM;
+      const int gr = min(m0 + r, M - 1);
+      base = (const bf16_t*)(p == 0 ? a.p0 : a.p1) + (size_t)gr * a.ld;
+    } else {
+      base = b.row(min(n0 + row - NP * BM, N - 1), BN);
+    }
+    src[q] = base + lc * 8;
+  }
+  const uint32_t lds0 = (uint32_t)(size_t)smem;
+
+  auto issue = [&](int kt, int stage) __attribute__((always_inline)) {
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int q = 0; q < LPT; ++q) {
+      const int blk = wid * LPT + q;
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(src[q] + k0),
+          (__attribute__((address_space(3))) void*)(size_t)(lds0 + stage * C::STAGE_BYTES + blk * 1024), 16, 0, 0);
+    }
+  };
+
+  f32x4 acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nloc = kt1 - kt0;
+  if (nloc > 0) issue(kt0, 0);
+  if (nloc > 1) issue(kt0 + 1, 1);
+  for (int it = 0; it < nloc; ++it) {
+    if (it + 1 < nloc) wait_vmcnt<LPT>();   // this tile landed; the next may still be in flight
+    else wait_vmcnt<0>();
+    stage_barrier();                         // all lanes' data visible; stage (it+2)%3 is free
+    if (it + 2 < nloc) issue(kt0 + it + 2, (it + 2) % 3);
+    const unsigned char* st = smem + (it % 3) * C::STAGE_BYTES;
+    const int lc = lane >> 4;
+    bf16x8 af[NP][4], bfr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int p = 0; p < NP; ++p) {
+        const int row = p * BM + wm * 64 + 16 * i + (lane & 15);
+        af[p][i] = as_bf16x8(*(const u32x4*)(st + row * 64 + ((lc ^ ((row >> 1) & 3)) << 4)));
+      }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int row = NP * BM + wn * 64 + 16 * j + (lane & 15);
+      bfr[j] = as_bf16x8(*(const u32x4*)(st + row * 64 + ((lc ^ ((row >> 1) & 3)) << 4)));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int p = 0; p < NP; ++p)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[p][i], bfr[j], acc[i][j], 0, 0, 0);
+  }
+  __syncthreads();   // every wave is done with the pipeline buffers
+
+  float* Cs = (float*)smem;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        Cs[(wm * 64 + 16 * i + 4 * (lane >> 4) + q) * C::LDC + wn * 64 + 16 * j + (lane & 15)] = acc[i][j][q];
+  __syncthreads();
+  if (ksplit > 1) {
+    float* dst = part + (size_t)ks * M * N;
+    constexpr int C4 = BN / 4;
+    for (int idx = tid; idx < BM * C4; idx += 256) {
+      const int r = idx / C4, c = (idx - r * C4) * 4;
+      if (m0 + r < M && n0 + c < N)
+        *(float4*)(dst + (size_t)(m0 + r) * N + n0 + c) = *(const float4*)(Cs + r * C::LDC + c);
+    }
+    return;
+  }
+  run_epilogue<KIND, BM, BN, 256, bf16_t>(Cs, C::LDC, m0, n0, M, N, e);
+}
+
+// Sum of the split-K partials of one BM x BN tile, in split order, then the epilogue.
+template <int BM, int BN, int KIND, typename TP>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, int ksplit, int M, int N,
+                                                             EpiParams e) {
+  constexpr int LDC = BN + 4;
+  __shared__ __attribute__((aligned(16))) float Cs[BM * LDC];
+  const int ntm = (M + BM - 1) / BM;
+  const int tm = blockIdx.x % ntm, tn = blockIdx.x / ntm;
+  const int m0 = tm * BM, n0 = tn * BN;
+  constexpr int C4 = BN / 4;
+  for (int idx = threadIdx.x; idx < BM * C4; idx += 256) {
+    const int r = idx / C4, c = (idx - r * C4) * 4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (m0 + r < M && n0 + c < N) {
+      for (int k = 0; k < ksplit; ++k) {
+        const float4 v = *(const float4*)(part + ((size_t)k * M + m0 + r) * N + n0 + c);
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      }
+    }
+    *(float4*)(Cs + r * LDC + c) = acc;
+  }
+  __syncthreads();
+  run_epilogue<KIND, BM, BN, 256, TP>(Cs, LDC, m0, n0, M, N, e);
 }
 
 // ---------------------------------------------------------------------------
@@ -377,17 +605,60 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(ActIn a, BRows<float> b, 
 }
 
 // ---------------------------------------------------------------------------
-int gemm_bn(int) { return 128; }
+int gemm_bn(int) { return 128; }   // LM-head partials cover 128 columns each
 
-template <int BM, int BN, int WM, int WN, bool HILO, int KIND>
-static hipError_t go_mfma(const GemmArgs& g, hipStream_t s) {
+// Tile configuration and K split of one GEMM.  cfg 0: 128x128 tile, four
+// 64x64 waves, one LDS buffer (two workgroups per CU).  cfg 1: 128x256 tile,
+// four 64x128 waves, double-buffered LDS (one workgroup per CU).  A split is
+// used only when the tiles alone leave CUs idle; with fixed_split the split
+// depends on N and K only (injection must give the same bits for any M).
+#ifndef DFLASH_WIDE_TILES
+#define DFLASH_WIDE_TILES 0
+#endif
+#ifndef DFLASH_KS_TARGET
+#define DFLASH_KS_TARGET 256
+#endif
+#ifndef DFLASH_DMA
+#define DFLASH_DMA 1
+#endif
+GemmPlan gemm_plan(int wdtype, int a_mode, int M, int N, int K, int kind, bool fixed_split) {
+  GemmPlan p{0, 1};
+  if (wdtype == 0) return p;
+  const int nkt = K / 64;
+  const bool wide = DFLASH_WIDE_TILES && ((kind == EPI_LMHEAD) || (kind == EPI_SWIGLU && (N / 2) % 128 == 0));
+  if (wide && !fixed_split) {
+    p.cfg = 1;
+    return p;
+  }
+  const int tn = (N + 127) / 128;
+  const int tiles = (fixed_split ? 1 : (M + 127) / 128) * tn;
+  int ks = (DFLASH_KS_TARGET + tiles - 1) / tiles;
+  ks = std::min(ks, std::max(1, nkt / 4));
+  ks = std::max(ks, 1);
+  if (kind == EPI_LMHEAD) ks = 1;
+  p.ksplit = ks;
+  if (DFLASH_DMA) p.cfg = 2;
+  (void)a_mode;
+  return p;
+}
+
+size_t gemm_partial_bytes(const GemmPlan& p, int M, int N) {
+  return p.ksplit > 1 ? (size_t)p.ksplit * M * N * 4 : 0;
+}
+
+template <int BM, int BN, int WM, int WN, int NP, int STAGES, int KIND>
+static hipError_t go_mfma(const GemmArgs& g, int ksplit, hipStream_t s) {
+  using C = MfmaCfg<BM, BN, WM, WN, NP, STAGES>;
   const int ntm = (g.M + BM - 1) / BM, ntn = (g.N + BN - 1) / BN;
-  const int total = ntm * ntn;
+  const int total = ntm * ntn * ksplit;
   const int grid = (total + 7) / 8 * 8;
-  constexpr int NT = (BM / WM) * (BN / WN) * 64;
   BRows<bf16_t> b{(const bf16_t*)g.b.b0, (const bf16_t*)g.b.b1, g.b.ldb, g.b.split, g.b.mode};
-  hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, HILO, KIND>), dim3(grid), dim3(NT), 0, s, g.a, b,
-                     g.M, g.N, g.K, g.e);
+  hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, NP, STAGES, KIND>), dim3(grid), dim3(C::NT), 0, s, g.a, b,
+                     g.M, g.N, g.K, ksplit, g.part, g.e);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || ksplit == 1) return err;
+  hipLaunchKernelGGL((splitk_reduce_kernel<BM, BN, KIND, bf16_t>), dim3(ntm * ntn), dim3(256), 0, s, g.part, ksplit,
+                     g.M, g.N, g.e);
   return hipGetLastError();
 }
 
@@ -398,6 +669,28 @@ static hipError_t go_f32(const GemmArgs& g, hipStream_t s) {
   BRows<float> b{(const float*)g.b.b0, (const float*)g.b.b1, g.b.ldb, g.b.split, g.b.mode};
   hipLaunchKernelGGL((gemm_f32_kernel<KIND>), dim3(grid), dim3(256), 0, s, g.a, b, g.M, g.N, g.K, g.e);
   return hipGetLastError();
+}
+
+template <int NP, int KIND>
+static hipError_t go_dma(const GemmArgs& g, int ksplit, hipStream_t s) {
+  const int ntm = (g.M + 127) / 128, ntn = (g.N + 127) / 128;
+  const int total = ntm * ntn * ksplit;
+  const int grid = (total + 7) / 8 * 8;
+  BRows<bf16_t> b{(const bf16_t*)g.b.b0, (const bf16_t*)g.b.b1, g.b.ldb, g.b.split, g.b.mode};
+  hipLaunchKernelGGL((gemm_dma_kernel<NP, KIND>), dim3(grid), dim3(256), 0, s, g.a, b, g.M, g.N, g.K, ksplit, g.part,
+                     g.e);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || ksplit == 1) return err;
+  hipLaunchKernelGGL((splitk_reduce_kernel<128, 128, KIND, bf16_t>), dim3(ntm * ntn), dim3(256), 0, s, g.part, ksplit,
+                     g.M, g.N, g.e);
+  return hipGetLastError();
+}
+
+template <int NP, int KIND>
+static hipError_t go_bf16(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
+  if (p.cfg == 1) return go_mfma<128, 256, 64, 128, NP, 2, KIND>(g, 1, s);
+  if (p.cfg == 2) return go_dma<NP, KIND>(g, p.ksplit, s);
+  return go_mfma<128, 128, 64, 64, NP, 1, KIND>(g, p.ksplit, s);
 }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
@@ -412,18 +705,19 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
     }
     return hipErrorInvalidValue;
   }
-  const bool hilo = g.a.mode == ACT_HILO;
-  if (hilo) {
+  const GemmPlan p = gemm_plan(g.wdtype, g.a.mode, g.M, g.N, g.K, g.kind, g.fixed_split);
+  if (p.ksplit > 1 && !g.part) return hipErrorInvalidValue;
+  if (g.a.mode == ACT_HILO) {
     switch (g.kind) {
-      case EPI_STORE: return go_mfma<128, 128, 64, 64, true, EPI_STORE>(g, s);
-      case EPI_ADD: return go_mfma<128, 128, 64, 64, true, EPI_ADD>(g, s);
-      case EPI_SWIGLU: return go_mfma<128, 128, 64, 64, true, EPI_SWIGLU>(g, s);
-      case EPI_KVSCATTER: return go_mfma<128, 128, 64, 64, true, EPI_KVSCATTER>(g, s);
+      case EPI_STORE: return go_bf16<2, EPI_STORE>(g, p, s);
+      case EPI_ADD: return go_bf16<2, EPI_ADD>(g, p, s);
+      case EPI_SWIGLU: return go_bf16<2, EPI_SWIGLU>(g, p, s);
+      case EPI_KVSCATTER: return go_bf16<2, EPI_KVSCATTER>(g, p, s);
     }
   } else {
     switch (g.kind) {
-      case EPI_STORE: return go_mfma<128, 128, 64, 64, false, EPI_STORE>(g, s);
-      case EPI_LMHEAD: return go_mfma<128, 128, 64, 64, false, EPI_LMHEAD>(g, s);
+      case EPI_STORE: return go_bf16<1, EPI_STORE>(g, p, s);
+      case EPI_LMHEAD: return go_bf16<1, EPI_LMHEAD>(g, p, s);
     }
   }
   return hipErrorInvalidValue;

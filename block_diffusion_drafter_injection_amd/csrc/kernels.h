@@ -54,10 +54,18 @@ struct GemmArgs {
   int M, N, K;
   int kind;
   EpiParams e;
+  bool fixed_split;      // K split chosen from (N, K) only: results independent of M
+  float* part;           // split-K partials (gemm_partial_bytes of the plan), or null
 };
 
+struct GemmPlan {
+  int cfg;               // tile configuration
+  int ksplit;            // K ranges reduced in fixed order (1 = none)
+};
+GemmPlan gemm_plan(int wdtype, int a_mode, int M, int N, int K, int kind, bool fixed_split);
+size_t gemm_partial_bytes(const GemmPlan& p, int M, int N);
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
-int gemm_bn(int wdtype);       // column tile width (LM-head partial count = ceil(N / bn))
+int gemm_bn(int wdtype);       // columns per LM-head partial (partial count = ceil(N / bn))
 
 // Attention of the block queries over paged context KV plus in-block keys.
 struct AttnParams {
