@@ -104,7 +104,10 @@ void attn_split(int bt, int nkv, int nqg, int ctx_cap, int& ns, int& pps) {
     return;
   }
   const int pairs = std::max(1, bt * nkv * nqg);
-  const int want = (2048 + pairs - 1) / pairs;
+#ifndef DFLASH_ATT_WG_TARGET
+#define DFLASH_ATT_WG_TARGET 512
+#endif
+  const int want = (DFLASH_ATT_WG_TARGET + pairs - 1) / pairs;
   const int max_ns = (pages + 1) / 2;
   const int min_ns = (pages + 511) / 512;   // the context kernel stages at most 512 page ids
   ns = std::max(min_ns, std::max(1, std::min(want, max_ns)));
@@ -117,7 +120,7 @@ int n_qgroups(const dflash_config* c, int B) { return ((c->n_q_heads / c->n_kv_h
 
 struct DraftWS {
   size_t h, u_hi, u_lo, qkv, o_hi, o_lo, act_hi, act_lo, y, row_map, part_f, part_i, att_o, att_lse, cs, tau,
-      committed, cand, conf, gemm_part, total;
+      committed, cand, conf, gemm_part, q_hi, q_lo, total;
   int ns, pps, ntiles;
 };
 
@@ -141,13 +144,15 @@ DraftWS draft_layout(const dflash_config* c, int bt, int B, int ctx_cap) {
   w.row_map = k.take(M * 4);
   w.part_f = k.take(M * w.ntiles * 16);
   w.part_i = k.take(M * w.ntiles * 4);
-  w.att_o = k.take((size_t)(w.ns + 1) * M * nq * d * 4);
-  w.att_lse = k.take((size_t)(w.ns + 1) * M * nq * 4);
+  w.att_o = k.take((size_t)std::max(w.ns, 1) * M * nq * d * 4);
+  w.att_lse = k.take((size_t)std::max(w.ns, 1) * M * nq * 4);
   w.cs = k.take(M * (d / 2) * 8);
   w.tau = k.take(M * 4);
   w.committed = k.take(M * 4);
   w.cand = k.take(M * 4);
   w.conf = k.take(M * 4);
+  w.q_hi = k.take(M * nq * d * 2);
+  w.q_lo = k.take(M * nq * d * 2);
   {
     const int wd = c->dtype == DFLASH_BF16;
     const int am = wd ? ACT_HILO : ACT_F32;
@@ -322,7 +327,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
   if (batch == 0) return DFLASH_OK;
   if (!ctx_len || !out_tokens || !block_table || (!kv_pool && max_ctx_len > 0)) return DFLASH_EINVAL;
   if (!workspace || ((uintptr_t)workspace & 255)) return DFLASH_EWORKSPACE;
-  const int ctx_cap = std::min<long long>(max_ctx_len, (long long)max_pages * 16);
+  const int ctx_cap = n_pages > 0 ? (int)std::min<long long>(max_ctx_len, (long long)max_pages * 16) : 0;
   const DraftWS L = draft_layout(cfg, batch, block_size, ctx_cap);
   if (L.total > ws_bytes) return DFLASH_EWORKSPACE;
 
@@ -368,6 +373,8 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
   ap.pps = L.pps;
   ap.part_o = (float*)at(workspace, L.att_o);
   ap.part_lse = (float*)at(workspace, L.att_lse);
+  ap.q_hi = (bf16_t*)at(workspace, L.q_hi);
+  ap.q_lo = (bf16_t*)at(workspace, L.q_lo);
 
   HIP_TRY(launch_rope_table_block(ctx_len, ctx_cap, batch, B, d, (double)cfg->rope_base, cs, stream));
   HIP_TRY(launch_block_init(tau, committed, M, cfg->mask_token_id, stream));
@@ -394,7 +401,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
 
       ap.layer = l;
       HIP_TRY(launch_attention(ap, bf, stream, g_prof.cls == DFLASH_PROF_ATTN ? prof_attn : nullptr));
-      HIP_TRY(launch_attn_combine(ap, o, stream));
+      HIP_TRY(launch_attn_finish(ap, o, stream));
 
       GemmArgs go{};
       go.wdtype = bf;

@@ -13,6 +13,8 @@
 // of O^T = V^T P^T, whose A operand comes from the dimension-major V page
 // (two 8-byte LDS reads per fragment, no transpose).  P is split hi/lo too.
 // fp32 pool and the in-block split: a VALU kernel, four lanes per query row.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace dflash {
@@ -37,18 +39,62 @@ __device__ __forceinline__ float rope_elem(const float* v, const float2* cs, int
 
 // ---------------------------------------------------------------------------
 constexpr int kMaxPPS = 512;   // pages per context split (bounded by the host)
+#ifndef DFLASH_ATT_STAGES
+#define DFLASH_ATT_STAGES 4
+#endif
+constexpr int kAttStages = DFLASH_ATT_STAGES;  // 32-token tiles resident per workgroup
 
-template <int D, int NW>
-__global__ __launch_bounds__(NW * 64) void attn_ctx_mfma_kernel(AttnParams p) {
-  constexpr int NT = NW * 64;
-  constexpr int KK = D / 32;         // 32-wide k-steps of QK^T
-  constexpr int NN = D / 16;         // 16-row tiles of O^T
-  constexpr int LDK = D + 8, LDV = 32 + 8;
-  constexpr int KPC = 32 * D / 8;    // 16-byte pieces of a 32-token K tile
-  constexpr int VPC = 4 * D;         // 16-byte pieces of the two V pages
-  constexpr int KP = (KPC + NT - 1) / NT, VP = (VPC + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) bf16_t Ks[32 * LDK];
-  __shared__ __attribute__((aligned(16))) bf16_t Vt[D * LDV];
+template <int N>
+__device__ __forceinline__ void att_wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// Barrier without the memory fence of __syncthreads(): the fence would also
+// wait for the later tiles' loads still in flight.  Each wave waits for its
+// own copies of the current tile (vmcnt) before arriving.
+__device__ __forceinline__ void att_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Rotated queries of every (sequence, kv head) group as (hi, lo) bf16 planes
+// in [b][kv head][r][d] order, r = j*B + i for head m*g + j and block
+// position i: the context kernel then loads its MFMA operands directly.
+__global__ __launch_bounds__(256) void attn_qprep_kernel(AttnParams p, bf16_t* qhi, bf16_t* qlo) {
+  const int D = p.d, g = p.nq / p.nkv, R = g * p.B;
+  const int ldq = (p.nq + 2 * p.nkv) * D;
+  const size_t total = (size_t)p.batch * p.nkv * R * (D / 2);
+  for (size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (size_t)gridDim.x * 256) {
+    const int e2 = (int)(idx % (D / 2));      // element pair (2 e2, 2 e2 + 1)
+    const size_t gr = idx / (D / 2);           // (b, m, r) row
+    const int r = (int)(gr % R), m = (int)((gr / R) % p.nkv), b = (int)(gr / ((size_t)R * p.nkv));
+    const int j = r / p.B, i = r - j * p.B, row = b * p.B + i, n = m * g + j;
+    const float* qv = p.qkv + (size_t)row * ldq + n * D;
+    const float2* cs = p.cs + (size_t)row * (D / 2);
+    uint32_t h, l;
+    split_hilo2(rope_elem(qv, cs, 2 * e2, D), rope_elem(qv, cs, 2 * e2 + 1, D), h, l);
+    ((uint32_t*)qhi)[gr * (D / 2) + e2] = h;
+    ((uint32_t*)qlo)[gr * (D / 2) + e2] = l;
+  }
+}
+
+// Context part of the block attention, one (context split, kv head, sequence,
+// 64-query group) per workgroup of four waves.  Tiles of 32 tokens (two
+// pages: K 2 x 4 KiB, V 2 x 4 KiB) are copied global -> LDS by
+// global_load_lds_dwordx4 (lane i of an instruction fills LDS bytes
+// base + 16 i), kAttStages deep.  K rows (256 B) keep chunk c at c ^ (row & 15)
+// and V rows (32 B) keep half h at h ^ ((d >> 2) & 1), so the MFMA operand
+// reads of 16 consecutive lanes hit distinct banks.
+template <int D>
+__global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
+  static_assert(D == 128, "context kernel is specialised for head_dim 128");
+  static_assert(kAttStages >= 2 && kAttStages <= 7, "wait table covers up to 5 tiles in flight");
+  constexpr int KK = D / 32, NN = D / 16;
+  constexpr int KBYTES = 32 * D * 2;          // K tile: 32 tokens x 256 B
+  constexpr int VBYTES = 2 * D * 32;          // V tile: 2 pages x D rows x 32 B
+  constexpr int TILE = KBYTES + VBYTES;       // 16 KiB
+  constexpr int PER_THREAD = TILE / 1024 / 4; // load instructions per wave per tile
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[kAttStages * TILE];
   __shared__ int ptab[kMaxPPS];
 
   const int g = p.nq / p.nkv, R = g * p.B;
@@ -59,163 +105,183 @@ __global__ __launch_bounds__(NW * 64) void attn_ctx_mfma_kernel(AttnParams p) {
   const int ctx = clamp_ctx(p, b);
   const int npages = (ctx + 15) >> 4;
   const int pg0 = split * p.pps, pg1 = min(pg0 + p.pps, npages);
+  const int ntiles = pg1 > pg0 ? (pg1 - pg0 + 1) >> 1 : 0;
 
-  for (int i = tid; i < pg1 - pg0; i += NT) ptab[i] = phys_page(p, b, pg0 + i);
+  for (int i = tid; i < pg1 - pg0; i += 256) ptab[i] = phys_page(p, b, pg0 + i);
 
   const int r = qg * 64 + wid * 16 + (lane & 15);
   const bool rvalid = r < R;
+  const bool wave_active = qg * 64 + wid * 16 < R;
   const int j = rvalid ? r / p.B : 0, i = rvalid ? r - (r / p.B) * p.B : 0;
   const int n = m * g + j, row = b * p.B + i;
   const int ldq = (p.nq + 2 * p.nkv) * D;
 
   bf16x8 qh[KK], ql[KK];
   {
-    const float* qv = p.qkv + (size_t)row * ldq + n * D;
-    const float2* cs = p.cs + (size_t)row * (D / 2);
+    const size_t qoff = (((size_t)b * p.nkv + m) * R + (rvalid ? r : 0)) * D + 8 * (lane >> 4);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-      bf16_t hv[8], lv[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int dd = 32 * kk + 8 * (lane >> 4) + e;
-        const float x = rvalid ? rope_elem(qv, cs, dd, D) : 0.f;
-        split_hilo(x, hv[e], lv[e]);
-      }
-      u32x4 hu, lu;
-      hu.x = hv[0] | ((uint32_t)hv[1] << 16); hu.y = hv[2] | ((uint32_t)hv[3] << 16);
-      hu.z = hv[4] | ((uint32_t)hv[5] << 16); hu.w = hv[6] | ((uint32_t)hv[7] << 16);
-      lu.x = lv[0] | ((uint32_t)lv[1] << 16); lu.y = lv[2] | ((uint32_t)lv[3] << 16);
-      lu.z = lv[4] | ((uint32_t)lv[5] << 16); lu.w = lv[6] | ((uint32_t)lv[7] << 16);
-      qh[kk] = as_bf16x8(hu);
-      ql[kk] = as_bf16x8(lu);
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      qh[kk] = as_bf16x8(rvalid ? *(const u32x4*)(p.q_hi + qoff + 32 * kk) : z);
+      ql[kk] = as_bf16x8(rvalid ? *(const u32x4*)(p.q_lo + qoff + 32 * kk) : z);
     }
   }
-  __syncthreads();   // ptab ready
+  __syncthreads();   // ptab ready (and no copies in flight yet)
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 ot[NN];
 #pragma unroll
   for (int nn = 0; nn < NN; ++nn) ot[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // this (layer, kv head)'s pages are contiguous: [page][K chunk, V chunk]
   const size_t chunk = 16 * D;
-  const size_t kv_stride = (size_t)p.nkv * chunk;                   // K region -> V region of one layer
-  const size_t page_stride = (size_t)p.n_layers * 2 * kv_stride;
-  const bf16_t* base = (const bf16_t*)p.pool + (size_t)p.layer * 2 * kv_stride + (size_t)m * chunk;
-  u32x4 rk[KP], rv[VP];
-  const u32x4 z4 = {0u, 0u, 0u, 0u};
+  const size_t page_stride = 2 * chunk;
+  const bf16_t* kbase = (const bf16_t*)p.pool + ((size_t)p.layer * p.nkv + m) * p.n_pages * page_stride;
+  const bf16_t* vbase = kbase + chunk;
+  const uint32_t lds0 = (uint32_t)(size_t)lds;
+  // fallback source for masked pages: the split's first page, else page 0
+  // (the host only attends to a context when the pool has at least one page)
+  const int first_ph = (ntiles && ptab[0] >= 0) ? ptab[0] : 0;
 
-  // Global -> registers for the 32-token tile starting at page pg (two pages).
-#define DFLASH_ATT_LOAD(pg)                                                                    \
-  do {                                                                                         \
-    _Pragma("unroll") for (int q = 0; q < KP; ++q) {                                           \
-      const int c = tid + q * NT;                                                              \
-      const int tok = c / (D / 8), part = c - tok * (D / 8);                                   \
-      const int pp = (pg) + (tok >> 4), slot = tok & 15;                                       \
-      u32x4 v = z4;                                                                            \
-      if (c < KPC && pp < pg1 && pp * 16 + slot < ctx) {                                       \
-        const int ph = ptab[pp - pg0];                                                         \
-        if (ph >= 0) v = *(const u32x4*)(base + (size_t)ph * page_stride + slot * D + part * 8); \
-      }                                                                                        \
-      rk[q] = v;                                                                               \
-    }                                                                                          \
-    _Pragma("unroll") for (int q = 0; q < VP; ++q) {                                           \
-      const int c = tid + q * NT;                                                              \
-      const int t = c / (2 * D), rem = c - t * 2 * D, dd = rem >> 1, half = rem & 1;           \
-      const int pp = (pg) + t;                                                                 \
-      u32x4 v = z4;                                                                            \
-      if (c < VPC && pp < pg1) {                                                               \
-        const int ph = ptab[pp - pg0];                                                         \
-        if (ph >= 0) {                                                                         \
-          v = *(const u32x4*)(base + kv_stride + (size_t)ph * page_stride + dd * 16 + half * 8); \
-          const int valid = ctx - (pp * 16 + half * 8);                                        \
-          if (valid < 8) {                                                                     \
-            _Pragma("unroll") for (int e = 0; e < 8; ++e)                                      \
-              if (e >= valid) v[e >> 1] &= (e & 1) ? 0x0000ffffu : 0xffff0000u;                \
-          }                                                                                    \
-        }                                                                                      \
-      }                                                                                        \
-      rv[q] = v;                                                                               \
-    }                                                                                          \
-  } while (0)
-
-  if (pg0 < pg1) DFLASH_ATT_LOAD(pg0);
-  for (int pg = pg0; pg < pg1; pg += 2) {
-    __syncthreads();   // the previous tile has been consumed
+  // Issue the copies of tile t (pages pg0 + 2t, +1) into stage st.  A page
+  // past the split, or one without a valid physical index, is read from the
+  // split's first page instead: its tokens are masked out of the softmax.
+  auto issue = [&](int t, int st) __attribute__((always_inline)) {
 #pragma unroll
-    for (int q = 0; q < KP; ++q) {
-      const int c = tid + q * NT;
-      if (c < KPC) {
-        const int tok = c / (D / 8), part = c - tok * (D / 8);
-        *(u32x4*)(Ks + tok * LDK + part * 8) = rk[q];
+    for (int q = 0; q < PER_THREAD; ++q) {
+      const int ins = wid * PER_THREAD + q;          // 0..15 over the workgroup
+      const unsigned char* src;
+      if (ins < 8) {                                  // K: rows 4*ins .. 4*ins+3
+        const int krow = ins * 4 + (lane >> 4);
+        const int pc = lane & 15, lc = pc ^ (krow & 15);
+        const int pp = pg0 + 2 * t + (krow >> 4);
+        int ph = pp < pg1 ? ptab[pp - pg0] : first_ph;
+        ph = ph >= 0 ? ph : first_ph;
+        src = (const unsigned char*)(kbase + (size_t)ph * page_stride) + (krow & 15) * (D * 2) + lc * 16;
+      } else {                                        // V: page (ins-8)/4, rows 32*((ins-8)%4) ..
+        const int vi = ins - 8, pg = vi >> 2;
+        const int d = (vi & 3) * 32 + (lane >> 1);
+        const int lh = (lane & 1) ^ ((d >> 2) & 1);
+        const int pp = pg0 + 2 * t + pg;
+        int ph = pp < pg1 ? ptab[pp - pg0] : first_ph;
+        ph = ph >= 0 ? ph : first_ph;
+        src = (const unsigned char*)(vbase + (size_t)ph * page_stride) + d * 32 + lh * 16;
       }
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
+                                       (__attribute__((address_space(3))) void*)(size_t)(lds0 + st * TILE + ins * 1024),
+                                       16, 0, 0);
     }
-#pragma unroll
-    for (int q = 0; q < VP; ++q) {
-      const int c = tid + q * NT;
-      if (c < VPC) {
-        const int t = c / (2 * D), rem = c - t * 2 * D, dd = rem >> 1, half = rem & 1;
-        *(u32x4*)(Vt + dd * LDV + t * 16 + half * 8) = rv[q];
-      }
-    }
-    __syncthreads();
-    if (pg + 2 < pg1) DFLASH_ATT_LOAD(pg + 2);   // next tile in flight during this one
+  };
 
-    f32x4 st[2];
+#pragma unroll
+  for (int t = 0; t < kAttStages - 1; ++t)
+    if (t < ntiles) issue(t, t);
+
+  // loop-invariant LDS operand offsets of this lane
+  int koff[KK], voff[NN];
+  {
+    const int krow = lane & 15;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) koff[kk] = krow * (D * 2) + (((4 * kk + (lane >> 4)) ^ krow) << 4);
+    const int gq = lane >> 4;   // slots 4gq .. 4gq+3 of each page
+#pragma unroll
+    for (int nn = 0; nn < NN; ++nn) {
+      const int d = 16 * nn + (lane & 15);
+      voff[nn] = d * 32 + (((gq >> 1) ^ ((d >> 2) & 1)) << 4) + (gq & 1) * 8;
+    }
+  }
+  const float sl2 = p.scale * 1.4426950408889634f;
+  const int tok_end = min(ctx, pg1 * 16);
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int later = min(ntiles - 1 - it, kAttStages - 2);   // tiles issued after this one
+    switch (later) {
+      case 0: att_wait_vmcnt<0>(); break;
+      case 1: att_wait_vmcnt<PER_THREAD>(); break;
+      case 2: att_wait_vmcnt<2 * PER_THREAD>(); break;
+      case 3: att_wait_vmcnt<3 * PER_THREAD>(); break;
+      case 4: att_wait_vmcnt<4 * PER_THREAD>(); break;
+      default: att_wait_vmcnt<5 * PER_THREAD>(); break;
+    }
+    att_barrier();
+    const int st = it % kAttStages;
+    unsigned char* kt_lds = lds + st * TILE;
+    unsigned char* vt_lds = kt_lds + KBYTES;
+    const int tok0 = (pg0 + 2 * it) * 16;
+    if (tok0 + 32 > ctx) {
+      // boundary tile: V slots at or past the context end may hold anything
+      // (a page never written); they are zeroed so that P = 0 meets V = 0.
+      for (int c = tid; c < 2 * D * 16; c += 256) {
+        const int pg = c / (D * 16), rem = c - pg * D * 16, d = rem >> 4, slot = rem & 15;
+        if (tok0 + pg * 16 + slot >= ctx) {
+          const int lh = (slot >> 3) ^ ((d >> 2) & 1);
+          *(bf16_t*)(vt_lds + pg * (D * 32) + d * 32 + lh * 16 + (slot & 7) * 2) = 0;
+        }
+      }
+      __syncthreads();
+    }
+    if (it + kAttStages - 1 < ntiles) issue(it + kAttStages - 1, (it + kAttStages - 1) % kAttStages);
+    if (!wave_active) continue;
+
+    f32x4 st2[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      st[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+      st2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) {
-        const bf16x8 a = as_bf16x8(*(const u32x4*)(Ks + (16 * t + (lane & 15)) * LDK + 32 * kk + 8 * (lane >> 4)));
-        st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[kk], st[t], 0, 0, 0);
-        st[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[kk], st[t], 0, 0, 0);
+        const bf16x8 a = as_bf16x8(*(const u32x4*)(kt_lds + koff[kk] + t * 16 * (D * 2)));
+        st2[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[kk], st2[t], 0, 0, 0);
+        st2[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[kk], st2[t], 0, 0, 0);
       }
     }
-    // lane owns query (lane & 15) and tokens 16t + 4(lane>>4) + e
+    // lane owns query (lane & 15) and tokens tok0 + 16t + 4(lane>>4) + e; scores
+    // are kept in base-2 units (scale * log2 e folded in) for v_exp_f32
     float s[8];
-    float mx = -INFINITY;
+    if (tok0 + 32 <= tok_end) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int tok = pg * 16 + 16 * t + 4 * (lane >> 4) + e;
-        const float v = (tok < pg1 * 16 && tok < ctx) ? st[t][e] * p.scale : -INFINITY;
-        s[t * 4 + e] = v;
-        mx = fmaxf(mx, v);
-      }
+        for (int e = 0; e < 4; ++e) s[t * 4 + e] = st2[t][e] * sl2;
+    } else {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int tok = tok0 + 16 * t + 4 * (lane >> 4) + e;
+          s[t * 4 + e] = tok < tok_end ? st2[t][e] * sl2 : -INFINITY;
+        }
+    }
+    float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
     mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
     const float m_new = fmaxf(m_run, mx);
     if (m_new == -INFINITY) continue;
-    const float alpha = expf(m_run - m_new);
-    float ps = 0.f;
-    bf16_t ph[8], pl[8];
+    float pv[8], ps = 0.f;
 #pragma unroll
     for (int k = 0; k < 8; ++k) {
-      const float pv = expf(s[k] - m_new);
-      ps += pv;
-      split_hilo(pv, ph[k], pl[k]);
+      pv[k] = __builtin_amdgcn_exp2f(s[k] - m_new);
+      ps += pv[k];
     }
-    l_run = l_run * alpha + ps;
+    if (__any(m_new != m_run)) {   // rescale only when some row's running max moved
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int nn = 0; nn < NN; ++nn) ot[nn] *= alpha;
+    }
+    l_run += ps;
     m_run = m_new;
     u32x4 hu, lu;
-    hu.x = ph[0] | ((uint32_t)ph[1] << 16); hu.y = ph[2] | ((uint32_t)ph[3] << 16);
-    hu.z = ph[4] | ((uint32_t)ph[5] << 16); hu.w = ph[6] | ((uint32_t)ph[7] << 16);
-    lu.x = pl[0] | ((uint32_t)pl[1] << 16); lu.y = pl[2] | ((uint32_t)pl[3] << 16);
-    lu.z = pl[4] | ((uint32_t)pl[5] << 16); lu.w = pl[6] | ((uint32_t)pl[7] << 16);
+    split_hilo8(pv, hu, lu);
     const bf16x8 pbh = as_bf16x8(hu), pbl = as_bf16x8(lu);
 #pragma unroll
     for (int nn = 0; nn < NN; ++nn) {
-      ot[nn] *= alpha;
-      const bf16_t* vr = Vt + (16 * nn + (lane & 15)) * LDV + 4 * (lane >> 4);
-      const u32x2 lo2 = *(const u32x2*)vr, hi2 = *(const u32x2*)(vr + 16);
+      const u32x2 lo2 = *(const u32x2*)(vt_lds + voff[nn]), hi2 = *(const u32x2*)(vt_lds + D * 32 + voff[nn]);
       const u32x4 vv = {lo2.x, lo2.y, hi2.x, hi2.y};
       const bf16x8 va = as_bf16x8(vv);
       ot[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbh, ot[nn], 0, 0, 0);
       ot[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbl, ot[nn], 0, 0, 0);
     }
   }
-#undef DFLASH_ATT_LOAD
 
   float l_tot = l_run;
   l_tot += __shfl_xor(l_tot, 16, kWave);
@@ -224,7 +290,8 @@ __global__ __launch_bounds__(NW * 64) void attn_ctx_mfma_kernel(AttnParams p) {
   const size_t Mq = (size_t)p.batch * p.B * p.nq;
   const size_t qrow = (size_t)row * p.nq + n;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if ((lane >> 4) == 0) p.part_lse[split * Mq + qrow] = l_tot > 0.f ? m_run + logf(l_tot) : -INFINITY;
+  if ((lane >> 4) == 0)
+    p.part_lse[split * Mq + qrow] = l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.6931471805599453f : -INFINITY;
   float* dst = p.part_o + (split * Mq + qrow) * D;
 #pragma unroll
   for (int nn = 0; nn < NN; ++nn) {
@@ -234,15 +301,14 @@ __global__ __launch_bounds__(NW * 64) void attn_ctx_mfma_kernel(AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// VALU attention: 64 query rows per workgroup, 4 lanes per row (D/4 dims each).
-// CTX: keys of context split blockIdx.x / nqg from the paged pool of type TP.
-// !CTX: the B in-block keys (fp32, rotated here), written as split n_splits.
+// VALU attention over a context split (fp32 pools, or head_dim 64): 64 query
+// rows per workgroup, 4 lanes per row (D/4 dims each).
 template <typename TP, int D, bool CTX>
 __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
   constexpr int DQ = D / 4;
   const int g = p.nq / p.nkv, R = g * p.B;
   const int nqg = (R + 63) / 64;
-  const int split = CTX ? blockIdx.x / nqg : p.n_splits;
+  const int split = blockIdx.x / nqg;
   const int qg = blockIdx.x % nqg;
   const int m = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, q4 = tid & 3;
@@ -274,7 +340,7 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
     m_run = m_new;
   };
 
-  if constexpr (CTX) {
+  {
     const int ctx = clamp_ctx(p, b);
     const int npages = (ctx + 15) >> 4;
     const int pg0 = split * p.pps, pg1 = min(pg0 + p.pps, npages);
@@ -283,8 +349,8 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
     for (int pg = pg0; pg < pg1; ++pg) {
       const int ph = phys_page(p, b, pg);
       if (ph < 0) continue;
-      const TP* Kc = pool + (((size_t)ph * p.n_layers + p.layer) * 2 * p.nkv + m) * chunk;
-      const TP* Vc = pool + ((((size_t)ph * p.n_layers + p.layer) * 2 + 1) * p.nkv + m) * chunk;
+      const TP* Kc = pool + ((((size_t)p.layer * p.nkv + m) * p.n_pages + ph) * 2) * chunk;
+      const TP* Vc = Kc + chunk;
       const int ns = min(16, ctx - pg * 16);
       for (int slot = 0; slot < ns; ++slot) {
         float sd = 0.f;
@@ -298,25 +364,6 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
         consume(sd, vv);
       }
     }
-  } else {
-    // the B block keys (rotated) and values of kv head m, staged once
-    __shared__ float kb[16 * D], vb[16 * D];
-    for (int c = tid; c < p.B * D; c += 256) {
-      const int jb = c / D, e = c - jb * D;
-      const int krow = b * p.B + jb;
-      const float* kv = p.qkv + (size_t)krow * ldq + p.nq * D + m * D;
-      kb[c] = rope_elem(kv, p.cs + (size_t)krow * (D / 2), e, D);
-      vb[c] = p.qkv[(size_t)krow * ldq + (p.nq + p.nkv) * D + m * D + e];
-    }
-    __syncthreads();
-    for (int jb = 0; jb < p.B; ++jb) {
-      float sd = 0.f;
-#pragma unroll
-      for (int e = 0; e < DQ; ++e) sd += q[e] * kb[jb * D + q4 * DQ + e];
-      sd += __shfl_xor(sd, 1, kWave);
-      sd += __shfl_xor(sd, 2, kWave);
-      consume(sd, vb + jb * D + q4 * DQ);
-    }
   }
   if (!rvalid) return;
   const size_t Mq = (size_t)p.batch * p.B * p.nq;
@@ -329,75 +376,132 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Merge the n_splits + 1 partials of every query row in split order.
+// Block keys and merge, per (16 query rows, kv head, sequence): the rotated
+// queries and the B block keys / values (fp32) are staged in LDS; each row
+// attends to the B keys (softmax in fp32); the result is merged with the
+// n_splits context partials in split order (block part last) and written in
+// the operand form of the output projection.
 template <int D>
-__global__ __launch_bounds__(256) void attn_combine_kernel(AttnParams p, ActOut out) {
-  const size_t Mq = (size_t)p.batch * p.B * p.nq;
-  const int per = 256 / (D / 4);
-  const size_t qrow = (size_t)blockIdx.x * per + threadIdx.x / (D / 4);
-  const int e4 = (threadIdx.x % (D / 4)) * 4;
-  if (qrow >= Mq) return;
-  const int S = p.n_splits + 1;
-  float mx = -INFINITY;
-  for (int s = 0; s < S; ++s) mx = fmaxf(mx, p.part_lse[s * Mq + qrow]);
-  float tot = 0.f;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < S; ++s) {
-    const float l = p.part_lse[s * Mq + qrow];
-    if (l == -INFINITY) continue;
-    const float w = expf(l - mx);
-    tot += w;
-    const float4 v = *(const float4*)(p.part_o + (s * Mq + qrow) * D + e4);
-    acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+__global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut out) {
+  constexpr int QR = 16, DPT = D / 16;
+  __shared__ float qs[QR][D + 1];
+  __shared__ float kb[16][D + 1], vb[16][D + 1];
+  __shared__ float pb[QR][17];
+  __shared__ float blse[QR];
+  const int g = p.nq / p.nkv, R = g * p.B;
+  const int qg = blockIdx.x, m = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int ldq = (p.nq + 2 * p.nkv) * D;
+  for (int c = tid; c < QR * D; c += 256) {
+    const int r = c / D, e = c - r * D, rr = qg * QR + r;
+    float v = 0.f;
+    if (rr < R) {
+      const int j = rr / p.B, i = rr - j * p.B, row = b * p.B + i, n = m * g + j;
+      v = rope_elem(p.qkv + (size_t)row * ldq + n * D, p.cs + (size_t)row * (D / 2), e, D);
+    }
+    qs[r][e] = v;
   }
-  const float inv = tot > 0.f ? 1.f / tot : 0.f;
-  acc.x *= inv; acc.y *= inv; acc.z *= inv; acc.w *= inv;
-  const int rowm = (int)(qrow / p.nq), n = (int)(qrow % p.nq);
-  act_store4(out, rowm, n * D + e4, acc);
+  for (int c = tid; c < p.B * D; c += 256) {
+    const int jb = c / D, e = c - jb * D, krow = b * p.B + jb;
+    kb[jb][e] = rope_elem(p.qkv + (size_t)krow * ldq + p.nq * D + m * D, p.cs + (size_t)krow * (D / 2), e, D);
+    vb[jb][e] = p.qkv[(size_t)krow * ldq + (p.nq + p.nkv) * D + m * D + e];
+  }
+  __syncthreads();
+  {
+    const int r = tid >> 4, key = tid & 15;
+    float sc = -INFINITY;
+    if (key < p.B) {
+      float dot = 0.f;
+#pragma unroll 8
+      for (int e = 0; e < D; ++e) dot = fmaf(qs[r][e], kb[key][e], dot);
+      sc = dot * p.scale;
+    }
+    float mx = sc;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
+    const float ex = key < p.B ? expf(sc - mx) : 0.f;
+    float sum = ex;
+#pragma unroll
+    for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, kWave);
+    pb[r][key] = ex / sum;
+    if (key == 0) blse[r] = mx + logf(sum);
+  }
+  __syncthreads();
+  const int r = tid >> 4, d0 = (tid & 15) * DPT, rr = qg * QR + r;
+  if (rr >= R) return;
+  const int j = rr / p.B, i = rr - j * p.B, row = b * p.B + i, n = m * g + j;
+  const size_t Mq = (size_t)p.batch * p.B * p.nq;
+  const size_t qrow = (size_t)row * p.nq + n;
+  float ob[DPT];
+#pragma unroll
+  for (int k = 0; k < DPT; ++k) ob[k] = 0.f;
+  for (int jb = 0; jb < p.B; ++jb) {
+    const float w = pb[r][jb];
+#pragma unroll
+    for (int k = 0; k < DPT; ++k) ob[k] = fmaf(w, vb[jb][d0 + k], ob[k]);
+  }
+  float mxl = blse[r];
+  for (int sp = 0; sp < p.n_splits; ++sp) mxl = fmaxf(mxl, p.part_lse[sp * Mq + qrow]);
+  float tot = 0.f, acc[DPT];
+#pragma unroll
+  for (int k = 0; k < DPT; ++k) acc[k] = 0.f;
+  for (int sp = 0; sp < p.n_splits; ++sp) {
+    const float l = p.part_lse[sp * Mq + qrow];
+    if (l == -INFINITY) continue;
+    const float w = expf(l - mxl);
+    tot += w;
+    const float* src = p.part_o + (sp * Mq + qrow) * D + d0;
+#pragma unroll
+    for (int k = 0; k < DPT; k += 4) {
+      const float4 v = *(const float4*)(src + k);
+      acc[k] = fmaf(w, v.x, acc[k]);
+      acc[k + 1] = fmaf(w, v.y, acc[k + 1]);
+      acc[k + 2] = fmaf(w, v.z, acc[k + 2]);
+      acc[k + 3] = fmaf(w, v.w, acc[k + 3]);
+    }
+  }
+  {
+    const float w = expf(blse[r] - mxl);
+    tot += w;
+#pragma unroll
+    for (int k = 0; k < DPT; ++k) acc[k] = fmaf(w, ob[k], acc[k]);
+  }
+  const float inv = 1.f / tot;
+#pragma unroll
+  for (int k = 0; k < DPT; k += 4)
+    act_store4(out, row, n * D + d0 + k, make_float4(acc[k] * inv, acc[k + 1] * inv, acc[k + 2] * inv, acc[k + 3] * inv));
 }
 
 // ---------------------------------------------------------------------------
 hipError_t launch_attention(const AttnParams& p, int wdtype, hipStream_t s, void (*mark)(int, hipStream_t)) {
+  if (p.n_splits <= 0) return hipSuccess;
   const int g = p.nq / p.nkv, R = g * p.B, nqg = (R + 63) / 64;
-  const dim3 gctx(p.n_splits * nqg, p.nkv, p.batch), gblk(nqg, p.nkv, p.batch);
-  if (p.n_splits > 0) {
+  const dim3 gctx(p.n_splits * nqg, p.nkv, p.batch);
+  if (wdtype == 1 && p.d == 128) {
+    const size_t total = (size_t)p.batch * p.nkv * R * (p.d / 2);
+    const int blocks = (int)std::min<size_t>((total + 255) / 256, 4096);
+    hipLaunchKernelGGL(attn_qprep_kernel, dim3(blocks), dim3(256), 0, s, p, p.q_hi, p.q_lo);
+  }
   if (mark) mark(0, s);
-  if (wdtype == 1) {
-    const int waves = min(4, (R + 15) / 16);
-#define DFLASH_ATT_GO(DD, NWV) hipLaunchKernelGGL((attn_ctx_mfma_kernel<DD, NWV>), gctx, dim3(64 * NWV), 0, s, p)
-    if (p.d == 128) {
-      if (waves == 4) DFLASH_ATT_GO(128, 4); else if (waves == 3) DFLASH_ATT_GO(128, 3);
-      else if (waves == 2) DFLASH_ATT_GO(128, 2); else DFLASH_ATT_GO(128, 1);
-    } else {
-      if (waves == 4) DFLASH_ATT_GO(64, 4); else if (waves == 3) DFLASH_ATT_GO(64, 3);
-      else if (waves == 2) DFLASH_ATT_GO(64, 2); else DFLASH_ATT_GO(64, 1);
-    }
-#undef DFLASH_ATT_GO
-  } else {
-    if (p.d == 128)
-      hipLaunchKernelGGL((attn_valu_kernel<float, 128, true>), gctx, dim3(256), 0, s, p);
-    else
-      hipLaunchKernelGGL((attn_valu_kernel<float, 64, true>), gctx, dim3(256), 0, s, p);
-  }
-  if (mark) mark(1, s);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
-  }
-  if (p.d == 128)
-    hipLaunchKernelGGL((attn_valu_kernel<float, 128, false>), gblk, dim3(256), 0, s, p);
+  if (wdtype == 1 && p.d == 128)
+    hipLaunchKernelGGL(attn_ctx_mfma_kernel<128>, gctx, dim3(256), 0, s, p);
+  else if (wdtype == 1)
+    hipLaunchKernelGGL((attn_valu_kernel<bf16_t, 64, true>), gctx, dim3(256), 0, s, p);
+  else if (p.d == 128)
+    hipLaunchKernelGGL((attn_valu_kernel<float, 128, true>), gctx, dim3(256), 0, s, p);
   else
-    hipLaunchKernelGGL((attn_valu_kernel<float, 64, false>), gblk, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((attn_valu_kernel<float, 64, true>), gctx, dim3(256), 0, s, p);
+  if (mark) mark(1, s);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_combine(const AttnParams& p, ActOut out, hipStream_t s) {
-  const size_t Mq = (size_t)p.batch * p.B * p.nq;
-  const int per = 256 / (p.d / 4);
-  const int grid = (int)((Mq + per - 1) / per);
+hipError_t launch_attn_finish(const AttnParams& p, ActOut out, hipStream_t s) {
+  const int R = (p.nq / p.nkv) * p.B;
+  const dim3 grid((R + 15) / 16, p.nkv, p.batch);
   if (p.d == 128)
-    hipLaunchKernelGGL(attn_combine_kernel<128>, dim3(grid), dim3(256), 0, s, p, out);
+    hipLaunchKernelGGL(attn_finish_kernel<128>, grid, dim3(256), 0, s, p, out);
   else
-    hipLaunchKernelGGL(attn_combine_kernel<64>, dim3(grid), dim3(256), 0, s, p, out);
+    hipLaunchKernelGGL(attn_finish_kernel<64>, grid, dim3(256), 0, s, p, out);
   return hipGetLastError();
 }
 

@@ -13,19 +13,37 @@ typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
 
-// float32 -> bfloat16, round to nearest even (NaN kept quiet).
-__device__ __forceinline__ bf16_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (bf16_t)(u >> 16);
-}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// float32 -> bfloat16 with round-to-nearest-even: gfx950's v_cvt_pk_bf16_f32
+// (the default rounding mode is nearest-even; NaN stays NaN).
+__device__ __forceinline__ bf16_t f2bf(float f) { return __builtin_bit_cast(bf16_t, (__bf16)f); }
 __device__ __forceinline__ float bf2f(bf16_t h) { return __uint_as_float((uint32_t)h << 16); }
+// Two values rounded at once, packed low | high << 16.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 
 // Two-term bfloat16 split: x ~= hi + lo with |x - hi - lo| <= 2^-16 |x|.
 __device__ __forceinline__ void split_hilo(float x, bf16_t& hi, bf16_t& lo) {
   hi = f2bf(x);
   lo = f2bf(x - bf2f(hi));
+}
+// The same for a pair, results packed as two bf16 per word.
+__device__ __forceinline__ void split_hilo2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = pack_bf16x2(a, b);
+  lo = pack_bf16x2(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xffff0000u));
+}
+
+// Eight values -> (hi, lo) operand fragments of one MFMA input (8 bf16 each).
+__device__ __forceinline__ void split_hilo8(const float* x, u32x4& hi, u32x4& lo) {
+  uint32_t h[4], l[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) split_hilo2(x[2 * k], x[2 * k + 1], h[k], l[k]);
+  hi = u32x4{h[0], h[1], h[2], h[3]};
+  lo = u32x4{l[0], l[1], l[2], l[3]};
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
@@ -66,22 +84,15 @@ __device__ __forceinline__ void act_store4(const ActOut& o, int row, int col, fl
   if (o.mode == ACT_F32) {
     *(float4*)((float*)o.p0 + i) = v;
   } else if (o.mode == ACT_HILO) {
-    bf16_t h0, l0, h1, l1, h2, l2, h3, l3;
-    split_hilo(v.x, h0, l0);
-    split_hilo(v.y, h1, l1);
-    split_hilo(v.z, h2, l2);
-    split_hilo(v.w, h3, l3);
     uint2 hv, lv;
-    hv.x = (uint32_t)h0 | ((uint32_t)h1 << 16);
-    hv.y = (uint32_t)h2 | ((uint32_t)h3 << 16);
-    lv.x = (uint32_t)l0 | ((uint32_t)l1 << 16);
-    lv.y = (uint32_t)l2 | ((uint32_t)l3 << 16);
+    split_hilo2(v.x, v.y, hv.x, lv.x);
+    split_hilo2(v.z, v.w, hv.y, lv.y);
     *(uint2*)((bf16_t*)o.p0 + i) = hv;
     *(uint2*)((bf16_t*)o.p1 + i) = lv;
   } else {
     uint2 hv;
-    hv.x = (uint32_t)f2bf(v.x) | ((uint32_t)f2bf(v.y) << 16);
-    hv.y = (uint32_t)f2bf(v.z) | ((uint32_t)f2bf(v.w) << 16);
+    hv.x = pack_bf16x2(v.x, v.y);
+    hv.y = pack_bf16x2(v.z, v.w);
     *(uint2*)((bf16_t*)o.p0 + i) = hv;
   }
 }

@@ -181,7 +181,7 @@ __device__ __forceinline__ void run_epilogue(const float* Cs, int ldc, int m0, i
       const int phys = e.block_table[(size_t)b * e.max_pages + lp];
       if (phys < 0 || phys >= e.n_pages) continue;
       const float x0 = Cs[r * ldc + hb * d + j], x1 = Cs[r * ldc + hb * d + j + hd];
-      TP* chunk = (TP*)e.pool + ((((size_t)phys * e.n_layers + l) * 2 + kv) * nkv + m) * (size_t)(16 * d);
+      TP* chunk = (TP*)e.pool + ((((size_t)l * nkv + m) * e.n_pages + phys) * 2 + kv) * (size_t)(16 * d);
       if (kv == 0) {
         const float2 cs = e.rope_cs[(size_t)row * hd + j];
         const float y0 = x0 * cs.x - x1 * cs.y, y1 = x1 * cs.x + x0 * cs.y;

@@ -80,11 +80,15 @@ struct AttnParams {
   int batch, B, nq, nkv, d, n_layers, layer;
   float scale;
   int n_splits, pps;      // context splits and pages per split (pps even)
-  float* part_o;          // [(n_splits + 1), M*nq, d]
-  float* part_lse;        // [(n_splits + 1), M*nq]
+  float* part_o;          // [n_splits, M*nq, d] normalised partial outputs
+  float* part_lse;        // [n_splits, M*nq] their log-sum-exp
+  bf16_t* q_hi;           // [batch, nkv, g*B, d] rotated queries, hi plane (bf16 pools)
+  bf16_t* q_lo;           // same, lo plane
 };
+// Context splits -> partials (no launch when there is no context).
 hipError_t launch_attention(const AttnParams& p, int wdtype, hipStream_t s, void (*mark)(int, hipStream_t));
-hipError_t launch_attn_combine(const AttnParams& p, ActOut out, hipStream_t s);
+// In-block keys + merge with the partials -> attention output as GEMM operand.
+hipError_t launch_attn_finish(const AttnParams& p, ActOut out, hipStream_t s);
 
 // Elementwise and bookkeeping kernels.
 hipError_t launch_rope_table_block(const int* ctx_len, int ctx_cap, int batch, int B, int d,
