@@ -91,7 +91,7 @@ def forward_hidden(cfg, W, pools, ctx_len, tau):
     bt, B = tau.shape
     ctx_len = np.asarray(ctx_len, dtype=np.int64)
     pos = ctx_len[:, None] + np.arange(B)[None, :]            # [bt, B]
-    h = np.asarray(W["embed"], F64)[tau]                       # [bt, B, H]
+    h = np.asarray(np.asarray(W["embed"])[tau], F64)           # [bt, B, H] (rows gathered, then widened)
     scale = 1.0 / np.sqrt(d)
     nkvd = nkv * d
     for l in range(L):
@@ -142,8 +142,11 @@ def _top2_gap(x):
 
 
 def draft_block(cfg, W, pools, ctx_len, block_size, n_steps, temperature=0.0, seed=0,
-                want_logits=True):
+                want_logits=True, seq_ids=None):
     """Denoise one [MASK] block per sequence in n_steps forwards.
+
+    seq_ids: batch index of each row in the Philox counter (default 0..bt-1),
+    so a subset of a batch can be redrawn with the noise it had in the batch.
 
     Returns a dict with
       tokens [bt, B]            committed tokens,
@@ -175,7 +178,8 @@ def draft_block(cfg, W, pools, ctx_len, block_size, n_steps, temperature=0.0, se
             zr = z[r]
             if temperature > 0:
                 zt = zr / temperature
-                score = zt + gumbel_noise(seed, b, s, i, V)
+                sid = b if seq_ids is None else int(seq_ids[b])
+                score = zt + gumbel_noise(seed, sid, s, i, V)
                 c = int(np.argmax(score))           # first maximum = lowest index
                 conf[b, s, i] = zt[c] - logsumexp(zt)
             else:

@@ -1,0 +1,348 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times.  Where the oracle cannot afford the whole batch it checks
+sampled sequences (the sequences of a batch are independent); loops check
+every step.  Near-ties (top-2 or commit-boundary gap below 1e-3) are excluded
+and counted, never hidden."""
+import time
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_diffusion_drafter_injection_amd import binding as Bn
+from block_diffusion_drafter_injection_amd import synth
+from gpu_util import (TIE, Drafter, alloc_pool, compare_draft, compare_pool_entries, ctx_tensor, f64, pack_pool,
+                      page_plan, unpack_pool, verify)
+
+pytestmark = pytest.mark.gpu
+
+
+def np_weights32(W):
+    """Exact stored weight values as float32 numpy arrays (the oracle widens per use)."""
+    out = {}
+    for k, v in W.items():
+        out[k] = [t.float().cpu().numpy() for t in v] if isinstance(v, list) else v.float().cpu().numpy()
+    return out
+
+
+def pack_contiguous(dims, pool, n_pages, first_page, K, V):
+    """Write logical K, V [L, T, n_kv, d] into consecutive physical pages starting at first_page."""
+    L, nkv, d = dims.n_layers, dims.n_kv_heads, dims.head_dim
+    T = K.shape[1]
+    npg = (T + 15) // 16
+    pad = npg * 16 - T
+    if pad:
+        K = torch.cat([K, torch.zeros(L, pad, nkv, d, dtype=K.dtype, device=K.device)], 1)
+        V = torch.cat([V, torch.zeros(L, pad, nkv, d, dtype=V.dtype, device=V.device)], 1)
+    p6 = pool.view(L, nkv, n_pages, 2, 16, d)
+    p6[:, :, first_page:first_page + npg, 0] = K.view(L, npg, 16, nkv, d).permute(0, 3, 1, 2, 4).to(pool.dtype)
+    v6 = pool.view(L, nkv, n_pages, 2, d, 16)
+    v6[:, :, first_page:first_page + npg, 1] = V.view(L, npg, 16, nkv, d).permute(0, 3, 1, 4, 2).to(pool.dtype)
+
+
+def log(msg):
+    print(msg, flush=True)
+
+
+def test_qwen3_4b_shape_end_to_end():
+    """Batch 1, block 8, context 2048: inject (whole pool vs oracle), draft on each side's own
+    pool, greedy verify on identical target logits."""
+    wl = synth.WORKLOADS["qwen3_4b_shape_b8"]
+    d, B, S, ctx = wl.dims, wl.block_size, wl.n_steps, 2048
+    t0 = time.time()
+    W = synth.make_weights(d, wl.seed, "cuda")
+    table, n_pages = page_plan([ctx], 0, seed=11)
+    tab = torch.from_numpy(table).cuda()
+    pool = alloc_pool(d, n_pages)
+    hid = synth.make_hiddens(d, ctx, wl.seed * 1000, "cuda")
+    dr = Drafter(d, W, max_batch=1, block_size=B, max_ctx=ctx, max_inject=1024)
+    seq = torch.zeros(ctx, dtype=torch.int32, device="cuda")
+    pos = torch.arange(ctx, dtype=torch.int32, device="cuda")
+    dr.inject(hid, seq, pos, pool, n_pages, tab, 1)
+    tok, lg, cf = dr.draft(pool, n_pages, tab, ctx_tensor([ctx]), ctx, B, S)
+    torch.cuda.synchronize()
+    log(f"gpu done {time.time() - t0:.1f}s")
+    Wn = np_weights32(W)
+    Ko, Vo = oracle.inject(d, Wn, f64(hid), np.arange(ctx))
+    K, V = unpack_pool(d, pool, n_pages, table, 0, ctx)
+    compare_pool_entries(K, Ko, "bf16", "K")
+    compare_pool_entries(V, Vo, "bf16", "V")
+    log(f"inject compared {time.time() - t0:.1f}s")
+    res = oracle.draft_block(d, Wn, [(Ko, Vo)], [ctx], B, S)
+    out = compare_draft(d, S, res, tok.cpu().numpy(), f64(lg), f64(cf))
+    log(f"draft: {out} {time.time() - t0:.1f}s")
+    zt = synth.make_greedy_target_logits(torch.from_numpy(res["tokens"]), d.vocab, wl.p_match, seed=7)
+    acc, o = verify(zt.cuda(), torch.from_numpy(res["tokens"].astype(np.int32)).cuda())
+    acc_o, out_o = oracle.verify_greedy(zt.numpy(), res["tokens"])
+    assert acc.cpu().numpy().tolist() == acc_o.tolist() and np.array_equal(o.cpu().numpy(), out_o)
+
+
+def test_qwen3_8b_shape_batch32_sampled():
+    """Batch 32, block 16, context 4096 each, as the benchmark launches it; the oracle
+    drafts two of the 32 sequences on the same pool contents."""
+    wl = synth.WORKLOADS["qwen3_8b_shape_b16_bs32"]
+    d, bt, B, S, ctx = wl.dims, wl.batch, wl.block_size, wl.n_steps, 4096
+    t0 = time.time()
+    W = synth.make_weights(d, wl.seed, "cuda")
+    n_pages = bt * ctx // 16 + 2
+    pool = alloc_pool(d, n_pages)
+    perm = torch.randperm(bt, generator=torch.Generator().manual_seed(5)).tolist()
+    table = np.zeros((bt, ctx // 16), dtype=np.int32)
+    sample = [3, 22]
+    host_pools = {}
+    for b in range(bt):
+        first = 1 + perm[b] * (ctx // 16)            # sequences placed out of order, page 0 unused
+        table[b] = np.arange(first, first + ctx // 16)
+        K, V = synth.make_pool_values(d, ctx, 100 + b, "cuda")
+        pack_contiguous(d, pool, n_pages, first, K, V)
+        if b in sample:
+            host_pools[b] = (f64(K), f64(V))
+        del K, V
+    tab = torch.from_numpy(table).cuda()
+    dr = Drafter(d, W, max_batch=bt, block_size=B, max_ctx=ctx, max_inject=1024)
+    tok, lg, cf = dr.draft(pool, n_pages, tab, ctx_tensor([ctx] * bt), ctx, B, S)
+    torch.cuda.synchronize()
+    log(f"gpu draft done {time.time() - t0:.1f}s")
+    Wn = np_weights32(W)
+    res = oracle.draft_block(d, Wn, [host_pools[b] for b in sample], [ctx] * len(sample), B, S)
+    out = compare_draft(d, S, res, tok.cpu().numpy()[sample], f64(lg[sample]), f64(cf[sample]))
+    log(f"draft sampled {sample}: {out} {time.time() - t0:.1f}s")
+
+
+def test_qwen3_8b_shape_injection_sampled():
+    """The 8B-shape injection path (fused-feature K = 20480, layer-batched KV N = 10240,
+    split-K) on a ragged token count, against the oracle."""
+    wl = synth.WORKLOADS["qwen3_8b_shape_b16_bs32"]
+    d = wl.dims
+    W = synth.make_weights(d, wl.seed, "cuda")
+    n, p0 = 300, 1000
+    lp0, lp1 = p0 // 16, (p0 + n - 1) // 16 + 1          # logical pages holding the tokens
+    n_pages = lp1 - lp0 + 3
+    perm = np.random.default_rng(12).permutation(n_pages).astype(np.int32)
+    table = np.full((1, lp1), -1, dtype=np.int32)        # pages below lp0 unmapped (skipped if touched)
+    table[0, lp0:lp1] = perm[:lp1 - lp0]
+    tab = torch.from_numpy(table).cuda()
+    pool = alloc_pool(d, n_pages)
+    hid = synth.make_hiddens(d, n, 77, "cuda")
+    dr = Drafter(d, W, max_batch=1, block_size=16, max_ctx=p0 + n, max_inject=128)
+    dr.inject(hid, torch.zeros(n, dtype=torch.int32, device="cuda"),
+              torch.arange(p0, p0 + n, dtype=torch.int32, device="cuda"), pool, n_pages, tab, 1)
+    torch.cuda.synchronize()
+    Wn = np_weights32(W)
+    Ko, Vo = oracle.inject(d, Wn, f64(hid), np.arange(p0, p0 + n))
+    readable = np.where(table < 0, 0, table)
+    K, V = unpack_pool(d, pool, n_pages, readable, 0, p0 + n)
+    compare_pool_entries(K[:, p0:], Ko, "bf16", "K")
+    compare_pool_entries(V[:, p0:], Vo, "bf16", "V")
+
+
+def test_longctx_temperature1_sampled():
+    """Contexts uniform in [16384, 32768], block 16, Gumbel-max drafting at T = 1; the oracle
+    redraws the shortest and the longest sequence with the same Philox noise."""
+    wl = synth.WORKLOADS["longctx_sampled_8b_shape_b16_bs32"]
+    d, bt, B, S, T = wl.dims, wl.batch, wl.block_size, wl.n_steps, wl.temperature
+    ctx = synth.context_lengths(wl).tolist()
+    t0 = time.time()
+    W = synth.make_weights(d, wl.seed, "cuda")
+    pages = [(c + 15) // 16 for c in ctx]
+    n_pages = sum(pages) + 1
+    pool = alloc_pool(d, n_pages)
+    table = np.zeros((bt, max(pages)), dtype=np.int32)
+    sample = [int(np.argmin(ctx)), int(np.argmax(ctx))]
+    host_pools = {}
+    nxt = 1
+    for b in range(bt):
+        table[b, :pages[b]] = np.arange(nxt, nxt + pages[b])
+        K, V = synth.make_pool_values(d, ctx[b], 300 + b, "cuda")
+        pack_contiguous(d, pool, n_pages, nxt, K, V)
+        if b in sample:
+            host_pools[b] = (f64(K), f64(V))
+        del K, V
+        nxt += pages[b]
+    tab = torch.from_numpy(table).cuda()
+    dr = Drafter(d, W, max_batch=bt, block_size=B, max_ctx=max(ctx))
+    tok, lg, cf = dr.draft(pool, n_pages, tab, ctx_tensor(ctx), max(ctx), B, S, T, seed=2024)
+    torch.cuda.synchronize()
+    log(f"gpu draft done {time.time() - t0:.1f}s, ctx {min(ctx)}..{max(ctx)}")
+    Wn = np_weights32(W)
+    log(f"oracle start {time.time() - t0:.1f}s")
+    res = oracle.draft_block(d, Wn, [host_pools[b] for b in sample], [ctx[b] for b in sample], B, S,
+                             temperature=T, seed=2024, seq_ids=sample)
+    out = compare_draft(d, S, res, tok.cpu().numpy()[sample], f64(lg[sample]), f64(cf[sample]))
+    log(f"T=1 draft sampled {sample}: {out} {time.time() - t0:.1f}s")
+
+
+# ---------------------------------------------------------------------------
+# Incremental injection loop with prefix sharing: inject the a+1 accepted
+# tokens of every sequence, draft a block, verify it, for many steps.
+
+def loop_hiddens(dims, ctx0, grow, shared, group, seed, device):
+    """Target hidden rows of every sequence by position; the first `shared` positions
+    are common to each group of `group` sequences (a shared prompt prefix)."""
+    rows = []
+    for b, c in enumerate(ctx0):
+        h = synth.make_hiddens(dims, c + grow, seed * 1000 + b, device)
+        if shared:
+            h[:shared] = synth.make_hiddens(dims, shared, seed * 1000 + 500 + b // group, device)
+        rows.append(h)
+    return rows
+
+
+def target_logits_for(tokens, vocab, p, seed, step):
+    return synth.make_greedy_target_logits(torch.as_tensor(tokens), vocab, p, seed=seed * 100 + step)
+
+
+def run_loop_gpu(dims, W, ctx0, hid, steps, B, S, p, seed, shared, group):
+    bt = len(ctx0)
+    grow = (steps + 1) * (B + 1)
+    table, n_pages = page_plan(ctx0, grow, seed=seed,
+                               shared=[(list(range(g, min(g + group, bt))), shared // 16)
+                                       for g in range(0, bt, group)] if shared else None)
+    tab = torch.from_numpy(table).cuda()
+    pool = alloc_pool(dims, n_pages)
+    dr = Drafter(dims, W, max_batch=bt, block_size=B, max_ctx=max(ctx0) + grow, max_inject=1024)
+    # initial contexts: a group's shared prefix is injected once, by its first sequence
+    seqs, poss, rows = [], [], []
+    for b, c in enumerate(ctx0):
+        start = shared if (shared and b % group) else 0
+        seqs += [b] * (c - start)
+        poss += list(range(start, c))
+        rows.append(hid[b][start:c])
+    dr.inject(torch.cat(rows), torch.tensor(seqs, dtype=torch.int32, device="cuda"),
+              torch.tensor(poss, dtype=torch.int32, device="cuda"), pool, n_pages, tab, bt)
+    ctx = list(ctx0)
+    accs, toks = [], []
+    for st in range(steps):
+        tok, _, _ = dr.draft(pool, n_pages, tab, ctx_tensor(ctx), max(ctx0) + grow, B, S, want_logits=False)
+        zt = target_logits_for(tok.cpu(), dims.vocab, p, seed, st).cuda()
+        acc, out = verify(zt, tok)
+        a = acc.cpu().numpy()
+        toks.append(tok.cpu().numpy())
+        accs.append(a)
+        seqs = [b for b in range(bt) for _ in range(int(a[b]) + 1)]
+        poss = [ctx[b] + k for b in range(bt) for k in range(int(a[b]) + 1)]
+        new = torch.cat([hid[b][ctx[b]:ctx[b] + int(a[b]) + 1] for b in range(bt)])
+        dr.inject(new, torch.tensor(seqs, dtype=torch.int32, device="cuda"),
+                  torch.tensor(poss, dtype=torch.int32, device="cuda"), pool, n_pages, tab, bt)
+        ctx = [ctx[b] + int(a[b]) + 1 for b in range(bt)]
+    torch.cuda.synchronize()
+    return dict(acc=np.array(accs), tok=np.array(toks), ctx=ctx, pool=pool, table=table, n_pages=n_pages, dr=dr)
+
+
+def run_loop_oracle(dims, Wn, ctx0, hid_np, steps, B, S, p, seed, only=None):
+    """The same loop on the oracle, each sequence with its own pool; `only` limits it to a
+    subset of sequences (independent of the others)."""
+    idx = list(range(len(ctx0))) if only is None else list(only)
+    pools = {b: oracle.inject(dims, Wn, hid_np[b][:ctx0[b]], np.arange(ctx0[b])) for b in idx}
+    ctx = {b: ctx0[b] for b in idx}
+    accs, toks, flags = [], [], []
+    for st in range(steps):
+        res = oracle.draft_block(dims, Wn, [pools[b] for b in idx], [ctx[b] for b in idx], B, S, want_logits=False)
+        tok = res["tokens"]
+        flag = np.zeros(len(idx), dtype=bool)
+        for r in range(len(idx)):
+            for s_ in range(S):
+                now = np.nonzero(res["committed_at"][r] == s_)[0]
+                if any(res["gap"][r, s_, i] < TIE for i in now) or (s_ < S - 1 and res["boundary_gap"][r, s_] < TIE):
+                    flag[r] = True
+        full = np.zeros((len(ctx0), B), dtype=np.int64)
+        full[idx] = tok
+        zt = target_logits_for(torch.from_numpy(full), dims.vocab, p, seed, st).numpy()[idx]
+        acc, _ = oracle.verify_greedy(zt, tok)
+        accs.append(acc)
+        toks.append(tok)
+        flags.append(flag)
+        for r, b in enumerate(idx):
+            n = int(acc[r]) + 1
+            Kn, Vn = oracle.inject(dims, Wn, hid_np[b][ctx[b]:ctx[b] + n], np.arange(ctx[b], ctx[b] + n))
+            pools[b] = (np.concatenate([pools[b][0], Kn], 1), np.concatenate([pools[b][1], Vn], 1))
+            ctx[b] += n
+    return dict(acc=np.array(accs), tok=np.array(toks), flags=np.array(flags), idx=idx)
+
+
+def compare_loops(g, o, log_every=16):
+    """Acceptance lengths bit-exact per step; a sequence whose oracle draft hits a near-tie
+    may legitimately diverge, and is dropped from that step on if it does."""
+    idx = o["idx"]
+    alive = np.ones(len(idx), dtype=bool)
+    dropped = compared = 0
+    for st in range(o["acc"].shape[0]):
+        for r, b in enumerate(idx):
+            if not alive[r]:
+                continue
+            compared += 1
+            same = np.array_equal(g["tok"][st][b], o["tok"][st][r]) and g["acc"][st][b] == o["acc"][st][r]
+            if not same:
+                assert o["flags"][st][r], f"step {st} seq {b}: GPU {g['tok'][st][b]} a={g['acc'][st][b]} " \
+                                          f"oracle {o['tok'][st][r]} a={o['acc'][st][r]} without a near-tie"
+                alive[r] = False
+                dropped += 1
+    return dict(steps=int(o["acc"].shape[0]), seqs=len(idx), pairs_compared=compared,
+                pairs_total=int(o["acc"].shape[0]) * len(idx), dropped_after_near_tie=dropped,
+                flagged_pairs=int(o["flags"].sum()), mean_accept=float(o["acc"].mean()))
+
+
+def test_incremental_loop_small_model_all_sequences():
+    """The incremental workload's structure at the small shape: 32 sequences, lognormal
+    contexts (scaled down 16x), groups of 4 sharing a 32-token prefix, block 8, 64 steps,
+    acceptance lengths of every sequence at every step against the oracle."""
+    dims = synth.small_dims()
+    wl = synth.WORKLOADS["incremental_8b_shape_b8_bs32"]
+    B, S, steps, p, seed = wl.block_size, wl.n_steps, wl.loop_steps, wl.p_match, 41
+    ctx0 = [max(48, int(c) // 16) for c in synth.context_lengths(wl).tolist()]
+    shared, group = 32, wl.group_size
+    W = synth.make_weights(dims, seed, "cuda")
+    hid = loop_hiddens(dims, ctx0, (steps + 1) * (B + 1), shared, group, seed, "cuda")
+    t0 = time.time()
+    g = run_loop_gpu(dims, W, ctx0, hid, steps, B, S, p, seed, shared, group)
+    log(f"gpu loop {time.time() - t0:.1f}s")
+    Wn = np_weights32(W)
+    o = run_loop_oracle(dims, Wn, ctx0, [f64(h) for h in hid], steps, B, S, p, seed)
+    out = compare_loops(g, o)
+    log(f"loop: {out} {time.time() - t0:.1f}s")
+    # every divergence happened at a flagged near-tie (asserted in compare_loops); most
+    # (step, sequence) pairs are still compared bit-exactly before one occurs
+    assert out["pairs_compared"] >= out["pairs_total"] // 4
+
+
+def test_incremental_loop_8b_shape():
+    """The incremental workload at the Qwen3-8B shape: 32 sequences, lognormal contexts in
+    [512, 8192], 8 groups of 4 sharing a 512-token prefix (32 shared pages), block 8, 64
+    steps on the GPU.  Checked: acceptance in [0, B] every step; the pool after 64 steps of
+    incremental injection is bit-identical to a one-shot injection of every final prefix;
+    the oracle replays the first steps of the two shortest sequences."""
+    wl = synth.WORKLOADS["incremental_8b_shape_b8_bs32"]
+    d, B, S, steps, p, seed = wl.dims, wl.block_size, wl.n_steps, wl.loop_steps, wl.p_match, wl.seed
+    ctx0 = synth.context_lengths(wl).tolist()
+    shared, group = wl.shared_prefix, wl.group_size
+    t0 = time.time()
+    W = synth.make_weights(d, seed, "cuda")
+    hid = loop_hiddens(d, ctx0, (steps + 1) * (B + 1), shared, group, seed, "cuda")
+    g = run_loop_gpu(d, W, ctx0, hid, steps, B, S, p, seed, shared, group)
+    log(f"gpu loop {time.time() - t0:.1f}s, mean accept {g['acc'].mean():.2f}")
+    assert np.all((g["acc"] >= 0) & (g["acc"] <= B))
+    # one-shot re-injection of every final prefix into a fresh pool with the same table
+    n_pages, table = g["n_pages"], g["table"]
+    fresh = alloc_pool(d, n_pages)
+    seqs, poss, rows = [], [], []
+    for b, c in enumerate(g["ctx"]):
+        start = shared if b % group else 0
+        seqs += [b] * (c - start)
+        poss += list(range(start, c))
+        rows.append(hid[b][start:c])
+    g["dr"].inject(torch.cat(rows), torch.tensor(seqs, dtype=torch.int32, device="cuda"),
+                   torch.tensor(poss, dtype=torch.int32, device="cuda"), fresh, n_pages,
+                   torch.from_numpy(table).cuda(), len(ctx0))
+    torch.cuda.synchronize()
+    used = np.unique(table[table >= 0])
+    p5a = g["pool"].view(d.n_layers, d.n_kv_heads, n_pages, -1)[:, :, used].view(torch.int16)
+    p5b = fresh.view(d.n_layers, d.n_kv_heads, n_pages, -1)[:, :, used].view(torch.int16)
+    # slots past a sequence's final length stay NaN-poisoned in both pools
+    assert torch.equal(p5a, p5b), "incremental pool differs from one-shot pool"
+    log(f"pool bitwise equal {time.time() - t0:.1f}s")
+    Wn = np_weights32(W)
+    only = list(np.argsort(ctx0)[:2])
+    o = run_loop_oracle(d, Wn, ctx0, {b: f64(hid[b]) for b in only}, 2, B, S, p, seed, only=only)
+    out = compare_loops(g, o)
+    log(f"oracle replay: {out} {time.time() - t0:.1f}s")
