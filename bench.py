@@ -35,8 +35,38 @@ def parse():
     ap.add_argument("--roofline-kernel", default="auto",
                     help="kernel class timed for the roofline object (auto: the one with the largest time)")
     ap.add_argument("--cpu-baseline", type=int, default=1, help="time the fp64 oracle on a bounded sample")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="after the timed steps, run one plain device copy of COPY_BYTES (for HBM counter scaling)")
+    ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="turn rocprofv3 csv output into profiles/ summaries and exit")
     ap.add_argument("--seed", type=int, default=0)
     return ap.parse_args()
+
+
+COPY_BYTES = 1 << 29          # 512 MiB read + 512 MiB written by the calibration copy
+# kernel class -> name pattern of the kernel it times (rocprofv3 kernel names)
+KERNEL_NAMES = {
+    "attn": "attn_ctx_mfma_kernel",
+    "gemm_qkv": "gemm_dma_kernel<2, 0>",
+    "gemm_o": "gemm_dma_kernel<2, 1>",
+    "gemm_down": "gemm_dma_kernel<2, 1>",
+    "gemm_gateup": "gemm_dma_kernel<2, 2>",
+    "lmhead": "gemm_dma_kernel<1, 3>",
+}
+KERNEL_SOURCES = ["common.h", "kernels.h", "gemm.hip", "attention.hip", "elementwise.hip", "verify.hip", "api.cpp"]
+
+
+def source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "block_diffusion_drafter_injection_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_file(workload, cls):
+    return os.path.join(ROOT, "profiles", f"traffic_{cls}_{workload}.json")
 
 
 def work_per_class(dims, bt, B, S, ctx, n_new):
@@ -68,6 +98,9 @@ def work_per_class(dims, bt, B, S, ctx, n_new):
 
 def main():
     a = parse()
+    if a.summarize:
+        summarize(*a.summarize)
+        return
     if a.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU; multi-GPU runs are not part of it "
                                    "(the draft step shards by sequence with no exchange)", "n_gpus": a.gpus}))
@@ -213,6 +246,13 @@ def main():
     kms, kn = Bn.dflash_prof_collect()
     Bn.dflash_prof_select("none")
 
+    if a.copy_calibration:
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     ms_step = float(np.mean(hot))
     accepted = float(np.mean([np.sum(x + 1) for x in accs]))
     value = accepted / (ms_step / 1e3)
@@ -226,7 +266,7 @@ def main():
             "achieved": round(achieved / (1e9 if unit == "byte" else 1e12), 2),
             "peak": round(peak / (1e9 if unit == "byte" else 1e12), 1),
             "unit": "GB/s" if unit == "byte" else "TFLOP/s",
-            "frac": round(achieved / peak, 4), "traffic": None,
+            "frac": round(achieved / peak, 4), "traffic": load_traffic(wl.name, cls),
             "launches": kn, "avg_launch_us": round(kms * 1e3 / max(kn, 1), 2)}
 
     res = {
@@ -250,9 +290,106 @@ def main():
     print(json.dumps(res))
 
 
-def cpu_baseline(dims, W, wl, B, S, ctx):
-    """The fp64 oracle, as it stands, on one sequence of the workload: inject 4
-    new tokens, draft one block, verify it.  Throughput = accepted tokens / time."""
+def load_traffic(workload, cls):
+    """HBM bytes per launch of the kernel from the committed counter summary, or None if
+    there is none or the kernel sources changed since the counters were taken."""
+    f = traffic_file(workload, cls)
+    if not os.path.exists(f):
+        return None
+    with open(f) as fh:
+        t = json.load(fh)
+    if t.get("source_hash") != source_hash():
+        return None
+    return t["bytes_per_launch"]
+
+
+def _read_csv(path):
+    import csv
+    with open(path) as fh:
+        return list(csv.DictReader(fh))
+
+
+def summarize(trace_dir, fetch_dir, write_dir):
+    """profiles/ summaries from rocprofv3 csv output: kernel time table of the benchmark run,
+    and HBM traffic per launch of each timed kernel class, scaled by the calibration copy."""
+    import glob
+    import numpy as np
+    wl_name = parse_workload_from(trace_dir)
+    stats = _read_csv(glob.glob(os.path.join(trace_dir, "*kernel_stats.csv"))[0])
+    counters = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = _read_csv(glob.glob(os.path.join(d, "*counter_collection.csv"))[0])
+        per = {}
+        for r in rows:
+            if r["Counter_Name"] != name:
+                continue
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        counters[name] = per
+    copy_name = [k for k in counters["FETCH_SIZE"] if "copy" in k.lower() and "bfloat16" not in k.lower()]
+    big = None
+    for k in copy_name:
+        vals = counters["FETCH_SIZE"][k]
+        if big is None or max(vals) > big[1]:
+            big = (k, max(vals))
+    fetch_scale = COPY_BYTES / (big[1] * 1024.0)
+    wvals = counters["WRITE_SIZE"].get(big[0], [0.0])
+    write_scale = COPY_BYTES / (max(wvals) * 1024.0) if max(wvals) > 0 else None
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    h = source_hash()
+    lines = [f"# rocprofv3 kernel statistics, {wl_name}", "",
+             "Command (run from the repository root, output csv):", "",
+             "    rocprofv3 --kernel-trace --stats --output-format csv -d <TRACE_DIR> -o run -- "
+             "python bench.py --steps 5 --warmup 2 --cpu-baseline 0", "",
+             f"Kernel sources hash: {h}", "",
+             "| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:20]:
+        nm = r["Name"].replace("dflash::", "")
+        nm = nm.split("(")[0] if "dflash" in r["Name"] else nm[:60]
+        lines.append(f"| `{nm}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.2f} | {float(r['Percentage']):.1f} |")
+    with open(os.path.join(ROOT, "profiles", f"kernel_stats_{wl_name}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    tl = [f"# HBM traffic per launch, {wl_name}", "",
+          "Commands (repository root, csv output):", "",
+          "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -o p -- "
+          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --copy-calibration 1",
+          "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -o p -- "
+          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --copy-calibration 1",
+          "    python bench.py --summarize <TRACE_DIR> <FETCH_DIR> <WRITE_DIR>", "",
+          f"Calibration: a {COPY_BYTES >> 20} MiB device copy (`{big[0][:60]}`) reads FETCH_SIZE = "
+          f"{big[1]:.0f} KiB -> fetch scale {fetch_scale:.4f}; WRITE_SIZE scale "
+          f"{write_scale if write_scale is None else round(write_scale, 4)}.", "",
+          f"Kernel sources hash: {h}", "",
+          "| class | kernel | FETCH KiB/launch | WRITE KiB/launch | scaled MB/launch |", "|---|---|---|---|---|"]
+    for cls, pat in KERNEL_NAMES.items():
+        ks = [k for k in counters["FETCH_SIZE"] if pat in k]
+        if not ks:
+            continue
+        f = float(np.mean([v for k in ks for v in counters["FETCH_SIZE"][k]]))
+        w = float(np.mean([v for k in ks for v in counters["WRITE_SIZE"].get(k, [0.0])]))
+        by = f * 1024 * fetch_scale + w * 1024 * (write_scale or 1.0)
+        tl.append(f"| {cls} | `{pat}` | {f:.0f} | {w:.0f} | {by / 1e6:.1f} |")
+        with open(traffic_file(wl_name, cls), "w") as fh:
+            json.dump({"workload": wl_name, "class": cls, "kernel": pat, "fetch_kib": f, "write_kib": w,
+                       "fetch_scale": fetch_scale, "write_scale": write_scale, "bytes_per_launch": round(by),
+                       "source_hash": h}, fh, indent=1)
+    with open(os.path.join(ROOT, "profiles", f"hbm_traffic_{wl_name}.md"), "w") as fh:
+        fh.write("\n".join(tl) + "\n")
+    print("\n".join(lines + [""] + tl))
+
+
+def parse_workload_from(trace_dir):
+    """Workload name recorded by the benchmark run next to the trace (default workload otherwise)."""
+    f = os.path.join(trace_dir, "workload.txt")
+    if os.path.exists(f):
+        return open(f).read().strip()
+    return "qwen3_8b_shape_b16_bs32"
+
+
+def cpu_baseline(dims, W, wl, B, S, ctx, min_seconds=10.0, max_seqs=4):
+    """The fp64 oracle, as it stands, on a bounded sample of the workload: one sequence
+    at a time (inject 4 new tokens, draft one block, verify it) until min_seconds of work
+    or max_seqs sequences.  Throughput = accepted tokens / oracle time."""
     import numpy as np
     import torch
     import oracle
@@ -264,21 +401,25 @@ def cpu_baseline(dims, W, wl, B, S, ctx):
         cores = os.cpu_count()
     Wn = {k: ([t.float().cpu().numpy() for t in v] if isinstance(v, list) else v.float().cpu().numpy())
           for k, v in W.items()}
-    K, V = synth.make_pool_values(dims, ctx, 99, "cpu")
-    K, V = K.double().numpy(), V.double().numpy()
-    x = synth.make_hiddens(dims, 4, 98, "cpu").double().numpy()
-    t0 = time.time()
-    Kn, Vn = oracle.inject(dims, Wn, x, np.arange(ctx, ctx + 4))
-    K = np.concatenate([K, Kn], axis=1)
-    V = np.concatenate([V, Vn], axis=1)
-    r = oracle.draft_block(dims, Wn, [(K, V)], [ctx + 4], B, S, want_logits=False)
-    tok = torch.from_numpy(r["tokens"].astype(np.int32))
-    zt = synth.make_greedy_target_logits(tok, dims.vocab, wl.p_match, seed=5).numpy()
-    acc, _ = oracle.verify_greedy(zt, r["tokens"])
-    dt = time.time() - t0
-    return {"value": round(float(acc[0] + 1) / dt, 4), "unit": "tok/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"1 of {wl.batch} sequences, one step (inject 4 tokens, {S}-step block-{B} draft at "
-                      f"ctx {ctx}, greedy verify), {dt:.1f} s"}
+    spent, accepted, n = 0.0, 0, 0
+    while n < max_seqs and (spent < min_seconds or n == 0):
+        K, V = synth.make_pool_values(dims, ctx, 99 + n, "cpu")
+        K, V = K.double().numpy(), V.double().numpy()
+        x = synth.make_hiddens(dims, 4, 98 + n, "cpu").double().numpy()
+        t0 = time.time()
+        Kn, Vn = oracle.inject(dims, Wn, x, np.arange(ctx, ctx + 4))
+        K = np.concatenate([K, Kn], axis=1)
+        V = np.concatenate([V, Vn], axis=1)
+        r = oracle.draft_block(dims, Wn, [(K, V)], [ctx + 4], B, S, want_logits=False)
+        tok = torch.from_numpy(r["tokens"].astype(np.int32))
+        zt = synth.make_greedy_target_logits(tok, dims.vocab, wl.p_match, seed=5 + n).numpy()
+        acc, _ = oracle.verify_greedy(zt, r["tokens"])
+        spent += time.time() - t0
+        accepted += int(acc[0]) + 1
+        n += 1
+    return {"value": round(accepted / spent, 4), "unit": "tok/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"{n} of {wl.batch} sequences, one step each (inject 4 tokens, {S}-step block-{B} "
+                      f"draft at context {ctx}, greedy verify): {accepted} accepted tokens in {spent:.1f} s"}
 
 
 if __name__ == "__main__":
