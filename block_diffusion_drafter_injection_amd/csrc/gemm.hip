@@ -527,17 +527,18 @@ __global__ __launch_bounds__(256, 2) void gemm_dma_kernel(ActIn a, BRows<bf16_t>
   run_epilogue<KIND, BM, BN, 256, bf16_t>(Cs, C::LDC, m0, n0, M, N, e);
 }
 
-// Sum of the split-K partials of one BM x BN tile, in split order, then the epilogue.
-template <int BM, int BN, int KIND, typename TP>
+// Sum of the split-K partials of RB rows x BN columns (a row slice of one GEMM
+// tile: every epilogue is row-independent), in split order, then the epilogue.
+template <int RB, int BN, int KIND, typename TP>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, int ksplit, int M, int N,
                                                              EpiParams e) {
   constexpr int LDC = BN + 4;
-  __shared__ __attribute__((aligned(16))) float Cs[BM * LDC];
-  const int ntm = (M + BM - 1) / BM;
-  const int tm = blockIdx.x % ntm, tn = blockIdx.x / ntm;
-  const int m0 = tm * BM, n0 = tn * BN;
+  __shared__ __attribute__((aligned(16))) float Cs[RB * LDC];
+  const int nrb = (M + RB - 1) / RB;
+  const int rb = blockIdx.x % nrb, tn = blockIdx.x / nrb;
+  const int m0 = rb * RB, n0 = tn * BN;
   constexpr int C4 = BN / 4;
-  for (int idx = threadIdx.x; idx < BM * C4; idx += 256) {
+  for (int idx = threadIdx.x; idx < RB * C4; idx += 256) {
     const int r = idx / C4, c = (idx - r * C4) * 4;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (m0 + r < M && n0 + c < N) {
@@ -549,7 +550,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, i
     *(float4*)(Cs + r * LDC + c) = acc;
   }
   __syncthreads();
-  run_epilogue<KIND, BM, BN, 256, TP>(Cs, LDC, m0, n0, M, N, e);
+  run_epilogue<KIND, RB, BN, 256, TP>(Cs, LDC, m0, n0, M, N, e);
 }
 
 // ---------------------------------------------------------------------------
@@ -657,8 +658,8 @@ static hipError_t go_mfma(const GemmArgs& g, int ksplit, hipStream_t s) {
                      g.M, g.N, g.K, ksplit, g.part, g.e);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || ksplit == 1) return err;
-  hipLaunchKernelGGL((splitk_reduce_kernel<BM, BN, KIND, bf16_t>), dim3(ntm * ntn), dim3(256), 0, s, g.part, ksplit,
-                     g.M, g.N, g.e);
+  hipLaunchKernelGGL((splitk_reduce_kernel<16, BN, KIND, bf16_t>), dim3((g.M + 15) / 16 * ntn), dim3(256), 0, s,
+                     g.part, ksplit, g.M, g.N, g.e);
   return hipGetLastError();
 }
 
@@ -681,8 +682,8 @@ static hipError_t go_dma(const GemmArgs& g, int ksplit, hipStream_t s) {
                      g.e);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || ksplit == 1) return err;
-  hipLaunchKernelGGL((splitk_reduce_kernel<128, 128, KIND, bf16_t>), dim3(ntm * ntn), dim3(256), 0, s, g.part, ksplit,
-                     g.M, g.N, g.e);
+  hipLaunchKernelGGL((splitk_reduce_kernel<16, 128, KIND, bf16_t>), dim3((g.M + 15) / 16 * ntn), dim3(256), 0, s,
+                     g.part, ksplit, g.M, g.N, g.e);
   return hipGetLastError();
 }
 

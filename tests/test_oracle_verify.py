@@ -1,5 +1,6 @@
 """Pins of the oracle's verification and counter-based sampling (CPU only)."""
 import itertools
+import os
 
 import numpy as np
 import pytest
@@ -128,15 +129,14 @@ def test_sampled_low_temperature_reduces_to_greedy():
 
 
 def test_philox_known_answer_vectors():
-    """Known-answer vectors published with the Random123 library (Salmon et al., SC'11)."""
-    kat = [
-        ([0, 0, 0, 0], [0, 0], [0x6627E8D5, 0xE169C58D, 0xBC57AC4C, 0x9B00DBD8]),
-        ([0xFFFFFFFF] * 4, [0xFFFFFFFF] * 2, [0x408F276D, 0x41C83B0E, 0xA20BC7C6, 0x6D5451FD]),
-        ([0x243F6A88, 0x85A308D3, 0x13198A2E, 0x03707344], [0xA4093822, 0x299F31D0],
-         [0xD16CFE09, 0x94FDCCEB, 0x5001E420, 0x24126EA1]),
-    ]
-    for ctr, key, want in kat:
-        assert oracle.philox4x32_10(ctr, key).tolist() == want
+    """Known-answer vectors published with the Random123 library (Salmon et al., SC'11),
+    stored in tests/golden/philox4x32_10_kat.txt."""
+    path = os.path.join(os.path.dirname(__file__), "golden", "philox4x32_10_kat.txt")
+    rows = [l.split() for l in open(path) if l.strip() and not l.startswith("#")]
+    assert len(rows) == 3
+    for r in rows:
+        w = [int(x, 16) for x in r]
+        assert oracle.philox4x32_10(w[0:4], w[4:6]).tolist() == w[6:10]
 
 
 def test_uniform_map_stays_inside_unit_interval():
