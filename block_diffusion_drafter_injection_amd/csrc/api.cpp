@@ -130,7 +130,7 @@ DraftWS draft_layout(const dflash_config* c, int bt, int B, int ctx_cap) {
   const size_t H = c->hidden, I = c->intermediate, d = c->head_dim, nq = c->n_q_heads, nkv = c->n_kv_heads;
   const size_t el = c->dtype == DFLASH_BF16 ? 2 : 4;  // one plane of an activation operand
   attn_split(bt, (int)nkv, n_qgroups(c, B), ctx_cap, w.ns, w.pps);
-  w.ntiles = (c->vocab + gemm_bn(c->dtype) - 1) / gemm_bn(c->dtype);
+  w.ntiles = (c->vocab + gemm_bn(c->dtype, c->hidden) - 1) / gemm_bn(c->dtype, c->hidden);
   Carve k;
   w.h = k.take(M * H * 4);
   w.u_hi = k.take(M * H * el);

@@ -104,7 +104,7 @@ __device__ __forceinline__ void run_epilogue(const float* Cs, int ldc, int m0, i
       }
     }
     constexpr int TPR = NT / BM;      // threads per row
-    constexpr int GRP = 128;          // columns per partial
+    constexpr int GRP = (BN % 128 == 0) ? 128 : 64;   // columns per partial
     constexpr int CPT = GRP / TPR;    // columns per thread within a group
     static_assert(NT % BM == 0 && GRP % TPR == 0 && BN % GRP == 0, "tile split");
     const int r = tid / TPR, q = tid - r * TPR;
@@ -527,6 +527,153 @@ __global__ __launch_bounds__(256, 2) void gemm_dma_kernel(ActIn a, BRows<bf16_t>
   run_epilogue<KIND, BM, BN, 256, bf16_t>(Cs, C::LDC, m0, n0, M, N, e);
 }
 
+// MFMA GEMM with direct global->LDS loads for large tiles: eight waves (two
+// per SIMD, one workgroup per CU) of (BM/WGM) x (BN/WGN), 32-deep K stages in
+// three LDS buffers, the same 64-byte swizzled rows as gemm_dma_kernel.  A
+// large tile keeps the L1 line lookups per MFMA low (each 1 KiB load touches
+// sixteen lines) and large wave tiles keep the LDS reads per MFMA low.  The
+// epilogue stages 64-row slices of the C tile through LDS and reuses the fused
+// epilogues.
+template <int BM, int BN, int WGM, int WGN, int NP>
+struct Dma8Cfg {
+  static constexpr int NT = 64 * WGM * WGN, NW = WGM * WGN, BK = 32, STAGES = 3;
+  static constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
+  static constexpr int ROWS = NP * BM + BN;          // LDS rows per stage (64 B each)
+  static constexpr int STAGE_BYTES = ROWS * 64;
+  static constexpr int BLOCKS = ROWS / 16;            // 1 KiB load instructions per stage
+  static constexpr int LPT = BLOCKS / NW;             // per wave
+  static constexpr int LDC = BN + 4;
+  static constexpr int SMEM_PIPE = STAGES * STAGE_BYTES;
+  static constexpr int SMEM_EPI = 64 * LDC * 4;
+  static constexpr int SMEM = SMEM_PIPE > SMEM_EPI ? SMEM_PIPE : SMEM_EPI;
+  static_assert(BLOCKS % NW == 0 && WM % 16 == 0 && WN % 16 == 0 && WM == 64, "tile shape");
+  static_assert(SMEM <= 160 * 1024, "LDS");
+  static_assert(LPT <= 63, "vmcnt range");
+};
+
+template <int BM, int BN, int WGM, int WGN, int NP, int KIND>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma8_kernel(ActIn a, BRows<bf16_t> b, int M, int N, int K,
+                                                                       int ksplit, float* part, EpiParams e) {
+  using C = Dma8Cfg<BM, BN, WGM, WGN, NP>;
+  constexpr int BK = C::BK, LPT = C::LPT, FM = C::FM, FN = C::FN, NT = C::NT;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::SMEM];
+
+  const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
+  int t;
+  {
+    const int per = gridDim.x / 8, L = blockIdx.x;
+    t = (per > 0) ? (L & 7) * per + (L >> 3) : L;
+    if (t >= ntm * ntn * ksplit) return;
+  }
+  const int tm = t % ntm, tn = (t / ntm) % ntn, ks = t / (ntm * ntn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nkt = K / BK;
+  const int kt0 = (int)((long long)ks * nkt / ksplit), kt1 = (int)((long long)(ks + 1) * nkt / ksplit);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / WGN, wn = wid - wm * WGN;
+
+  // source pointers of this lane's LPT load blocks (fixed over K)
+  const bf16_t* src[LPT];
+#pragma unroll
+  for (int q = 0; q < LPT; ++q) {
+    const int blk = wid * LPT + q;
+    const int row = blk * 16 + (lane >> 2);
+    const int pc = lane & 3, lc = pc ^ ((row >> 1) & 3);
+    const bf16_t* base;
+    if (row < NP * BM) {
+      const int p = row / BM, r = row - p * BM;
+      const int gr = min(m0 + r, M - 1);
+      base = (const bf16_t*)(p == 0 ? a.p0 : a.p1) + (size_t)gr * a.ld;
+    } else {
+      base = b.row(min(n0 + row - NP * BM, N - 1), BN);
+    }
+    src[q] = base + lc * 8;
+  }
+  const uint32_t lds0 = (uint32_t)(size_t)smem;
+
+#define DMA8_ISSUE(KT, STAGE)                                                                                    \
+  do {                                                                                                           \
+    const int k0_ = (KT) * BK;                                                                                   \
+    _Pragma("unroll") for (int q = 0; q < LPT; ++q) {                                                            \
+      __builtin_amdgcn_global_load_lds(                                                                          \
+          (const __attribute__((address_space(1))) void*)(src[q] + k0_),                                         \
+          (__attribute__((address_space(3))) void*)(size_t)(lds0 + (STAGE) * C::STAGE_BYTES +                   \
+                                                            (wid * LPT + q) * 1024),                             \
+          16, 0, 0);                                                                                             \
+    }                                                                                                            \
+  } while (0)
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nloc = kt1 - kt0;
+  if (nloc > 0) DMA8_ISSUE(kt0, 0);
+  if (nloc > 1) DMA8_ISSUE(kt0 + 1, 1);
+  const int lr = lane & 15, lc = lane >> 4;
+  for (int it = 0; it < nloc; ++it) {
+    if (it + 1 < nloc) wait_vmcnt<LPT>();   // this tile landed; the next may still be in flight
+    else wait_vmcnt<0>();
+    stage_barrier();                         // all lanes' data visible; stage (it+2)%3 is free
+    if (it + 2 < nloc) DMA8_ISSUE(kt0 + it + 2, (it + 2) % 3);
+    const unsigned char* st = smem + (it % 3) * C::STAGE_BYTES;
+    bf16x8 af[NP][FM], bfr[FN];
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int row = p * BM + wm * C::WM + 16 * i + lr;
+        af[p][i] = as_bf16x8(*(const u32x4*)(st + row * 64 + ((lc ^ ((row >> 1) & 3)) << 4)));
+      }
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int row = NP * BM + wn * C::WN + 16 * j + lr;
+      bfr[j] = as_bf16x8(*(const u32x4*)(st + row * 64 + ((lc ^ ((row >> 1) & 3)) << 4)));
+    }
+#pragma unroll
+    for (int p = 0; p < NP; ++p)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[p][i], bfr[j], acc[i][j], 0, 0, 0);
+  }
+#undef DMA8_ISSUE
+  __syncthreads();   // every wave is done with the pipeline buffers
+
+  // epilogue over 64-row slices of the tile (slice sl = the rows of wave row wm == sl)
+  float* Cs = (float*)smem;
+#pragma unroll
+  for (int sl = 0; sl < WGM; ++sl) {
+    if (m0 + sl * 64 >= M) break;
+    if (wm == sl) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            Cs[(16 * i + 4 * lc + q) * C::LDC + wn * C::WN + 16 * j + lr] = acc[i][j][q];
+    }
+    __syncthreads();
+    const int ms = m0 + sl * 64;
+    if (ksplit > 1) {
+      float* dst = part + (size_t)ks * M * N;
+      constexpr int C4 = BN / 4;
+      for (int idx = tid; idx < 64 * C4; idx += NT) {
+        const int r = idx / C4, c = (idx - r * C4) * 4;
+        if (ms + r < M && n0 + c < N)
+          *(float4*)(dst + (size_t)(ms + r) * N + n0 + c) = *(const float4*)(Cs + r * C::LDC + c);
+      }
+    } else {
+      run_epilogue<KIND, 64, BN, NT, bf16_t>(Cs, C::LDC, ms, n0, M, N, e);
+    }
+    __syncthreads();
+  }
+}
+
 // Sum of the split-K partials of RB rows x BN columns (a row slice of one GEMM
 // tile: every epilogue is row-independent), in split order, then the epilogue.
 template <int RB, int BN, int KIND, typename TP>
@@ -606,7 +753,28 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(ActIn a, BRows<float> b, 
 }
 
 // ---------------------------------------------------------------------------
-int gemm_bn(int) { return 128; }   // LM-head partials cover 128 columns each
+// Tile choice per GEMM kind (bf16 weights):
+//   2: 128x128, four 64x64 waves, two workgroups per CU (gemm_dma_kernel)
+//   3: 128x384, eight 64x96 waves      4: 256x256, eight 64x128 waves
+//   5: 128x256, eight 64x64 waves      6: 512x128, eight 64x128 waves
+//   (gemm_dma8_kernel, one workgroup per CU)
+#ifndef DFLASH_T_SWIGLU
+#define DFLASH_T_SWIGLU 3
+#endif
+#ifndef DFLASH_T_LMHEAD
+#define DFLASH_T_LMHEAD 4
+#endif
+#ifndef DFLASH_T_ADD
+#define DFLASH_T_ADD 4
+#endif
+#ifndef DFLASH_T_STORE
+#define DFLASH_T_STORE 4
+#endif
+static int tile_bn(int cfg) { return cfg == 3 ? 384 : cfg == 4 || cfg == 5 ? 256 : 128; }
+static int tile_bm(int cfg) { return cfg == 4 ? 256 : cfg == 6 ? 512 : 128; }
+
+// LM-head partials cover 128 columns each, or 64 when the tile width is not a multiple of 128
+int gemm_bn(int wdtype, int K) { return wdtype && K % 32 == 0 && tile_bn(DFLASH_T_LMHEAD) % 128 ? 64 : 128; }
 
 // Tile configuration and K split of one GEMM.  cfg 0: 128x128 tile, four
 // 64x64 waves, one LDS buffer (two workgroups per CU).  cfg 1: 128x256 tile,
@@ -625,20 +793,39 @@ int gemm_bn(int) { return 128; }   // LM-head partials cover 128 columns each
 GemmPlan gemm_plan(int wdtype, int a_mode, int M, int N, int K, int kind, bool fixed_split) {
   GemmPlan p{0, 1};
   if (wdtype == 0) return p;
-  const int nkt = K / 64;
-  const bool wide = DFLASH_WIDE_TILES && ((kind == EPI_LMHEAD) || (kind == EPI_SWIGLU && (N / 2) % 128 == 0));
-  if (wide && !fixed_split) {
-    p.cfg = 1;
+  int cfg = 2;
+  if (!fixed_split && K % 32 == 0) {
+    if (kind == EPI_SWIGLU) cfg = DFLASH_T_SWIGLU;
+    else if (kind == EPI_LMHEAD) cfg = DFLASH_T_LMHEAD;
+    else if (kind == EPI_ADD) cfg = DFLASH_T_ADD;
+    else if (kind == EPI_STORE) cfg = DFLASH_T_STORE;
+    const bool one_plane = a_mode != ACT_HILO;
+    if (cfg == 6 && !one_plane) cfg = 4;     // 512-row tiles of both planes exceed the LDS
+    // SwiGLU tiles hold BN/2 gate and BN/2 up columns of the same rows
+    if (kind == EPI_SWIGLU && (N / 2) % (tile_bn(cfg) / 2) != 0) cfg = 2;
+  }
+  p.cfg = cfg;
+  if (cfg == 2) {
+    const int nkt = K / 32;
+    const int tn = (N + 127) / 128;
+    const int tiles = (fixed_split ? 1 : (M + 127) / 128) * tn;
+    int ks = (DFLASH_KS_TARGET + tiles - 1) / tiles;
+    ks = std::min(ks, std::max(1, nkt / 4));
+    ks = std::max(ks, 1);
+    if (kind == EPI_LMHEAD) ks = 1;
+    p.ksplit = ks;
     return p;
   }
-  const int tn = (N + 127) / 128;
-  const int tiles = (fixed_split ? 1 : (M + 127) / 128) * tn;
-  int ks = (DFLASH_KS_TARGET + tiles - 1) / tiles;
-  ks = std::min(ks, std::max(1, nkt / 4));
-  ks = std::max(ks, 1);
-  if (kind == EPI_LMHEAD) ks = 1;
-  p.ksplit = ks;
-  if (DFLASH_DMA) p.cfg = 2;
+  // one workgroup per CU: pick the split that minimises rounds per unit of work
+  const int bm = tile_bm(cfg), bn = tile_bn(cfg);
+  const int tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+  const int cap = kind == EPI_LMHEAD ? 1 : std::max(1, K / 32 / 16);
+  const int cus = 256;
+  double best = 1e30;
+  for (int ks = 1; ks <= std::min(cap, 8); ++ks) {
+    const double cost = (double)((tiles * ks + cus - 1) / cus) / ks;
+    if (cost < best - 1e-9) { best = cost; p.ksplit = ks; }
+  }
   (void)a_mode;
   return p;
 }
@@ -687,11 +874,33 @@ static hipError_t go_dma(const GemmArgs& g, int ksplit, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int BM, int BN, int WGM, int WGN, int NP, int KIND>
+static hipError_t go_dma8(const GemmArgs& g, int ksplit, hipStream_t s) {
+  const int ntm = (g.M + BM - 1) / BM, ntn = (g.N + BN - 1) / BN;
+  const int total = ntm * ntn * ksplit;
+  const int grid = (total + 7) / 8 * 8;
+  BRows<bf16_t> b{(const bf16_t*)g.b.b0, (const bf16_t*)g.b.b1, g.b.ldb, g.b.split, g.b.mode};
+  hipLaunchKernelGGL((gemm_dma8_kernel<BM, BN, WGM, WGN, NP, KIND>), dim3(grid), dim3(64 * WGM * WGN), 0, s, g.a, b,
+                     g.M, g.N, g.K, ksplit, g.part, g.e);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || ksplit == 1) return err;
+  hipLaunchKernelGGL((splitk_reduce_kernel<16, BN, KIND, bf16_t>), dim3((g.M + 15) / 16 * ntn), dim3(256), 0, s,
+                     g.part, ksplit, g.M, g.N, g.e);
+  return hipGetLastError();
+}
+
 template <int NP, int KIND>
 static hipError_t go_bf16(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
-  if (p.cfg == 1) return go_mfma<128, 256, 64, 128, NP, 2, KIND>(g, 1, s);
-  if (p.cfg == 2) return go_dma<NP, KIND>(g, p.ksplit, s);
-  return go_mfma<128, 128, 64, 64, NP, 1, KIND>(g, p.ksplit, s);
+  constexpr bool scatter = KIND == EPI_KVSCATTER;
+  switch (p.cfg) {
+    case 2: return go_dma<NP, KIND>(g, p.ksplit, s);
+    case 3: if constexpr (!scatter) return go_dma8<128, 384, 2, 4, NP, KIND>(g, p.ksplit, s); break;
+    case 4: if constexpr (!scatter) return go_dma8<256, 256, 4, 2, NP, KIND>(g, p.ksplit, s); break;
+    case 5: if constexpr (!scatter) return go_dma8<128, 256, 2, 4, NP, KIND>(g, p.ksplit, s); break;
+    case 6: if constexpr (NP == 1 && !scatter) return go_dma8<512, 128, 8, 1, 1, KIND>(g, p.ksplit, s); break;
+    default: break;
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {

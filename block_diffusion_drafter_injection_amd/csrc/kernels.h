@@ -65,7 +65,7 @@ struct GemmPlan {
 GemmPlan gemm_plan(int wdtype, int a_mode, int M, int N, int K, int kind, bool fixed_split);
 size_t gemm_partial_bytes(const GemmPlan& p, int M, int N);
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
-int gemm_bn(int wdtype);       // columns per LM-head partial (partial count = ceil(N / bn))
+int gemm_bn(int wdtype, int K);  // columns per LM-head partial (partial count = ceil(N / bn))
 
 // Attention of the block queries over paged context KV plus in-block keys.
 struct AttnParams {

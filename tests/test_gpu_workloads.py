@@ -230,15 +230,33 @@ def run_loop_gpu(dims, W, ctx0, hid, steps, B, S, p, seed, shared, group):
     return dict(acc=np.array(accs), tok=np.array(toks), ctx=ctx, pool=pool, table=table, n_pages=n_pages, dr=dr)
 
 
-def run_loop_oracle(dims, Wn, ctx0, hid_np, steps, B, S, p, seed, only=None):
+def run_loop_oracle(dims, Wn, ctx0, hid_np, steps, B, S, p, seed, only=None, gpu=None):
     """The same loop on the oracle, each sequence with its own pool; `only` limits it to a
-    subset of sequences (independent of the others)."""
+    subset of sequences (independent of the others).
+
+    With `gpu` (the GPU loop's result) each draft reads the pool the GPU injected, so both
+    drafts see identical inputs.  Pool entries of positions below a sequence's length never
+    change once injected, so the final GPU pool's prefix is the pool of every earlier step.
+    The oracle's own injection is kept alongside and checked against that prefix within the
+    bf16 flip tolerance.  A sequence whose trajectory left the GPU's falls back to its own
+    pool (it is no longer compared)."""
     idx = list(range(len(ctx0))) if only is None else list(only)
     pools = {b: oracle.inject(dims, Wn, hid_np[b][:ctx0[b]], np.arange(ctx0[b])) for b in idx}
+    gkv = {}
+    if gpu is not None:
+        for b in idx:
+            gkv[b] = unpack_pool(dims, gpu["pool"], gpu["n_pages"], gpu["table"], b, int(gpu["ctx"][b]))
+    same_path = {b: gpu is not None for b in idx}
     ctx = {b: ctx0[b] for b in idx}
     accs, toks, flags = [], [], []
     for st in range(steps):
-        res = oracle.draft_block(dims, Wn, [pools[b] for b in idx], [ctx[b] for b in idx], B, S, want_logits=False)
+        draft_pools = []
+        for b in idx:
+            if same_path[b]:
+                draft_pools.append((gkv[b][0][:, :ctx[b]], gkv[b][1][:, :ctx[b]]))
+            else:
+                draft_pools.append(pools[b])
+        res = oracle.draft_block(dims, Wn, draft_pools, [ctx[b] for b in idx], B, S, want_logits=False)
         tok = res["tokens"]
         flag = np.zeros(len(idx), dtype=bool)
         for r in range(len(idx)):
@@ -254,10 +272,18 @@ def run_loop_oracle(dims, Wn, ctx0, hid_np, steps, B, S, p, seed, only=None):
         toks.append(tok)
         flags.append(flag)
         for r, b in enumerate(idx):
+            if same_path[b] and not (np.array_equal(gpu["tok"][st][b], tok[r]) and gpu["acc"][st][b] == acc[r]):
+                same_path[b] = False
             n = int(acc[r]) + 1
             Kn, Vn = oracle.inject(dims, Wn, hid_np[b][ctx[b]:ctx[b] + n], np.arange(ctx[b], ctx[b] + n))
             pools[b] = (np.concatenate([pools[b][0], Kn], 1), np.concatenate([pools[b][1], Vn], 1))
             ctx[b] += n
+    if gpu is not None:
+        for b in idx:
+            if same_path[b]:
+                T = ctx[b]
+                for name, own, got in (("K", pools[b][0], gkv[b][0]), ("V", pools[b][1], gkv[b][1])):
+                    compare_pool_entries(got[:, :T], own[:, :T], dims.dtype, f"seq {b} {name}")
     return dict(acc=np.array(accs), tok=np.array(toks), flags=np.array(flags), idx=idx)
 
 
@@ -298,7 +324,7 @@ def test_incremental_loop_small_model_all_sequences():
     g = run_loop_gpu(dims, W, ctx0, hid, steps, B, S, p, seed, shared, group)
     log(f"gpu loop {time.time() - t0:.1f}s")
     Wn = np_weights32(W)
-    o = run_loop_oracle(dims, Wn, ctx0, [f64(h) for h in hid], steps, B, S, p, seed)
+    o = run_loop_oracle(dims, Wn, ctx0, [f64(h) for h in hid], steps, B, S, p, seed, gpu=g)
     out = compare_loops(g, o)
     log(f"loop: {out} {time.time() - t0:.1f}s")
     # every divergence happened at a flagged near-tie (asserted in compare_loops); most
@@ -343,6 +369,6 @@ def test_incremental_loop_8b_shape():
     log(f"pool bitwise equal {time.time() - t0:.1f}s")
     Wn = np_weights32(W)
     only = list(np.argsort(ctx0)[:2])
-    o = run_loop_oracle(d, Wn, ctx0, {b: f64(hid[b]) for b in only}, 2, B, S, p, seed, only=only)
+    o = run_loop_oracle(d, Wn, ctx0, {b: f64(hid[b]) for b in only}, 2, B, S, p, seed, only=only, gpu=g)
     out = compare_loops(g, o)
     log(f"oracle replay: {out} {time.time() - t0:.1f}s")
