@@ -54,6 +54,12 @@ __device__ __forceinline__ LMPart lm_merge(const LMPart& a, const LMPart& b) {
   return r;
 }
 
+// x / (1 + e^-x) with the hardware exp2 and reciprocal (about 1 ulp each);
+// e^-x overflowing to infinity gives 0, the limit.
+__device__ __forceinline__ float silu_fast(float x) {
+  return x * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-1.4426950408889634f * x));
+}
+
 template <int KIND, int BM, int BN, int NT, typename TP>
 __device__ __forceinline__ void run_epilogue(const float* Cs, int ldc, int m0, int n0, int M, int N,
                                              const EpiParams& e) {
@@ -83,10 +89,10 @@ __device__ __forceinline__ void run_epilogue(const float* Cs, int ldc, int m0, i
       const float4 g = *(const float4*)(Cs + r * ldc + c);
       const float4 u = *(const float4*)(Cs + r * ldc + H2 + c);
       float4 a;
-      a.x = g.x / (1.f + expf(-g.x)) * u.x;
-      a.y = g.y / (1.f + expf(-g.y)) * u.y;
-      a.z = g.z / (1.f + expf(-g.z)) * u.z;
-      a.w = g.w / (1.f + expf(-g.w)) * u.w;
+      a.x = silu_fast(g.x) * u.x;
+      a.y = silu_fast(g.y) * u.y;
+      a.z = silu_fast(g.z) * u.z;
+      a.w = silu_fast(g.w) * u.w;
       act_store4(e.out, row, col, a);
     }
   } else if constexpr (KIND == EPI_LMHEAD) {
@@ -414,6 +420,13 @@ __device__ __forceinline__ void stage_barrier() {
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
+// The same, after this wave's LDS reads have completed: the buffer they read
+// may be refilled by any wave once every wave has passed the barrier.
+__device__ __forceinline__ void lds_reads_done_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
 
 template <int NP, int KIND>
 __global__ __launch_bounds__(256, 2) void gemm_dma_kernel(ActIn a, BRows<bf16_t> b, int M, int N, int K, int ksplit,
@@ -534,9 +547,23 @@ __global__ __launch_bounds__(256, 2) void gemm_dma_kernel(ActIn a, BRows<bf16_t>
 // sixteen lines) and large wave tiles keep the LDS reads per MFMA low.  The
 // epilogue stages 64-row slices of the C tile through LDS and reuses the fused
 // epilogues.
-template <int BM, int BN, int WGM, int WGN, int NP>
+// Scheduling of one pipeline step: the R fragment reads of the next stage are
+// spread over the Q MFMAs of the current one (Q/R MFMAs, then one read), so
+// their LDS traffic overlaps the matrix work instead of following it (MFMAs
+// first: the fragments they use are already in registers).
+template <int R, int Q>
+__device__ __forceinline__ void dma8_interleave() {
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    __builtin_amdgcn_sched_group_barrier(0x008, Q / R, 0);  // Q/R MFMAs
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // one LDS read
+  }
+  if constexpr (Q % R != 0) __builtin_amdgcn_sched_group_barrier(0x008, Q % R, 0);
+}
+
+template <int BM, int BN, int WGM, int WGN, int NP, int STAGES_ = 3>
 struct Dma8Cfg {
-  static constexpr int NT = 64 * WGM * WGN, NW = WGM * WGN, BK = 32, STAGES = 3;
+  static constexpr int NT = 64 * WGM * WGN, NW = WGM * WGN, BK = 32, STAGES = STAGES_;
   static constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
   static constexpr int ROWS = NP * BM + BN;          // LDS rows per stage (64 B each)
   static constexpr int STAGE_BYTES = ROWS * 64;
@@ -548,13 +575,13 @@ struct Dma8Cfg {
   static constexpr int SMEM = SMEM_PIPE > SMEM_EPI ? SMEM_PIPE : SMEM_EPI;
   static_assert(BLOCKS % NW == 0 && WM % 16 == 0 && WN % 16 == 0 && WM == 64, "tile shape");
   static_assert(SMEM <= 160 * 1024, "LDS");
-  static_assert(LPT <= 63, "vmcnt range");
+  static_assert(LPT * (STAGES - 2) <= 63 && STAGES >= 3 && STAGES <= 4, "vmcnt range");
 };
 
-template <int BM, int BN, int WGM, int WGN, int NP, int KIND>
+template <int BM, int BN, int WGM, int WGN, int NP, int STAGES, int KIND>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma8_kernel(ActIn a, BRows<bf16_t> b, int M, int N, int K,
                                                                        int ksplit, float* part, EpiParams e) {
-  using C = Dma8Cfg<BM, BN, WGM, WGN, NP>;
+  using C = Dma8Cfg<BM, BN, WGM, WGN, NP, STAGES>;
   constexpr int BK = C::BK, LPT = C::LPT, FM = C::FM, FN = C::FN, NT = C::NT;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::SMEM];
 
@@ -609,37 +636,67 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma8_kernel(ActIn a, B
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int nloc = kt1 - kt0;
-  if (nloc > 0) DMA8_ISSUE(kt0, 0);
-  if (nloc > 1) DMA8_ISSUE(kt0 + 1, 1);
+  // Fragments of stage it+1 are read from LDS while the MFMAs of stage it run
+  // (two register sets).  Iteration it: wait for stage it+1, barrier (every
+  // wave has its stage-it fragments in registers, so that buffer is free),
+  // issue stage it+3 into it, read stage it+1, multiply stage it.
   const int lr = lane & 15, lc = lane >> 4;
-  for (int it = 0; it < nloc; ++it) {
-    if (it + 1 < nloc) wait_vmcnt<LPT>();   // this tile landed; the next may still be in flight
+#define DMA8_LOAD(F, STG)                                                                                      \
+  do {                                                                                                         \
+    const unsigned char* st_ = smem + (STG) * C::STAGE_BYTES;                                                  \
+    _Pragma("unroll") for (int p = 0; p < NP; ++p) _Pragma("unroll") for (int i = 0; i < FM; ++i) {            \
+      const int row = p * BM + wm * C::WM + 16 * i + lr;                                                       \
+      F##a[p][i] = as_bf16x8(*(const u32x4*)(st_ + row * 64 + ((lc ^ ((row >> 1) & 3)) << 4)));               \
+    }                                                                                                          \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                                           \
+      const int row = NP * BM + wn * C::WN + 16 * j + lr;                                                      \
+      F##b[j] = as_bf16x8(*(const u32x4*)(st_ + row * 64 + ((lc ^ ((row >> 1) & 3)) << 4)));                  \
+    }                                                                                                          \
+  } while (0)
+#define DMA8_MMA(F)                                                                                            \
+  do {                                                                                                         \
+    _Pragma("unroll") for (int p = 0; p < NP; ++p) _Pragma("unroll") for (int i = 0; i < FM; ++i)             \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j) acc[i][j] =                                             \
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(F##a[p][i], F##b[j], acc[i][j], 0, 0, 0);                  \
+  } while (0)
+#define DMA8_STEP(CUR, NXT, IT)                                                                                \
+  do {                                                                                                         \
+    if ((IT) + 1 < nloc) {                                                                                     \
+      const int pend_ = min(STAGES - 2, nloc - 2 - (IT));                                                      \
+      if (STAGES > 3 && pend_ >= 2) wait_vmcnt<(STAGES > 3 ? 2 : 1) * LPT>();                                  \
+      else if (pend_ >= 1) wait_vmcnt<LPT>();                                                                  \
+      else wait_vmcnt<0>();                                                                                    \
+      lds_reads_done_barrier();                                                                                \
+      if ((IT) + STAGES < nloc) DMA8_ISSUE(kt0 + (IT) + STAGES, (IT) % STAGES);                                \
+    }                                                                                                          \
+    /* unconditional, so the MFMAs below wait only for their own fragments (the */                             \
+    /* last step reads a stale buffer whose values are never used) */                                          \
+    DMA8_LOAD(NXT, ((IT) + 1) % STAGES);                                                                       \
+    DMA8_MMA(CUR);                                                                                             \
+    dma8_interleave<NP * FM + FN, NP * FM * FN>();                                                             \
+  } while (0)
+
+  const int nloc = kt1 - kt0;
+  bf16x8 f0a[NP][FM], f0b[FN], f1a[NP][FM], f1b[FN];
+#pragma unroll
+  for (int s0 = 0; s0 < STAGES - 1; ++s0)
+    if (s0 < nloc) DMA8_ISSUE(kt0 + s0, s0);
+  if (nloc > 0) {
+    const int pend = min(STAGES - 2, nloc - 1);   // stages issued after stage 0
+    if (STAGES > 3 && pend >= 2) wait_vmcnt<(STAGES > 3 ? 2 : 1) * LPT>();
+    else if (pend >= 1) wait_vmcnt<LPT>();
     else wait_vmcnt<0>();
-    stage_barrier();                         // all lanes' data visible; stage (it+2)%3 is free
-    if (it + 2 < nloc) DMA8_ISSUE(kt0 + it + 2, (it + 2) % 3);
-    const unsigned char* st = smem + (it % 3) * C::STAGE_BYTES;
-    bf16x8 af[NP][FM], bfr[FN];
-#pragma unroll
-    for (int p = 0; p < NP; ++p)
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int row = p * BM + wm * C::WM + 16 * i + lr;
-        af[p][i] = as_bf16x8(*(const u32x4*)(st + row * 64 + ((lc ^ ((row >> 1) & 3)) << 4)));
-      }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int row = NP * BM + wn * C::WN + 16 * j + lr;
-      bfr[j] = as_bf16x8(*(const u32x4*)(st + row * 64 + ((lc ^ ((row >> 1) & 3)) << 4)));
-    }
-#pragma unroll
-    for (int p = 0; p < NP; ++p)
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[p][i], bfr[j], acc[i][j], 0, 0, 0);
+    stage_barrier();
+    if (STAGES - 1 < nloc) DMA8_ISSUE(kt0 + STAGES - 1, STAGES - 1);
+    DMA8_LOAD(f0, 0);
   }
+  for (int it = 0; it < nloc; it += 2) {
+    DMA8_STEP(f0, f1, it);
+    if (it + 1 < nloc) DMA8_STEP(f1, f0, it + 1);
+  }
+#undef DMA8_LOAD
+#undef DMA8_MMA
+#undef DMA8_STEP
 #undef DMA8_ISSUE
   __syncthreads();   // every wave is done with the pipeline buffers
 
@@ -656,6 +713,235 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma8_kernel(ActIn a, B
 #pragma unroll
           for (int q = 0; q < 4; ++q)
             Cs[(16 * i + 4 * lc + q) * C::LDC + wn * C::WN + 16 * j + lr] = acc[i][j][q];
+    }
+    __syncthreads();
+    const int ms = m0 + sl * 64;
+    if (ksplit > 1) {
+      float* dst = part + (size_t)ks * M * N;
+      constexpr int C4 = BN / 4;
+      for (int idx = tid; idx < 64 * C4; idx += NT) {
+        const int r = idx / C4, c = (idx - r * C4) * 4;
+        if (ms + r < M && n0 + c < N)
+          *(float4*)(dst + (size_t)(ms + r) * N + n0 + c) = *(const float4*)(Cs + r * C::LDC + c);
+      }
+    } else {
+      run_epilogue<KIND, 64, BN, NT, bf16_t>(Cs, C::LDC, ms, n0, M, N, e);
+    }
+    __syncthreads();
+  }
+}
+
+// The same eight-wave tiles with 64-deep K stages in two LDS buffers: each
+// 1 KiB direct load covers eight whole 128-byte rows, so it holds eight L1
+// line slots instead of sixteen half-used ones, which doubles what the loads
+// deliver per outstanding request.  LDS rows are 128 bytes with 16-byte chunk
+// c of row r stored at chunk c ^ ((r >> 1) & 7) (the sixteen rows one operand
+// read touches land on distinct bank groups).  The fragment pipeline runs in
+// 32-deep half stages: the reads of the next half overlap the MFMAs of the
+// current one, and the one barrier per stage sits between the two halves.
+template <int BM, int BN, int WGM, int WGN, int NP>
+struct FlCfg {
+  static constexpr int NT = 64 * WGM * WGN, NW = WGM * WGN, BK = 64;
+  static constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
+  static constexpr int ROWS = NP * BM + BN;          // LDS rows per stage (128 B each)
+  static constexpr int STAGE_BYTES = ROWS * 128;
+  static constexpr int BLOCKS = ROWS / 8;             // 1 KiB load instructions per stage
+  static constexpr int LPT = BLOCKS / NW;             // per wave
+  static constexpr int LDC = BN + 4;
+  static constexpr int SMEM_PIPE = 2 * STAGE_BYTES;
+  static constexpr int SMEM_EPI = 64 * LDC * 4;
+  static constexpr int SMEM = SMEM_PIPE > SMEM_EPI ? SMEM_PIPE : SMEM_EPI;
+  static_assert(BLOCKS % NW == 0 && WM % 16 == 0 && WN % 16 == 0 && WM == 64, "tile shape");
+  static_assert(SMEM <= 160 * 1024, "LDS");
+  static_assert(LPT <= 63, "vmcnt range");
+};
+
+template <int BM, int BN, int WGM, int WGN, int NP, int KIND>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_fl_kernel(ActIn a, BRows<bf16_t> b, int M, int N, int K,
+                                                                     int ksplit, float* part, EpiParams e) {
+  using C = FlCfg<BM, BN, WGM, WGN, NP>;
+  constexpr int BK = C::BK, LPT = C::LPT, FM = C::FM, FN = C::FN, NT = C::NT;
+  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::SMEM];
+
+  const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
+  int t;
+  {
+    const int per = gridDim.x / 8, L = blockIdx.x;
+    t = (per > 0) ? (L & 7) * per + (L >> 3) : L;
+    if (t >= ntm * ntn * ksplit) return;
+  }
+  const int tm = t % ntm, tn = (t / ntm) % ntn, ks = t / (ntm * ntn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nkt = K / BK;
+  const int kt0 = (int)((long long)ks * nkt / ksplit), kt1 = (int)((long long)(ks + 1) * nkt / ksplit);
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int wm = wid / WGN, wn = wid - wm * WGN;
+
+  // Load blocks of eight rows never straddle two buffers (the plane, split and
+  // SwiGLU-half boundaries are multiples of eight rows), so each block has a
+  // wave-uniform base pointer and a 32-bit per-lane byte offset.
+  const int wid_u = __builtin_amdgcn_readfirstlane(wid);
+  const bf16_t* bbase[LPT];
+  uint32_t boff[LPT];
+#pragma unroll
+  for (int q = 0; q < LPT; ++q) {
+    const int blk = wid_u * LPT + q;
+    const int row0 = blk * 8, dr = lane >> 3;
+    const int row = row0 + dr;
+    const int pc = lane & 7, lc = pc ^ ((row >> 1) & 7);
+    if (row0 < NP * BM) {
+      const int p = row0 / BM, r = row - p * BM;
+      const int gr = min(m0 + r, M - 1);
+      bbase[q] = (const bf16_t*)(p == 0 ? a.p0 : a.p1);
+      boff[q] = (uint32_t)(((size_t)gr * a.ld + lc * 8) * 2);
+    } else {
+      const int first = min(n0 + row0 - NP * BM, N - 1);
+      const bf16_t* rb = b.row(first, BN);
+      bbase[q] = rb;
+      boff[q] = (uint32_t)((b.row(min(n0 + row - NP * BM, N - 1), BN) - rb + lc * 8) * 2);
+    }
+  }
+  const uint32_t lds0 = (uint32_t)(size_t)smem;
+
+#define FL_ISSUE(KT, STAGE)                                                                                      \
+  do {                                                                                                           \
+    const uint32_t k0_ = (uint32_t)(KT) * (BK * 2);                                                              \
+    _Pragma("unroll") for (int q = 0; q < LPT; ++q) {                                                            \
+      __builtin_amdgcn_global_load_lds(                                                                          \
+          (const __attribute__((address_space(1))) void*)((const char*)bbase[q] + (size_t)(boff[q] + k0_)),      \
+          (__attribute__((address_space(3))) void*)(size_t)(lds0 + (STAGE) * C::STAGE_BYTES +                   \
+                                                            (wid * LPT + q) * 1024),                             \
+          16, 0, 0);                                                                                             \
+    }                                                                                                            \
+  } while (0)
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int lr = lane & 15, lq = lane >> 4;
+#define FL_LOAD(F, STG, H)                                                                                     \
+  do {                                                                                                         \
+    const unsigned char* st_ = smem + (STG) * C::STAGE_BYTES;                                                  \
+    const int lc_ = 4 * (H) + lq;                                                                              \
+    _Pragma("unroll") for (int p = 0; p < NP; ++p) _Pragma("unroll") for (int i = 0; i < FM; ++i) {            \
+      const int row = p * BM + wm * C::WM + 16 * i + lr;                                                       \
+      F##a[p][i] = as_bf16x8(*(const u32x4*)(st_ + row * 128 + ((lc_ ^ ((row >> 1) & 7)) << 4)));             \
+    }                                                                                                          \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                                           \
+      const int row = NP * BM + wn * C::WN + 16 * j + lr;                                                      \
+      F##b[j] = as_bf16x8(*(const u32x4*)(st_ + row * 128 + ((lc_ ^ ((row >> 1) & 7)) << 4)));                \
+    }                                                                                                          \
+  } while (0)
+#define FL_MMA(F)                                                                                              \
+  do {                                                                                                         \
+    _Pragma("unroll") for (int p = 0; p < NP; ++p) _Pragma("unroll") for (int i = 0; i < FM; ++i)             \
+        _Pragma("unroll") for (int j = 0; j < FN; ++j) acc[i][j] =                                             \
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(F##a[p][i], F##b[j], acc[i][j], 0, 0, 0);                  \
+  } while (0)
+
+  const int nloc = kt1 - kt0;
+  bf16x8 f0a[NP][FM], f0b[FN], f1a[NP][FM], f1b[FN];
+  if (nloc > 0) FL_ISSUE(kt0, 0);
+  if (nloc > 1) FL_ISSUE(kt0 + 1, 1);
+  if (nloc > 0) {
+    if (nloc > 1) wait_vmcnt<LPT>();
+    else wait_vmcnt<0>();
+    stage_barrier();
+    FL_LOAD(f0, 0, 0);
+  }
+  for (int it = 0; it < nloc; ++it) {
+    const int cur = it & 1;
+    // first half: MFMAs of half 0 of stage it, reads of its half 1
+    FL_LOAD(f1, cur, 1);
+    FL_MMA(f0);
+    dma8_interleave<NP * FM + FN, NP * FM * FN>();
+    // stage boundary: stage it+1 landed, every wave holds all of stage it in
+    // registers, so its buffer takes stage it+2
+    if (it + 1 < nloc) {
+      wait_vmcnt<0>();
+      lds_reads_done_barrier();
+      if (it + 2 < nloc) FL_ISSUE(kt0 + it + 2, cur);
+    }
+    // second half: MFMAs of half 1, reads of half 0 of stage it+1 (stale and
+    // unused after the last stage; unconditional so the MFMAs wait only for
+    // their own fragments)
+    FL_LOAD(f0, cur ^ 1, 0);
+    FL_MMA(f1);
+    dma8_interleave<NP * FM + FN, NP * FM * FN>();
+  }
+#undef FL_LOAD
+#undef FL_MMA
+#undef FL_ISSUE
+  if constexpr (KIND == EPI_LMHEAD && C::WN == 128) {
+    // Greedy LM-head partials straight from the accumulators: a wave's 128
+    // columns are one partial group; lane (lq, lr) holds rows 16i+4lq+q at
+    // columns 16j+lr, so a row is reduced over j in the lane, then over the
+    // sixteen lanes sharing lq.  Ties keep the lowest column.
+    if (ksplit == 1 && e.temperature == 0.f) {
+      const int cbase = n0 + wn * 128;
+      if (cbase < N) {
+        constexpr float kL2E = 1.4426950408889634f;
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int r = m0 + wm * C::WM + 16 * i + 4 * lq + q;
+            float mx = -INFINITY;
+            int ix = -1;
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+              const int v = cbase + 16 * j + lr;
+              const float z = acc[i][j][q];
+              if (v < N && (ix < 0 || z > mx)) { mx = z; ix = v; }
+            }
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) {
+              const float qm = __shfl_xor(mx, o, kWave);
+              const int qi = __shfl_xor(ix, o, kWave);
+              if (qi >= 0 && (ix < 0 || qm > mx || (qm == mx && qi < ix))) { mx = qm; ix = qi; }
+            }
+            float sm = 0.f;
+#pragma unroll
+            for (int j = 0; j < FN; ++j)
+              if (cbase + 16 * j + lr < N) sm += __builtin_amdgcn_exp2f((acc[i][j][q] - mx) * kL2E);
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) sm += __shfl_xor(sm, o, kWave);
+            if (r < M) {
+              if (lr == 0) {
+                const size_t pi = (size_t)r * e.ntiles + cbase / 128;
+                e.part_f[pi] = make_float4(mx, mx, sm, mx);
+                e.part_i[pi] = ix;
+              }
+              if (e.logits) {
+                const size_t base = (size_t)e.row_map[r] * N;
+#pragma unroll
+                for (int j = 0; j < FN; ++j)
+                  if (cbase + 16 * j + lr < N) e.logits[base + cbase + 16 * j + lr] = acc[i][j][q];
+              }
+            }
+          }
+      }
+      return;
+    }
+  }
+  __syncthreads();   // every wave is done with the pipeline buffers
+
+  // epilogue over 64-row slices of the tile (slice sl = the rows of wave row wm == sl)
+  float* Cs = (float*)smem;
+#pragma unroll
+  for (int sl = 0; sl < WGM; ++sl) {
+    if (m0 + sl * 64 >= M) break;
+    if (wm == sl) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            Cs[(16 * i + 4 * lq + q) * C::LDC + wn * C::WN + 16 * j + lr] = acc[i][j][q];
     }
     __syncthreads();
     const int ms = m0 + sl * 64;
@@ -757,21 +1043,24 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(ActIn a, BRows<float> b, 
 //   2: 128x128, four 64x64 waves, two workgroups per CU (gemm_dma_kernel)
 //   3: 128x384, eight 64x96 waves      4: 256x256, eight 64x128 waves
 //   5: 128x256, eight 64x64 waves      6: 512x128, eight 64x128 waves
+//   7, 8, 9: 3, 5 and 4 (one plane) with four LDS stages
 //   (gemm_dma8_kernel, one workgroup per CU)
 #ifndef DFLASH_T_SWIGLU
-#define DFLASH_T_SWIGLU 3
+#define DFLASH_T_SWIGLU 10
 #endif
 #ifndef DFLASH_T_LMHEAD
-#define DFLASH_T_LMHEAD 4
+#define DFLASH_T_LMHEAD 11
 #endif
 #ifndef DFLASH_T_ADD
-#define DFLASH_T_ADD 4
+#define DFLASH_T_ADD 12
 #endif
 #ifndef DFLASH_T_STORE
-#define DFLASH_T_STORE 4
+#define DFLASH_T_STORE 10
 #endif
-static int tile_bn(int cfg) { return cfg == 3 ? 384 : cfg == 4 || cfg == 5 ? 256 : 128; }
-static int tile_bm(int cfg) { return cfg == 4 ? 256 : cfg == 6 ? 512 : 128; }
+static int tile_bn(int cfg) {
+  return cfg == 3 || cfg == 7 || cfg == 10 ? 384 : cfg == 4 || cfg == 5 || cfg == 8 || cfg == 9 || cfg == 11 || cfg == 12 ? 256 : 128;
+}
+static int tile_bm(int cfg) { return cfg == 4 || cfg == 9 || cfg == 11 ? 256 : cfg == 6 ? 512 : 128; }
 
 // LM-head partials cover 128 columns each, or 64 when the tile width is not a multiple of 128
 int gemm_bn(int wdtype, int K) { return wdtype && K % 32 == 0 && tile_bn(DFLASH_T_LMHEAD) % 128 ? 64 : 128; }
@@ -800,7 +1089,9 @@ GemmPlan gemm_plan(int wdtype, int a_mode, int M, int N, int K, int kind, bool f
     else if (kind == EPI_ADD) cfg = DFLASH_T_ADD;
     else if (kind == EPI_STORE) cfg = DFLASH_T_STORE;
     const bool one_plane = a_mode != ACT_HILO;
-    if (cfg == 6 && !one_plane) cfg = 4;     // 512-row tiles of both planes exceed the LDS
+    if ((cfg == 6 || cfg == 9) && !one_plane) cfg = 4;   // these tiles of both planes exceed the LDS
+    if (cfg == 11 && !one_plane) cfg = 12;
+    if (cfg >= 10 && K % 64 != 0) cfg = 2;
     // SwiGLU tiles hold BN/2 gate and BN/2 up columns of the same rows
     if (kind == EPI_SWIGLU && (N / 2) % (tile_bn(cfg) / 2) != 0) cfg = 2;
   }
@@ -874,13 +1165,28 @@ static hipError_t go_dma(const GemmArgs& g, int ksplit, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WGM, int WGN, int NP, int KIND>
+template <int BM, int BN, int WGM, int WGN, int NP, int KIND, int STAGES = 3>
 static hipError_t go_dma8(const GemmArgs& g, int ksplit, hipStream_t s) {
   const int ntm = (g.M + BM - 1) / BM, ntn = (g.N + BN - 1) / BN;
   const int total = ntm * ntn * ksplit;
   const int grid = (total + 7) / 8 * 8;
   BRows<bf16_t> b{(const bf16_t*)g.b.b0, (const bf16_t*)g.b.b1, g.b.ldb, g.b.split, g.b.mode};
-  hipLaunchKernelGGL((gemm_dma8_kernel<BM, BN, WGM, WGN, NP, KIND>), dim3(grid), dim3(64 * WGM * WGN), 0, s, g.a, b,
+  hipLaunchKernelGGL((gemm_dma8_kernel<BM, BN, WGM, WGN, NP, STAGES, KIND>), dim3(grid), dim3(64 * WGM * WGN), 0, s, g.a, b,
+                     g.M, g.N, g.K, ksplit, g.part, g.e);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || ksplit == 1) return err;
+  hipLaunchKernelGGL((splitk_reduce_kernel<16, BN, KIND, bf16_t>), dim3((g.M + 15) / 16 * ntn), dim3(256), 0, s,
+                     g.part, ksplit, g.M, g.N, g.e);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WGM, int WGN, int NP, int KIND>
+static hipError_t go_fl(const GemmArgs& g, int ksplit, hipStream_t s) {
+  const int ntm = (g.M + BM - 1) / BM, ntn = (g.N + BN - 1) / BN;
+  const int total = ntm * ntn * ksplit;
+  const int grid = (total + 7) / 8 * 8;
+  BRows<bf16_t> b{(const bf16_t*)g.b.b0, (const bf16_t*)g.b.b1, g.b.ldb, g.b.split, g.b.mode};
+  hipLaunchKernelGGL((gemm_fl_kernel<BM, BN, WGM, WGN, NP, KIND>), dim3(grid), dim3(64 * WGM * WGN), 0, s, g.a, b,
                      g.M, g.N, g.K, ksplit, g.part, g.e);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || ksplit == 1) return err;
@@ -898,6 +1204,12 @@ static hipError_t go_bf16(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
     case 4: if constexpr (!scatter) return go_dma8<256, 256, 4, 2, NP, KIND>(g, p.ksplit, s); break;
     case 5: if constexpr (!scatter) return go_dma8<128, 256, 2, 4, NP, KIND>(g, p.ksplit, s); break;
     case 6: if constexpr (NP == 1 && !scatter) return go_dma8<512, 128, 8, 1, 1, KIND>(g, p.ksplit, s); break;
+    case 7: if constexpr (!scatter) return go_dma8<128, 384, 2, 4, NP, KIND, 4>(g, p.ksplit, s); break;
+    case 8: if constexpr (!scatter) return go_dma8<128, 256, 2, 4, NP, KIND, 4>(g, p.ksplit, s); break;
+    case 9: if constexpr (NP == 1 && !scatter) return go_dma8<256, 256, 4, 2, 1, KIND, 4>(g, p.ksplit, s); break;
+    case 10: if constexpr (!scatter) return go_fl<128, 384, 2, 4, NP, KIND>(g, p.ksplit, s); break;
+    case 11: if constexpr (NP == 1 && !scatter) return go_fl<256, 256, 4, 2, 1, KIND>(g, p.ksplit, s); break;
+    case 12: if constexpr (!scatter) return go_fl<128, 256, 2, 4, NP, KIND>(g, p.ksplit, s); break;
     default: break;
   }
   return hipErrorInvalidValue;
