@@ -11,7 +11,7 @@
 // in registers as hi/lo bf16), so each lane owns query (lane % 16) and 8
 // tokens; the online-softmax probabilities are then already the B operand
 // of O^T = V^T P^T, whose A operand comes from the dimension-major V page
-// (two 8-byte LDS reads per fragment, no transpose).  P is split hi/lo too.
+// (one 16-byte LDS read per fragment, no transpose).  P is split hi/lo too.
 // fp32 pool and the in-block split: a VALU kernel, four lanes per query row.
 #include <algorithm>
 
@@ -59,10 +59,13 @@ __device__ __forceinline__ void att_barrier() {
 
 // Rotated queries of every (sequence, kv head) group as (hi, lo) bf16 planes
 // in [b][kv head][r][d] order, r = j*B + i for head m*g + j and block
-// position i: the context kernel then loads its MFMA operands directly.
+// position i: the context kernel then loads its MFMA operands directly.  The
+// queries carry the softmax scale times log2 e, so the scores come out ready
+// for the base-2 exponential.
 __global__ __launch_bounds__(256) void attn_qprep_kernel(AttnParams p, bf16_t* qhi, bf16_t* qlo) {
   const int D = p.d, g = p.nq / p.nkv, R = g * p.B;
   const int ldq = (p.nq + 2 * p.nkv) * D;
+  const float qscale = p.scale * 1.4426950408889634f;   // scores come out in base-2 units
   const size_t total = (size_t)p.batch * p.nkv * R * (D / 2);
   for (size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (size_t)gridDim.x * 256) {
     const int e2 = (int)(idx % (D / 2));      // element pair (2 e2, 2 e2 + 1)
@@ -72,7 +75,7 @@ __global__ __launch_bounds__(256) void attn_qprep_kernel(AttnParams p, bf16_t* q
     const float* qv = p.qkv + (size_t)row * ldq + n * D;
     const float2* cs = p.cs + (size_t)row * (D / 2);
     uint32_t h, l;
-    split_hilo2(rope_elem(qv, cs, 2 * e2, D), rope_elem(qv, cs, 2 * e2 + 1, D), h, l);
+    split_hilo2(rope_elem(qv, cs, 2 * e2, D) * qscale, rope_elem(qv, cs, 2 * e2 + 1, D) * qscale, h, l);
     ((uint32_t*)qhi)[gr * (D / 2) + e2] = h;
     ((uint32_t*)qlo)[gr * (D / 2) + e2] = l;
   }
@@ -82,9 +85,17 @@ __global__ __launch_bounds__(256) void attn_qprep_kernel(AttnParams p, bf16_t* q
 // 64-query group) per workgroup of four waves.  Tiles of 32 tokens (two
 // pages: K 2 x 4 KiB, V 2 x 4 KiB) are copied global -> LDS by
 // global_load_lds_dwordx4 (lane i of an instruction fills LDS bytes
-// base + 16 i), kAttStages deep.  K rows (256 B) keep chunk c at c ^ (row & 15)
-// and V rows (32 B) keep half h at h ^ ((d >> 2) & 1), so the MFMA operand
-// reads of 16 consecutive lanes hit distinct banks.
+// base + 16 i), kAttStages deep; wave w copies page w & 1 of the tile, K for
+// w < 2 and V otherwise, so it looks up one physical page per tile.
+//
+// Within a tile, MFMA block t (t = 0, 1) of S^T = K Q^T takes the 16 tokens
+// 8(r / 4) + 4t + (r % 4), r = 0..15: lane (gq, q) then holds the scores of
+// tokens 8 gq .. 8 gq + 7 in order, which are also the 8 consecutive tokens
+// its V^T operand needs (one 16-byte read of a V row).  K rows (256 B) keep
+// chunk c at c ^ kswz(row), V rows (32 B) keep half h at h ^ ((d >> 3) & 1):
+// the sixteen rows one operand read touches land on distinct bank groups.
+__device__ __forceinline__ int kswz(int krow) { return (krow & 15) ^ (((krow >> 4) & 1) << 2); }
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
   static_assert(D == 128, "context kernel is specialised for head_dim 128");
@@ -114,7 +125,6 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
   const bool wave_active = qg * 64 + wid * 16 < R;
   const int j = rvalid ? r / p.B : 0, i = rvalid ? r - (r / p.B) * p.B : 0;
   const int n = m * g + j, row = b * p.B + i;
-  const int ldq = (p.nq + 2 * p.nkv) * D;
 
   bf16x8 qh[KK], ql[KK];
   {
@@ -143,59 +153,104 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
   // (the host only attends to a context when the pool has at least one page)
   const int first_ph = (ntiles && ptab[0] >= 0) ? ptab[0] : 0;
 
-  // Issue the copies of tile t (pages pg0 + 2t, +1) into stage st.  A page
-  // past the split, or one without a valid physical index, is read from the
-  // split's first page instead: its tokens are masked out of the softmax.
-  auto issue = [&](int t, int st) __attribute__((always_inline)) {
+  // copy role of this wave and the per-lane byte offsets of its PER_THREAD
+  // loads within a page chunk (instruction ins = 4 wid + q fills LDS bytes
+  // ins * 1024 .. + 1023 of the tile)
+  const int wrole = __builtin_amdgcn_readfirstlane(wid);
+  const int wpage = wrole & 1;
+  const bf16_t* srcbase = wrole < 2 ? kbase : vbase;
+  uint32_t loff[PER_THREAD];
 #pragma unroll
-    for (int q = 0; q < PER_THREAD; ++q) {
-      const int ins = wid * PER_THREAD + q;          // 0..15 over the workgroup
-      const unsigned char* src;
-      if (ins < 8) {                                  // K: rows 4*ins .. 4*ins+3
-        const int krow = ins * 4 + (lane >> 4);
-        const int pc = lane & 15, lc = pc ^ (krow & 15);
-        const int pp = pg0 + 2 * t + (krow >> 4);
-        int ph = pp < pg1 ? ptab[pp - pg0] : first_ph;
-        ph = ph >= 0 ? ph : first_ph;
-        src = (const unsigned char*)(kbase + (size_t)ph * page_stride) + (krow & 15) * (D * 2) + lc * 16;
-      } else {                                        // V: page (ins-8)/4, rows 32*((ins-8)%4) ..
-        const int vi = ins - 8, pg = vi >> 2;
-        const int d = (vi & 3) * 32 + (lane >> 1);
-        const int lh = (lane & 1) ^ ((d >> 2) & 1);
-        const int pp = pg0 + 2 * t + pg;
-        int ph = pp < pg1 ? ptab[pp - pg0] : first_ph;
-        ph = ph >= 0 ? ph : first_ph;
-        src = (const unsigned char*)(vbase + (size_t)ph * page_stride) + d * 32 + lh * 16;
-      }
-      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)src,
-                                       (__attribute__((address_space(3))) void*)(size_t)(lds0 + st * TILE + ins * 1024),
-                                       16, 0, 0);
-    }
-  };
-
-#pragma unroll
-  for (int t = 0; t < kAttStages - 1; ++t)
-    if (t < ntiles) issue(t, t);
-
-  // loop-invariant LDS operand offsets of this lane
-  int koff[KK], voff[NN];
-  {
-    const int krow = lane & 15;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) koff[kk] = krow * (D * 2) + (((4 * kk + (lane >> 4)) ^ krow) << 4);
-    const int gq = lane >> 4;   // slots 4gq .. 4gq+3 of each page
-#pragma unroll
-    for (int nn = 0; nn < NN; ++nn) {
-      const int d = 16 * nn + (lane & 15);
-      voff[nn] = d * 32 + (((gq >> 1) ^ ((d >> 2) & 1)) << 4) + (gq & 1) * 8;
+  for (int q = 0; q < PER_THREAD; ++q) {
+    if (wrole < 2) {
+      const int krow = 16 * wpage + 4 * q + (lane >> 4);
+      const int lc = (lane & 15) ^ kswz(krow);
+      loff[q] = (uint32_t)((krow & 15) * (D * 2) + lc * 16);
+    } else {
+      const int d = 32 * q + (lane >> 1);
+      const int lh = (lane & 1) ^ ((d >> 3) & 1);
+      loff[q] = (uint32_t)(d * 32 + lh * 16);
     }
   }
-  const float sl2 = p.scale * 1.4426950408889634f;
-  const int tok_end = min(ctx, pg1 * 16);
+  // physical page this wave copies for tile t: past the split, or without a
+  // valid index, the split's first page is read (its tokens are masked out)
+  auto page_of = [&](int t) __attribute__((always_inline)) {
+    const int pp = pg0 + 2 * t + wpage;
+    int ph = pp < pg1 ? ptab[pp - pg0] : first_ph;
+    return ph >= 0 ? ph : first_ph;
+  };
+  auto issue = [&](int ph, int st) __attribute__((always_inline)) {
+    const char* base = (const char*)(srcbase + (size_t)__builtin_amdgcn_readfirstlane(ph) * page_stride);
+#pragma unroll
+    for (int q = 0; q < PER_THREAD; ++q)
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + loff[q]),
+                                       (__attribute__((address_space(3))) void*)(size_t)(lds0 + st * TILE +
+                                                                                         (4 * wrole + q) * 1024),
+                                       16, 0, 0);
+  };
 
-  for (int it = 0; it < ntiles; ++it) {
-    const int later = min(ntiles - 1 - it, kAttStages - 2);   // tiles issued after this one
-    switch (later) {
+  // loop-invariant LDS operand offsets of this lane
+  int koff[2][KK], voff[NN];
+  {
+    const int rr = lane & 15, gq = lane >> 4;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int krow = 8 * (rr >> 2) + 4 * t + (rr & 3);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) koff[t][kk] = krow * (D * 2) + (((4 * kk + gq) ^ kswz(krow)) << 4);
+    }
+#pragma unroll
+    for (int nn = 0; nn < NN; ++nn) {
+      const int d = 16 * nn + rr;
+      voff[nn] = (gq >> 1) * (D * 32) + d * 32 + (((gq & 1) ^ ((d >> 3) & 1)) << 4);
+    }
+  }
+  const int tok_end = min(ctx, pg1 * 16);
+  const int tl = 8 * (lane >> 4);   // first of this lane's 8 tokens in a tile
+
+  // V slots at or past the context end may hold anything (a page never
+  // written); in the last tile they are zeroed so that P = 0 meets V = 0.
+  auto zero_tail = [&](int t) __attribute__((always_inline)) {
+    const int tok0 = (pg0 + 2 * t) * 16;
+    if (tok0 + 32 > ctx) {
+      unsigned char* vt = lds + (t % kAttStages) * TILE + KBYTES;
+      for (int c = tid; c < 2 * D * 16; c += 256) {
+        const int pg = c / (D * 16), rem = c - pg * D * 16, d = rem >> 4, slot = rem & 15;
+        if (tok0 + pg * 16 + slot >= ctx) {
+          const int lh = (slot >> 3) ^ ((d >> 3) & 1);
+          *(bf16_t*)(vt + pg * (D * 32) + d * 32 + lh * 16 + (slot & 7) * 2) = 0;
+        }
+      }
+      __syncthreads();
+    }
+  };
+#define ATT_SCORES(T, O0, O1)                                                                                 \
+  do {                                                                                                        \
+    const unsigned char* kt_ = lds + ((T) % kAttStages) * TILE;                                               \
+    O0 = f32x4{0.f, 0.f, 0.f, 0.f};                                                                           \
+    O1 = f32x4{0.f, 0.f, 0.f, 0.f};                                                                           \
+    _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) {                                                       \
+      const bf16x8 a0_ = as_bf16x8(*(const u32x4*)(kt_ + koff[0][kk]));                                       \
+      const bf16x8 a1_ = as_bf16x8(*(const u32x4*)(kt_ + koff[1][kk]));                                       \
+      O0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0_, qh[kk], O0, 0, 0, 0);                                 \
+      O1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1_, qh[kk], O1, 0, 0, 0);                                 \
+      O0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0_, ql[kk], O0, 0, 0, 0);                                 \
+      O1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1_, ql[kk], O1, 0, 0, 0);                                 \
+    }                                                                                                         \
+  } while (0)
+
+  // Software pipeline: iteration it waits for tile it+1, computes its scores
+  // (MFMA) and then the softmax and P V of tile it, whose scores were computed
+  // one iteration earlier, so the matrix and vector work of neighbouring tiles
+  // overlap inside a wave.  Tile it-1's buffer is refilled after the barrier
+  // of iteration it (every wave is past its P V by then).
+  int issued = 0;   // tiles issued so far
+#pragma unroll
+  for (int t = 0; t < kAttStages; ++t)
+    if (t < ntiles) { issue(page_of(t), t); ++issued; }
+  int ph_next = page_of(kAttStages);   // read one issue ahead
+  auto wait_tile = [&](int t) __attribute__((always_inline)) {
+    switch (min(issued - 1 - t, 5)) {   // tiles issued after tile t
       case 0: att_wait_vmcnt<0>(); break;
       case 1: att_wait_vmcnt<PER_THREAD>(); break;
       case 2: att_wait_vmcnt<2 * PER_THREAD>(); break;
@@ -203,85 +258,79 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
       case 4: att_wait_vmcnt<4 * PER_THREAD>(); break;
       default: att_wait_vmcnt<5 * PER_THREAD>(); break;
     }
-    att_barrier();
-    const int st = it % kAttStages;
-    unsigned char* kt_lds = lds + st * TILE;
-    unsigned char* vt_lds = kt_lds + KBYTES;
-    const int tok0 = (pg0 + 2 * it) * 16;
-    if (tok0 + 32 > ctx) {
-      // boundary tile: V slots at or past the context end may hold anything
-      // (a page never written); they are zeroed so that P = 0 meets V = 0.
-      for (int c = tid; c < 2 * D * 16; c += 256) {
-        const int pg = c / (D * 16), rem = c - pg * D * 16, d = rem >> 4, slot = rem & 15;
-        if (tok0 + pg * 16 + slot >= ctx) {
-          const int lh = (slot >> 3) ^ ((d >> 2) & 1);
-          *(bf16_t*)(vt_lds + pg * (D * 32) + d * 32 + lh * 16 + (slot & 7) * 2) = 0;
-        }
-      }
-      __syncthreads();
-    }
-    if (it + kAttStages - 1 < ntiles) issue(it + kAttStages - 1, (it + kAttStages - 1) % kAttStages);
-    if (!wave_active) continue;
+  };
 
-    f32x4 st2[2];
+  f32x4 stc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  if (ntiles > 0) {
+    wait_tile(0);
+    att_barrier();
+    zero_tail(0);
+    if (wave_active) ATT_SCORES(0, stc[0], stc[1]);
+  }
+  for (int it = 0; it < ntiles; ++it) {
+    f32x4 stn[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    if (it + 1 < ntiles) {
+      wait_tile(it + 1);
+      att_barrier();
+      if (it >= 1 && issued < ntiles) {
+        issue(ph_next, (it - 1) % kAttStages);   // tile it+kAttStages-1 into tile it-1's buffer
+        ++issued;
+        ph_next = page_of(issued);
+      }
+      zero_tail(it + 1);
+      if (wave_active) ATT_SCORES(it + 1, stn[0], stn[1]);
+    }
+    if (wave_active) {
+      const int tok0 = (pg0 + 2 * it) * 16;
+      // lane owns query (lane & 15) and tokens tok0 + tl + 4t + e, scores in
+      // base-2 units (the queries carry scale * log2 e)
+      float s[8];
+      if (tok0 + 32 <= tok_end) {
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      st2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const bf16x8 a = as_bf16x8(*(const u32x4*)(kt_lds + koff[kk] + t * 16 * (D * 2)));
-        st2[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qh[kk], st2[t], 0, 0, 0);
-        st2[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, ql[kk], st2[t], 0, 0, 0);
+          for (int e = 0; e < 4; ++e) s[t * 4 + e] = stc[t][e];
+      } else {
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) s[t * 4 + e] = tok0 + tl + 4 * t + e < tok_end ? stc[t][e] : -INFINITY;
+      }
+      float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
+      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      const float m_new = fmaxf(m_run, mx);
+      if (m_new != -INFINITY) {
+        float pv[8], ps = 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          pv[k] = __builtin_amdgcn_exp2f(s[k] - m_new);
+          ps += pv[k];
+        }
+        if (__any(m_new != m_run)) {   // rescale only when some row's running max moved
+          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          l_run *= alpha;
+#pragma unroll
+          for (int nn = 0; nn < NN; ++nn) ot[nn] *= alpha;
+        }
+        l_run += ps;
+        m_run = m_new;
+        u32x4 hu, lu;
+        split_hilo8(pv, hu, lu);
+        const bf16x8 pbh = as_bf16x8(hu), pbl = as_bf16x8(lu);
+        const unsigned char* vt = lds + (it % kAttStages) * TILE + KBYTES;
+#pragma unroll
+        for (int nn = 0; nn < NN; ++nn) {
+          const bf16x8 va = as_bf16x8(*(const u32x4*)(vt + voff[nn]));
+          ot[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbh, ot[nn], 0, 0, 0);
+          ot[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbl, ot[nn], 0, 0, 0);
+        }
       }
     }
-    // lane owns query (lane & 15) and tokens tok0 + 16t + 4(lane>>4) + e; scores
-    // are kept in base-2 units (scale * log2 e folded in) for v_exp_f32
-    float s[8];
-    if (tok0 + 32 <= tok_end) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) s[t * 4 + e] = st2[t][e] * sl2;
-    } else {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int tok = tok0 + 16 * t + 4 * (lane >> 4) + e;
-          s[t * 4 + e] = tok < tok_end ? st2[t][e] * sl2 : -INFINITY;
-        }
-    }
-    float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-    mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
-    const float m_new = fmaxf(m_run, mx);
-    if (m_new == -INFINITY) continue;
-    float pv[8], ps = 0.f;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      pv[k] = __builtin_amdgcn_exp2f(s[k] - m_new);
-      ps += pv[k];
-    }
-    if (__any(m_new != m_run)) {   // rescale only when some row's running max moved
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int nn = 0; nn < NN; ++nn) ot[nn] *= alpha;
-    }
-    l_run += ps;
-    m_run = m_new;
-    u32x4 hu, lu;
-    split_hilo8(pv, hu, lu);
-    const bf16x8 pbh = as_bf16x8(hu), pbl = as_bf16x8(lu);
-#pragma unroll
-    for (int nn = 0; nn < NN; ++nn) {
-      const u32x2 lo2 = *(const u32x2*)(vt_lds + voff[nn]), hi2 = *(const u32x2*)(vt_lds + D * 32 + voff[nn]);
-      const u32x4 vv = {lo2.x, lo2.y, hi2.x, hi2.y};
-      const bf16x8 va = as_bf16x8(vv);
-      ot[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbh, ot[nn], 0, 0, 0);
-      ot[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbl, ot[nn], 0, 0, 0);
-    }
+    stc[0] = stn[0];
+    stc[1] = stn[1];
   }
+#undef ATT_SCORES
 
   float l_tot = l_run;
   l_tot += __shfl_xor(l_tot, 16, kWave);
@@ -392,7 +441,10 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
   const int qg = blockIdx.x, m = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int ldq = (p.nq + 2 * p.nkv) * D;
-  for (int c = tid; c < QR * D; c += 256) {
+  // fixed trip counts, unrolled: every load of the staging is in flight at once
+#pragma unroll
+  for (int k = 0; k < QR * D / 256; ++k) {
+    const int c = tid + 256 * k;
     const int r = c / D, e = c - r * D, rr = qg * QR + r;
     float v = 0.f;
     if (rr < R) {
@@ -401,10 +453,14 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
     }
     qs[r][e] = v;
   }
-  for (int c = tid; c < p.B * D; c += 256) {
+#pragma unroll
+  for (int k = 0; k < 16 * D / 256; ++k) {
+    const int c = tid + 256 * k;
     const int jb = c / D, e = c - jb * D, krow = b * p.B + jb;
-    kb[jb][e] = rope_elem(p.qkv + (size_t)krow * ldq + p.nq * D + m * D, p.cs + (size_t)krow * (D / 2), e, D);
-    vb[jb][e] = p.qkv[(size_t)krow * ldq + (p.nq + p.nkv) * D + m * D + e];
+    if (jb < p.B) {
+      kb[jb][e] = rope_elem(p.qkv + (size_t)krow * ldq + p.nq * D + m * D, p.cs + (size_t)krow * (D / 2), e, D);
+      vb[jb][e] = p.qkv[(size_t)krow * ldq + (p.nq + p.nkv) * D + m * D + e];
+    }
   }
   __syncthreads();
   {
