@@ -65,6 +65,7 @@ dflash_status check_cfg(const dflash_config* c) {
   if (c->head_dim != 64 && c->head_dim != 128) return DFLASH_ESHAPE;
   if (c->n_q_heads % c->n_kv_heads) return DFLASH_ESHAPE;
   if (c->hidden % 64 || c->intermediate % 64 || (c->n_fuse * c->target_hidden) % 64) return DFLASH_ESHAPE;
+  if (c->hidden > 8192) return DFLASH_ESHAPE;
   if (c->page_size != 16) return DFLASH_ESHAPE;
   if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab) return DFLASH_EINVAL;
   if (!(c->rope_base > 0.f) || !(c->rms_eps >= 0.f)) return DFLASH_EINVAL;

@@ -62,23 +62,21 @@ __device__ __forceinline__ void att_barrier() {
 // position i: the context kernel then loads its MFMA operands directly.  The
 // queries carry the softmax scale times log2 e, so the scores come out ready
 // for the base-2 exponential.
-__global__ __launch_bounds__(256) void attn_qprep_kernel(AttnParams p, bf16_t* qhi, bf16_t* qlo) {
+__global__ __launch_bounds__(64) void attn_qprep_kernel(AttnParams p, bf16_t* qhi, bf16_t* qlo) {
+  // grid (R, n_kv, batch), one thread per element pair (2 e2, 2 e2 + 1)
   const int D = p.d, g = p.nq / p.nkv, R = g * p.B;
   const int ldq = (p.nq + 2 * p.nkv) * D;
   const float qscale = p.scale * 1.4426950408889634f;   // scores come out in base-2 units
-  const size_t total = (size_t)p.batch * p.nkv * R * (D / 2);
-  for (size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x; idx < total; idx += (size_t)gridDim.x * 256) {
-    const int e2 = (int)(idx % (D / 2));      // element pair (2 e2, 2 e2 + 1)
-    const size_t gr = idx / (D / 2);           // (b, m, r) row
-    const int r = (int)(gr % R), m = (int)((gr / R) % p.nkv), b = (int)(gr / ((size_t)R * p.nkv));
-    const int j = r / p.B, i = r - j * p.B, row = b * p.B + i, n = m * g + j;
-    const float* qv = p.qkv + (size_t)row * ldq + n * D;
-    const float2* cs = p.cs + (size_t)row * (D / 2);
-    uint32_t h, l;
-    split_hilo2(rope_elem(qv, cs, 2 * e2, D) * qscale, rope_elem(qv, cs, 2 * e2 + 1, D) * qscale, h, l);
-    ((uint32_t*)qhi)[gr * (D / 2) + e2] = h;
-    ((uint32_t*)qlo)[gr * (D / 2) + e2] = l;
-  }
+  const int r = blockIdx.x, m = blockIdx.y, b = blockIdx.z, e2 = threadIdx.x;
+  if (e2 >= D / 2) return;
+  const int j = r / p.B, i = r - j * p.B, row = b * p.B + i, n = m * g + j;
+  const float* qv = p.qkv + (size_t)row * ldq + n * D;
+  const float2* cs = p.cs + (size_t)row * (D / 2);
+  uint32_t h, l;
+  split_hilo2(rope_elem(qv, cs, 2 * e2, D) * qscale, rope_elem(qv, cs, 2 * e2 + 1, D) * qscale, h, l);
+  const size_t gr = ((size_t)b * p.nkv + m) * R + r;
+  ((uint32_t*)qhi)[gr * (D / 2) + e2] = h;
+  ((uint32_t*)qlo)[gr * (D / 2) + e2] = l;
 }
 
 // Context part of the block attention, one (context split, kv head, sequence,
@@ -534,9 +532,7 @@ hipError_t launch_attention(const AttnParams& p, int wdtype, hipStream_t s, void
   const int g = p.nq / p.nkv, R = g * p.B, nqg = (R + 63) / 64;
   const dim3 gctx(p.n_splits * nqg, p.nkv, p.batch);
   if (wdtype == 1 && p.d == 128) {
-    const size_t total = (size_t)p.batch * p.nkv * R * (p.d / 2);
-    const int blocks = (int)std::min<size_t>((total + 255) / 256, 4096);
-    hipLaunchKernelGGL(attn_qprep_kernel, dim3(blocks), dim3(256), 0, s, p, p.q_hi, p.q_lo);
+    hipLaunchKernelGGL(attn_qprep_kernel, dim3(R, p.nkv, p.batch), dim3(p.d / 2), 0, s, p, p.q_hi, p.q_lo);
   }
   if (mark) mark(0, s);
   if (wdtype == 1 && p.d == 128)

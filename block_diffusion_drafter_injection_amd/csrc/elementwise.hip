@@ -54,6 +54,8 @@ __global__ void embed_kernel(const int* tau, const T* embed, int vocab, float* h
 // One workgroup per output row.  With committed != null the output rows are
 // the still-open positions of each sequence in position order (n_open per
 // sequence) and row_map receives b*B + i for each.
+constexpr int kRmsVec = 8;   // float4 per thread: rows up to 8192 wide
+
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, const float* gain, ActOut out, int H,
                                                       float eps, const int* committed, int B, int n_open,
                                                       int* row_map) {
@@ -77,22 +79,32 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, const floa
     src_s = src;
   }
   __syncthreads();
+  // the row is read once into registers (H <= 256 * 4 * kRmsVec); squares are
+  // summed in fp32 per thread (at most 4 * kRmsVec terms) and in double across
+  // threads
   const float* x = h + (size_t)src_s * H;
-  double ss = 0.0;
-  for (int c = tid; c < H; c += 256) {
-    const double v = x[c];
-    ss += v * v;
-  }
+  float4 v[kRmsVec];
+  float ss = 0.f;
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, kWave);
-  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  for (int k = 0; k < kRmsVec; ++k) {
+    const int c = tid * 4 + 1024 * k;
+    v[k] = c < H ? *(const float4*)(x + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
+  }
+  double sd = ss;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sd += __shfl_xor(sd, o, kWave);
+  if ((tid & 63) == 0) red[tid >> 6] = sd;
   __syncthreads();
   const double tot = red[0] + red[1] + red[2] + red[3];
   const float rs = (float)(1.0 / sqrt(tot / (double)H + (double)eps));
-  for (int c = tid * 4; c < H; c += 1024) {
-    const float4 v = *(const float4*)(x + c);
-    const float4 gg = *(const float4*)(gain + c);
-    act_store4(out, r, c, make_float4(v.x * rs * gg.x, v.y * rs * gg.y, v.z * rs * gg.z, v.w * rs * gg.w));
+#pragma unroll
+  for (int k = 0; k < kRmsVec; ++k) {
+    const int c = tid * 4 + 1024 * k;
+    if (c < H) {
+      const float4 gg = *(const float4*)(gain + c);
+      act_store4(out, r, c, make_float4(v[k].x * rs * gg.x, v[k].y * rs * gg.y, v[k].z * rs * gg.z, v[k].w * rs * gg.w));
+    }
   }
 }
 

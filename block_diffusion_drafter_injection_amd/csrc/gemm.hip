@@ -29,6 +29,19 @@ struct BRows {
   }
 };
 
+// SwiGLU rows interleaved per 32 columns of a BN tile: 16 gate rows (b0),
+// then the same 16 up rows (b1).
+__device__ __forceinline__ const bf16_t* swiglu_il_row(const BRows<bf16_t>& b, int n, int BN) {
+  const int h = BN / 2, t = n / BN, c = n - t * BN, q = c >> 5, w = c & 31;
+  return (w < 16 ? b.b0 : b.b1) + (size_t)(t * h + q * 16 + (w & 15)) * b.ldb;
+}
+// Tile column (interleaved order) -> column in the gate-half / up-half order
+// the split-K reduce expects.
+__device__ __forceinline__ int swiglu_il_col(int c, int BN) {
+  const int q = c >> 5, w = c & 31;
+  return w < 16 ? q * 16 + w : BN / 2 + q * 16 + (w - 16);
+}
+
 // ---------------------------------------------------------------------------
 // LM-head partials: over a run of columns, (max of the score the candidate
 // maximises, its first index, max and sum-exp of z/T, z/T at that index).
@@ -761,6 +774,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_fl_kernel(ActIn a, BRo
                                                                      int ksplit, float* part, EpiParams e) {
   using C = FlCfg<BM, BN, WGM, WGN, NP>;
   constexpr int BK = C::BK, LPT = C::LPT, FM = C::FM, FN = C::FN, NT = C::NT;
+  // SwiGLU tiles load gate and up rows interleaved per 32 columns, so each
+  // wave holds both halves of its output columns
+  constexpr bool IL = KIND == EPI_SWIGLU && C::WN % 32 == 0;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::SMEM];
 
   const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
@@ -795,10 +811,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_fl_kernel(ActIn a, BRo
       bbase[q] = (const bf16_t*)(p == 0 ? a.p0 : a.p1);
       boff[q] = (uint32_t)(((size_t)gr * a.ld + lc * 8) * 2);
     } else {
+      // rows of a block are consecutive rows of one buffer (a clamped row only
+      // occurs in a block that lies past the split / half boundaries)
       const int first = min(n0 + row0 - NP * BM, N - 1);
-      const bf16_t* rb = b.row(first, BN);
+      const bf16_t* rb = IL ? swiglu_il_row(b, first, BN) : b.row(first, BN);
       bbase[q] = rb;
-      boff[q] = (uint32_t)((b.row(min(n0 + row - NP * BM, N - 1), BN) - rb + lc * 8) * 2);
+      boff[q] = (uint32_t)(((size_t)(min(n0 + row - NP * BM, N - 1) - first) * b.ldb + lc * 8) * 2);
     }
   }
   const uint32_t lds0 = (uint32_t)(size_t)smem;
@@ -875,6 +893,35 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_fl_kernel(ActIn a, BRo
 #undef FL_LOAD
 #undef FL_MMA
 #undef FL_ISSUE
+  if constexpr (IL) {
+    // MFMA blocks 2k and 2k+1 of a wave are the gate and up values of the
+    // same 16 output columns, so SiLU(g) * u is formed and stored straight
+    // from the accumulators.
+    // Each wave stages its 64 x (WN/2) outputs in a private LDS slice, then
+    // stores four consecutive columns per lane (8-byte hi and lo stores).
+    if (ksplit == 1) {
+      constexpr int OW = C::WN / 2, LDW = OW + 4;
+      static_assert(8 * 64 * LDW * 4 <= C::SMEM, "per-wave output slices");
+      float* wl = (float*)smem + wid * (64 * LDW);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+#pragma unroll
+          for (int k = 0; k < FN / 2; ++k)
+            wl[(16 * i + 4 * lq + q) * LDW + 16 * k + lr] = silu_fast(acc[i][2 * k][q]) * acc[i][2 * k + 1][q];
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's slice is written
+      const int ocol0 = n0 / 2 + wn * OW;
+      constexpr int C4 = OW / 4;
+#pragma unroll
+      for (int t = 0; t < 64 * C4 / 64; ++t) {
+        const int idx = lane + 64 * t, r = idx / C4, c = (idx - r * C4) * 4;
+        const int row = m0 + wm * C::WM + r;
+        if (row < M && ocol0 + c < N / 2) act_store4(e.out, row, ocol0 + c, *(const float4*)(wl + r * LDW + c));
+      }
+      return;
+    }
+  }
   if constexpr (KIND == EPI_LMHEAD && C::WN == 128) {
     // Greedy LM-head partials straight from the accumulators: a wave's 128
     // columns are one partial group; lane (lq, lr) holds rows 16i+4lq+q at
@@ -950,8 +997,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_fl_kernel(ActIn a, BRo
       constexpr int C4 = BN / 4;
       for (int idx = tid; idx < 64 * C4; idx += NT) {
         const int r = idx / C4, c = (idx - r * C4) * 4;
+        // interleaved SwiGLU columns go back to gate-half / up-half order (runs
+        // of four stay within one 16-column group)
+        const int cd = IL ? swiglu_il_col(c, BN) : c;
         if (ms + r < M && n0 + c < N)
-          *(float4*)(dst + (size_t)(ms + r) * N + n0 + c) = *(const float4*)(Cs + r * C::LDC + c);
+          *(float4*)(dst + (size_t)(ms + r) * N + n0 + cd) = *(const float4*)(Cs + r * C::LDC + c);
       }
     } else {
       run_epilogue<KIND, 64, BN, NT, bf16_t>(Cs, C::LDC, ms, n0, M, N, e);

@@ -12,7 +12,9 @@ enum EpiKind : int { EPI_STORE = 0, EPI_ADD = 1, EPI_SWIGLU = 2, EPI_LMHEAD = 3,
 
 // Rows of W.  mode 0: row n of b0.  mode 1: rows [0, split) of b0 then b1.
 // mode 2 (SwiGLU): each tile of BN columns holds BN/2 rows of b0 (gate) then
-// the same BN/2 rows of b1 (up).
+// the same BN/2 rows of b1 (up); a kernel may load them interleaved (16 gate
+// rows, then the same 16 up rows, per 32 columns) as long as its output
+// follows the same contract.
 struct BRowsArgs {
   const void* b0;
   const void* b1;

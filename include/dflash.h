@@ -65,7 +65,7 @@ typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 
 /* Draft model dimensions.  Limits: head_dim in {64, 128}; n_q_heads a
  * multiple of n_kv_heads; hidden, intermediate, n_fuse*target_hidden and
- * n_q_heads*head_dim multiples of 64; page_size 16; 0 <= mask_token_id <
+ * n_q_heads*head_dim multiples of 64; hidden <= 8192; page_size 16; 0 <= mask_token_id <
  * vocab.  rope_base > 0 (rotate-half pairing (x_j, x_{j+d/2}), frequency
  * rope_base^(-2j/d)).  rms_eps >= 0. */
 typedef struct {

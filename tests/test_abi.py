@@ -56,6 +56,7 @@ def test_workspace_size_rejects_bad_configs(L):
     assert B.dflash_workspace_size(_cfg(dtype=7), 4, 8, 64, 512) == 0
     assert B.dflash_workspace_size(_cfg(), 4, 17, 64, 512) == 0
     assert B.dflash_workspace_size(_cfg(hidden=500), 4, 8, 64, 512) == 0
+    assert B.dflash_workspace_size(_cfg(hidden=8256), 4, 8, 64, 512) == 0   # rows wider than 8192
 
 
 def test_workspace_grows_with_batch_and_context(L):
