@@ -13,6 +13,7 @@ Prints one JSON line (see --help for options).
 """
 import argparse
 import json
+import re
 import math
 import os
 import sys
@@ -44,14 +45,15 @@ def parse():
 
 
 COPY_BYTES = 1 << 29          # 512 MiB read + 512 MiB written by the calibration copy
-# kernel class -> name pattern of the kernel it times (rocprofv3 kernel names)
+# Kernel name patterns (regular expressions) of each timed class: GEMM kernels
+# end their template arguments with (operand planes, epilogue kind).
 KERNEL_NAMES = {
-    "attn": "attn_ctx_mfma_kernel",
-    "gemm_qkv": "gemm_dma_kernel<2, 0>",
-    "gemm_o": "gemm_dma_kernel<2, 1>",
-    "gemm_down": "gemm_dma_kernel<2, 1>",
-    "gemm_gateup": "gemm_dma_kernel<2, 2>",
-    "lmhead": "gemm_dma_kernel<1, 3>",
+    "attn": r"attn_ctx_mfma_kernel",
+    "gemm_qkv": r"gemm_\w+_kernel<[^>]*, 2, 0>",
+    "gemm_o": r"gemm_\w+_kernel<[^>]*, 2, 1>",
+    "gemm_down": r"gemm_\w+_kernel<[^>]*, 2, 1>",
+    "gemm_gateup": r"gemm_\w+_kernel<[^>]*, 2, 2>",
+    "lmhead": r"gemm_\w+_kernel<[^>]*, 1, 3>",
 }
 KERNEL_SOURCES = ["common.h", "kernels.h", "gemm.hip", "attention.hip", "elementwise.hip", "verify.hip", "api.cpp"]
 
@@ -362,7 +364,7 @@ def summarize(trace_dir, fetch_dir, write_dir):
           f"Kernel sources hash: {h}", "",
           "| class | kernel | FETCH KiB/launch | WRITE KiB/launch | scaled MB/launch |", "|---|---|---|---|---|"]
     for cls, pat in KERNEL_NAMES.items():
-        ks = [k for k in counters["FETCH_SIZE"] if pat in k]
+        ks = [k for k in counters["FETCH_SIZE"] if re.search(pat, k)]
         if not ks:
             continue
         f = float(np.mean([v for k in ks for v in counters["FETCH_SIZE"][k]]))
