@@ -121,7 +121,7 @@ int n_qgroups(const dflash_config* c, int B) { return ((c->n_q_heads / c->n_kv_h
 
 struct DraftWS {
   size_t h, u_hi, u_lo, qkv, o_hi, o_lo, act_hi, act_lo, y, row_map, part_f, part_i, att_o, att_lse, cs, tau,
-      committed, cand, conf, gemm_part, q_hi, q_lo, total;
+      committed, cand, conf, gemm_part, q_hi, q_lo, kblk, total;
   int ns, pps, ntiles;
 };
 
@@ -154,6 +154,7 @@ DraftWS draft_layout(const dflash_config* c, int bt, int B, int ctx_cap) {
   w.conf = k.take(M * 4);
   w.q_hi = k.take(M * nq * d * 2);
   w.q_lo = k.take(M * nq * d * 2);
+  w.kblk = k.take(M * nkv * d * 4);
   {
     const int wd = c->dtype == DFLASH_BF16;
     const int am = wd ? ACT_HILO : ACT_F32;
@@ -376,6 +377,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
   ap.part_lse = (float*)at(workspace, L.att_lse);
   ap.q_hi = (bf16_t*)at(workspace, L.q_hi);
   ap.q_lo = (bf16_t*)at(workspace, L.q_lo);
+  ap.kblk = (float*)at(workspace, L.kblk);
 
   HIP_TRY(launch_rope_table_block(ctx_len, ctx_cap, batch, B, d, (double)cfg->rope_base, cs, stream));
   HIP_TRY(launch_block_init(tau, committed, M, cfg->mask_token_id, stream));
@@ -402,7 +404,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
 
       ap.layer = l;
       HIP_TRY(launch_attention(ap, bf, stream, g_prof.cls == DFLASH_PROF_ATTN ? prof_attn : nullptr));
-      HIP_TRY(launch_attn_finish(ap, o, stream));
+      HIP_TRY(launch_attn_finish(ap, bf, o, stream));
 
       GemmArgs go{};
       go.wdtype = bf;

@@ -61,7 +61,8 @@ __device__ __forceinline__ void att_barrier() {
 // in [b][kv head][r][d] order, r = j*B + i for head m*g + j and block
 // position i: the context kernel then loads its MFMA operands directly.  The
 // queries carry the softmax scale times log2 e, so the scores come out ready
-// for the base-2 exponential.
+// for the base-2 exponential.  The rotated block keys (fp32) are written too,
+// [b][kv head][i][d], for the in-block part of the attention.
 __global__ __launch_bounds__(64) void attn_qprep_kernel(AttnParams p, bf16_t* qhi, bf16_t* qlo) {
   // grid (R, n_kv, batch), one thread per element pair (2 e2, 2 e2 + 1)
   const int D = p.d, g = p.nq / p.nkv, R = g * p.B;
@@ -77,6 +78,15 @@ __global__ __launch_bounds__(64) void attn_qprep_kernel(AttnParams p, bf16_t* qh
   const size_t gr = ((size_t)b * p.nkv + m) * R + r;
   ((uint32_t*)qhi)[gr * (D / 2) + e2] = h;
   ((uint32_t*)qlo)[gr * (D / 2) + e2] = l;
+  if (r < p.B) {   // the block key of position r, rotated (fp32)
+    const int krow = b * p.B + r;
+    const float* kv = p.qkv + (size_t)krow * ldq + p.nq * D + m * D;
+    const float2* kcs = p.cs + (size_t)krow * (D / 2);
+    float2 kr;
+    kr.x = rope_elem(kv, kcs, 2 * e2, D);
+    kr.y = rope_elem(kv, kcs, 2 * e2 + 1, D);
+    *(float2*)(p.kblk + (((size_t)b * p.nkv + m) * p.B + r) * D + 2 * e2) = kr;
+  }
 }
 
 // Context part of the block attention, one (context split, kv head, sequence,
@@ -423,82 +433,131 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Block keys and merge, per (16 query rows, kv head, sequence): the rotated
-// queries and the B block keys / values (fp32) are staged in LDS; each row
-// attends to the B keys (softmax in fp32); the result is merged with the
-// n_splits context partials in split order (block part last) and written in
-// the operand form of the output projection.
-template <int D>
+// Block keys and merge, per (16 query rows, kv head, sequence), sixteen
+// threads per query row: the B rotated block keys and their values (fp32) are
+// staged in LDS; each thread keeps 1/16 of its row's rotated query in
+// registers, the partial dot products of a key are summed over the row's
+// lanes, the row attends to the B keys (softmax in fp32), and the result is
+// merged with the n_splits context partials in split order (block part last)
+// and written in the operand form of the output projection.
+// Value of another lane of the same 16-lane row, by a DPP control (quad
+// permutation or row rotation): no LDS round trip.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+template <int D, bool PREP>
 __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut out) {
-  constexpr int QR = 16, DPT = D / 16;
-  __shared__ float qs[QR][D + 1];
-  __shared__ float kb[16][D + 1], vb[16][D + 1];
-  __shared__ float pb[QR][17];
-  __shared__ float blse[QR];
-  const int g = p.nq / p.nkv, R = g * p.B;
+  constexpr int QR = 16, DPT = D / 16;   // 16 threads per query row, DPT dims each
+  static_assert(DPT % 4 == 0, "dims per thread");
+  __shared__ __attribute__((aligned(16))) float kb[16][D];
+  __shared__ __attribute__((aligned(16))) float vb[16][D];
+  const int g = p.nq / p.nkv, R = g * p.B, h = D / 2;
   const int qg = blockIdx.x, m = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int ldq = (p.nq + 2 * p.nkv) * D;
-  // fixed trip counts, unrolled: every load of the staging is in flight at once
+  // Every global read is unconditional and four wide: block rows past B and
+  // query rows past the group are clamped to a valid row (and masked or
+  // dropped later), so all reads are in flight before the first use.
+  constexpr int KV4 = 16 * D / 4 / 256;   // float4 of K (and of V) per thread
 #pragma unroll
-  for (int k = 0; k < QR * D / 256; ++k) {
-    const int c = tid + 256 * k;
-    const int r = c / D, e = c - r * D, rr = qg * QR + r;
-    float v = 0.f;
-    if (rr < R) {
-      const int j = rr / p.B, i = rr - j * p.B, row = b * p.B + i, n = m * g + j;
-      v = rope_elem(p.qkv + (size_t)row * ldq + n * D, p.cs + (size_t)row * (D / 2), e, D);
+  for (int k = 0; k < KV4; ++k) {
+    const int c4 = tid + 256 * k, jb = (4 * c4) / D, e = 4 * c4 - jb * D;
+    const int jc = min(jb, p.B - 1), krow = b * p.B + jc;
+    const float4 vv = *(const float4*)(p.qkv + (size_t)krow * ldq + (p.nq + p.nkv) * D + m * D + e);
+    float4 kk;
+    if constexpr (PREP) {
+      kk = *(const float4*)(p.kblk + (((size_t)b * p.nkv + m) * p.B + jc) * D + e);
+    } else {
+      const float* kv = p.qkv + (size_t)krow * ldq + p.nq * D + m * D;
+      const float2* cs = p.cs + (size_t)krow * h;
+      kk = make_float4(rope_elem(kv, cs, e, D), rope_elem(kv, cs, e + 1, D), rope_elem(kv, cs, e + 2, D),
+                       rope_elem(kv, cs, e + 3, D));
     }
-    qs[r][e] = v;
+    *(float4*)&kb[jb][e] = kk;
+    *(float4*)&vb[jb][e] = vv;
   }
+  const int rl = tid >> 4, part = tid & 15, rr = qg * QR + rl;
+  const bool rv = rr < R;
+  const int rc = rv ? rr : R - 1;
+  const int j = rc / p.B, i = rc - j * p.B;
+  const int row = b * p.B + i, n = m * g + j;
+  const int d0 = part * DPT;   // this thread's dims d0 .. d0 + DPT - 1
+  float q[DPT];
+  if constexpr (PREP) {
+    // prepared rotated query (hi + lo), carrying scale * log2 e
+    const size_t qoff = (((size_t)b * p.nkv + m) * R + rc) * D + d0;
 #pragma unroll
-  for (int k = 0; k < 16 * D / 256; ++k) {
-    const int c = tid + 256 * k;
-    const int jb = c / D, e = c - jb * D, krow = b * p.B + jb;
-    if (jb < p.B) {
-      kb[jb][e] = rope_elem(p.qkv + (size_t)krow * ldq + p.nq * D + m * D, p.cs + (size_t)krow * (D / 2), e, D);
-      vb[jb][e] = p.qkv[(size_t)krow * ldq + (p.nq + p.nkv) * D + m * D + e];
+    for (int k = 0; k < DPT; k += 4) {
+      // a bf16 is the high half of an fp32: element 2t of a word is w << 16,
+      // element 2t+1 is w & 0xffff0000
+      const u32x2 hv = *(const u32x2*)(p.q_hi + qoff + k), lv = *(const u32x2*)(p.q_lo + qoff + k);
+      q[k] = __uint_as_float(hv.x << 16) + __uint_as_float(lv.x << 16);
+      q[k + 1] = __uint_as_float(hv.x & 0xffff0000u) + __uint_as_float(lv.x & 0xffff0000u);
+      q[k + 2] = __uint_as_float(hv.y << 16) + __uint_as_float(lv.y << 16);
+      q[k + 3] = __uint_as_float(hv.y & 0xffff0000u) + __uint_as_float(lv.y & 0xffff0000u);
     }
+  } else {
+    const float* qv = p.qkv + (size_t)row * ldq + n * D;
+    const float2* cs = p.cs + (size_t)row * h;
+#pragma unroll
+    for (int e = 0; e < DPT; ++e) q[e] = rope_elem(qv, cs, d0 + e, D) * p.scale * 1.4426950408889634f;
   }
   __syncthreads();
-  {
-    const int r = tid >> 4, key = tid & 15;
-    float sc = -INFINITY;
-    if (key < p.B) {
-      float dot = 0.f;
-#pragma unroll 8
-      for (int e = 0; e < D; ++e) dot = fmaf(qs[r][e], kb[key][e], dot);
-      sc = dot * p.scale;
+  // scores in base-2 units: partial dot over this thread's dims, summed over
+  // the row's sixteen lanes (DPP: lane ^ 1, lane ^ 2, then rotations by 4, 8)
+  float sc[16];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    float a = 0.f;
+#pragma unroll
+    for (int e = 0; e < DPT; e += 4) {
+      const float4 kv = *(const float4*)&kb[k][d0 + e];
+      a = fmaf(q[e], kv.x, a);
+      a = fmaf(q[e + 1], kv.y, a);
+      a = fmaf(q[e + 2], kv.z, a);
+      a = fmaf(q[e + 3], kv.w, a);
     }
-    float mx = sc;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, kWave));
-    const float ex = key < p.B ? expf(sc - mx) : 0.f;
-    float sum = ex;
-#pragma unroll
-    for (int o = 1; o < 16; o <<= 1) sum += __shfl_xor(sum, o, kWave);
-    pb[r][key] = ex / sum;
-    if (key == 0) blse[r] = mx + logf(sum);
+    a += dpp_mov<0xB1>(a);
+    a += dpp_mov<0x4E>(a);
+    a += dpp_mov<0x124>(a);   // row_ror:4
+    a += dpp_mov<0x128>(a);   // row_ror:8
+    sc[k] = k < p.B ? a : -INFINITY;
+    mx = fmaxf(mx, sc[k]);
   }
-  __syncthreads();
-  const int r = tid >> 4, d0 = (tid & 15) * DPT, rr = qg * QR + r;
-  if (rr >= R) return;
-  const int j = rr / p.B, i = rr - j * p.B, row = b * p.B + i, n = m * g + j;
-  const size_t Mq = (size_t)p.batch * p.B * p.nq;
-  const size_t qrow = (size_t)row * p.nq + n;
+  float sum = 0.f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    sc[k] = k < p.B ? __builtin_amdgcn_exp2f(sc[k] - mx) : 0.f;
+    sum += sc[k];
+  }
+  const float blse = (mx + __log2f(sum)) * 0.6931471805599453f;   // natural log, as the context partials
+  const float rs = 1.f / sum;
   float ob[DPT];
 #pragma unroll
-  for (int k = 0; k < DPT; ++k) ob[k] = 0.f;
-  for (int jb = 0; jb < p.B; ++jb) {
-    const float w = pb[r][jb];
+  for (int e = 0; e < DPT; ++e) ob[e] = 0.f;
 #pragma unroll
-    for (int k = 0; k < DPT; ++k) ob[k] = fmaf(w, vb[jb][d0 + k], ob[k]);
+  for (int k = 0; k < 16; ++k) {
+    const float w = sc[k] * rs;
+#pragma unroll
+    for (int e = 0; e < DPT; e += 4) {
+      const float4 vv = *(const float4*)&vb[k][d0 + e];
+      ob[e] = fmaf(w, vv.x, ob[e]);
+      ob[e + 1] = fmaf(w, vv.y, ob[e + 1]);
+      ob[e + 2] = fmaf(w, vv.z, ob[e + 2]);
+      ob[e + 3] = fmaf(w, vv.w, ob[e + 3]);
+    }
   }
-  float mxl = blse[r];
+  if (!rv) return;
+  const size_t Mq = (size_t)p.batch * p.B * p.nq;
+  const size_t qrow = (size_t)row * p.nq + n;
+  float mxl = blse;
   for (int sp = 0; sp < p.n_splits; ++sp) mxl = fmaxf(mxl, p.part_lse[sp * Mq + qrow]);
   float tot = 0.f, acc[DPT];
 #pragma unroll
-  for (int k = 0; k < DPT; ++k) acc[k] = 0.f;
+  for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
   for (int sp = 0; sp < p.n_splits; ++sp) {
     const float l = p.part_lse[sp * Mq + qrow];
     if (l == -INFINITY) continue;
@@ -506,34 +565,36 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
     tot += w;
     const float* src = p.part_o + (sp * Mq + qrow) * D + d0;
 #pragma unroll
-    for (int k = 0; k < DPT; k += 4) {
-      const float4 v = *(const float4*)(src + k);
-      acc[k] = fmaf(w, v.x, acc[k]);
-      acc[k + 1] = fmaf(w, v.y, acc[k + 1]);
-      acc[k + 2] = fmaf(w, v.z, acc[k + 2]);
-      acc[k + 3] = fmaf(w, v.w, acc[k + 3]);
+    for (int e = 0; e < DPT; e += 4) {
+      const float4 v = *(const float4*)(src + e);
+      acc[e] = fmaf(w, v.x, acc[e]);
+      acc[e + 1] = fmaf(w, v.y, acc[e + 1]);
+      acc[e + 2] = fmaf(w, v.z, acc[e + 2]);
+      acc[e + 3] = fmaf(w, v.w, acc[e + 3]);
     }
   }
   {
-    const float w = expf(blse[r] - mxl);
+    const float w = expf(blse - mxl);
     tot += w;
 #pragma unroll
-    for (int k = 0; k < DPT; ++k) acc[k] = fmaf(w, ob[k], acc[k]);
+    for (int e = 0; e < DPT; ++e) acc[e] = fmaf(w, ob[e], acc[e]);
   }
   const float inv = 1.f / tot;
 #pragma unroll
-  for (int k = 0; k < DPT; k += 4)
-    act_store4(out, row, n * D + d0 + k, make_float4(acc[k] * inv, acc[k + 1] * inv, acc[k + 2] * inv, acc[k + 3] * inv));
+  for (int e = 0; e < DPT; e += 4)
+    act_store4(out, row, n * D + d0 + e, make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv));
 }
 
 // ---------------------------------------------------------------------------
 hipError_t launch_attention(const AttnParams& p, int wdtype, hipStream_t s, void (*mark)(int, hipStream_t)) {
-  if (p.n_splits <= 0) return hipSuccess;
   const int g = p.nq / p.nkv, R = g * p.B, nqg = (R + 63) / 64;
-  const dim3 gctx(p.n_splits * nqg, p.nkv, p.batch);
+  // the prepared queries and block keys also feed the finish kernel, with or
+  // without context
   if (wdtype == 1 && p.d == 128) {
     hipLaunchKernelGGL(attn_qprep_kernel, dim3(R, p.nkv, p.batch), dim3(p.d / 2), 0, s, p, p.q_hi, p.q_lo);
   }
+  if (p.n_splits <= 0) return hipGetLastError();
+  const dim3 gctx(p.n_splits * nqg, p.nkv, p.batch);
   if (mark) mark(0, s);
   if (wdtype == 1 && p.d == 128)
     hipLaunchKernelGGL(attn_ctx_mfma_kernel<128>, gctx, dim3(256), 0, s, p);
@@ -547,13 +608,15 @@ hipError_t launch_attention(const AttnParams& p, int wdtype, hipStream_t s, void
   return hipGetLastError();
 }
 
-hipError_t launch_attn_finish(const AttnParams& p, ActOut out, hipStream_t s) {
+hipError_t launch_attn_finish(const AttnParams& p, int wdtype, ActOut out, hipStream_t s) {
   const int R = (p.nq / p.nkv) * p.B;
   const dim3 grid((R + 15) / 16, p.nkv, p.batch);
-  if (p.d == 128)
-    hipLaunchKernelGGL(attn_finish_kernel<128>, grid, dim3(256), 0, s, p, out);
+  if (wdtype == 1 && p.d == 128)   // the query prep ran: prepared queries and block keys
+    hipLaunchKernelGGL((attn_finish_kernel<128, true>), grid, dim3(256), 0, s, p, out);
+  else if (p.d == 128)
+    hipLaunchKernelGGL((attn_finish_kernel<128, false>), grid, dim3(256), 0, s, p, out);
   else
-    hipLaunchKernelGGL(attn_finish_kernel<64>, grid, dim3(256), 0, s, p, out);
+    hipLaunchKernelGGL((attn_finish_kernel<64, false>), grid, dim3(256), 0, s, p, out);
   return hipGetLastError();
 }
 

@@ -86,11 +86,12 @@ struct AttnParams {
   float* part_lse;        // [n_splits, M*nq] their log-sum-exp
   bf16_t* q_hi;           // [batch, nkv, g*B, d] rotated queries, hi plane (bf16 pools)
   bf16_t* q_lo;           // same, lo plane
+  float* kblk;            // [batch, nkv, B, d] rotated block keys, fp32 (bf16 pools)
 };
 // Context splits -> partials (no launch when there is no context).
 hipError_t launch_attention(const AttnParams& p, int wdtype, hipStream_t s, void (*mark)(int, hipStream_t));
 // In-block keys + merge with the partials -> attention output as GEMM operand.
-hipError_t launch_attn_finish(const AttnParams& p, ActOut out, hipStream_t s);
+hipError_t launch_attn_finish(const AttnParams& p, int wdtype, ActOut out, hipStream_t s);
 
 // Elementwise and bookkeeping kernels.
 hipError_t launch_rope_table_block(const int* ctx_len, int ctx_cap, int batch, int B, int d,
