@@ -388,8 +388,12 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
     const int n_open = B - done;
     const int last = s == S - 1;
     HIP_TRY(launch_embed(tau, w->embed, bf, cfg->vocab, h, M, H, stream));
+    int pending_ks = 0;   // K splits of a down projection whose partials the next norm folds in
     for (int l = 0; l < cfg->n_layers; ++l) {
-      HIP_TRY(launch_rmsnorm(h, w->attn_norm[l], u, M, H, cfg->rms_eps, nullptr, B, 0, nullptr, stream));
+      // the previous layer's down projection left its K-split partials to this norm
+      HIP_TRY(launch_rmsnorm(h, w->attn_norm[l], u, M, H, cfg->rms_eps, nullptr, B, 0, nullptr, stream,
+                             pending_ks > 1 ? gpart : nullptr, pending_ks));
+      pending_ks = 0;
       GemmArgs g{};
       g.wdtype = bf;
       g.a = act_in(u);
@@ -417,9 +421,12 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
       go.kind = EPI_ADD;
       go.e.resid = h;
       go.e.ldr = H;
+      go.defer_reduce = true;   // folded into the MLP norm below
+      const int ks_o = gemm_ksplit(go);
       HIP_TRY(gemm(DFLASH_PROF_GEMM_O, go, stream));
 
-      HIP_TRY(launch_rmsnorm(h, w->mlp_norm[l], u, M, H, cfg->rms_eps, nullptr, B, 0, nullptr, stream));
+      HIP_TRY(launch_rmsnorm(h, w->mlp_norm[l], u, M, H, cfg->rms_eps, nullptr, B, 0, nullptr, stream,
+                             ks_o > 1 ? gpart : nullptr, ks_o));
       GemmArgs gu{};
       gu.wdtype = bf;
       gu.a = act_in(u);
@@ -443,6 +450,8 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
       gd.kind = EPI_ADD;
       gd.e.resid = h;
       gd.e.ldr = H;
+      gd.defer_reduce = l + 1 < cfg->n_layers;   // folded into the next layer's attention norm
+      if (gd.defer_reduce) pending_ks = gemm_ksplit(gd);
       HIP_TRY(gemm(DFLASH_PROF_GEMM_DOWN, gd, stream));
     }
     const int Ms = batch * n_open;

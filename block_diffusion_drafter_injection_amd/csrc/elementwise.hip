@@ -56,9 +56,9 @@ __global__ void embed_kernel(const int* tau, const T* embed, int vocab, float* h
 // sequence) and row_map receives b*B + i for each.
 constexpr int kRmsVec = 8;   // float4 per thread: rows up to 8192 wide
 
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, const float* gain, ActOut out, int H,
+__global__ __launch_bounds__(256) void rmsnorm_kernel(float* h, const float* gain, ActOut out, int H,
                                                       float eps, const int* committed, int B, int n_open,
-                                                      int* row_map) {
+                                                      int* row_map, const float* part, int ksplit, int M) {
   __shared__ double red[4];
   __shared__ int src_s;
   const int r = blockIdx.x, tid = threadIdx.x;
@@ -82,13 +82,24 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* h, const floa
   // the row is read once into registers (H <= 256 * 4 * kRmsVec); squares are
   // summed in fp32 per thread (at most 4 * kRmsVec terms) and in double across
   // threads
-  const float* x = h + (size_t)src_s * H;
+  float* x = h + (size_t)src_s * H;
   float4 v[kRmsVec];
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < kRmsVec; ++k) {
     const int c = tid * 4 + 1024 * k;
     v[k] = c < H ? *(const float4*)(x + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    if (part && c < H) {
+      // residual += sum of the split-K partials, in split order (the same sums
+      // the split-K reduce would form)
+      float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int sp = 0; sp < ksplit; ++sp) {
+        const float4 pv = *(const float4*)(part + ((size_t)sp * M + src_s) * H + c);
+        a.x += pv.x; a.y += pv.y; a.z += pv.z; a.w += pv.w;
+      }
+      v[k].x += a.x; v[k].y += a.y; v[k].z += a.z; v[k].w += a.w;
+      *(float4*)(x + c) = v[k];
+    }
     ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
   }
   double sd = ss;
@@ -206,11 +217,13 @@ hipError_t launch_embed(const int* tau, const void* embed, int wdtype, int vocab
   return hipGetLastError();
 }
 
-hipError_t launch_rmsnorm(const float* h, const float* gain, ActOut out, int M, int H, float eps,
-                          const int* committed, int B, int n_open, int* row_map, hipStream_t s) {
+hipError_t launch_rmsnorm(float* h, const float* gain, ActOut out, int M, int H, float eps,
+                          const int* committed, int B, int n_open, int* row_map, hipStream_t s,
+                          const float* part, int ksplit) {
   if (M <= 0) return hipSuccess;
+  if (committed) part = nullptr;   // the gathered form never folds partials
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(256), 0, s, h, gain, out, H, eps, committed, B, n_open,
-                     row_map);
+                     row_map, part, part ? ksplit : 0, M);
   return hipGetLastError();
 }
 

@@ -1101,6 +1101,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(ActIn a, BRows<float> b, 
 #ifndef DFLASH_T_LMHEAD
 #define DFLASH_T_LMHEAD 11
 #endif
+#ifndef DFLASH_T_LMHEAD_SMALL   // LM head with at most 256 rows (fewer idle CUs in the last round)
+#define DFLASH_T_LMHEAD_SMALL 11
+#endif
 #ifndef DFLASH_T_ADD
 #define DFLASH_T_ADD 12
 #endif
@@ -1135,7 +1138,7 @@ GemmPlan gemm_plan(int wdtype, int a_mode, int M, int N, int K, int kind, bool f
   int cfg = 2;
   if (!fixed_split && K % 32 == 0) {
     if (kind == EPI_SWIGLU) cfg = DFLASH_T_SWIGLU;
-    else if (kind == EPI_LMHEAD) cfg = DFLASH_T_LMHEAD;
+    else if (kind == EPI_LMHEAD) cfg = M > 256 ? DFLASH_T_LMHEAD : DFLASH_T_LMHEAD_SMALL;
     else if (kind == EPI_ADD) cfg = DFLASH_T_ADD;
     else if (kind == EPI_STORE) cfg = DFLASH_T_STORE;
     const bool one_plane = a_mode != ACT_HILO;
@@ -1185,7 +1188,7 @@ static hipError_t go_mfma(const GemmArgs& g, int ksplit, hipStream_t s) {
   hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, NP, STAGES, KIND>), dim3(grid), dim3(C::NT), 0, s, g.a, b,
                      g.M, g.N, g.K, ksplit, g.part, g.e);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || ksplit == 1) return err;
+  if (err != hipSuccess || ksplit == 1 || (g.defer_reduce && KIND == EPI_ADD)) return err;
   hipLaunchKernelGGL((splitk_reduce_kernel<16, BN, KIND, bf16_t>), dim3((g.M + 15) / 16 * ntn), dim3(256), 0, s,
                      g.part, ksplit, g.M, g.N, g.e);
   return hipGetLastError();
@@ -1209,7 +1212,7 @@ static hipError_t go_dma(const GemmArgs& g, int ksplit, hipStream_t s) {
   hipLaunchKernelGGL((gemm_dma_kernel<NP, KIND>), dim3(grid), dim3(256), 0, s, g.a, b, g.M, g.N, g.K, ksplit, g.part,
                      g.e);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || ksplit == 1) return err;
+  if (err != hipSuccess || ksplit == 1 || (g.defer_reduce && KIND == EPI_ADD)) return err;
   hipLaunchKernelGGL((splitk_reduce_kernel<16, 128, KIND, bf16_t>), dim3((g.M + 15) / 16 * ntn), dim3(256), 0, s,
                      g.part, ksplit, g.M, g.N, g.e);
   return hipGetLastError();
@@ -1224,7 +1227,7 @@ static hipError_t go_dma8(const GemmArgs& g, int ksplit, hipStream_t s) {
   hipLaunchKernelGGL((gemm_dma8_kernel<BM, BN, WGM, WGN, NP, STAGES, KIND>), dim3(grid), dim3(64 * WGM * WGN), 0, s, g.a, b,
                      g.M, g.N, g.K, ksplit, g.part, g.e);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || ksplit == 1) return err;
+  if (err != hipSuccess || ksplit == 1 || (g.defer_reduce && KIND == EPI_ADD)) return err;
   hipLaunchKernelGGL((splitk_reduce_kernel<16, BN, KIND, bf16_t>), dim3((g.M + 15) / 16 * ntn), dim3(256), 0, s,
                      g.part, ksplit, g.M, g.N, g.e);
   return hipGetLastError();
@@ -1239,7 +1242,7 @@ static hipError_t go_fl(const GemmArgs& g, int ksplit, hipStream_t s) {
   hipLaunchKernelGGL((gemm_fl_kernel<BM, BN, WGM, WGN, NP, KIND>), dim3(grid), dim3(64 * WGM * WGN), 0, s, g.a, b,
                      g.M, g.N, g.K, ksplit, g.part, g.e);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || ksplit == 1) return err;
+  if (err != hipSuccess || ksplit == 1 || (g.defer_reduce && KIND == EPI_ADD)) return err;
   hipLaunchKernelGGL((splitk_reduce_kernel<16, BN, KIND, bf16_t>), dim3((g.M + 15) / 16 * ntn), dim3(256), 0, s,
                      g.part, ksplit, g.M, g.N, g.e);
   return hipGetLastError();
@@ -1263,6 +1266,11 @@ static hipError_t go_bf16(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
     default: break;
   }
   return hipErrorInvalidValue;
+}
+
+int gemm_ksplit(const GemmArgs& g) {
+  if (g.wdtype == 0) return 1;
+  return gemm_plan(g.wdtype, g.a.mode, g.M, g.N, g.K, g.kind, g.fixed_split).ksplit;
 }
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {

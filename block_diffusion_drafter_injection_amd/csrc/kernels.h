@@ -58,6 +58,7 @@ struct GemmArgs {
   EpiParams e;
   bool fixed_split;      // K split chosen from (N, K) only: results independent of M
   float* part;           // split-K partials (gemm_partial_bytes of the plan), or null
+  bool defer_reduce;     // EPI_ADD with a K split: leave the partials for the next RMSNorm to fold in
 };
 
 struct GemmPlan {
@@ -67,6 +68,7 @@ struct GemmPlan {
 GemmPlan gemm_plan(int wdtype, int a_mode, int M, int N, int K, int kind, bool fixed_split);
 size_t gemm_partial_bytes(const GemmPlan& p, int M, int N);
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
+int gemm_ksplit(const GemmArgs& g);   // K split launch_gemm uses for g
 int gemm_bn(int wdtype, int K);  // columns per LM-head partial (partial count = ceil(N / bn))
 
 // Attention of the block queries over paged context KV plus in-block keys.
@@ -101,8 +103,11 @@ hipError_t launch_rope_table_tokens(const int* tok_pos, int n, int d, double bas
 hipError_t launch_block_init(int* tau, int* committed, int M, int mask_id, hipStream_t s);
 hipError_t launch_embed(const int* tau, const void* embed, int wdtype, int vocab, float* h, int M,
                         int H, hipStream_t s);
-hipError_t launch_rmsnorm(const float* h, const float* gain, ActOut out, int M, int H, float eps,
-                          const int* committed, int B, int n_open, int* row_map, hipStream_t s);
+// With part != null (and no row gather), h += sum over the ksplit partials
+// [ksplit][M][H] (in split order) first, and h is written back.
+hipError_t launch_rmsnorm(float* h, const float* gain, ActOut out, int M, int H, float eps,
+                          const int* committed, int B, int n_open, int* row_map, hipStream_t s,
+                          const float* part = nullptr, int ksplit = 0);
 hipError_t launch_lm_combine(const float4* part_f, const int* part_i, int ntiles, int rows,
                              const int* row_map, int* cand, float* conf, hipStream_t s);
 hipError_t launch_commit(const int* cand, const float* conf, int* tau, int* committed,
