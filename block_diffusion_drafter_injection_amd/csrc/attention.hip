@@ -307,22 +307,25 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
       float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
       mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
       mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      // Lazy rescaling: the reference maximum m_run moves (and the running
+      // sums are rescaled) only when some row's maximum exceeds it by more
+      // than 8, so the probabilities stay below 2^8 and the rescale is rare.
       const float m_new = fmaxf(m_run, mx);
-      if (m_new != -INFINITY) {
+      if (__any(m_new > m_run + 8.f)) {
+        const float alpha = m_run == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int nn = 0; nn < NN; ++nn) ot[nn] *= alpha;
+        m_run = m_new;
+      }
+      if (m_run != -INFINITY) {
         float pv[8], ps = 0.f;
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          pv[k] = __builtin_amdgcn_exp2f(s[k] - m_new);
+          pv[k] = __builtin_amdgcn_exp2f(s[k] - m_run);
           ps += pv[k];
         }
-        if (__any(m_new != m_run)) {   // rescale only when some row's running max moved
-          const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-          l_run *= alpha;
-#pragma unroll
-          for (int nn = 0; nn < NN; ++nn) ot[nn] *= alpha;
-        }
         l_run += ps;
-        m_run = m_new;
         u32x4 hu, lu;
         split_hilo8(pv, hu, lu);
         const bf16x8 pbh = as_bf16x8(hu), pbl = as_bf16x8(lu);
