@@ -121,7 +121,7 @@ int n_qgroups(const dflash_config* c, int B) { return ((c->n_q_heads / c->n_kv_h
 
 struct DraftWS {
   size_t h, u_hi, u_lo, qkv, o_hi, o_lo, act_hi, act_lo, y, row_map, part_f, part_i, att_o, att_lse, cs, tau,
-      committed, cand, conf, gemm_part, q_hi, q_lo, kblk, total;
+      committed, cand, conf, gemm_part, q_hi, q_lo, kblk, vblk, total;
   int ns, pps, ntiles;
 };
 
@@ -155,6 +155,7 @@ DraftWS draft_layout(const dflash_config* c, int bt, int B, int ctx_cap) {
   w.q_hi = k.take(M * nq * d * 2);
   w.q_lo = k.take(M * nq * d * 2);
   w.kblk = k.take(M * nkv * d * 4);
+  w.vblk = k.take(M * nkv * d * 4);
   {
     const int wd = c->dtype == DFLASH_BF16;
     const int am = wd ? ACT_HILO : ACT_F32;
@@ -378,6 +379,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
   ap.q_hi = (bf16_t*)at(workspace, L.q_hi);
   ap.q_lo = (bf16_t*)at(workspace, L.q_lo);
   ap.kblk = (float*)at(workspace, L.kblk);
+  ap.vblk = (float*)at(workspace, L.vblk);
 
   HIP_TRY(launch_rope_table_block(ctx_len, ctx_cap, batch, B, d, (double)cfg->rope_base, cs, stream));
   HIP_TRY(launch_block_init(tau, committed, M, cfg->mask_token_id, stream));
@@ -404,6 +406,11 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
       g.K = H;
       g.kind = EPI_STORE;
       g.e.out = ActOut{qkv, nullptr, Nqkv, ACT_F32};
+      // the query prep (bf16 pools, head_dim 128) sums a K split itself
+      g.defer_reduce = bf && d == 128;
+      const int ks_qkv = g.defer_reduce ? gemm_ksplit(g) : 1;
+      ap.qkv_part = ks_qkv > 1 ? gpart : nullptr;
+      ap.qkv_ks = ks_qkv;
       HIP_TRY(gemm(DFLASH_PROF_GEMM_QKV, g, stream));
 
       ap.layer = l;

@@ -61,31 +61,58 @@ __device__ __forceinline__ void att_barrier() {
 // in [b][kv head][r][d] order, r = j*B + i for head m*g + j and block
 // position i: the context kernel then loads its MFMA operands directly.  The
 // queries carry the softmax scale times log2 e, so the scores come out ready
-// for the base-2 exponential.  The rotated block keys (fp32) are written too,
-// [b][kv head][i][d], for the in-block part of the attention.
-__global__ __launch_bounds__(64) void attn_qprep_kernel(AttnParams p, bf16_t* qhi, bf16_t* qlo) {
-  // grid (R, n_kv, batch), one thread per element pair (2 e2, 2 e2 + 1)
-  const int D = p.d, g = p.nq / p.nkv, R = g * p.B;
+// for the base-2 exponential.  The rotated block keys and the block values
+// (fp32) are written too, [b][kv head][i][d], for the in-block part of the
+// attention.  When the q/k/v projection left K-split partials, they are
+// summed here in split order (the sums a separate reduction would form).
+__device__ __forceinline__ float2 qkv_pair(const AttnParams& p, size_t off, size_t plane) {
+  if (p.qkv_ks <= 1) return *(const float2*)(p.qkv + off);
+  float2 a = make_float2(0.f, 0.f);
+  for (int s = 0; s < p.qkv_ks; ++s) {
+    const float2 v = *(const float2*)(p.qkv_part + s * plane + off);
+    a.x += v.x;
+    a.y += v.y;
+  }
+  return a;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void attn_qprep_kernel(AttnParams p) {
+  // D/4 threads per row; thread e covers dims 2e, 2e+1 and their rotate-half
+  // partners h+2e, h+2e+1
+  constexpr int TPR = D / 4, RPB = 256 / TPR, h = D / 2;
+  const int g = p.nq / p.nkv, R = g * p.B;
   const int ldq = (p.nq + 2 * p.nkv) * D;
+  const size_t plane = (size_t)p.batch * p.B * ldq;
+  const int e = threadIdx.x % TPR, r = blockIdx.x * RPB + threadIdx.x / TPR;
+  const int m = blockIdx.y, b = blockIdx.z;
+  if (r >= R) return;
   const float qscale = p.scale * 1.4426950408889634f;   // scores come out in base-2 units
-  const int r = blockIdx.x, m = blockIdx.y, b = blockIdx.z, e2 = threadIdx.x;
-  if (e2 >= D / 2) return;
   const int j = r / p.B, i = r - j * p.B, row = b * p.B + i, n = m * g + j;
-  const float* qv = p.qkv + (size_t)row * ldq + n * D;
-  const float2* cs = p.cs + (size_t)row * (D / 2);
-  uint32_t h, l;
-  split_hilo2(rope_elem(qv, cs, 2 * e2, D) * qscale, rope_elem(qv, cs, 2 * e2 + 1, D) * qscale, h, l);
-  const size_t gr = ((size_t)b * p.nkv + m) * R + r;
-  ((uint32_t*)qhi)[gr * (D / 2) + e2] = h;
-  ((uint32_t*)qlo)[gr * (D / 2) + e2] = l;
-  if (r < p.B) {   // the block key of position r, rotated (fp32)
+  {
+    const size_t off = (size_t)row * ldq + n * D + 2 * e;
+    const float2 x0 = qkv_pair(p, off, plane), x1 = qkv_pair(p, off + h, plane);
+    const float4 c = *(const float4*)(p.cs + (size_t)row * h + 2 * e);   // (cos, sin) of dims 2e, 2e+1
+    uint32_t h0, l0, h1, l1;
+    split_hilo2((x0.x * c.x - x1.x * c.y) * qscale, (x0.y * c.z - x1.y * c.w) * qscale, h0, l0);
+    split_hilo2((x1.x * c.x + x0.x * c.y) * qscale, (x1.y * c.z + x0.y * c.w) * qscale, h1, l1);
+    const size_t gr = (((size_t)b * p.nkv + m) * R + r) * (D / 2);
+    ((uint32_t*)p.q_hi)[gr + e] = h0;
+    ((uint32_t*)p.q_lo)[gr + e] = l0;
+    ((uint32_t*)p.q_hi)[gr + h / 2 + e] = h1;
+    ((uint32_t*)p.q_lo)[gr + h / 2 + e] = l1;
+  }
+  if (r < p.B) {   // key (rotated) and value of block position r
     const int krow = b * p.B + r;
-    const float* kv = p.qkv + (size_t)krow * ldq + p.nq * D + m * D;
-    const float2* kcs = p.cs + (size_t)krow * (D / 2);
-    float2 kr;
-    kr.x = rope_elem(kv, kcs, 2 * e2, D);
-    kr.y = rope_elem(kv, kcs, 2 * e2 + 1, D);
-    *(float2*)(p.kblk + (((size_t)b * p.nkv + m) * p.B + r) * D + 2 * e2) = kr;
+    const size_t koff = (size_t)krow * ldq + p.nq * D + m * D + 2 * e, voff = koff + p.nkv * D;
+    const float2 k0 = qkv_pair(p, koff, plane), k1 = qkv_pair(p, koff + h, plane);
+    const float2 v0 = qkv_pair(p, voff, plane), v1 = qkv_pair(p, voff + h, plane);
+    const float4 c = *(const float4*)(p.cs + (size_t)krow * h + 2 * e);
+    const size_t o = (((size_t)b * p.nkv + m) * p.B + r) * D + 2 * e;
+    *(float2*)(p.kblk + o) = make_float2(k0.x * c.x - k1.x * c.y, k0.y * c.z - k1.y * c.w);
+    *(float2*)(p.kblk + o + h) = make_float2(k1.x * c.x + k0.x * c.y, k1.y * c.z + k0.y * c.w);
+    *(float2*)(p.vblk + o) = v0;
+    *(float2*)(p.vblk + o + h) = v1;
   }
 }
 
@@ -468,11 +495,13 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
   for (int k = 0; k < KV4; ++k) {
     const int c4 = tid + 256 * k, jb = (4 * c4) / D, e = 4 * c4 - jb * D;
     const int jc = min(jb, p.B - 1), krow = b * p.B + jc;
-    const float4 vv = *(const float4*)(p.qkv + (size_t)krow * ldq + (p.nq + p.nkv) * D + m * D + e);
-    float4 kk;
+    float4 kk, vv;
     if constexpr (PREP) {
-      kk = *(const float4*)(p.kblk + (((size_t)b * p.nkv + m) * p.B + jc) * D + e);
+      const size_t o = (((size_t)b * p.nkv + m) * p.B + jc) * D + e;
+      kk = *(const float4*)(p.kblk + o);
+      vv = *(const float4*)(p.vblk + o);
     } else {
+      vv = *(const float4*)(p.qkv + (size_t)krow * ldq + (p.nq + p.nkv) * D + m * D + e);
       const float* kv = p.qkv + (size_t)krow * ldq + p.nq * D + m * D;
       const float2* cs = p.cs + (size_t)krow * h;
       kk = make_float4(rope_elem(kv, cs, e, D), rope_elem(kv, cs, e + 1, D), rope_elem(kv, cs, e + 2, D),
@@ -594,7 +623,7 @@ hipError_t launch_attention(const AttnParams& p, int wdtype, hipStream_t s, void
   // the prepared queries and block keys also feed the finish kernel, with or
   // without context
   if (wdtype == 1 && p.d == 128) {
-    hipLaunchKernelGGL(attn_qprep_kernel, dim3(R, p.nkv, p.batch), dim3(p.d / 2), 0, s, p, p.q_hi, p.q_lo);
+    hipLaunchKernelGGL(attn_qprep_kernel<128>, dim3((R + 7) / 8, p.nkv, p.batch), dim3(256), 0, s, p);
   }
   if (p.n_splits <= 0) return hipGetLastError();
   const dim3 gctx(p.n_splits * nqg, p.nkv, p.batch);
@@ -614,7 +643,7 @@ hipError_t launch_attention(const AttnParams& p, int wdtype, hipStream_t s, void
 hipError_t launch_attn_finish(const AttnParams& p, int wdtype, ActOut out, hipStream_t s) {
   const int R = (p.nq / p.nkv) * p.B;
   const dim3 grid((R + 15) / 16, p.nkv, p.batch);
-  if (wdtype == 1 && p.d == 128)   // the query prep ran: prepared queries and block keys
+  if (wdtype == 1 && p.d == 128)   // the query prep ran: prepared queries, block keys and values
     hipLaunchKernelGGL((attn_finish_kernel<128, true>), grid, dim3(256), 0, s, p, out);
   else if (p.d == 128)
     hipLaunchKernelGGL((attn_finish_kernel<128, false>), grid, dim3(256), 0, s, p, out);

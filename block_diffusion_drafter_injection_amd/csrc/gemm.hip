@@ -901,7 +901,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_fl_kernel(ActIn a, BRo
     // stores four consecutive columns per lane (8-byte hi and lo stores).
     if (ksplit == 1) {
       constexpr int OW = C::WN / 2, LDW = OW + 4;
-      static_assert(8 * 64 * LDW * 4 <= C::SMEM, "per-wave output slices");
+      static_assert(C::NW * 64 * LDW * 4 <= C::SMEM, "per-wave output slices");
       float* wl = (float*)smem + wid * (64 * LDW);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -1188,7 +1188,7 @@ static hipError_t go_mfma(const GemmArgs& g, int ksplit, hipStream_t s) {
   hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, NP, STAGES, KIND>), dim3(grid), dim3(C::NT), 0, s, g.a, b,
                      g.M, g.N, g.K, ksplit, g.part, g.e);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || ksplit == 1 || (g.defer_reduce && KIND == EPI_ADD)) return err;
+  if (err != hipSuccess || ksplit == 1 || (g.defer_reduce && (KIND == EPI_ADD || KIND == EPI_STORE))) return err;
   hipLaunchKernelGGL((splitk_reduce_kernel<16, BN, KIND, bf16_t>), dim3((g.M + 15) / 16 * ntn), dim3(256), 0, s,
                      g.part, ksplit, g.M, g.N, g.e);
   return hipGetLastError();
@@ -1212,7 +1212,7 @@ static hipError_t go_dma(const GemmArgs& g, int ksplit, hipStream_t s) {
   hipLaunchKernelGGL((gemm_dma_kernel<NP, KIND>), dim3(grid), dim3(256), 0, s, g.a, b, g.M, g.N, g.K, ksplit, g.part,
                      g.e);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || ksplit == 1 || (g.defer_reduce && KIND == EPI_ADD)) return err;
+  if (err != hipSuccess || ksplit == 1 || (g.defer_reduce && (KIND == EPI_ADD || KIND == EPI_STORE))) return err;
   hipLaunchKernelGGL((splitk_reduce_kernel<16, 128, KIND, bf16_t>), dim3((g.M + 15) / 16 * ntn), dim3(256), 0, s,
                      g.part, ksplit, g.M, g.N, g.e);
   return hipGetLastError();
@@ -1227,7 +1227,7 @@ static hipError_t go_dma8(const GemmArgs& g, int ksplit, hipStream_t s) {
   hipLaunchKernelGGL((gemm_dma8_kernel<BM, BN, WGM, WGN, NP, STAGES, KIND>), dim3(grid), dim3(64 * WGM * WGN), 0, s, g.a, b,
                      g.M, g.N, g.K, ksplit, g.part, g.e);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || ksplit == 1 || (g.defer_reduce && KIND == EPI_ADD)) return err;
+  if (err != hipSuccess || ksplit == 1 || (g.defer_reduce && (KIND == EPI_ADD || KIND == EPI_STORE))) return err;
   hipLaunchKernelGGL((splitk_reduce_kernel<16, BN, KIND, bf16_t>), dim3((g.M + 15) / 16 * ntn), dim3(256), 0, s,
                      g.part, ksplit, g.M, g.N, g.e);
   return hipGetLastError();
@@ -1242,7 +1242,7 @@ static hipError_t go_fl(const GemmArgs& g, int ksplit, hipStream_t s) {
   hipLaunchKernelGGL((gemm_fl_kernel<BM, BN, WGM, WGN, NP, KIND>), dim3(grid), dim3(64 * WGM * WGN), 0, s, g.a, b,
                      g.M, g.N, g.K, ksplit, g.part, g.e);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || ksplit == 1 || (g.defer_reduce && KIND == EPI_ADD)) return err;
+  if (err != hipSuccess || ksplit == 1 || (g.defer_reduce && (KIND == EPI_ADD || KIND == EPI_STORE))) return err;
   hipLaunchKernelGGL((splitk_reduce_kernel<16, BN, KIND, bf16_t>), dim3((g.M + 15) / 16 * ntn), dim3(256), 0, s,
                      g.part, ksplit, g.M, g.N, g.e);
   return hipGetLastError();

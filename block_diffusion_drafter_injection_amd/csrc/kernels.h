@@ -58,7 +58,8 @@ struct GemmArgs {
   EpiParams e;
   bool fixed_split;      // K split chosen from (N, K) only: results independent of M
   float* part;           // split-K partials (gemm_partial_bytes of the plan), or null
-  bool defer_reduce;     // EPI_ADD with a K split: leave the partials for the next RMSNorm to fold in
+  bool defer_reduce;     // EPI_ADD / EPI_STORE with a K split: leave the partials to the consumer
+                         // (the next RMSNorm, or the query prep of the attention)
 };
 
 struct GemmPlan {
@@ -89,6 +90,9 @@ struct AttnParams {
   bf16_t* q_hi;           // [batch, nkv, g*B, d] rotated queries, hi plane (bf16 pools)
   bf16_t* q_lo;           // same, lo plane
   float* kblk;            // [batch, nkv, B, d] rotated block keys, fp32 (bf16 pools)
+  float* vblk;            // [batch, nkv, B, d] block values, fp32 (bf16 pools)
+  const float* qkv_part;  // [qkv_ks, M, (nq + 2 nkv) d] K-split partials of qkv, or null
+  int qkv_ks;             // number of partials (the query prep sums them in split order)
 };
 // Context splits -> partials (no launch when there is no context).
 hipError_t launch_attention(const AttnParams& p, int wdtype, hipStream_t s, void (*mark)(int, hipStream_t));
