@@ -178,11 +178,11 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
 #pragma unroll
   for (int nn = 0; nn < NN; ++nn) ot[nn] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // this (layer, kv head)'s pages are contiguous: [page][K chunk, V chunk]
+  // page-major pool: page ph holds [layer][K, V][kv head] chunks
   const size_t chunk = 16 * D;
-  const size_t page_stride = 2 * chunk;
-  const bf16_t* kbase = (const bf16_t*)p.pool + ((size_t)p.layer * p.nkv + m) * p.n_pages * page_stride;
-  const bf16_t* vbase = kbase + chunk;
+  const size_t page_stride = (size_t)p.n_layers * 2 * p.nkv * chunk;
+  const bf16_t* kbase = (const bf16_t*)p.pool + ((size_t)p.layer * 2 * p.nkv + m) * chunk;
+  const bf16_t* vbase = kbase + (size_t)p.nkv * chunk;
   const uint32_t lds0 = (uint32_t)(size_t)lds;
   // fallback source for masked pages: the split's first page, else page 0
   // (the host only attends to a context when the pool has at least one page)
@@ -436,8 +436,8 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
     for (int pg = pg0; pg < pg1; ++pg) {
       const int ph = phys_page(p, b, pg);
       if (ph < 0) continue;
-      const TP* Kc = pool + ((((size_t)p.layer * p.nkv + m) * p.n_pages + ph) * 2) * chunk;
-      const TP* Vc = Kc + chunk;
+      const TP* Kc = pool + (((size_t)ph * p.n_layers + p.layer) * 2 * p.nkv + m) * chunk;
+      const TP* Vc = Kc + (size_t)p.nkv * chunk;
       const int ns = min(16, ctx - pg * 16);
       for (int slot = 0; slot < ns; ++slot) {
         float sd = 0.f;

@@ -192,7 +192,7 @@ __device__ __forceinline__ void run_epilogue(const float* Cs, int ldc, int m0, i
       const int row = m0 + r, col0 = n0 + hb * d;
       if (row >= M || col0 >= N) continue;
       const int head = col0 / d;           // ((l * 2 + kv) * nkv + m)
-      const int m = head % nkv, kv = (head / nkv) & 1, l = head / (2 * nkv);
+      const int m = head % nkv, kv = (head / nkv) & 1, l = head / (2 * nkv), L = e.n_layers;
       const int b = e.tok_seq[row], pos = e.tok_pos[row];
       if (b < 0 || b >= e.n_seqs || pos < 0) continue;
       const int lp = pos >> 4, slot = pos & 15;
@@ -200,7 +200,7 @@ __device__ __forceinline__ void run_epilogue(const float* Cs, int ldc, int m0, i
       const int phys = e.block_table[(size_t)b * e.max_pages + lp];
       if (phys < 0 || phys >= e.n_pages) continue;
       const float x0 = Cs[r * ldc + hb * d + j], x1 = Cs[r * ldc + hb * d + j + hd];
-      TP* chunk = (TP*)e.pool + ((((size_t)l * nkv + m) * e.n_pages + phys) * 2 + kv) * (size_t)(16 * d);
+      TP* chunk = (TP*)e.pool + ((((size_t)phys * L + l) * 2 + kv) * nkv + m) * (size_t)(16 * d);
       if (kv == 0) {
         const float2 cs = e.rope_cs[(size_t)row * hd + j];
         const float y0 = x0 * cs.x - x1 * cs.y, y1 = x1 * cs.x + x0 * cs.y;

@@ -33,10 +33,11 @@
  *
  * KV pool layout (one allocation shared by all sequences; prefix sharing =
  * several block-table rows naming the same physical page):
- *   pool[n_layers][n_kv_heads][n_pages][2][chunk]  with chunk = page_size*head_dim
+ *   pool[n_pages][n_layers][2][n_kv_heads][chunk]  with chunk = page_size*head_dim
+ *   (index 0 of the third axis holds K, index 1 V)
  *   K chunk: [page_size][head_dim]   (token-major)
  *   V chunk: [head_dim][page_size]   (dimension-major)
- * so the pages one (layer, kv head) reads are contiguous, K beside V.
+ * A page holds every layer's K and V of its page_size tokens in one block.
  * Token t of sequence b lives in physical page block_table[b*max_pages + t/page_size],
  * slot t % page_size.  K is stored after rotary embedding at position t.
  */

@@ -61,8 +61,8 @@ def alloc_pool(dims, n_pages, device="cuda", poison=True):
 
 
 def _pool5(dims, pool, n_pages):
-    """[n_layers, n_kv, n_pages, 2, page*d] view of the pool."""
-    return pool.view(dims.n_layers, dims.n_kv_heads, n_pages, 2, dims.page_size * dims.head_dim)
+    """[n_pages, n_layers, 2, n_kv, page*d] view of the pool."""
+    return pool.view(n_pages, dims.n_layers, 2, dims.n_kv_heads, dims.page_size * dims.head_dim)
 
 
 def pack_pool(dims, pool, n_pages, table, b, K, V):
@@ -73,8 +73,8 @@ def pack_pool(dims, pool, n_pages, table, b, K, V):
     for j in range((T + 15) // 16):
         t0, t1 = 16 * j, min(16 * j + 16, T)
         ph = int(table[b, j])
-        kc = p5[:, :, ph, 0].view(L, nkv, 16, d)
-        vc = p5[:, :, ph, 1].view(L, nkv, d, 16)
+        kc = p5[ph, :, 0].view(L, nkv, 16, d)
+        vc = p5[ph, :, 1].view(L, nkv, d, 16)
         kc[:, :, : t1 - t0, :] = K[:, t0:t1].permute(0, 2, 1, 3).to(pool.dtype)
         vc[:, :, :, : t1 - t0] = V[:, t0:t1].permute(0, 2, 3, 1).to(pool.dtype)
 
@@ -88,8 +88,8 @@ def unpack_pool(dims, pool, n_pages, table, b, T):
     for j in range((T + 15) // 16):
         t0, t1 = 16 * j, min(16 * j + 16, T)
         ph = int(table[b, j])
-        kc = p5[:, :, ph, 0].view(L, nkv, 16, d)
-        vc = p5[:, :, ph, 1].view(L, nkv, d, 16)
+        kc = p5[ph, :, 0].view(L, nkv, 16, d)
+        vc = p5[ph, :, 1].view(L, nkv, d, 16)
         K[:, t0:t1] = kc[:, :, : t1 - t0, :].permute(0, 2, 1, 3).double().cpu()
         V[:, t0:t1] = vc[:, :, :, : t1 - t0].permute(0, 3, 1, 2).double().cpu()
     return K.numpy(), V.numpy()
