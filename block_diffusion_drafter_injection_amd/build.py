@@ -16,6 +16,10 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdflash.so")
 SOURCES = ["api.cpp", "gemm.hip", "attention.hip", "elementwise.hip", "verify.hip"]
 ARCH = os.environ.get("DFLASH_ARCH", "gfx950")
+# per-source flags: the attention kernels keep their MFMA accumulators in
+# ordinary VGPRs (the default form parks them in AGPRs and copies them back
+# and forth around the softmax rescale)
+FILE_FLAGS = {"attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc():
@@ -39,7 +43,8 @@ def build(jobs=5, verbose=False, defines=(), out=None, objdir=None):
 
     def one(src):
         obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *compile_flags(), *[f"-D{d}" for d in defines], "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *compile_flags(), *FILE_FLAGS.get(src, []), *[f"-D{d}" for d in defines], "-c",
+               os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError(f"hipcc failed on {src}:\n{r.stderr[-6000:]}")

@@ -44,9 +44,13 @@ constexpr int kMaxPPS = 512;   // pages per context split (bounded by the host)
 #endif
 constexpr int kAttStages = DFLASH_ATT_STAGES;  // 32-token tiles resident per workgroup
 
+// s_waitcnt on the vector-memory counter only, through the builtin so that
+// the compiler's own wait insertion knows which loads have completed
+// (vmcnt bits 3:0 and 15:14, expcnt and lgkmcnt left at their maxima).
 template <int N>
 __device__ __forceinline__ void att_wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 // Barrier without the memory fence of __syncthreads(): the fence would also
 // wait for the later tiles' loads still in flight.  Each wave waits for its
@@ -131,6 +135,15 @@ __global__ __launch_bounds__(256) void attn_qprep_kernel(AttnParams p) {
 // the sixteen rows one operand read touches land on distinct bank groups.
 __device__ __forceinline__ int kswz(int krow) { return (krow & 15) ^ (((krow >> 4) & 1) << 2); }
 
+// Maximum over lanes l, l ^ 16, l ^ 32 and l ^ 48 (lane swaps across the
+// 32-lane halves and the 16-lane rows, no LDS traffic).
+__device__ __forceinline__ float row_max4(float x) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
   static_assert(D == 128, "context kernel is specialised for head_dim 128");
@@ -171,7 +184,8 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
       ql[kk] = as_bf16x8(rvalid ? *(const u32x4*)(p.q_lo + qoff + 32 * kk) : z);
     }
   }
-  __syncthreads();   // ptab ready (and no copies in flight yet)
+  att_wait_vmcnt<0>();   // query fragments loaded (before any tile copy is in flight)
+  __syncthreads();       // ptab ready
 
   float m_run = -INFINITY, l_run = 0.f;
   f32x4 ot[NN];
@@ -303,8 +317,8 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
     if (wave_active) ATT_SCORES(0, stc[0], stc[1]);
   }
   for (int it = 0; it < ntiles; ++it) {
-    f32x4 stn[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    if (it + 1 < ntiles) {
+    const bool more = it + 1 < ntiles;
+    if (more) {
       wait_tile(it + 1);
       att_barrier();
       if (it >= 1 && issued < ntiles) {
@@ -313,9 +327,23 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
         ph_next = page_of(issued);
       }
       zero_tail(it + 1);
-      if (wave_active) ATT_SCORES(it + 1, stn[0], stn[1]);
     }
     if (wave_active) {
+      // Operand reads first: K of tile it+1 (stale and unused after the last
+      // tile) and V of tile it, so their latency hides behind the softmax.
+      bf16x8 kf[2][KK], vf[NN];
+      {
+        const unsigned char* kt = lds + ((it + 1) % kAttStages) * TILE;
+        const unsigned char* vt = lds + (it % kAttStages) * TILE + KBYTES;
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          kf[0][kk] = as_bf16x8(*(const u32x4*)(kt + koff[0][kk]));
+          kf[1][kk] = as_bf16x8(*(const u32x4*)(kt + koff[1][kk]));
+        }
+#pragma unroll
+        for (int nn = 0; nn < NN; ++nn) vf[nn] = as_bf16x8(*(const u32x4*)(vt + voff[nn]));
+      }
+      __builtin_amdgcn_sched_barrier(0);
       const int tok0 = (pg0 + 2 * it) * 16;
       // lane owns query (lane & 15) and tokens tok0 + tl + 4t + e, scores in
       // base-2 units (the queries carry scale * log2 e)
@@ -331,9 +359,9 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) s[t * 4 + e] = tok0 + tl + 4 * t + e < tok_end ? stc[t][e] : -INFINITY;
       }
-      float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, kWave));
-      mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
+      // row maximum over the four lanes holding this query's 32 tokens
+      const float mx = row_max4(fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),
+                                      fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7]))));
       // Lazy rescaling: the reference maximum m_run moves (and the running
       // sums are rescaled) only when some row's maximum exceeds it by more
       // than 8, so the probabilities stay below 2^8 and the rescale is rare.
@@ -345,28 +373,34 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
         for (int nn = 0; nn < NN; ++nn) ot[nn] *= alpha;
         m_run = m_new;
       }
-      if (m_run != -INFINITY) {
-        float pv[8], ps = 0.f;
+      // a row with no unmasked token yet (m_run = -inf) contributes P = 0
+      const bool live = m_run != -INFINITY;
+      float pv[8], ps = 0.f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          pv[k] = __builtin_amdgcn_exp2f(s[k] - m_run);
-          ps += pv[k];
-        }
-        l_run += ps;
-        u32x4 hu, lu;
-        split_hilo8(pv, hu, lu);
-        const bf16x8 pbh = as_bf16x8(hu), pbl = as_bf16x8(lu);
-        const unsigned char* vt = lds + (it % kAttStages) * TILE + KBYTES;
-#pragma unroll
-        for (int nn = 0; nn < NN; ++nn) {
-          const bf16x8 va = as_bf16x8(*(const u32x4*)(vt + voff[nn]));
-          ot[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbh, ot[nn], 0, 0, 0);
-          ot[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pbl, ot[nn], 0, 0, 0);
-        }
+      for (int k = 0; k < 8; ++k) {
+        pv[k] = live ? __builtin_amdgcn_exp2f(s[k] - m_run) : 0.f;
+        ps += pv[k];
       }
+      l_run += ps;
+      u32x4 hu, lu;
+      split_hilo8(pv, hu, lu);
+      const bf16x8 pbh = as_bf16x8(hu), pbl = as_bf16x8(lu);
+      f32x4 stn[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        stn[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][kk], qh[kk], stn[0], 0, 0, 0);
+        stn[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][kk], qh[kk], stn[1], 0, 0, 0);
+        stn[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][kk], ql[kk], stn[0], 0, 0, 0);
+        stn[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][kk], ql[kk], stn[1], 0, 0, 0);
+      }
+#pragma unroll
+      for (int nn = 0; nn < NN; ++nn) {
+        ot[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[nn], pbh, ot[nn], 0, 0, 0);
+        ot[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[nn], pbl, ot[nn], 0, 0, 0);
+      }
+      stc[0] = stn[0];
+      stc[1] = stn[1];
     }
-    stc[0] = stn[0];
-    stc[1] = stn[1];
   }
 #undef ATT_SCORES
 

@@ -420,9 +420,15 @@ struct DmaCfg {
   static_assert(BLOCKS % 4 == 0, "blocks per wave");
 };
 
+// s_waitcnt on the vector-memory counter only, through the builtin so that
+// the compiler's own wait insertion knows the copies to LDS have landed (it
+// would otherwise wait for every outstanding store before each LDS read of the
+// epilogue).  vmcnt sits in bits 3:0 and 15:14; expcnt and lgkmcnt stay at
+// their maxima.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 // Workgroup barrier without the memory fence of __syncthreads(): the fence
 // would also wait for the next tile's loads still in flight.  LDS data of the
@@ -893,6 +899,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_fl_kernel(ActIn a, BRo
 #undef FL_LOAD
 #undef FL_MMA
 #undef FL_ISSUE
+  wait_vmcnt<0>();   // every copy has landed (no-op here; tells the compiler's wait insertion)
   if constexpr (IL) {
     // MFMA blocks 2k and 2k+1 of a wave are the gate and up values of the
     // same 16 output columns, so SiLU(g) * u is formed and stored straight
@@ -913,11 +920,18 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_fl_kernel(ActIn a, BRo
       asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's slice is written
       const int ocol0 = n0 / 2 + wn * OW;
       constexpr int C4 = OW / 4;
+      // all slice reads first, then the stores
+      float4 ov[C4];
 #pragma unroll
-      for (int t = 0; t < 64 * C4 / 64; ++t) {
+      for (int t = 0; t < C4; ++t) {
+        const int idx = lane + 64 * t, r = idx / C4, c = (idx - r * C4) * 4;
+        ov[t] = *(const float4*)(wl + r * LDW + c);
+      }
+#pragma unroll
+      for (int t = 0; t < C4; ++t) {
         const int idx = lane + 64 * t, r = idx / C4, c = (idx - r * C4) * 4;
         const int row = m0 + wm * C::WM + r;
-        if (row < M && ocol0 + c < N / 2) act_store4(e.out, row, ocol0 + c, *(const float4*)(wl + r * LDW + c));
+        if (row < M && ocol0 + c < N / 2) act_store4(e.out, row, ocol0 + c, ov[t]);
       }
       return;
     }
