@@ -457,12 +457,13 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
       gd.kind = EPI_ADD;
       gd.e.resid = h;
       gd.e.ldr = H;
-      gd.defer_reduce = l + 1 < cfg->n_layers;   // folded into the next layer's attention norm
-      if (gd.defer_reduce) pending_ks = gemm_ksplit(gd);
+      gd.defer_reduce = true;   // folded into the next attention norm, or the final norm
+      pending_ks = gemm_ksplit(gd);
       HIP_TRY(gemm(DFLASH_PROF_GEMM_DOWN, gd, stream));
     }
     const int Ms = batch * n_open;
-    HIP_TRY(launch_rmsnorm(h, w->final_norm, y, Ms, H, cfg->rms_eps, committed, B, n_open, row_map, stream));
+    HIP_TRY(launch_rmsnorm(h, w->final_norm, y, Ms, H, cfg->rms_eps, committed, B, n_open, row_map, stream,
+                           pending_ks > 1 ? gpart : nullptr, pending_ks, M));
     GemmArgs gl{};
     gl.wdtype = bf;
     gl.a = ActIn{y.p0, nullptr, H, y.mode};

@@ -53,12 +53,14 @@ __global__ void embed_kernel(const int* tau, const T* embed, int vocab, float* h
 
 // One workgroup per output row.  With committed != null the output rows are
 // the still-open positions of each sequence in position order (n_open per
-// sequence) and row_map receives b*B + i for each.
+// sequence) and row_map receives b*B + i for each.  With part != null the
+// source row first takes the sum of its K-split partials ([ksplit][Mp][H],
+// indexed by the source row), which is also written back to h.
 constexpr int kRmsVec = 8;   // float4 per thread: rows up to 8192 wide
 
 __global__ __launch_bounds__(256) void rmsnorm_kernel(float* h, const float* gain, ActOut out, int H,
                                                       float eps, const int* committed, int B, int n_open,
-                                                      int* row_map, const float* part, int ksplit, int M) {
+                                                      int* row_map, const float* part, int ksplit, int Mp) {
   __shared__ double red[4];
   __shared__ int src_s;
   const int r = blockIdx.x, tid = threadIdx.x;
@@ -94,7 +96,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* h, const float* gai
       // the split-K reduce would form)
       float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
       for (int sp = 0; sp < ksplit; ++sp) {
-        const float4 pv = *(const float4*)(part + ((size_t)sp * M + src_s) * H + c);
+        const float4 pv = *(const float4*)(part + ((size_t)sp * Mp + src_s) * H + c);
         a.x += pv.x; a.y += pv.y; a.z += pv.z; a.w += pv.w;
       }
       v[k].x += a.x; v[k].y += a.y; v[k].z += a.z; v[k].w += a.w;
@@ -219,11 +221,10 @@ hipError_t launch_embed(const int* tau, const void* embed, int wdtype, int vocab
 
 hipError_t launch_rmsnorm(float* h, const float* gain, ActOut out, int M, int H, float eps,
                           const int* committed, int B, int n_open, int* row_map, hipStream_t s,
-                          const float* part, int ksplit) {
+                          const float* part, int ksplit, int part_rows) {
   if (M <= 0) return hipSuccess;
-  if (committed) part = nullptr;   // the gathered form never folds partials
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(256), 0, s, h, gain, out, H, eps, committed, B, n_open,
-                     row_map, part, part ? ksplit : 0, M);
+                     row_map, part, part ? ksplit : 0, part_rows > 0 ? part_rows : M);
   return hipGetLastError();
 }
 

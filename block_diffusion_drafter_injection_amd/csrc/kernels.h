@@ -107,11 +107,12 @@ hipError_t launch_rope_table_tokens(const int* tok_pos, int n, int d, double bas
 hipError_t launch_block_init(int* tau, int* committed, int M, int mask_id, hipStream_t s);
 hipError_t launch_embed(const int* tau, const void* embed, int wdtype, int vocab, float* h, int M,
                         int H, hipStream_t s);
-// With part != null (and no row gather), h += sum over the ksplit partials
-// [ksplit][M][H] (in split order) first, and h is written back.
+// With part != null, h += sum over the ksplit partials [ksplit][part_rows][H]
+// (in split order, part_rows = M when 0) first, and the rows read are written
+// back to h.
 hipError_t launch_rmsnorm(float* h, const float* gain, ActOut out, int M, int H, float eps,
                           const int* committed, int B, int n_open, int* row_map, hipStream_t s,
-                          const float* part = nullptr, int ksplit = 0);
+                          const float* part = nullptr, int ksplit = 0, int part_rows = 0);
 hipError_t launch_lm_combine(const float4* part_f, const int* part_i, int ntiles, int rows,
                              const int* row_map, int* cand, float* conf, hipStream_t s);
 hipError_t launch_commit(const int* cand, const float* conf, int* tau, int* committed,
