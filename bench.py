@@ -98,6 +98,27 @@ def work_per_class(dims, bt, B, S, ctx, n_new):
     return out
 
 
+def draft_roofline_ms(dims, bt, B, S, ctx):
+    """Roofline time of one draft call: the sum over its kernels of max(flops / MFMA peak,
+    HBM bytes / HBM peak), with weights streamed once per forward, every context token's
+    K and V read once per layer and forward, and the LM head over the still-open rows only."""
+    H, L, I, V = dims.hidden, dims.n_layers, dims.intermediate, dims.vocab
+    nq, nkv, d = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    el = 2 if dims.dtype == "bf16" else 4
+    peak = PEAK_BF16 if dims.dtype == "bf16" else PEAK_FP32
+    M = bt * B
+    gemms = [((nq + 2 * nkv) * d, H), (H, nq * d), (2 * I, H), (H, I)]
+    t, done = 0.0, 0
+    for s in range(S):
+        for N, K in gemms:
+            t += L * max(2.0 * M * N * K / peak, N * K * el / PEAK_HBM)
+        t += L * float(sum(ctx)) * nkv * d * 2 * el / PEAK_HBM
+        rows = bt * (B - done)
+        t += max(2.0 * rows * V * H / peak, V * H * el / PEAK_HBM)
+        done += (s + 1) * B // S - s * B // S
+    return t * 1e3
+
+
 def main():
     a = parse()
     if a.summarize:
@@ -260,6 +281,7 @@ def main():
     value = accepted / (ms_step / 1e3)
     n_new_mean = float(np.mean(news))
     work = work_per_class(dims, bt, B, S, (ctx_before + ctx) / 2.0, n_new_mean)
+    t_roof = draft_roofline_ms(dims, bt, B, S, ctx_before)   # the state the draft-only timing ran on
     amount, unit, launches_per_step = work[cls]
     bound = "hbm" if unit == "byte" else "mfma"
     peak = PEAK_HBM if unit == "byte" else (PEAK_BF16 if dims.dtype == "bf16" else PEAK_FP32)
@@ -285,6 +307,9 @@ def main():
         "mean_accept_plus_bonus": round(accepted / bt, 3),
         "wall_ms_per_step": round(wall * 1e3 / a.steps, 3),
         "roofline": roof,
+        "draft_roofline": {"t_roof_ms": round(t_roof, 4), "draft_ms": round(draft_ms, 4),
+                           "frac": round(t_roof / draft_ms, 4),
+                           "definition": "sum over the draft's kernels of max(flops/2.5 PFLOP/s, bytes/8 TB/s)"},
     }
     if a.cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(dims, W, wl, B, S, int(ctx_before[0]))
