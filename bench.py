@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="turn rocprofv3 csv output into profiles/ summaries and exit")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--block-sweep", type=int, default=1,
+                    help="also time the draft call alone at block sizes 4, 8 and 16 on the same batch and pool")
     return ap.parse_args()
 
 
@@ -311,6 +313,28 @@ def main():
                            "frac": round(t_roof / draft_ms, 4),
                            "definition": "sum over the draft's kernels of max(flops/2.5 PFLOP/s, bytes/8 TB/s)"},
     }
+    if a.block_sweep:
+        sweep = []
+        for Bs in (4, 8, 16):
+            wsb = Bn.dflash_workspace_size(cfg, bt, Bs, max_inject, max_ctx)
+            wss = ws if wsb <= ws_bytes else torch.empty(wsb, dtype=torch.uint8, device=dev)
+            toks = torch.empty(bt, Bs, dtype=torch.int32, device=dev)
+            for _ in range(2):
+                Bn.dflash_draft_block(cfg, w, pool, n_pages, table, pages_per, ctx_dev, max_ctx, bt, Bs, S, 0.0, 0,
+                                      toks, None, None, wss, max(wsb, 0))
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(nd):
+                Bn.dflash_draft_block(cfg, w, pool, n_pages, table, pages_per, ctx_dev, max_ctx, bt, Bs, S, 0.0, 0,
+                                      toks, None, None, wss, max(wsb, 0))
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms_b = e0.elapsed_time(e1) / nd
+            tr = draft_roofline_ms(dims, bt, Bs, S, ctx)
+            sweep.append({"block": Bs, "draft_ms": round(ms_b, 4), "drafted_tok_s": round(bt * Bs / (ms_b / 1e3), 1),
+                          "t_roof_ms": round(tr, 4), "frac": round(tr / ms_b, 4)})
+            del wss
+        res["block_sweep"] = sweep
     if a.cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(dims, W, wl, B, S, int(ctx_before[0]))
     res["setup_s"] = round(setup_s, 1)

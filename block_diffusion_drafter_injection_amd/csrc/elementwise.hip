@@ -121,41 +121,55 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* h, const float* gai
   }
 }
 
-// Row combine of the LM-head tile partials, in tile order (one wave per row).
-__global__ __launch_bounds__(64) void lm_combine_kernel(const float4* part_f, const int* part_i, int ntiles,
-                                                        const int* row_map, int* cand, float* conf) {
-  const int r = blockIdx.x, lane = threadIdx.x;
-  float pmax = -INFINITY, zmax = -INFINITY, zsum = 0.f, zc = -INFINITY;
-  int idx = -1;
-  for (int t = lane; t < ntiles; t += 64) {
+// Row combine of the LM-head tile partials (four waves per row): a running
+// (argmax score, index, z at argmax) and a running (max z, sum of exp)
+// pair per lane over a strided set of tiles, then across lanes and waves.
+// Ties of the argmax score resolve to the smallest index.
+struct LmAcc {
+  float pmax, zmax, zsum, zc;
+  int idx;
+};
+__device__ __forceinline__ void lm_merge(LmAcc& a, float qp, float qz, float qs, float qc, int qi) {
+  if (qi >= 0 && (a.idx < 0 || qp > a.pmax || (qp == a.pmax && qi < a.idx))) {
+    a.pmax = qp;
+    a.idx = qi;
+    a.zc = qc;
+  }
+  const float M = fmaxf(a.zmax, qz);
+  float s = 0.f;
+  if (a.zsum > 0.f) s += a.zsum * __expf(a.zmax - M);
+  if (qs > 0.f) s += qs * __expf(qz - M);
+  a.zmax = M;
+  a.zsum = s;
+}
+
+__global__ __launch_bounds__(256) void lm_combine_kernel(const float4* part_f, const int* part_i, int ntiles,
+                                                         const int* row_map, int* cand, float* conf) {
+  __shared__ float sh[4][4];
+  __shared__ int shi[4];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  LmAcc a{-INFINITY, -INFINITY, 0.f, -INFINITY, -1};
+  for (int t = tid; t < ntiles; t += 256) {
     const float4 f = part_f[(size_t)r * ntiles + t];
-    const int ii = part_i[(size_t)r * ntiles + t];
-    if (ii >= 0 && (idx < 0 || f.x > pmax)) { pmax = f.x; idx = ii; zc = f.w; }
-    const float M = fmaxf(zmax, f.y);
-    float s = 0.f;
-    if (zsum > 0.f) s += zsum * expf(zmax - M);
-    if (f.z > 0.f) s += f.z * expf(f.y - M);
-    zmax = M;
-    zsum = s;
+    lm_merge(a, f.x, f.y, f.z, f.w, part_i[(size_t)r * ntiles + t]);
   }
-  // lanes hold strided tile sets; argmax ties resolve to the smallest index
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float qp = __shfl_xor(pmax, o, kWave), qz = __shfl_xor(zmax, o, kWave);
-    const float qs = __shfl_xor(zsum, o, kWave), qc = __shfl_xor(zc, o, kWave);
-    const int qi = __shfl_xor(idx, o, kWave);
-    if (qi >= 0 && (idx < 0 || qp > pmax || (qp == pmax && qi < idx))) { pmax = qp; idx = qi; zc = qc; }
-    const float M = fmaxf(zmax, qz);
-    float s = 0.f;
-    if (zsum > 0.f) s += zsum * expf(zmax - M);
-    if (qs > 0.f) s += qs * expf(qz - M);
-    zmax = M;
-    zsum = s;
-  }
+  for (int o = 32; o > 0; o >>= 1)
+    lm_merge(a, __shfl_xor(a.pmax, o, kWave), __shfl_xor(a.zmax, o, kWave), __shfl_xor(a.zsum, o, kWave),
+             __shfl_xor(a.zc, o, kWave), __shfl_xor(a.idx, o, kWave));
   if (lane == 0) {
+    sh[w][0] = a.pmax;
+    sh[w][1] = a.zmax;
+    sh[w][2] = a.zsum;
+    sh[w][3] = a.zc;
+    shi[w] = a.idx;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    for (int k = 1; k < 4; ++k) lm_merge(a, sh[k][0], sh[k][1], sh[k][2], sh[k][3], shi[k]);
     const int dst = row_map[r];
-    cand[dst] = idx;
-    conf[dst] = zc - (zmax + logf(zsum));
+    cand[dst] = a.idx;
+    conf[dst] = a.zc - (a.zmax + logf(a.zsum));
   }
 }
 
@@ -231,7 +245,7 @@ hipError_t launch_rmsnorm(float* h, const float* gain, ActOut out, int M, int H,
 hipError_t launch_lm_combine(const float4* part_f, const int* part_i, int ntiles, int rows, const int* row_map,
                              int* cand, float* conf, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(lm_combine_kernel, dim3(rows), dim3(64), 0, s, part_f, part_i, ntiles, row_map, cand, conf);
+  hipLaunchKernelGGL(lm_combine_kernel, dim3(rows), dim3(256), 0, s, part_f, part_i, ntiles, row_map, cand, conf);
   return hipGetLastError();
 }
 
