@@ -109,7 +109,7 @@ void attn_split(int bt, int nkv, int nqg, int ctx_cap, int& ns, int& pps) {
 #define DFLASH_ATT_WG_TARGET 512
 #endif
   const int want = (DFLASH_ATT_WG_TARGET + pairs - 1) / pairs;
-  const int max_ns = (pages + 1) / 2;
+  const int max_ns = std::max(1, pages / 8);   // at least four 32-token tiles per split
   const int min_ns = (pages + 511) / 512;   // the context kernel stages at most 512 page ids
   ns = std::max(min_ns, std::max(1, std::min(want, max_ns)));
   pps = (pages + ns - 1) / ns;

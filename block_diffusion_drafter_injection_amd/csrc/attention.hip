@@ -330,7 +330,8 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
     }
     if (wave_active) {
       // Operand reads first: K of tile it+1 (stale and unused after the last
-      // tile) and V of tile it, so their latency hides behind the softmax.
+      // tile) and V of tile it, so the V reads complete behind the score
+      // MFMAs and the softmax.
       bf16x8 kf[2][KK], vf[NN];
       {
         const unsigned char* kt = lds + ((it + 1) % kAttStages) * TILE;
@@ -344,6 +345,16 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
         for (int nn = 0; nn < NN; ++nn) vf[nn] = as_bf16x8(*(const u32x4*)(vt + voff[nn]));
       }
       __builtin_amdgcn_sched_barrier(0);
+      // scores of tile it+1 (garbage after the last tile, never used); the
+      // matrix cores run them while the softmax below runs on the VALU
+      f32x4 stn[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        stn[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][kk], qh[kk], stn[0], 0, 0, 0);
+        stn[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][kk], qh[kk], stn[1], 0, 0, 0);
+        stn[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][kk], ql[kk], stn[0], 0, 0, 0);
+        stn[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][kk], ql[kk], stn[1], 0, 0, 0);
+      }
       const int tok0 = (pg0 + 2 * it) * 16;
       // lane owns query (lane & 15) and tokens tok0 + tl + 4t + e, scores in
       // base-2 units (the queries carry scale * log2 e)
@@ -385,14 +396,6 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
       u32x4 hu, lu;
       split_hilo8(pv, hu, lu);
       const bf16x8 pbh = as_bf16x8(hu), pbl = as_bf16x8(lu);
-      f32x4 stn[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        stn[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][kk], qh[kk], stn[0], 0, 0, 0);
-        stn[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][kk], qh[kk], stn[1], 0, 0, 0);
-        stn[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[0][kk], ql[kk], stn[0], 0, 0, 0);
-        stn[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][kk], ql[kk], stn[1], 0, 0, 0);
-      }
 #pragma unroll
       for (int nn = 0; nn < NN; ++nn) {
         ot[nn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[nn], pbh, ot[nn], 0, 0, 0);
@@ -624,9 +627,11 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
   float tot = 0.f, acc[DPT];
 #pragma unroll
   for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
+  // an empty split has lse = -inf and o = 0, so it adds nothing; no branch,
+  // so the loads of several splits are in flight together
+#pragma unroll 4
   for (int sp = 0; sp < p.n_splits; ++sp) {
     const float l = p.part_lse[sp * Mq + qrow];
-    if (l == -INFINITY) continue;
     const float w = expf(l - mxl);
     tot += w;
     const float* src = p.part_o + (sp * Mq + qrow) * D + d0;

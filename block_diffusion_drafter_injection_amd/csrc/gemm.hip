@@ -1160,7 +1160,7 @@ GemmPlan gemm_plan(int wdtype, int a_mode, int M, int N, int K, int kind, bool f
     if (cfg == 11 && !one_plane) cfg = 12;
     if (cfg >= 10 && K % 64 != 0) cfg = 2;
     // SwiGLU tiles hold BN/2 gate and BN/2 up columns of the same rows
-    if (kind == EPI_SWIGLU && (N / 2) % (tile_bn(cfg) / 2) != 0) cfg = 2;
+    if (kind == EPI_SWIGLU && (N / 2) % (tile_bn(cfg) / 2) != 0) cfg = (N / 2) % 128 == 0 && K % 64 == 0 ? 12 : 2;
   }
   p.cfg = cfg;
   if (cfg == 2) {
