@@ -1109,6 +1109,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(ActIn a, BRows<float> b, 
 //   5: 128x256, eight 64x64 waves      6: 512x128, eight 64x128 waves
 //   7, 8, 9: 3, 5 and 4 (one plane) with four LDS stages
 //   (gemm_dma8_kernel, one workgroup per CU)
+//   10: 128x384, eight 64x96 waves     11: 256x256, eight 64x128 waves (one plane)
+//   12: 128x256, eight 64x64 waves     13: 64x256, eight 64x32 waves (one plane, at most 64 rows)
+//   (gemm_fl_kernel)
 #ifndef DFLASH_T_SWIGLU
 #define DFLASH_T_SWIGLU 10
 #endif
@@ -1125,9 +1128,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(ActIn a, BRows<float> b, 
 #define DFLASH_T_STORE 10
 #endif
 static int tile_bn(int cfg) {
-  return cfg == 3 || cfg == 7 || cfg == 10 ? 384 : cfg == 4 || cfg == 5 || cfg == 8 || cfg == 9 || cfg == 11 || cfg == 12 ? 256 : 128;
+  return cfg == 3 || cfg == 7 || cfg == 10 ? 384 : cfg == 4 || cfg == 5 || cfg == 8 || cfg == 9 || cfg >= 11 ? 256 : 128;
 }
-static int tile_bm(int cfg) { return cfg == 4 || cfg == 9 || cfg == 11 ? 256 : cfg == 6 ? 512 : 128; }
+static int tile_bm(int cfg) { return cfg == 4 || cfg == 9 || cfg == 11 ? 256 : cfg == 6 ? 512 : cfg == 13 ? 64 : 128; }
 
 // LM-head partials cover 128 columns each, or 64 when the tile width is not a multiple of 128
 int gemm_bn(int wdtype, int K) { return wdtype && K % 32 == 0 && tile_bn(DFLASH_T_LMHEAD) % 128 ? 64 : 128; }
@@ -1152,12 +1155,12 @@ GemmPlan gemm_plan(int wdtype, int a_mode, int M, int N, int K, int kind, bool f
   int cfg = 2;
   if (!fixed_split && K % 32 == 0) {
     if (kind == EPI_SWIGLU) cfg = DFLASH_T_SWIGLU;
-    else if (kind == EPI_LMHEAD) cfg = M > 256 ? DFLASH_T_LMHEAD : DFLASH_T_LMHEAD_SMALL;
+    else if (kind == EPI_LMHEAD) cfg = M > 256 ? DFLASH_T_LMHEAD : M > 64 ? DFLASH_T_LMHEAD_SMALL : 13;
     else if (kind == EPI_ADD) cfg = DFLASH_T_ADD;
     else if (kind == EPI_STORE) cfg = DFLASH_T_STORE;
     const bool one_plane = a_mode != ACT_HILO;
     if ((cfg == 6 || cfg == 9) && !one_plane) cfg = 4;   // these tiles of both planes exceed the LDS
-    if (cfg == 11 && !one_plane) cfg = 12;
+    if ((cfg == 11 || cfg == 13) && !one_plane) cfg = 12;
     if (cfg >= 10 && K % 64 != 0) cfg = 2;
     // SwiGLU tiles hold BN/2 gate and BN/2 up columns of the same rows
     if (kind == EPI_SWIGLU && (N / 2) % (tile_bn(cfg) / 2) != 0) cfg = (N / 2) % 128 == 0 && K % 64 == 0 ? 12 : 2;
@@ -1277,6 +1280,7 @@ static hipError_t go_bf16(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
     case 10: if constexpr (!scatter) return go_fl<128, 384, 2, 4, NP, KIND>(g, p.ksplit, s); break;
     case 11: if constexpr (NP == 1 && !scatter) return go_fl<256, 256, 4, 2, 1, KIND>(g, p.ksplit, s); break;
     case 12: if constexpr (!scatter) return go_fl<128, 256, 2, 4, NP, KIND>(g, p.ksplit, s); break;
+    case 13: if constexpr (NP == 1 && !scatter) return go_fl<64, 256, 1, 8, 1, KIND>(g, p.ksplit, s); break;
     default: break;
   }
   return hipErrorInvalidValue;
