@@ -45,7 +45,8 @@ class dflash_weights(ctypes.Structure):
 
 _lib = None
 EXPORTS = ["dflash_workspace_size", "dflash_inject_kv", "dflash_draft_block", "dflash_verify_workspace_size",
-           "dflash_verify_block", "dflash_status_string", "dflash_prof_select", "dflash_prof_collect"]
+           "dflash_verify_block", "dflash_advance_context", "dflash_status_string", "dflash_prof_select",
+           "dflash_prof_collect"]
 
 
 def lib():
@@ -69,6 +70,8 @@ def lib():
     L.dflash_verify_workspace_size.restype = sz
     L.dflash_verify_block.argtypes = [i32, i32, i32, vp, vp, f32, vp, vp, vp, vp, vp, sz, vp]
     L.dflash_verify_block.restype = i32
+    L.dflash_advance_context.argtypes = [i32, i32, vp, vp, vp, vp, vp]
+    L.dflash_advance_context.restype = i32
     L.dflash_status_string.argtypes = [i32]
     L.dflash_status_string.restype = ctypes.c_char_p
     L.dflash_prof_select.argtypes = [i32]
@@ -156,6 +159,12 @@ def dflash_verify_block(batch, block_size, vocab, target_logits, draft_tokens, t
                                      float(temperature), _ptr(draft_logits), _ptr(uniforms), _ptr(accept_len),
                                      _ptr(out_tokens), _ptr(workspace), ws_bytes, _stream(stream))
     _check("dflash_verify_block", code)
+
+
+def dflash_advance_context(batch, block_size, accept_len, ctx_len, tok_seq, tok_pos, stream=None):
+    code = lib().dflash_advance_context(batch, block_size, _ptr(accept_len), _ptr(ctx_len), _ptr(tok_seq),
+                                        _ptr(tok_pos), _stream(stream))
+    _check("dflash_advance_context", code)
 
 
 def dflash_status_string(code):

@@ -519,6 +519,17 @@ dflash_status dflash_verify_block(int32_t batch, int32_t block_size, int32_t voc
   return e == hipSuccess ? DFLASH_OK : DFLASH_EHIP;
 }
 
+dflash_status dflash_advance_context(int32_t batch, int32_t block_size, const int32_t* accept_len,
+                                     int32_t* ctx_len, int32_t* tok_seq, int32_t* tok_pos, hipStream_t stream) {
+  if (batch < 0) return DFLASH_EINVAL;
+  if (block_size < 1 || block_size > 16) return DFLASH_ECAPACITY;
+  if (batch == 0) return DFLASH_OK;
+  if (!accept_len || !ctx_len || !tok_seq || !tok_pos) return DFLASH_EINVAL;
+  return launch_advance_context(batch, block_size, accept_len, ctx_len, tok_seq, tok_pos, stream) == hipSuccess
+             ? DFLASH_OK
+             : DFLASH_EHIP;
+}
+
 dflash_status dflash_prof_select(int32_t kernel_class) {
   if (kernel_class < DFLASH_PROF_NONE || kernel_class > DFLASH_PROF_VERIFY) return DFLASH_EINVAL;
   g_prof.cls = kernel_class;

@@ -242,6 +242,28 @@ hipError_t launch_rmsnorm(float* h, const float* gain, ActOut out, int M, int H,
   return hipGetLastError();
 }
 
+// One workgroup per sequence: rows j = 0..B of the next injection, then the
+// context length advances (after every row has read the old value).
+__global__ __launch_bounds__(64) void advance_context_kernel(int B, const int* accept_len, int* ctx_len,
+                                                             int* tok_seq, int* tok_pos) {
+  const int b = blockIdx.x, j = threadIdx.x;
+  const int a = min(max(accept_len[b], 0), B);
+  const int c = ctx_len[b];
+  if (j <= B) {
+    tok_seq[b * (B + 1) + j] = j <= a ? b : -1;
+    tok_pos[b * (B + 1) + j] = c + j;
+  }
+  __syncthreads();
+  if (j == 0) ctx_len[b] = c + a + 1;
+}
+
+hipError_t launch_advance_context(int batch, int B, const int* accept_len, int* ctx_len, int* tok_seq,
+                                  int* tok_pos, hipStream_t s) {
+  if (batch <= 0) return hipSuccess;
+  hipLaunchKernelGGL(advance_context_kernel, dim3(batch), dim3(64), 0, s, B, accept_len, ctx_len, tok_seq, tok_pos);
+  return hipGetLastError();
+}
+
 hipError_t launch_lm_combine(const float4* part_f, const int* part_i, int ntiles, int rows, const int* row_map,
                              int* cand, float* conf, hipStream_t s) {
   if (rows <= 0) return hipSuccess;

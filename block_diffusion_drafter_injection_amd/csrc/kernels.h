@@ -113,6 +113,9 @@ hipError_t launch_embed(const int* tau, const void* embed, int wdtype, int vocab
 hipError_t launch_rmsnorm(float* h, const float* gain, ActOut out, int M, int H, float eps,
                           const int* committed, int B, int n_open, int* row_map, hipStream_t s,
                           const float* part = nullptr, int ksplit = 0, int part_rows = 0);
+// Injection rows of the tokens a verification committed, and ctx_len += a + 1.
+hipError_t launch_advance_context(int batch, int B, const int* accept_len, int* ctx_len, int* tok_seq,
+                                  int* tok_pos, hipStream_t s);
 hipError_t launch_lm_combine(const float4* part_f, const int* part_i, int ntiles, int rows,
                              const int* row_map, int* cand, float* conf, hipStream_t s);
 hipError_t launch_commit(const int* cand, const float* conf, int* tau, int* committed,

@@ -130,8 +130,9 @@ size_t dflash_workspace_size(const dflash_config* cfg, int32_t max_batch, int32_
  *   tok_pos (device) [n_tok] absolute position of each token in its sequence
  *   kv_pool (device) pool of n_pages pages (layout above)
  *   block_table (device) [n_seqs, max_pages] physical page per logical page
- * Tokens whose sequence, logical page or physical page is out of range are
- * skipped.  Tokens are processed in chunks of the rows the workspace holds. */
+ * Tokens whose sequence (tok_seq = -1, say), logical page or physical page
+ * is out of range are skipped.  Tokens are processed in chunks of the rows
+ * the workspace holds. */
 dflash_status dflash_inject_kv(const dflash_config* cfg, const dflash_weights* w,
                                const void* target_hidden, const int32_t* tok_seq,
                                const int32_t* tok_pos, int32_t n_tok, void* kv_pool,
@@ -166,6 +167,29 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
                                  uint64_t seed, int32_t* out_tokens, float* out_logits,
                                  float* out_conf, void* workspace, size_t ws_bytes,
                                  hipStream_t stream);
+
+/* Device-side bookkeeping between two drafter steps, so that inject -> draft
+ * -> verify -> advance repeats with no host round trip and can be captured
+ * in a HIP graph (host work between steps leaves the GPU idle: [Deep] 3.2
+ * Overlap 调度; [Note] Spec V2 引擎优化).  Verification committed
+ * accept_len[b] + 1 tokens of sequence b (the accepted prefix and the bonus
+ * token) at positions ctx_len[b] .. ctx_len[b] + accept_len[b].  For
+ * j = 0..block_size this writes injection row r = b*(block_size+1) + j:
+ *   tok_seq[r] = (j <= accept_len[b]) ? b : -1,  tok_pos[r] = ctx_len[b] + j
+ * and then advances ctx_len[b] by accept_len[b] + 1.  dflash_inject_kv skips
+ * rows with tok_seq = -1, so the next injection takes n_tok =
+ * batch*(block_size+1) rows of target hidden states laid out [b][j] (the
+ * target's states at the block_size+1 verified positions of each sequence).
+ *   accept_len (device) [batch], as dflash_verify_block writes it (values
+ *              are clamped to [0, block_size])
+ *   ctx_len (device) [batch], read and advanced in place
+ *   tok_seq, tok_pos (device) [batch*(block_size+1)] int32, written
+ * The block table must already map the pages of the new positions;
+ * positions past it are skipped by the injection like any unmapped one.
+ * Limits: batch >= 0; 1 <= block_size <= 16. */
+dflash_status dflash_advance_context(int32_t batch, int32_t block_size, const int32_t* accept_len,
+                                     int32_t* ctx_len, int32_t* tok_seq, int32_t* tok_pos,
+                                     hipStream_t stream);
 
 /* Bytes of workspace dflash_verify_block needs. */
 size_t dflash_verify_workspace_size(int32_t batch, int32_t block_size, int32_t vocab);

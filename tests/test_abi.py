@@ -121,6 +121,16 @@ def test_verify_and_inject_argument_errors(L):
     assert g(ctypes.byref(cfg), ctypes.byref(w), 8, 8, 8, 5, 8, 4, 8, 1, 4, 256, 16, None) == -5
 
 
+def test_advance_context_argument_errors(L):
+    f = L.dflash_advance_context
+    assert f(-1, 8, 8, 8, 8, 8, None) == -1
+    assert f(2, 0, 8, 8, 8, 8, None) == -4
+    assert f(2, 17, 8, 8, 8, 8, None) == -4
+    assert f(2, 8, None, 8, 8, 8, None) == -1
+    assert f(2, 8, 8, 8, None, 8, None) == -1
+    assert f(0, 8, None, None, None, None, None) == 0
+
+
 def test_profiler_select_validates_class(L):
     assert L.dflash_prof_select(99) == -1
     assert L.dflash_prof_select(0) == 0
