@@ -69,22 +69,34 @@ __device__ __forceinline__ void att_barrier() {
 // (fp32) are written too, [b][kv head][i][d], for the in-block part of the
 // attention.  When the q/k/v projection left K-split partials, they are
 // summed here in split order (the sums a separate reduction would form).
-__device__ __forceinline__ float2 qkv_pair(const AttnParams& p, size_t off, size_t plane) {
-  if (p.qkv_ks <= 1) return *(const float2*)(p.qkv + off);
-  float2 a = make_float2(0.f, 0.f);
+__device__ __forceinline__ float4 qkv_quad(const AttnParams& p, size_t off, size_t plane) {
+  if (p.qkv_ks <= 1) return *(const float4*)(p.qkv + off);
+  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
   for (int s = 0; s < p.qkv_ks; ++s) {
-    const float2 v = *(const float2*)(p.qkv_part + s * plane + off);
+    const float4 v = *(const float4*)(p.qkv_part + s * plane + off);
     a.x += v.x;
     a.y += v.y;
+    a.z += v.z;
+    a.w += v.w;
   }
   return a;
 }
 
+// Rotate-half RoPE of four consecutive first-half dims x0 (4e .. 4e+3) and
+// their partners x1 (h+4e ..): y0 = x0 cos - x1 sin, y1 = x1 cos + x0 sin.
+__device__ __forceinline__ void rope4(const float4& x0, const float4& x1, const float4& c01, const float4& c23,
+                                      float4& y0, float4& y1) {
+  y0 = make_float4(x0.x * c01.x - x1.x * c01.y, x0.y * c01.z - x1.y * c01.w, x0.z * c23.x - x1.z * c23.y,
+                   x0.w * c23.z - x1.w * c23.w);
+  y1 = make_float4(x1.x * c01.x + x0.x * c01.y, x1.y * c01.z + x0.y * c01.w, x1.z * c23.x + x0.z * c23.y,
+                   x1.w * c23.z + x0.w * c23.w);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_qprep_kernel(AttnParams p) {
-  // D/4 threads per row; thread e covers dims 2e, 2e+1 and their rotate-half
-  // partners h+2e, h+2e+1
-  constexpr int TPR = D / 4, RPB = 256 / TPR, h = D / 2;
+  // D/8 threads per row; thread e covers dims 4e .. 4e+3 and their
+  // rotate-half partners h+4e .. h+4e+3
+  constexpr int TPR = D / 8, RPB = 256 / TPR, h = D / 2;
   const int g = p.nq / p.nkv, R = g * p.B;
   const int ldq = (p.nq + 2 * p.nkv) * D;
   const size_t plane = (size_t)p.batch * p.B * ldq;
@@ -94,29 +106,35 @@ __global__ __launch_bounds__(256) void attn_qprep_kernel(AttnParams p) {
   const float qscale = p.scale * 1.4426950408889634f;   // scores come out in base-2 units
   const int j = r / p.B, i = r - j * p.B, row = b * p.B + i, n = m * g + j;
   {
-    const size_t off = (size_t)row * ldq + n * D + 2 * e;
-    const float2 x0 = qkv_pair(p, off, plane), x1 = qkv_pair(p, off + h, plane);
-    const float4 c = *(const float4*)(p.cs + (size_t)row * h + 2 * e);   // (cos, sin) of dims 2e, 2e+1
-    uint32_t h0, l0, h1, l1;
-    split_hilo2((x0.x * c.x - x1.x * c.y) * qscale, (x0.y * c.z - x1.y * c.w) * qscale, h0, l0);
-    split_hilo2((x1.x * c.x + x0.x * c.y) * qscale, (x1.y * c.z + x0.y * c.w) * qscale, h1, l1);
-    const size_t gr = (((size_t)b * p.nkv + m) * R + r) * (D / 2);
-    ((uint32_t*)p.q_hi)[gr + e] = h0;
-    ((uint32_t*)p.q_lo)[gr + e] = l0;
-    ((uint32_t*)p.q_hi)[gr + h / 2 + e] = h1;
-    ((uint32_t*)p.q_lo)[gr + h / 2 + e] = l1;
+    const size_t off = (size_t)row * ldq + n * D + 4 * e;
+    const float4 x0 = qkv_quad(p, off, plane), x1 = qkv_quad(p, off + h, plane);
+    const float4* cs = (const float4*)(p.cs + (size_t)row * h + 4 * e);   // (cos, sin) of dims 4e .. 4e+3
+    float4 y0, y1;
+    rope4(x0, x1, cs[0], cs[1], y0, y1);
+    uint32_t h0, l0, h1, l1, h2, l2, h3, l3;
+    split_hilo2(y0.x * qscale, y0.y * qscale, h0, l0);
+    split_hilo2(y0.z * qscale, y0.w * qscale, h1, l1);
+    split_hilo2(y1.x * qscale, y1.y * qscale, h2, l2);
+    split_hilo2(y1.z * qscale, y1.w * qscale, h3, l3);
+    const size_t gr = (((size_t)b * p.nkv + m) * R + r) * (D / 2);   // in 32-bit words
+    *(u32x2*)((uint32_t*)p.q_hi + gr + 2 * e) = u32x2{h0, h1};
+    *(u32x2*)((uint32_t*)p.q_lo + gr + 2 * e) = u32x2{l0, l1};
+    *(u32x2*)((uint32_t*)p.q_hi + gr + h / 2 + 2 * e) = u32x2{h2, h3};
+    *(u32x2*)((uint32_t*)p.q_lo + gr + h / 2 + 2 * e) = u32x2{l2, l3};
   }
   if (r < p.B) {   // key (rotated) and value of block position r
     const int krow = b * p.B + r;
-    const size_t koff = (size_t)krow * ldq + p.nq * D + m * D + 2 * e, voff = koff + p.nkv * D;
-    const float2 k0 = qkv_pair(p, koff, plane), k1 = qkv_pair(p, koff + h, plane);
-    const float2 v0 = qkv_pair(p, voff, plane), v1 = qkv_pair(p, voff + h, plane);
-    const float4 c = *(const float4*)(p.cs + (size_t)krow * h + 2 * e);
-    const size_t o = (((size_t)b * p.nkv + m) * p.B + r) * D + 2 * e;
-    *(float2*)(p.kblk + o) = make_float2(k0.x * c.x - k1.x * c.y, k0.y * c.z - k1.y * c.w);
-    *(float2*)(p.kblk + o + h) = make_float2(k1.x * c.x + k0.x * c.y, k1.y * c.z + k0.y * c.w);
-    *(float2*)(p.vblk + o) = v0;
-    *(float2*)(p.vblk + o + h) = v1;
+    const size_t koff = (size_t)krow * ldq + p.nq * D + m * D + 4 * e, voff = koff + p.nkv * D;
+    const float4 k0 = qkv_quad(p, koff, plane), k1 = qkv_quad(p, koff + h, plane);
+    const float4 v0 = qkv_quad(p, voff, plane), v1 = qkv_quad(p, voff + h, plane);
+    const float4* cs = (const float4*)(p.cs + (size_t)krow * h + 4 * e);
+    float4 y0, y1;
+    rope4(k0, k1, cs[0], cs[1], y0, y1);
+    const size_t o = (((size_t)b * p.nkv + m) * p.B + r) * D + 4 * e;
+    *(float4*)(p.kblk + o) = y0;
+    *(float4*)(p.kblk + o + h) = y1;
+    *(float4*)(p.vblk + o) = v0;
+    *(float4*)(p.vblk + o + h) = v1;
   }
 }
 
@@ -662,7 +680,7 @@ hipError_t launch_attention(const AttnParams& p, int wdtype, hipStream_t s, void
   // the prepared queries and block keys also feed the finish kernel, with or
   // without context
   if (wdtype == 1 && p.d == 128) {
-    hipLaunchKernelGGL(attn_qprep_kernel<128>, dim3((R + 7) / 8, p.nkv, p.batch), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attn_qprep_kernel<128>, dim3((R + 15) / 16, p.nkv, p.batch), dim3(256), 0, s, p);
   }
   if (p.n_splits <= 0) return hipGetLastError();
   const dim3 gctx(p.n_splits * nqg, p.nkv, p.batch);
