@@ -95,17 +95,18 @@ __device__ __forceinline__ void rope4(const float4& x0, const float4& x1, const 
 template <int D>
 __global__ __launch_bounds__(256) void attn_qprep_kernel(AttnParams p) {
   // D/8 threads per row; thread e covers dims 4e .. 4e+3 and their
-  // rotate-half partners h+4e .. h+4e+3
+  // rotate-half partners h+4e .. h+4e+3.  Row slots u < R are queries, then
+  // B block keys, then B block values, so every workgroup does equal work.
   constexpr int TPR = D / 8, RPB = 256 / TPR, h = D / 2;
   const int g = p.nq / p.nkv, R = g * p.B;
   const int ldq = (p.nq + 2 * p.nkv) * D;
   const size_t plane = (size_t)p.batch * p.B * ldq;
-  const int e = threadIdx.x % TPR, r = blockIdx.x * RPB + threadIdx.x / TPR;
+  const int e = threadIdx.x % TPR, u = blockIdx.x * RPB + threadIdx.x / TPR;
   const int m = blockIdx.y, b = blockIdx.z;
-  if (r >= R) return;
-  const float qscale = p.scale * 1.4426950408889634f;   // scores come out in base-2 units
-  const int j = r / p.B, i = r - j * p.B, row = b * p.B + i, n = m * g + j;
-  {
+  if (u >= R + 2 * p.B) return;
+  if (u < R) {
+    const float qscale = p.scale * 1.4426950408889634f;   // scores come out in base-2 units
+    const int r = u, j = r / p.B, i = r - j * p.B, row = b * p.B + i, n = m * g + j;
     const size_t off = (size_t)row * ldq + n * D + 4 * e;
     const float4 x0 = qkv_quad(p, off, plane), x1 = qkv_quad(p, off + h, plane);
     const float4* cs = (const float4*)(p.cs + (size_t)row * h + 4 * e);   // (cos, sin) of dims 4e .. 4e+3
@@ -121,20 +122,23 @@ __global__ __launch_bounds__(256) void attn_qprep_kernel(AttnParams p) {
     *(u32x2*)((uint32_t*)p.q_lo + gr + 2 * e) = u32x2{l0, l1};
     *(u32x2*)((uint32_t*)p.q_hi + gr + h / 2 + 2 * e) = u32x2{h2, h3};
     *(u32x2*)((uint32_t*)p.q_lo + gr + h / 2 + 2 * e) = u32x2{l2, l3};
+    return;
   }
-  if (r < p.B) {   // key (rotated) and value of block position r
-    const int krow = b * p.B + r;
-    const size_t koff = (size_t)krow * ldq + p.nq * D + m * D + 4 * e, voff = koff + p.nkv * D;
-    const float4 k0 = qkv_quad(p, koff, plane), k1 = qkv_quad(p, koff + h, plane);
-    const float4 v0 = qkv_quad(p, voff, plane), v1 = qkv_quad(p, voff + h, plane);
+  const bool is_k = u < R + p.B;
+  const int r = is_k ? u - R : u - R - p.B;   // block position
+  const int krow = b * p.B + r;
+  const size_t off = (size_t)krow * ldq + (p.nq + (is_k ? 0 : p.nkv)) * D + m * D + 4 * e;
+  const float4 x0 = qkv_quad(p, off, plane), x1 = qkv_quad(p, off + h, plane);
+  const size_t o = (((size_t)b * p.nkv + m) * p.B + r) * D + 4 * e;
+  if (is_k) {   // rotated key
     const float4* cs = (const float4*)(p.cs + (size_t)krow * h + 4 * e);
     float4 y0, y1;
-    rope4(k0, k1, cs[0], cs[1], y0, y1);
-    const size_t o = (((size_t)b * p.nkv + m) * p.B + r) * D + 4 * e;
+    rope4(x0, x1, cs[0], cs[1], y0, y1);
     *(float4*)(p.kblk + o) = y0;
     *(float4*)(p.kblk + o + h) = y1;
-    *(float4*)(p.vblk + o) = v0;
-    *(float4*)(p.vblk + o + h) = v1;
+  } else {
+    *(float4*)(p.vblk + o) = x0;
+    *(float4*)(p.vblk + o + h) = x1;
   }
 }
 
@@ -571,6 +575,21 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
   const int j = rc / p.B, i = rc - j * p.B;
   const int row = b * p.B + i, n = m * g + j;
   const int d0 = part * DPT;   // this thread's dims d0 .. d0 + DPT - 1
+  // the first context partials of this row, loaded now so their latency
+  // overlaps the in-block attention (the merge below uses them in split order)
+  constexpr int NPF = 2;
+  const size_t Mq = (size_t)p.batch * p.B * p.nq;
+  const size_t qrow = (size_t)row * p.nq + n;
+  float pl[NPF];
+  float4 po[NPF][DPT / 4];
+#pragma unroll
+  for (int k = 0; k < NPF; ++k) {
+    pl[k] = k < p.n_splits ? p.part_lse[k * Mq + qrow] : -INFINITY;
+#pragma unroll
+    for (int e = 0; e < DPT; e += 4)
+      po[k][e / 4] = k < p.n_splits ? *(const float4*)(p.part_o + (k * Mq + qrow) * D + d0 + e)
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
   float q[DPT];
   if constexpr (PREP) {
     // prepared rotated query (hi + lo), carrying scale * log2 e
@@ -638,17 +657,29 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
     }
   }
   if (!rv) return;
-  const size_t Mq = (size_t)p.batch * p.B * p.nq;
-  const size_t qrow = (size_t)row * p.nq + n;
   float mxl = blse;
-  for (int sp = 0; sp < p.n_splits; ++sp) mxl = fmaxf(mxl, p.part_lse[sp * Mq + qrow]);
+#pragma unroll
+  for (int k = 0; k < NPF; ++k) mxl = fmaxf(mxl, pl[k]);
+  for (int sp = NPF; sp < p.n_splits; ++sp) mxl = fmaxf(mxl, p.part_lse[sp * Mq + qrow]);
   float tot = 0.f, acc[DPT];
 #pragma unroll
   for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
-  // an empty split has lse = -inf and o = 0, so it adds nothing; no branch,
-  // so the loads of several splits are in flight together
+  // an empty split has lse = -inf and o = 0, so it adds nothing (no branch)
+#pragma unroll
+  for (int k = 0; k < NPF; ++k) {
+    const float w = expf(pl[k] - mxl);
+    tot += w;
+#pragma unroll
+    for (int e = 0; e < DPT; e += 4) {
+      const float4 v = po[k][e / 4];
+      acc[e] = fmaf(w, v.x, acc[e]);
+      acc[e + 1] = fmaf(w, v.y, acc[e + 1]);
+      acc[e + 2] = fmaf(w, v.z, acc[e + 2]);
+      acc[e + 3] = fmaf(w, v.w, acc[e + 3]);
+    }
+  }
 #pragma unroll 4
-  for (int sp = 0; sp < p.n_splits; ++sp) {
+  for (int sp = NPF; sp < p.n_splits; ++sp) {
     const float l = p.part_lse[sp * Mq + qrow];
     const float w = expf(l - mxl);
     tot += w;
@@ -680,7 +711,7 @@ hipError_t launch_attention(const AttnParams& p, int wdtype, hipStream_t s, void
   // the prepared queries and block keys also feed the finish kernel, with or
   // without context
   if (wdtype == 1 && p.d == 128) {
-    hipLaunchKernelGGL(attn_qprep_kernel<128>, dim3((R + 15) / 16, p.nkv, p.batch), dim3(256), 0, s, p);
+    hipLaunchKernelGGL(attn_qprep_kernel<128>, dim3((R + 2 * p.B + 15) / 16, p.nkv, p.batch), dim3(256), 0, s, p);
   }
   if (p.n_splits <= 0) return hipGetLastError();
   const dim3 gctx(p.n_splits * nqg, p.nkv, p.batch);
