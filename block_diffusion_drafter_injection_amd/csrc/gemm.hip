@@ -238,167 +238,6 @@ __device__ __forceinline__ bool tile_of(int ntm, int total, int& tm, int& tn) {
 }
 
 // ---------------------------------------------------------------------------
-// MFMA GEMM.  NP = 2: A is a (hi, lo) bf16 pair, two MFMAs per product.
-// STAGES = 2 double-buffers LDS (one barrier per K-tile), 1 uses one buffer.
-// ksplit > 1: this workgroup covers one contiguous range of K-tiles and
-// writes its raw fp32 tile to part[ks][M][N]; splitk_reduce_kernel then sums
-// the ranges in fixed order and runs the epilogue (deterministic, and the
-// same for every M).
-template <int BM, int BN, int WM, int WN, int NP, int STAGES>
-struct MfmaCfg {
-  static constexpr int BK = 64, LDK = BK + 8;
-  static constexpr int NWN = BN / WN, NT = (BM / WM) * NWN * 64;
-  static constexpr int TM = WM / 16, TN = WN / 16;
-  static constexpr int APER = BM * BK / 8 / NT, BPER = BN * BK / 8 / NT;
-  static constexpr int LDC = BN + 4;
-  static constexpr int STAGE_ELEMS = (NP * BM + BN) * LDK;
-  static constexpr int STAGE_BYTES = STAGES * STAGE_ELEMS * 2;
-  static constexpr int EPI_BYTES = BM * LDC * 4;
-  static constexpr int SMEM = STAGE_BYTES > EPI_BYTES ? STAGE_BYTES : EPI_BYTES;
-  // waves per SIMD to keep resident: two workgroups per CU when LDS allows it
-  static constexpr int MINW = SMEM <= 80 * 1024 ? 2 : 1;
-  static_assert(APER * NT == BM * BK / 8 && BPER * NT == BN * BK / 8, "load split");
-};
-
-template <int BM, int BN, int WM, int WN, int NP, int STAGES, int KIND>
-__global__ __launch_bounds__((MfmaCfg<BM, BN, WM, WN, NP, STAGES>::NT), (MfmaCfg<BM, BN, WM, WN, NP, STAGES>::MINW)) void gemm_mfma_kernel(
-    ActIn a, BRows<bf16_t> b, int M, int N, int K, int ksplit, float* part, EpiParams e) {
-  using C = MfmaCfg<BM, BN, WM, WN, NP, STAGES>;
-  constexpr int BK = C::BK, LDK = C::LDK, NT = C::NT, TM = C::TM, TN = C::TN;
-  constexpr int APER = C::APER, BPER = C::BPER, NWN = C::NWN;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[C::SMEM];
-
-  const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
-  int t;
-  {
-    const int per = gridDim.x / 8, L = blockIdx.x;
-    t = (per > 0) ? (L & 7) * per + (L >> 3) : L;
-    if (t >= ntm * ntn * ksplit) return;
-  }
-  const int tm = t % ntm, tn = (t / ntm) % ntn, ks = t / (ntm * ntn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int nkt = K / BK;
-  const int kt0 = (int)((long long)ks * nkt / ksplit), kt1 = (int)((long long)(ks + 1) * nkt / ksplit);
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid / NWN, wn = wid - (wid / NWN) * NWN;
-
-  // Per-thread load slots are fixed for the whole K loop.  Rows past M (or
-  // columns past N) are clamped to the last valid one: they only feed output
-  // rows / columns that are never stored, so every load is unconditional.
-  const bf16_t* a_src[NP][APER];
-  const bf16_t* b_src[BPER];
-  int lds_a[APER], lds_b[BPER];
-#pragma unroll
-  for (int j = 0; j < APER; ++j) {
-    const int c = tid + j * NT, r = c >> 3, kc = (c & 7) * 8;
-    const int row = min(m0 + r, M - 1);
-    a_src[0][j] = (const bf16_t*)a.p0 + (size_t)row * a.ld + kc;
-    if constexpr (NP == 2) a_src[NP - 1][j] = (const bf16_t*)a.p1 + (size_t)row * a.ld + kc;
-    lds_a[j] = r * LDK + kc;
-  }
-#pragma unroll
-  for (int j = 0; j < BPER; ++j) {
-    const int c = tid + j * NT, r = c >> 3, kc = (c & 7) * 8;
-    b_src[j] = b.row(min(n0 + r, N - 1), BN) + kc;
-    lds_b[j] = r * LDK + kc;
-  }
-  u32x4 ra[NP][APER], rb[BPER];
-
-#define DFLASH_GLOAD(kt)                                                                            \
-  do {                                                                                              \
-    const int k0_ = (kt) * BK;                                                                      \
-    _Pragma("unroll") for (int j = 0; j < APER; ++j) {                                              \
-      _Pragma("unroll") for (int p = 0; p < NP; ++p) ra[p][j] = *(const u32x4*)(a_src[p][j] + k0_); \
-    }                                                                                               \
-    _Pragma("unroll") for (int j = 0; j < BPER; ++j) rb[j] = *(const u32x4*)(b_src[j] + k0_);       \
-  } while (0)
-#define DFLASH_SSTORE(buf)                                                                          \
-  do {                                                                                              \
-    bf16_t* st_ = (bf16_t*)smem + (buf) * C::STAGE_ELEMS;                                          \
-    _Pragma("unroll") for (int j = 0; j < APER; ++j) {                                              \
-      _Pragma("unroll") for (int p = 0; p < NP; ++p) *(u32x4*)(st_ + p * BM * LDK + lds_a[j]) = ra[p][j]; \
-    }                                                                                               \
-    _Pragma("unroll") for (int j = 0; j < BPER; ++j) *(u32x4*)(st_ + NP * BM * LDK + lds_b[j]) = rb[j]; \
-  } while (0)
-
-  f32x4 acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  auto compute = [&](const bf16_t* As, const bf16_t* Bs) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kq = 0; kq < BK / 32; ++kq) {
-      const int kof = kq * 32 + 8 * (lane >> 4);
-      bf16x8 af[NP][TM], bfr[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int p = 0; p < NP; ++p)
-          af[p][i] = as_bf16x8(*(const u32x4*)(As + (p * BM + wm * TM * 16 + 16 * i + (lane & 15)) * LDK + kof));
-#pragma unroll
-      for (int j = 0; j < TN; ++j)
-        bfr[j] = as_bf16x8(*(const u32x4*)(Bs + (wn * TN * 16 + 16 * j + (lane & 15)) * LDK + kof));
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-#pragma unroll
-          for (int p = 0; p < NP; ++p)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[p][i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-  };
-
-  if (kt0 < kt1) {
-    DFLASH_GLOAD(kt0);
-    DFLASH_SSTORE(0);
-    __syncthreads();
-  }
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const bool more = kt + 1 < kt1;
-    if (more) DFLASH_GLOAD(kt + 1);
-    if constexpr (STAGES == 2) {
-      const int cur = (kt - kt0) & 1;
-      const bf16_t* st = (const bf16_t*)smem + cur * C::STAGE_ELEMS;
-      compute(st, st + NP * BM * LDK);
-      if (more) DFLASH_SSTORE(cur ^ 1);
-      __syncthreads();
-    } else {
-      const bf16_t* st = (const bf16_t*)smem;
-      compute(st, st + NP * BM * LDK);
-      __syncthreads();
-      if (more) {
-        DFLASH_SSTORE(0);
-        __syncthreads();
-      }
-    }
-  }
-#undef DFLASH_GLOAD
-#undef DFLASH_SSTORE
-
-  float* Cs = (float*)smem;
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        Cs[(wm * TM * 16 + 16 * i + 4 * (lane >> 4) + q) * C::LDC + wn * TN * 16 + 16 * j + (lane & 15)] = acc[i][j][q];
-  __syncthreads();
-  if (ksplit > 1) {
-    float* dst = part + (size_t)ks * M * N;
-    constexpr int C4 = BN / 4;
-    for (int idx = tid; idx < BM * C4; idx += NT) {
-      const int r = idx / C4, c = (idx - r * C4) * 4;
-      if (m0 + r < M && n0 + c < N)
-        *(float4*)(dst + (size_t)(m0 + r) * N + n0 + c) = *(const float4*)(Cs + r * C::LDC + c);
-    }
-    return;
-  }
-  run_epilogue<KIND, BM, BN, NT, bf16_t>(Cs, C::LDC, m0, n0, M, N, e);
-}
-
 // MFMA GEMM with direct global->LDS loads (gfx950 global_load_lds_dwordx4):
 // 128x128x32 tiles, four 64x64 waves, three LDS stages, one barrier per
 // K-tile and no staging registers.  Each 16-byte load instruction of a wave
@@ -559,19 +398,12 @@ __global__ __launch_bounds__(256, 2) void gemm_dma_kernel(ActIn a, BRows<bf16_t>
   run_epilogue<KIND, BM, BN, 256, bf16_t>(Cs, C::LDC, m0, n0, M, N, e);
 }
 
-// MFMA GEMM with direct global->LDS loads for large tiles: eight waves (two
-// per SIMD, one workgroup per CU) of (BM/WGM) x (BN/WGN), 32-deep K stages in
-// three LDS buffers, the same 64-byte swizzled rows as gemm_dma_kernel.  A
-// large tile keeps the L1 line lookups per MFMA low (each 1 KiB load touches
-// sixteen lines) and large wave tiles keep the LDS reads per MFMA low.  The
-// epilogue stages 64-row slices of the C tile through LDS and reuses the fused
-// epilogues.
 // Scheduling of one pipeline step: the R fragment reads of the next stage are
 // spread over the Q MFMAs of the current one (Q/R MFMAs, then one read), so
 // their LDS traffic overlaps the matrix work instead of following it (MFMAs
 // first: the fragments they use are already in registers).
 template <int R, int Q>
-__device__ __forceinline__ void dma8_interleave() {
+__device__ __forceinline__ void mfma_read_interleave() {
 #pragma unroll
   for (int r = 0; r < R; ++r) {
     __builtin_amdgcn_sched_group_barrier(0x008, Q / R, 0);  // Q/R MFMAs
@@ -580,180 +412,11 @@ __device__ __forceinline__ void dma8_interleave() {
   if constexpr (Q % R != 0) __builtin_amdgcn_sched_group_barrier(0x008, Q % R, 0);
 }
 
-template <int BM, int BN, int WGM, int WGN, int NP, int STAGES_ = 3>
-struct Dma8Cfg {
-  static constexpr int NT = 64 * WGM * WGN, NW = WGM * WGN, BK = 32, STAGES = STAGES_;
-  static constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
-  static constexpr int ROWS = NP * BM + BN;          // LDS rows per stage (64 B each)
-  static constexpr int STAGE_BYTES = ROWS * 64;
-  static constexpr int BLOCKS = ROWS / 16;            // 1 KiB load instructions per stage
-  static constexpr int LPT = BLOCKS / NW;             // per wave
-  static constexpr int LDC = BN + 4;
-  static constexpr int SMEM_PIPE = STAGES * STAGE_BYTES;
-  static constexpr int SMEM_EPI = 64 * LDC * 4;
-  static constexpr int SMEM = SMEM_PIPE > SMEM_EPI ? SMEM_PIPE : SMEM_EPI;
-  static_assert(BLOCKS % NW == 0 && WM % 16 == 0 && WN % 16 == 0 && WM == 64, "tile shape");
-  static_assert(SMEM <= 160 * 1024, "LDS");
-  static_assert(LPT * (STAGES - 2) <= 63 && STAGES >= 3 && STAGES <= 4, "vmcnt range");
-};
-
-template <int BM, int BN, int WGM, int WGN, int NP, int STAGES, int KIND>
-__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_dma8_kernel(ActIn a, BRows<bf16_t> b, int M, int N, int K,
-                                                                       int ksplit, float* part, EpiParams e) {
-  using C = Dma8Cfg<BM, BN, WGM, WGN, NP, STAGES>;
-  constexpr int BK = C::BK, LPT = C::LPT, FM = C::FM, FN = C::FN, NT = C::NT;
-  __shared__ __attribute__((aligned(1024))) unsigned char smem[C::SMEM];
-
-  const int ntm = (M + BM - 1) / BM, ntn = (N + BN - 1) / BN;
-  int t;
-  {
-    const int per = gridDim.x / 8, L = blockIdx.x;
-    t = (per > 0) ? (L & 7) * per + (L >> 3) : L;
-    if (t >= ntm * ntn * ksplit) return;
-  }
-  const int tm = t % ntm, tn = (t / ntm) % ntn, ks = t / (ntm * ntn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const int nkt = K / BK;
-  const int kt0 = (int)((long long)ks * nkt / ksplit), kt1 = (int)((long long)(ks + 1) * nkt / ksplit);
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid / WGN, wn = wid - wm * WGN;
-
-  // source pointers of this lane's LPT load blocks (fixed over K)
-  const bf16_t* src[LPT];
-#pragma unroll
-  for (int q = 0; q < LPT; ++q) {
-    const int blk = wid * LPT + q;
-    const int row = blk * 16 + (lane >> 2);
-    const int pc = lane & 3, lc = pc ^ ((row >> 1) & 3);
-    const bf16_t* base;
-    if (row < NP * BM) {
-      const int p = row / BM, r = row - p * BM;
-      const int gr = min(m0 + r, M - 1);
-      base = (const bf16_t*)(p == 0 ? a.p0 : a.p1) + (size_t)gr * a.ld;
-    } else {
-      base = b.row(min(n0 + row - NP * BM, N - 1), BN);
-    }
-    src[q] = base + lc * 8;
-  }
-  const uint32_t lds0 = (uint32_t)(size_t)smem;
-
-#define DMA8_ISSUE(KT, STAGE)                                                                                    \
-  do {                                                                                                           \
-    const int k0_ = (KT) * BK;                                                                                   \
-    _Pragma("unroll") for (int q = 0; q < LPT; ++q) {                                                            \
-      __builtin_amdgcn_global_load_lds(                                                                          \
-          (const __attribute__((address_space(1))) void*)(src[q] + k0_),                                         \
-          (__attribute__((address_space(3))) void*)(size_t)(lds0 + (STAGE) * C::STAGE_BYTES +                   \
-                                                            (wid * LPT + q) * 1024),                             \
-          16, 0, 0);                                                                                             \
-    }                                                                                                            \
-  } while (0)
-
-  f32x4 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // Fragments of stage it+1 are read from LDS while the MFMAs of stage it run
-  // (two register sets).  Iteration it: wait for stage it+1, barrier (every
-  // wave has its stage-it fragments in registers, so that buffer is free),
-  // issue stage it+3 into it, read stage it+1, multiply stage it.
-  const int lr = lane & 15, lc = lane >> 4;
-#define DMA8_LOAD(F, STG)                                                                                      \
-  do {                                                                                                         \
-    const unsigned char* st_ = smem + (STG) * C::STAGE_BYTES;                                                  \
-    _Pragma("unroll") for (int p = 0; p < NP; ++p) _Pragma("unroll") for (int i = 0; i < FM; ++i) {            \
-      const int row = p * BM + wm * C::WM + 16 * i + lr;                                                       \
-      F##a[p][i] = as_bf16x8(*(const u32x4*)(st_ + row * 64 + ((lc ^ ((row >> 1) & 3)) << 4)));               \
-    }                                                                                                          \
-    _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                                           \
-      const int row = NP * BM + wn * C::WN + 16 * j + lr;                                                      \
-      F##b[j] = as_bf16x8(*(const u32x4*)(st_ + row * 64 + ((lc ^ ((row >> 1) & 3)) << 4)));                  \
-    }                                                                                                          \
-  } while (0)
-#define DMA8_MMA(F)                                                                                            \
-  do {                                                                                                         \
-    _Pragma("unroll") for (int p = 0; p < NP; ++p) _Pragma("unroll") for (int i = 0; i < FM; ++i)             \
-        _Pragma("unroll") for (int j = 0; j < FN; ++j) acc[i][j] =                                             \
-            __builtin_amdgcn_mfma_f32_16x16x32_bf16(F##a[p][i], F##b[j], acc[i][j], 0, 0, 0);                  \
-  } while (0)
-#define DMA8_STEP(CUR, NXT, IT)                                                                                \
-  do {                                                                                                         \
-    if ((IT) + 1 < nloc) {                                                                                     \
-      const int pend_ = min(STAGES - 2, nloc - 2 - (IT));                                                      \
-      if (STAGES > 3 && pend_ >= 2) wait_vmcnt<(STAGES > 3 ? 2 : 1) * LPT>();                                  \
-      else if (pend_ >= 1) wait_vmcnt<LPT>();                                                                  \
-      else wait_vmcnt<0>();                                                                                    \
-      lds_reads_done_barrier();                                                                                \
-      if ((IT) + STAGES < nloc) DMA8_ISSUE(kt0 + (IT) + STAGES, (IT) % STAGES);                                \
-    }                                                                                                          \
-    /* unconditional, so the MFMAs below wait only for their own fragments (the */                             \
-    /* last step reads a stale buffer whose values are never used) */                                          \
-    DMA8_LOAD(NXT, ((IT) + 1) % STAGES);                                                                       \
-    DMA8_MMA(CUR);                                                                                             \
-    dma8_interleave<NP * FM + FN, NP * FM * FN>();                                                             \
-  } while (0)
-
-  const int nloc = kt1 - kt0;
-  bf16x8 f0a[NP][FM], f0b[FN], f1a[NP][FM], f1b[FN];
-#pragma unroll
-  for (int s0 = 0; s0 < STAGES - 1; ++s0)
-    if (s0 < nloc) DMA8_ISSUE(kt0 + s0, s0);
-  if (nloc > 0) {
-    const int pend = min(STAGES - 2, nloc - 1);   // stages issued after stage 0
-    if (STAGES > 3 && pend >= 2) wait_vmcnt<(STAGES > 3 ? 2 : 1) * LPT>();
-    else if (pend >= 1) wait_vmcnt<LPT>();
-    else wait_vmcnt<0>();
-    stage_barrier();
-    if (STAGES - 1 < nloc) DMA8_ISSUE(kt0 + STAGES - 1, STAGES - 1);
-    DMA8_LOAD(f0, 0);
-  }
-  for (int it = 0; it < nloc; it += 2) {
-    DMA8_STEP(f0, f1, it);
-    if (it + 1 < nloc) DMA8_STEP(f1, f0, it + 1);
-  }
-#undef DMA8_LOAD
-#undef DMA8_MMA
-#undef DMA8_STEP
-#undef DMA8_ISSUE
-  __syncthreads();   // every wave is done with the pipeline buffers
-
-  // epilogue over 64-row slices of the tile (slice sl = the rows of wave row wm == sl)
-  float* Cs = (float*)smem;
-#pragma unroll
-  for (int sl = 0; sl < WGM; ++sl) {
-    if (m0 + sl * 64 >= M) break;
-    if (wm == sl) {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            Cs[(16 * i + 4 * lc + q) * C::LDC + wn * C::WN + 16 * j + lr] = acc[i][j][q];
-    }
-    __syncthreads();
-    const int ms = m0 + sl * 64;
-    if (ksplit > 1) {
-      float* dst = part + (size_t)ks * M * N;
-      constexpr int C4 = BN / 4;
-      for (int idx = tid; idx < 64 * C4; idx += NT) {
-        const int r = idx / C4, c = (idx - r * C4) * 4;
-        if (ms + r < M && n0 + c < N)
-          *(float4*)(dst + (size_t)(ms + r) * N + n0 + c) = *(const float4*)(Cs + r * C::LDC + c);
-      }
-    } else {
-      run_epilogue<KIND, 64, BN, NT, bf16_t>(Cs, C::LDC, ms, n0, M, N, e);
-    }
-    __syncthreads();
-  }
-}
-
-// The same eight-wave tiles with 64-deep K stages in two LDS buffers: each
-// 1 KiB direct load covers eight whole 128-byte rows, so it holds eight L1
-// line slots instead of sixteen half-used ones, which doubles what the loads
-// deliver per outstanding request.  LDS rows are 128 bytes with 16-byte chunk
+// MFMA GEMM with direct global->LDS loads for large tiles: eight waves (two
+// per SIMD, one workgroup per CU) of 64 x (BN/WGN), 64-deep K stages in two
+// LDS buffers.  Each 1 KiB direct load covers eight whole 128-byte rows, so
+// it holds eight L1 line slots instead of sixteen half-used ones (32-deep
+// stages would leave each 128-byte line half used per load).  LDS rows are 128 bytes with 16-byte chunk
 // c of row r stored at chunk c ^ ((r >> 1) & 7) (the sixteen rows one operand
 // read touches land on distinct bank groups).  The fragment pipeline runs in
 // 32-deep half stages: the reads of the next half overlap the MFMAs of the
@@ -881,7 +544,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_fl_kernel(ActIn a, BRo
     // first half: MFMAs of half 0 of stage it, reads of its half 1
     FL_LOAD(f1, cur, 1);
     FL_MMA(f0);
-    dma8_interleave<NP * FM + FN, NP * FM * FN>();
+    mfma_read_interleave<NP * FM + FN, NP * FM * FN>();
     // stage boundary: stage it+1 landed, every wave holds all of stage it in
     // registers, so its buffer takes stage it+2
     if (it + 1 < nloc) {
@@ -894,7 +557,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_fl_kernel(ActIn a, BRo
     // their own fragments)
     FL_LOAD(f0, cur ^ 1, 0);
     FL_MMA(f1);
-    dma8_interleave<NP * FM + FN, NP * FM * FN>();
+    mfma_read_interleave<NP * FM + FN, NP * FM * FN>();
   }
 #undef FL_LOAD
 #undef FL_MMA
@@ -1104,14 +767,11 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(ActIn a, BRows<float> b, 
 
 // ---------------------------------------------------------------------------
 // Tile choice per GEMM kind (bf16 weights):
-//   2: 128x128, four 64x64 waves, two workgroups per CU (gemm_dma_kernel)
-//   3: 128x384, eight 64x96 waves      4: 256x256, eight 64x128 waves
-//   5: 128x256, eight 64x64 waves      6: 512x128, eight 64x128 waves
-//   7, 8, 9: 3, 5 and 4 (one plane) with four LDS stages
-//   (gemm_dma8_kernel, one workgroup per CU)
+//   2: 128x128, four 64x64 waves, two workgroups per CU (gemm_dma_kernel;
+//      injection, and K not a multiple of 64)
 //   10: 128x384, eight 64x96 waves     11: 256x256, eight 64x128 waves (one plane)
 //   12: 128x256, eight 64x64 waves     13: 64x256, eight 64x32 waves (one plane, at most 64 rows)
-//   (gemm_fl_kernel)
+//   (gemm_fl_kernel, one workgroup per CU, two for 13)
 #ifndef DFLASH_T_SWIGLU
 #define DFLASH_T_SWIGLU 10
 #endif
@@ -1128,26 +788,18 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(ActIn a, BRows<float> b, 
 #define DFLASH_T_STORE 10
 #endif
 static int tile_bn(int cfg) {
-  return cfg == 3 || cfg == 7 || cfg == 10 ? 384 : cfg == 4 || cfg == 5 || cfg == 8 || cfg == 9 || cfg >= 11 ? 256 : 128;
+  return cfg == 10 ? 384 : cfg >= 11 ? 256 : 128;
 }
-static int tile_bm(int cfg) { return cfg == 4 || cfg == 9 || cfg == 11 ? 256 : cfg == 6 ? 512 : cfg == 13 ? 64 : 128; }
+static int tile_bm(int cfg) { return cfg == 11 ? 256 : cfg == 13 ? 64 : 128; }
 
 // LM-head partials cover 128 columns each, or 64 when the tile width is not a multiple of 128
 int gemm_bn(int wdtype, int K) { return wdtype && K % 32 == 0 && tile_bn(DFLASH_T_LMHEAD) % 128 ? 64 : 128; }
 
-// Tile configuration and K split of one GEMM.  cfg 0: 128x128 tile, four
-// 64x64 waves, one LDS buffer (two workgroups per CU).  cfg 1: 128x256 tile,
-// four 64x128 waves, double-buffered LDS (one workgroup per CU).  A split is
+// Tile configuration and K split of one GEMM (the table above).  A split is
 // used only when the tiles alone leave CUs idle; with fixed_split the split
 // depends on N and K only (injection must give the same bits for any M).
-#ifndef DFLASH_WIDE_TILES
-#define DFLASH_WIDE_TILES 0
-#endif
 #ifndef DFLASH_KS_TARGET
 #define DFLASH_KS_TARGET 256
-#endif
-#ifndef DFLASH_DMA
-#define DFLASH_DMA 1
 #endif
 GemmPlan gemm_plan(int wdtype, int a_mode, int M, int N, int K, int kind, bool fixed_split) {
   GemmPlan p{0, 1};
@@ -1159,7 +811,6 @@ GemmPlan gemm_plan(int wdtype, int a_mode, int M, int N, int K, int kind, bool f
     else if (kind == EPI_ADD) cfg = DFLASH_T_ADD;
     else if (kind == EPI_STORE) cfg = DFLASH_T_STORE;
     const bool one_plane = a_mode != ACT_HILO;
-    if ((cfg == 6 || cfg == 9) && !one_plane) cfg = 4;   // these tiles of both planes exceed the LDS
     if ((cfg == 11 || cfg == 13) && !one_plane) cfg = 12;
     if (cfg >= 10 && K % 64 != 0) cfg = 2;
     // SwiGLU tiles hold BN/2 gate and BN/2 up columns of the same rows
@@ -1195,22 +846,6 @@ size_t gemm_partial_bytes(const GemmPlan& p, int M, int N) {
   return p.ksplit > 1 ? (size_t)p.ksplit * M * N * 4 : 0;
 }
 
-template <int BM, int BN, int WM, int WN, int NP, int STAGES, int KIND>
-static hipError_t go_mfma(const GemmArgs& g, int ksplit, hipStream_t s) {
-  using C = MfmaCfg<BM, BN, WM, WN, NP, STAGES>;
-  const int ntm = (g.M + BM - 1) / BM, ntn = (g.N + BN - 1) / BN;
-  const int total = ntm * ntn * ksplit;
-  const int grid = (total + 7) / 8 * 8;
-  BRows<bf16_t> b{(const bf16_t*)g.b.b0, (const bf16_t*)g.b.b1, g.b.ldb, g.b.split, g.b.mode};
-  hipLaunchKernelGGL((gemm_mfma_kernel<BM, BN, WM, WN, NP, STAGES, KIND>), dim3(grid), dim3(C::NT), 0, s, g.a, b,
-                     g.M, g.N, g.K, ksplit, g.part, g.e);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || ksplit == 1 || (g.defer_reduce && (KIND == EPI_ADD || KIND == EPI_STORE))) return err;
-  hipLaunchKernelGGL((splitk_reduce_kernel<16, BN, KIND, bf16_t>), dim3((g.M + 15) / 16 * ntn), dim3(256), 0, s,
-                     g.part, ksplit, g.M, g.N, g.e);
-  return hipGetLastError();
-}
-
 template <int KIND>
 static hipError_t go_f32(const GemmArgs& g, hipStream_t s) {
   const int total = ((g.M + 63) / 64) * ((g.N + 127) / 128);
@@ -1235,21 +870,6 @@ static hipError_t go_dma(const GemmArgs& g, int ksplit, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WGM, int WGN, int NP, int KIND, int STAGES = 3>
-static hipError_t go_dma8(const GemmArgs& g, int ksplit, hipStream_t s) {
-  const int ntm = (g.M + BM - 1) / BM, ntn = (g.N + BN - 1) / BN;
-  const int total = ntm * ntn * ksplit;
-  const int grid = (total + 7) / 8 * 8;
-  BRows<bf16_t> b{(const bf16_t*)g.b.b0, (const bf16_t*)g.b.b1, g.b.ldb, g.b.split, g.b.mode};
-  hipLaunchKernelGGL((gemm_dma8_kernel<BM, BN, WGM, WGN, NP, STAGES, KIND>), dim3(grid), dim3(64 * WGM * WGN), 0, s, g.a, b,
-                     g.M, g.N, g.K, ksplit, g.part, g.e);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || ksplit == 1 || (g.defer_reduce && (KIND == EPI_ADD || KIND == EPI_STORE))) return err;
-  hipLaunchKernelGGL((splitk_reduce_kernel<16, BN, KIND, bf16_t>), dim3((g.M + 15) / 16 * ntn), dim3(256), 0, s,
-                     g.part, ksplit, g.M, g.N, g.e);
-  return hipGetLastError();
-}
-
 template <int BM, int BN, int WGM, int WGN, int NP, int KIND>
 static hipError_t go_fl(const GemmArgs& g, int ksplit, hipStream_t s) {
   const int ntm = (g.M + BM - 1) / BM, ntn = (g.N + BN - 1) / BN;
@@ -1270,13 +890,6 @@ static hipError_t go_bf16(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
   constexpr bool scatter = KIND == EPI_KVSCATTER;
   switch (p.cfg) {
     case 2: return go_dma<NP, KIND>(g, p.ksplit, s);
-    case 3: if constexpr (!scatter) return go_dma8<128, 384, 2, 4, NP, KIND>(g, p.ksplit, s); break;
-    case 4: if constexpr (!scatter) return go_dma8<256, 256, 4, 2, NP, KIND>(g, p.ksplit, s); break;
-    case 5: if constexpr (!scatter) return go_dma8<128, 256, 2, 4, NP, KIND>(g, p.ksplit, s); break;
-    case 6: if constexpr (NP == 1 && !scatter) return go_dma8<512, 128, 8, 1, 1, KIND>(g, p.ksplit, s); break;
-    case 7: if constexpr (!scatter) return go_dma8<128, 384, 2, 4, NP, KIND, 4>(g, p.ksplit, s); break;
-    case 8: if constexpr (!scatter) return go_dma8<128, 256, 2, 4, NP, KIND, 4>(g, p.ksplit, s); break;
-    case 9: if constexpr (NP == 1 && !scatter) return go_dma8<256, 256, 4, 2, 1, KIND, 4>(g, p.ksplit, s); break;
     case 10: if constexpr (!scatter) return go_fl<128, 384, 2, 4, NP, KIND>(g, p.ksplit, s); break;
     case 11: if constexpr (NP == 1 && !scatter) return go_fl<256, 256, 4, 2, 1, KIND>(g, p.ksplit, s); break;
     case 12: if constexpr (!scatter) return go_fl<128, 256, 2, 4, NP, KIND>(g, p.ksplit, s); break;
