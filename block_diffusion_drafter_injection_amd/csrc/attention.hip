@@ -37,6 +37,17 @@ __device__ __forceinline__ float rope_elem(const float* v, const float2* cs, int
   return dd < h ? v[dd] * c.x - v[dd + h] * c.y : v[dd] * c.x + v[dd - h] * c.y;
 }
 
+// Pages [pg0, pg1) of context split `split` of a sequence with npages pages:
+// the sequence's 32-token tiles are dealt evenly to the n_splits splits (so
+// the splits of every sequence are balanced whatever bound the grid was sized
+// for); at most p.pps pages per split.
+__device__ __forceinline__ void split_pages(const AttnParams& p, int npages, int split, int& pg0, int& pg1) {
+  const int tiles = (npages + 1) >> 1;
+  const int tps = (tiles + p.n_splits - 1) / p.n_splits;
+  pg0 = min(2 * split * tps, npages);
+  pg1 = min(pg0 + 2 * tps, npages);
+}
+
 // ---------------------------------------------------------------------------
 constexpr int kMaxPPS = 512;   // pages per context split (bounded by the host)
 #ifndef DFLASH_ATT_STAGES
@@ -185,7 +196,8 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int ctx = clamp_ctx(p, b);
   const int npages = (ctx + 15) >> 4;
-  const int pg0 = split * p.pps, pg1 = min(pg0 + p.pps, npages);
+  int pg0, pg1;
+  split_pages(p, npages, split, pg0, pg1);
   const int ntiles = pg1 > pg0 ? (pg1 - pg0 + 1) >> 1 : 0;
 
   for (int i = tid; i < pg1 - pg0; i += 256) ptab[i] = phys_page(p, b, pg0 + i);
@@ -489,7 +501,8 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
   {
     const int ctx = clamp_ctx(p, b);
     const int npages = (ctx + 15) >> 4;
-    const int pg0 = split * p.pps, pg1 = min(pg0 + p.pps, npages);
+    int pg0, pg1;
+    split_pages(p, npages, split, pg0, pg1);
     const TP* pool = (const TP*)p.pool;
     const size_t chunk = 16 * D;
     for (int pg = pg0; pg < pg1; ++pg) {
