@@ -41,6 +41,9 @@ def parse():
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="turn rocprofv3 csv output into profiles/ summaries and exit")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--ceilings", type=int, default=1,
+                    help="measure the vendor GEMM rate and a device copy's HBM rate on this GPU, and price "
+                         "the draft's executed work against them")
     ap.add_argument("--device-loop", type=int, default=1,
                     help="also time the step loop kept on the GPU (dflash_advance_context, HIP graph replay)")
     ap.add_argument("--block-sweep", type=int, default=1,
@@ -102,25 +105,72 @@ def work_per_class(dims, bt, B, S, ctx, n_new):
     return out
 
 
-def draft_roofline_ms(dims, bt, B, S, ctx):
+def draft_roofline_ms(dims, bt, B, S, ctx, peak=None, hbm=PEAK_HBM, executed=False):
     """Roofline time of one draft call: the sum over its kernels of max(flops / MFMA peak,
     HBM bytes / HBM peak), with weights streamed once per forward, every context token's
-    K and V read once per layer and forward, and the LM head over the still-open rows only."""
+    K and V read once per layer and forward, and the LM head over the still-open rows only.
+    executed=True counts the layer GEMMs' second (lo-plane) MFMA as work, as the kernels
+    execute it (bf16 only)."""
     H, L, I, V = dims.hidden, dims.n_layers, dims.intermediate, dims.vocab
     nq, nkv, d = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
     el = 2 if dims.dtype == "bf16" else 4
-    peak = PEAK_BF16 if dims.dtype == "bf16" else PEAK_FP32
+    if peak is None:
+        peak = PEAK_BF16 if dims.dtype == "bf16" else PEAK_FP32
+    planes = 2.0 if (executed and dims.dtype == "bf16") else 1.0
     M = bt * B
     gemms = [((nq + 2 * nkv) * d, H), (H, nq * d), (2 * I, H), (H, I)]
     t, done = 0.0, 0
     for s in range(S):
         for N, K in gemms:
-            t += L * max(2.0 * M * N * K / peak, N * K * el / PEAK_HBM)
-        t += L * float(sum(ctx)) * nkv * d * 2 * el / PEAK_HBM
+            t += L * max(planes * 2.0 * M * N * K / peak, N * K * el / hbm)
+        t += L * float(sum(ctx)) * nkv * d * 2 * el / hbm
         rows = bt * (B - done)
-        t += max(2.0 * rows * V * H / peak, V * H * el / PEAK_HBM)
+        t += max(2.0 * rows * V * H / peak, V * H * el / hbm)
         done += (s + 1) * B // S - s * B // S
     return t * 1e3
+
+
+def measured_ceilings(dims, bt, B):
+    """What this GPU sustains on plain library work, measured live: the bf16 rate of the
+    vendor GEMM (torch.matmul, hipBLASLt) on a large square product and on each of the
+    draft's GEMM shapes (one bf16 plane), and the HBM rate of a 1 GiB device copy
+    (bytes read + written)."""
+    import torch
+    dev = "cuda"
+
+    def timed(fn, n):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n / 1e3
+
+    out = {}
+    H, I, V = dims.hidden, dims.intermediate, dims.vocab
+    nq, nkv, d = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    M = bt * B
+    shapes = {"square_8192": (8192, 8192, 8192), "qkv": (M, (nq + 2 * nkv) * d, H), "o": (M, H, nq * d),
+              "gate_up": (M, 2 * I, H), "down": (M, H, I), "lm_head": (M, V, H)}
+    gemm = {}
+    for name, (m, n, k) in shapes.items():
+        a = torch.randn(m, k, device=dev, dtype=torch.bfloat16)
+        w = torch.randn(n, k, device=dev, dtype=torch.bfloat16)
+        sec = timed(lambda: torch.matmul(a, w.t()), 10)
+        gemm[name] = {"m": m, "n": n, "k": k, "us": round(sec * 1e6, 1), "tflops": round(2.0 * m * n * k / sec / 1e12, 1)}
+        del a, w
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    sec = timed(lambda: dst.copy_(src), 10)
+    out["hbm_copy_gbs"] = round(2.0 * src.numel() * 4 / sec / 1e9, 1)
+    del src, dst
+    out["mfma_bf16_tflops"] = gemm["square_8192"]["tflops"]
+    out["vendor_gemm"] = gemm
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -315,6 +365,15 @@ def main():
                            "frac": round(t_roof / draft_ms, 4),
                            "definition": "sum over the draft's kernels of max(flops/2.5 PFLOP/s, bytes/8 TB/s)"},
     }
+    if a.ceilings and dims.dtype == "bf16":
+        c = measured_ceilings(dims, bt, B)
+        t_ex = draft_roofline_ms(dims, bt, B, S, ctx_before, peak=c["mfma_bf16_tflops"] * 1e12,
+                                 hbm=c["hbm_copy_gbs"] * 1e9, executed=True)
+        res["measured_ceilings"] = c
+        res["draft_roofline"]["measured"] = {
+            "t_roof_ms": round(t_ex, 4), "frac": round(t_ex / draft_ms, 4),
+            "definition": "sum over the draft's kernels of max(executed flops (hi/lo counted twice) / the "
+                          "vendor GEMM's bf16 rate on an 8192^3 product, bytes / a 1 GiB device copy's rate)"}
     if a.device_loop:
         res["device_loop"] = device_loop(a, Bn, cfg, w, dims, bt, B, S, pool, n_pages, table, pages_per, max_ctx,
                                          ctx_dev, acc, tok, outt, new_hid, z0, zmax, zmin, wl.p_match, g, ws,
@@ -458,7 +517,7 @@ def summarize(trace_dir, fetch_dir, write_dir):
     lines = [f"# rocprofv3 kernel statistics, {wl_name}", "",
              "Command (run from the repository root, output csv):", "",
              "    rocprofv3 --kernel-trace --stats --output-format csv -d <TRACE_DIR> -o run -- "
-             "python bench.py --steps 5 --warmup 2 --cpu-baseline 0 --device-loop 0 --block-sweep 0", "",
+             "python bench.py --steps 5 --warmup 2 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0", "",
              f"Kernel sources hash: {h}", "",
              "| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:20]:
@@ -471,9 +530,9 @@ def summarize(trace_dir, fetch_dir, write_dir):
     tl = [f"# HBM traffic per launch, {wl_name}", "",
           "Commands (repository root, csv output):", "",
           "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -o p -- "
-          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --copy-calibration 1",
+          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --copy-calibration 1",
           "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -o p -- "
-          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --copy-calibration 1",
+          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --copy-calibration 1",
           "    python bench.py --summarize <TRACE_DIR> <FETCH_DIR> <WRITE_DIR>", "",
           f"Calibration: a {COPY_BYTES >> 20} MiB device copy (`{big[0][:60]}`) reads FETCH_SIZE = "
           f"{big[1]:.0f} KiB -> fetch scale {fetch_scale:.4f}; WRITE_SIZE scale "
