@@ -14,6 +14,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("DFLASH_LIB") or os.path.join(_PKG, "libdflash.so")
 
 DFLASH_F32, DFLASH_BF16 = 0, 1
+SCHEDULES = {"progressive": 0, "repredict": 1}   # dflash_schedule
 PROF = dict(none=0, attn=1, gemm_qkv=2, gemm_o=3, gemm_gateup=4, gemm_down=5, lmhead=6, inject_fc=7,
             inject_kv=8, verify=9)
 STATUS = {0: "ok", -1: "invalid argument", -2: "unsupported or inconsistent shape", -3: "unknown dtype",
@@ -30,7 +31,8 @@ class dflash_config(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "hidden", "n_layers", "n_q_heads", "n_kv_heads", "head_dim", "intermediate", "vocab", "n_fuse",
         "target_hidden", "page_size", "mask_token_id")] + [
-        ("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32)]
+        ("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32),
+        ("denoise_schedule", ctypes.c_int32)]
 
 
 _PP = ctypes.POINTER(ctypes.c_void_p)
@@ -101,12 +103,12 @@ def _check(fn, code):
         raise DflashError(fn, code)
 
 
-def make_config(dims):
-    """dflash_config from a ModelDims-like object."""
+def make_config(dims, schedule="progressive"):
+    """dflash_config from a ModelDims-like object; schedule is 'progressive' or 'repredict'."""
     return dflash_config(dims.hidden, dims.n_layers, dims.n_q_heads, dims.n_kv_heads, dims.head_dim,
                          dims.intermediate, dims.vocab, dims.n_fuse, dims.target_hidden, dims.page_size,
                          dims.mask_token_id, float(dims.rope_base), float(dims.rms_eps),
-                         DFLASH_BF16 if dims.dtype == "bf16" else DFLASH_F32)
+                         DFLASH_BF16 if dims.dtype == "bf16" else DFLASH_F32, SCHEDULES[schedule])
 
 
 class Weights:

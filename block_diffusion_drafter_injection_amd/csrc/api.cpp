@@ -68,6 +68,8 @@ dflash_status check_cfg(const dflash_config* c) {
   if (c->hidden > 8192) return DFLASH_ESHAPE;
   if (c->page_size != 16) return DFLASH_ESHAPE;
   if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab) return DFLASH_EINVAL;
+  if (c->denoise_schedule != DFLASH_SCHEDULE_PROGRESSIVE && c->denoise_schedule != DFLASH_SCHEDULE_REPREDICT)
+    return DFLASH_EINVAL;
   if (!(c->rope_base > 0.f) || !(c->rms_eps >= 0.f)) return DFLASH_EINVAL;
   return DFLASH_OK;
 }
@@ -384,9 +386,11 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
   HIP_TRY(launch_rope_table_block(ctx_len, ctx_cap, batch, B, d, (double)cfg->rope_base, cs, stream));
   HIP_TRY(launch_block_init(tau, committed, M, cfg->mask_token_id, stream));
 
+  // re-predict schedule: every position stays open and takes its candidate at every step
+  const bool repredict = cfg->denoise_schedule == DFLASH_SCHEDULE_REPREDICT;
   int done = 0;
   for (int s = 0; s < S; ++s) {
-    const int k_s = ((s + 1) * B) / S - (s * B) / S;
+    const int k_s = repredict ? B : ((s + 1) * B) / S - (s * B) / S;
     const int n_open = B - done;
     const int last = s == S - 1;
     HIP_TRY(launch_embed(tau, w->embed, bf, cfg->vocab, h, M, H, stream));
@@ -484,8 +488,9 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
     gl.e.step = s;
     HIP_TRY(gemm(DFLASH_PROF_LMHEAD, gl, stream));
     HIP_TRY(launch_lm_combine(gl.e.part_f, gl.e.part_i, L.ntiles, Ms, row_map, cand, conf, stream));
-    HIP_TRY(launch_commit(cand, conf, tau, committed, out_conf, out_tokens, batch, B, S, s, k_s, last, stream));
-    done += k_s;
+    HIP_TRY(launch_commit(cand, conf, tau, committed, out_conf, out_tokens, batch, B, S, s, k_s, last, repredict,
+                          stream));
+    if (!repredict) done += k_s;
   }
   return DFLASH_OK;
 }

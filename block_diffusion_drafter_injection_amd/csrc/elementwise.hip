@@ -175,10 +175,11 @@ __global__ __launch_bounds__(256) void lm_combine_kernel(const float4* part_f, c
 
 // Denoise commit for one sequence (one wave, lane = block position): the
 // k_step most confident open positions (ties to the lower position) take
-// their candidate; at the last step every open position does.
+// their candidate; at the last step every open position does.  Re-predict:
+// every position takes its candidate and stays open for the next step.
 __global__ __launch_bounds__(64) void commit_kernel(const int* cand, const float* conf, int* tau, int* committed,
                                                     float* out_conf, int* out_tokens, int B, int S, int step,
-                                                    int k_step, int last) {
+                                                    int k_step, int last, int repredict) {
   __shared__ float cs[16];
   __shared__ int open[16];
   const int b = blockIdx.x, i = threadIdx.x;
@@ -190,7 +191,9 @@ __global__ __launch_bounds__(64) void commit_kernel(const int* cand, const float
   __syncthreads();
   if (i < B) {
     if (out_conf) out_conf[((size_t)b * S + step) * B + i] = open[i] ? cs[i] : __int_as_float(0x7fc00000);
-    if (open[i]) {
+    if (repredict) {
+      tau[row] = cand[row];
+    } else if (open[i]) {
       int rank = 0;
       for (int k = 0; k < B; ++k)
         if (open[k] && (cs[k] > cs[i] || (cs[k] == cs[i] && k < i))) ++rank;
@@ -272,9 +275,10 @@ hipError_t launch_lm_combine(const float4* part_f, const int* part_i, int ntiles
 }
 
 hipError_t launch_commit(const int* cand, const float* conf, int* tau, int* committed, float* out_conf,
-                         int* out_tokens, int batch, int B, int S, int step, int k_step, int last, hipStream_t s) {
+                         int* out_tokens, int batch, int B, int S, int step, int k_step, int last, bool repredict,
+                         hipStream_t s) {
   hipLaunchKernelGGL(commit_kernel, dim3(batch), dim3(64), 0, s, cand, conf, tau, committed, out_conf, out_tokens,
-                     B, S, step, k_step, last);
+                     B, S, step, k_step, last, repredict ? 1 : 0);
   return hipGetLastError();
 }
 

@@ -118,9 +118,9 @@ hipError_t launch_advance_context(int batch, int B, const int* accept_len, int* 
                                   int* tok_pos, hipStream_t s);
 hipError_t launch_lm_combine(const float4* part_f, const int* part_i, int ntiles, int rows,
                              const int* row_map, int* cand, float* conf, hipStream_t s);
-hipError_t launch_commit(const int* cand, const float* conf, int* tau, int* committed,
-                         float* out_conf, int* out_tokens, int batch, int B, int S, int step,
-                         int k_step, int last, hipStream_t s);
+hipError_t launch_commit(const int* cand, const float* conf, int* tau, int* committed, float* out_conf,
+                         int* out_tokens, int batch, int B, int S, int step, int k_step, int last, bool repredict,
+                         hipStream_t s);
 
 // Verification.
 int verify_chunks(int vocab);

@@ -64,6 +64,18 @@ typedef enum {
 
 typedef enum { DFLASH_F32 = 0, DFLASH_BF16 = 1 } dflash_dtype;
 
+/* How the block is denoised over the n_steps forwards ([Deep] 2.3 says only
+ * that a few rounds progressively fix the block's tokens; both readings are
+ * offered):
+ *   DFLASH_SCHEDULE_PROGRESSIVE  step s fixes the floor(sB/S)-floor((s-1)B/S)
+ *       most confident still-open positions, which stay fixed (masked
+ *       diffusion decoding by confidence);
+ *   DFLASH_SCHEDULE_REPREDICT    every step predicts every position again
+ *       from the previous step's tokens (step 1 from the all-mask block) and
+ *       the block is the last step's prediction.
+ * With n_steps = 1 both are one forward plus argmax. */
+typedef enum { DFLASH_SCHEDULE_PROGRESSIVE = 0, DFLASH_SCHEDULE_REPREDICT = 1 } dflash_schedule;
+
 /* Draft model dimensions.  Limits: head_dim in {64, 128}; n_q_heads a
  * multiple of n_kv_heads; hidden, intermediate, n_fuse*target_hidden and
  * n_q_heads*head_dim multiples of 64; hidden <= 8192; page_size 16; 0 <= mask_token_id <
@@ -84,6 +96,7 @@ typedef struct {
   float rope_base;
   float rms_eps;
   int32_t dtype;          /* dflash_dtype */
+  int32_t denoise_schedule; /* dflash_schedule */
 } dflash_config;
 
 /* Draft weights (all device pointers; per-layer entries are host arrays of
@@ -145,19 +158,22 @@ dflash_status dflash_inject_kv(const dflash_config* cfg, const dflash_weights* w
  * ctx_len[b]+block_size-1.  The block starts as all mask_token_id; each of
  * n_steps forwards runs every draft layer (RMSNorm, grouped-query attention
  * of the block over the sequence's injected context KV plus all block keys,
- * SwiGLU MLP) and the LM head; step s commits floor(sB/S)-floor((s-1)B/S)
- * still-open positions with the highest confidence (log-probability of
- * their candidate; ties to the lower position), the last step commits the
- * rest.  Candidates: argmax (temperature 0, ties to the lowest id) or
+ * SwiGLU MLP) and the LM head.  Progressive schedule: step s commits
+ * floor(sB/S)-floor((s-1)B/S) still-open positions with the highest
+ * confidence (log-probability of their candidate; ties to the lower
+ * position), the last step commits the rest.  Re-predict schedule: every
+ * step replaces every position's token by its candidate.  Candidates:
+ * argmax (temperature 0, ties to the lowest id) or
  * Gumbel-max with Philox4x32-10 noise keyed by seed and counter
  * (v/4, i, s, b) (temperature > 0).
  *   ctx_len (device) [batch]; entries are clamped to [0, min(max_ctx_len, max_pages*page_size)]
  *   max_ctx_len (host) upper bound of ctx_len, sizes the attention grid
  *   out_tokens (device) [batch, block_size]
  *   out_logits (device, optional) [batch, block_size, vocab] fp32: each position's
- *              logits at the step that committed it
+ *              logits at the step that committed it (re-predict: the last step)
  *   out_conf (device, optional) [batch, n_steps, block_size] fp32: confidence of each
  *              open position at each step, NaN where the position was already committed
+ *              (re-predict: every position is open at every step)
  * Limits: 1 <= block_size <= 16; 1 <= n_steps <= block_size; temperature >= 0. */
 dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights* w,
                                  const void* kv_pool, int32_t n_pages,

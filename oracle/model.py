@@ -142,8 +142,17 @@ def _top2_gap(x):
 
 
 def draft_block(cfg, W, pools, ctx_len, block_size, n_steps, temperature=0.0, seed=0,
-                want_logits=True, seq_ids=None):
+                want_logits=True, seq_ids=None, schedule="progressive"):
     """Denoise one [MASK] block per sequence in n_steps forwards.
+
+    The pages ("DFLASH + Spec V2 深度解析", 2.3 块扩散) say only that a few
+    denoising rounds progressively settle the block.  schedule picks the reading:
+      'progressive'  step s fixes the floor(sB/S)-floor((s-1)B/S) most confident
+                     open positions (ties to the lower position); the last step
+                     fixes the rest; fixed positions keep their token;
+      'repredict'    every step predicts every position again from the previous
+                     step's tokens (step 1 from the all-[MASK] block); the block is
+                     the last step's prediction.
 
     seq_ids: batch index of each row in the Philox counter (default 0..bt-1),
     so a subset of a batch can be redrawn with the noise it had in the batch.
@@ -153,12 +162,15 @@ def draft_block(cfg, W, pools, ctx_len, block_size, n_steps, temperature=0.0, se
       logits [bt, B, V]         each position's logits at its commit step (if want_logits),
       conf [bt, S, B]           confidence of every still-open position at each step (nan otherwise),
       cand [bt, S, B]           candidate token of every open position at each step (-1 otherwise),
-      committed_at [bt, B]      step index (0-based) at which each position was committed,
+      committed_at [bt, B]      step index (0-based) at which each position was committed
+                                (re-predict: the last step),
       gap [bt, S, B]            top-1 minus top-2 of the score the candidate maximises
                                 (logits at T=0, logits/T + Gumbel at T>0),
       boundary_gap [bt, S]      confidence gap between the last committed and the first
                                 left-open position (inf when nothing is left open).
     """
+    if schedule not in ("progressive", "repredict"):
+        raise ValueError(schedule)
     B, S, V = block_size, n_steps, cfg.vocab
     bt = len(ctx_len)
     tau = np.full((bt, B), cfg.mask_token_id, dtype=np.int64)
@@ -190,6 +202,10 @@ def draft_block(cfg, W, pools, ctx_len, block_size, n_steps, temperature=0.0, se
             gap[b, s, i] = _top2_gap(score)
             if want_logits:
                 logits[b, i] = zr
+        if schedule == "repredict":
+            tau = cand[:, s].copy()
+            committed_at[:] = s
+            continue
         for b in range(bt):
             open_i = np.nonzero(~committed[b])[0]
             # most confident first; equal confidence -> lower position first

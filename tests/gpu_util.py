@@ -133,15 +133,18 @@ def compare_pool_entries(got, ref, dtype, label=""):
     return err
 
 
-def compare_draft(dims, S, res, tokens, logits, conf, tie=TIE, logit_tol=None):
+def compare_draft(dims, S, res, tokens, logits, conf, tie=TIE, logit_tol=None, schedule="progressive"):
     """Compare GPU draft outputs with the oracle's result dict.
 
     A sequence whose step s < S-1 commits a position with a top-2 gap below
     `tie`, or whose commit boundary at step s is closer than `tie`, is compared
     only on the positions committed before s (and its confidences up to step
     s, whose inputs are still identical).  At the last step only the near-tie
-    positions themselves are left out.  Asserts: every compared token equal,
-    logits and confidences within logit_tol of each row's max |z|."""
+    positions themselves are left out.  Re-predict schedule: every position is
+    re-predicted at every step, so a near-tie anywhere before the last step
+    leaves the whole sequence out (its confidences up to that step are still
+    compared).  Asserts: every compared token equal, logits and confidences
+    within logit_tol of each row's max |z|."""
     tol = logit_tol if logit_tol is not None else (2e-2 if dims.dtype == "bf16" else 1e-4)
     tok_o = res["tokens"]
     bt, Bk = tok_o.shape
@@ -149,6 +152,16 @@ def compare_draft(dims, S, res, tokens, logits, conf, tie=TIE, logit_tol=None):
     first_flag = np.full(bt, S)
     compare = np.ones((bt, Bk), dtype=bool)
     for b in range(bt):
+        if schedule == "repredict":
+            for s in range(S):
+                near = res["gap"][b, s] < tie
+                if s < S - 1 and near.any():
+                    first_flag[b] = s
+                    compare[b] = False
+                    break
+                if s == S - 1:
+                    compare[b, near] = False
+            continue
         for s in range(S):
             committed_now = np.nonzero(at[b] == s)[0]
             near = [i for i in committed_now if res["gap"][b, s, i] < tie]
@@ -188,9 +201,10 @@ def ctx_tensor(ctx, device="cuda"):
 class Drafter:
     """Owns the device buffers of one configuration and calls the three entry points."""
 
-    def __init__(self, dims, W, max_batch, block_size, max_ctx, max_inject=4096, device="cuda"):
+    def __init__(self, dims, W, max_batch, block_size, max_ctx, max_inject=4096, device="cuda",
+                 schedule="progressive"):
         self.dims = dims
-        self.cfg = B.make_config(dims)
+        self.cfg = B.make_config(dims, schedule)
         self.W = W
         self.w = B.Weights(W)
         self.ws_bytes = B.dflash_workspace_size(self.cfg, max_batch, block_size, max_inject, max_ctx)

@@ -57,6 +57,8 @@ def test_workspace_size_rejects_bad_configs(L):
     assert B.dflash_workspace_size(_cfg(), 4, 17, 64, 512) == 0
     assert B.dflash_workspace_size(_cfg(hidden=500), 4, 8, 64, 512) == 0
     assert B.dflash_workspace_size(_cfg(hidden=8256), 4, 8, 64, 512) == 0   # rows wider than 8192
+    assert B.dflash_workspace_size(_cfg(denoise_schedule=1), 4, 8, 64, 512) > 0
+    assert B.dflash_workspace_size(_cfg(denoise_schedule=3), 4, 8, 64, 512) == 0
 
 
 def test_workspace_grows_with_batch_and_context(L):
@@ -99,6 +101,8 @@ def test_draft_argument_errors_return_before_launch(L):
     assert _draft(L, cfg, w, ws_bytes=1024) == -5               # too small
     assert _draft(L, _cfg(dtype=5), w) == -3
     assert _draft(L, _cfg(mask_token_id=-1), w) == -1
+    assert _draft(L, _cfg(denoise_schedule=2), w) == -1         # unknown schedule
+    assert _draft(L, _cfg(denoise_schedule=-1), w) == -1
     assert _draft(L, cfg, w, batch=0) == 0                      # nothing to do
     w2, keep2 = _weights_stub(cfg.n_layers)
     keep2[1] = None

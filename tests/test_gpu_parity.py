@@ -72,7 +72,7 @@ def test_incremental_injection_is_bitwise_one_shot():
     assert torch.equal(one.view(torch.int16), inc.view(torch.int16))
 
 
-def _draft_case(dims, ctx, B, S, T, seed, want_logits=True):
+def _draft_case(dims, ctx, B, S, T, seed, want_logits=True, schedule="progressive"):
     W = synth.make_weights(dims, seed, "cuda")
     table, n_pages = page_plan(ctx, 0, seed=seed + 1)
     tab = torch.from_numpy(table).cuda()
@@ -86,11 +86,12 @@ def _draft_case(dims, ctx, B, S, T, seed, want_logits=True):
             pack_pool(dims, pool, n_pages, table, b, Kb, Vb)
         pools.append((f64(Kb), f64(Vb)))
         off += c
-    dr = Drafter(dims, W, max_batch=len(ctx), block_size=B, max_ctx=max(ctx))
+    dr = Drafter(dims, W, max_batch=len(ctx), block_size=B, max_ctx=max(ctx), schedule=schedule)
     tok, lg, cf = dr.draft(pool, n_pages, tab, ctx_tensor(ctx), max(ctx), B, S, T, seed=1234 + seed,
                            want_logits=want_logits)
     torch.cuda.synchronize()
-    res = oracle.draft_block(dims, np_weights(W), pools, ctx, B, S, temperature=T, seed=1234 + seed)
+    res = oracle.draft_block(dims, np_weights(W), pools, ctx, B, S, temperature=T, seed=1234 + seed,
+                             schedule=schedule)
     return res, tok.cpu().numpy(), (f64(lg) if lg is not None else None), f64(cf), (dr, pool, n_pages, tab)
 
 
@@ -108,6 +109,20 @@ def test_draft_matches_oracle(name, ctx, B, S, T):
     res, tok, lg, cf, _ = _draft_case(dims, ctx, B, S, T, seed=20 + B + S)
     out = compare_draft(dims, S, res, tok, lg, cf)
     print(f"draft {name} ctx={ctx} B={B} S={S} T={T}: {out}")
+    assert out["compared"] >= tok.size // 2
+
+
+@pytest.mark.parametrize("name,ctx,B,S,T", [
+    ("tiny", [64, 5], 4, 2, 0.0),
+    ("small", [0, 37, 300], 8, 2, 0.0),
+    ("small", [130, 16], 16, 3, 0.0),
+    ("small", [77, 8], 8, 2, 1.0),
+])
+def test_draft_repredict_matches_oracle(name, ctx, B, S, T):
+    dims = _dims(name)
+    res, tok, lg, cf, _ = _draft_case(dims, ctx, B, S, T, seed=60 + B + S, schedule="repredict")
+    out = compare_draft(dims, S, res, tok, lg, cf, schedule="repredict")
+    print(f"draft (re-predict) {name} ctx={ctx} B={B} S={S} T={T}: {out}")
     assert out["compared"] >= tok.size // 2
 
 

@@ -187,6 +187,47 @@ def test_two_step_commit_schedule():
     assert np.array_equal(r["tokens"][rest], np.argmax(z, -1)[rest])
 
 
+def test_repredict_schedule_is_iterated_forward_plus_argmax():
+    # every re-predict step is one forward of the previous step's tokens (the
+    # first of the all-[MASK] block) and an argmax; forwards by the loop twin
+    W = np_weights(TINY, 27, std=0.3)
+    ctx = [2, 11]
+    pools = [rand_pool(TINY, T, 70 + T) for T in ctx]
+    B, S = 4, 3
+    r = oracle.draft_block(TINY, W, pools, ctx, block_size=B, n_steps=S, schedule="repredict")
+    tau = np.full((2, B), TINY.mask_token_id)
+    for s in range(S):
+        y = np.array(brute.forward(TINY, W, pools, ctx, tau))
+        z = y @ W["lm_head"].T
+        assert np.array_equal(r["cand"][:, s], np.argmax(z, -1)), s
+        lse = np.log(np.exp(z - z.max(-1, keepdims=True)).sum(-1)) + z.max(-1)
+        assert np.allclose(r["conf"][:, s], z.max(-1) - lse, rtol=1e-9, atol=1e-12)
+        tau = np.argmax(z, -1)
+    assert np.array_equal(r["tokens"], tau)
+    assert np.allclose(r["logits"], z, rtol=1e-9, atol=1e-12)
+    assert np.all(r["committed_at"] == S - 1) and np.all(np.isinf(r["boundary_gap"]))
+
+
+def test_repredict_special_cases():
+    W = np_weights(TINY, 28, std=0.3)
+    ctx = [0, 9]
+    pools = [rand_pool(TINY, T, 80 + T) for T in ctx]
+    # one step: both readings are a single forward plus argmax
+    a = oracle.draft_block(TINY, W, pools, ctx, block_size=6, n_steps=1, schedule="repredict")
+    b = oracle.draft_block(TINY, W, pools, ctx, block_size=6, n_steps=1)
+    assert np.array_equal(a["tokens"], b["tokens"]) and np.array_equal(a["logits"], b["logits"])
+    assert np.array_equal(a["conf"], b["conf"])
+    # token-independent embeddings: the block's input never changes, so re-predicting is a no-op
+    W1 = dict(W)
+    W1["embed"] = np.repeat(W["embed"][:1], TINY.vocab, axis=0)
+    r = oracle.draft_block(TINY, W1, pools, ctx, block_size=6, n_steps=3, schedule="repredict")
+    for s in (1, 2):
+        assert np.array_equal(r["cand"][:, s], r["cand"][:, 0])
+        assert np.array_equal(r["conf"][:, s], r["conf"][:, 0])
+    with pytest.raises(ValueError):
+        oracle.draft_block(TINY, W, pools, ctx, block_size=6, n_steps=1, schedule="other")
+
+
 def test_lm_head_ties_pick_lowest_index():
     W = np_weights(TINY, 27, std=0.3)
     W["lm_head"][9] = W["lm_head"][30]
