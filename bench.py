@@ -400,6 +400,15 @@ def main():
                           "t_roof_ms": round(tr, 4), "frac": round(tr / ms_b, 4)})
             del wss
         res["block_sweep"] = sweep
+        # the adaptive block size this run's acceptances call for, with the measured draft times
+        # of each block size as the step times (host policy, dflash_adaptive_block_size)
+        a_obs = np.concatenate(accs).astype(int).tolist()
+        choice, p_hat = Bn.dflash_adaptive_block_size(a_obs, [B] * len(a_obs), [x["block"] for x in sweep],
+                                                      [x["draft_ms"] for x in sweep])
+        res["adaptive_block"] = {
+            "p_match_estimate": round(p_hat, 4), "choice": choice,
+            "predicted_accepted_tok_s": {str(x["block"]): round(
+                bt * sum(p_hat ** k for k in range(x["block"] + 1)) / (x["draft_ms"] / 1e3), 1) for x in sweep}}
     if a.block_sweep:
         # the other denoise reading on the same batch and pool: every step re-predicts every
         # position, so the second step's LM head covers all rows

@@ -47,8 +47,8 @@ class dflash_weights(ctypes.Structure):
 
 _lib = None
 EXPORTS = ["dflash_workspace_size", "dflash_inject_kv", "dflash_draft_block", "dflash_verify_workspace_size",
-           "dflash_verify_block", "dflash_advance_context", "dflash_status_string", "dflash_prof_select",
-           "dflash_prof_collect"]
+           "dflash_verify_block", "dflash_advance_context", "dflash_adaptive_block_size", "dflash_status_string",
+           "dflash_prof_select", "dflash_prof_collect"]
 
 
 def lib():
@@ -74,6 +74,9 @@ def lib():
     L.dflash_verify_block.restype = i32
     L.dflash_advance_context.argtypes = [i32, i32, vp, vp, vp, vp, vp]
     L.dflash_advance_context.restype = i32
+    ip, fp = ctypes.POINTER(i32), ctypes.POINTER(f32)
+    L.dflash_adaptive_block_size.argtypes = [ip, ip, i32, ip, fp, i32, f32, f32, fp]
+    L.dflash_adaptive_block_size.restype = i32
     L.dflash_status_string.argtypes = [i32]
     L.dflash_status_string.restype = ctypes.c_char_p
     L.dflash_prof_select.argtypes = [i32]
@@ -167,6 +170,23 @@ def dflash_advance_context(batch, block_size, accept_len, ctx_len, tok_seq, tok_
     code = lib().dflash_advance_context(batch, block_size, _ptr(accept_len), _ptr(ctx_len), _ptr(tok_seq),
                                         _ptr(tok_pos), _stream(stream))
     _check("dflash_advance_context", code)
+
+
+def dflash_adaptive_block_size(accept_len, block_of, cand_block, step_time, prior_a=1.0, prior_b=1.0):
+    """Host lists in, (chosen block size, estimated match probability) out."""
+    n, m = len(accept_len), len(cand_block)
+    if len(block_of) != n or len(step_time) != m:
+        raise ValueError("accept_len/block_of and cand_block/step_time must pair up")
+    i32a, f32a = ctypes.c_int32, ctypes.c_float
+    a = (i32a * max(n, 1))(*[int(x) for x in accept_len])
+    b = (i32a * max(n, 1))(*[int(x) for x in block_of])
+    c = (i32a * m)(*[int(x) for x in cand_block])
+    t = (f32a * m)(*[float(x) for x in step_time])
+    p = f32a(0.0)
+    code = lib().dflash_adaptive_block_size(a, b, n, c, t, m, float(prior_a), float(prior_b), ctypes.byref(p))
+    if code < 0:
+        raise DflashError("dflash_adaptive_block_size", code)
+    return int(code), float(p.value)
 
 
 def dflash_status_string(code):

@@ -524,6 +524,43 @@ dflash_status dflash_verify_block(int32_t batch, int32_t block_size, int32_t voc
   return e == hipSuccess ? DFLASH_OK : DFLASH_EHIP;
 }
 
+int32_t dflash_adaptive_block_size(const int32_t* accept_len, const int32_t* block_of, int32_t n_obs,
+                                   const int32_t* cand_block, const float* step_time, int32_t n_cand,
+                                   float prior_a, float prior_b, float* p_match) {
+  if (n_obs < 0 || n_cand < 1 || !cand_block || !step_time) return DFLASH_EINVAL;
+  if (n_obs > 0 && (!accept_len || !block_of)) return DFLASH_EINVAL;
+  if (!(prior_a >= 0.f) || !(prior_b >= 0.f)) return DFLASH_EINVAL;
+  // maximum-likelihood match probability of the truncated-geometric acceptances
+  double matches = prior_a, misses = prior_b;
+  for (int32_t i = 0; i < n_obs; ++i) {
+    const int32_t a = accept_len[i], b = block_of[i];
+    if (b < 1 || b > 16) return DFLASH_ECAPACITY;
+    if (a < 0 || a > b) return DFLASH_EINVAL;
+    matches += a;
+    misses += a < b ? 1.0 : 0.0;
+  }
+  const double p = matches + misses > 0.0 ? matches / (matches + misses) : 0.5;
+  if (p_match) *p_match = (float)p;
+  int32_t best = -1;
+  double best_rate = -1.0;
+  for (int32_t j = 0; j < n_cand; ++j) {
+    const int32_t B = cand_block[j];
+    if (B < 1 || B > 16) return DFLASH_ECAPACITY;
+    if (!(step_time[j] > 0.f)) return DFLASH_EINVAL;
+    double e = 0.0, pk = 1.0;   // 1 + p + ... + p^B
+    for (int32_t k = 0; k <= B; ++k) {
+      e += pk;
+      pk *= p;
+    }
+    const double rate = e / (double)step_time[j];
+    if (rate > best_rate || (rate == best_rate && B < best)) {
+      best_rate = rate;
+      best = B;
+    }
+  }
+  return best;
+}
+
 dflash_status dflash_advance_context(int32_t batch, int32_t block_size, const int32_t* accept_len,
                                      int32_t* ctx_len, int32_t* tok_seq, int32_t* tok_pos, hipStream_t stream) {
   if (batch < 0) return DFLASH_EINVAL;

@@ -234,6 +234,31 @@ dflash_status dflash_verify_block(int32_t batch, int32_t block_size, int32_t voc
                                   int32_t* out_tokens, void* workspace, size_t ws_bytes,
                                   hipStream_t stream);
 
+/* Block size for the next drafter step, chosen from the acceptance seen so
+ * far.  The pages name block sizes that adapt to how hard the input is as a
+ * direction ([Deep] 7.3 短期趋势) and note that too large a block wastes draft
+ * work while too small a one gives up speed ([Blog] 局限性); they give no
+ * rule.  Reading taken here: acceptance is the observable measure of how
+ * predictable the text is.  Each draft position matches the target with
+ * probability p, independently, so a step with block B accepts
+ * a = min(first mismatch, B) tokens.  The maximum-likelihood estimate of p
+ * over the observed steps, with a Beta(prior_a, prior_b) prior, is
+ *   p = (sum a + prior_a) / (sum a + #(a < B) + prior_a + prior_b)
+ * (0.5 when that is 0/0), and the expected tokens one step commits per
+ * sequence are E[a + 1 | B] = 1 + p + ... + p^B.  The choice is the
+ * candidate maximising E[a + 1 | B] / step_time(B), ties to the smaller block.
+ * Host-only: no device memory, no GPU work, no stream.
+ *   accept_len, block_of (host) [n_obs]: accepted draft tokens of one sequence
+ *              at one step (bonus excluded), and the block size it drafted with
+ *   cand_block (host) [n_cand] in 1..16; step_time (host) [n_cand] > 0, any unit
+ *   p_match (host, optional): receives the estimate of p
+ * Returns the chosen block size, or a negative dflash_status (EINVAL: a NULL
+ * array with a nonzero count, n_cand < 1, a time not > 0, a negative prior,
+ * or a_i outside [0, block_of_i]; ECAPACITY: a block size outside 1..16). */
+int32_t dflash_adaptive_block_size(const int32_t* accept_len, const int32_t* block_of, int32_t n_obs,
+                                   const int32_t* cand_block, const float* step_time, int32_t n_cand,
+                                   float prior_a, float prior_b, float* p_match);
+
 /* Human-readable name of a status code (static string). */
 const char* dflash_status_string(dflash_status s);
 

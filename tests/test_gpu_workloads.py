@@ -193,15 +193,23 @@ def target_logits_for(tokens, vocab, p, seed, step):
     return synth.make_greedy_target_logits(torch.as_tensor(tokens), vocab, p, seed=seed * 100 + step)
 
 
-def run_loop_gpu(dims, W, ctx0, hid, steps, B, S, p, seed, shared, group):
+def _block_at(B, st, accs, blocks):
+    """Block size of step st: a fixed int, a per-step list, or a callable of the history."""
+    if callable(B):
+        return int(B(st, accs, blocks))
+    return int(B[st]) if isinstance(B, (list, tuple)) else int(B)
+
+
+def run_loop_gpu(dims, W, ctx0, hid, steps, B, S, p, seed, shared, group, max_block=None):
     bt = len(ctx0)
-    grow = (steps + 1) * (B + 1)
+    Bmax = max_block or (B if isinstance(B, int) else 16)
+    grow = (steps + 1) * (Bmax + 1)
     table, n_pages = page_plan(ctx0, grow, seed=seed,
                                shared=[(list(range(g, min(g + group, bt))), shared // 16)
                                        for g in range(0, bt, group)] if shared else None)
     tab = torch.from_numpy(table).cuda()
     pool = alloc_pool(dims, n_pages)
-    dr = Drafter(dims, W, max_batch=bt, block_size=B, max_ctx=max(ctx0) + grow, max_inject=1024)
+    dr = Drafter(dims, W, max_batch=bt, block_size=Bmax, max_ctx=max(ctx0) + grow, max_inject=1024)
     # initial contexts: a group's shared prefix is injected once, by its first sequence
     seqs, poss, rows = [], [], []
     for b, c in enumerate(ctx0):
@@ -212,9 +220,11 @@ def run_loop_gpu(dims, W, ctx0, hid, steps, B, S, p, seed, shared, group):
     dr.inject(torch.cat(rows), torch.tensor(seqs, dtype=torch.int32, device="cuda"),
               torch.tensor(poss, dtype=torch.int32, device="cuda"), pool, n_pages, tab, bt)
     ctx = list(ctx0)
-    accs, toks = [], []
+    accs, toks, blocks = [], [], []
     for st in range(steps):
-        tok, _, _ = dr.draft(pool, n_pages, tab, ctx_tensor(ctx), max(ctx0) + grow, B, S, want_logits=False)
+        Bt = _block_at(B, st, accs, blocks)
+        blocks.append(Bt)
+        tok, _, _ = dr.draft(pool, n_pages, tab, ctx_tensor(ctx), max(ctx0) + grow, Bt, S, want_logits=False)
         zt = target_logits_for(tok.cpu(), dims.vocab, p, seed, st).cuda()
         acc, out = verify(zt, tok)
         a = acc.cpu().numpy()
@@ -227,7 +237,8 @@ def run_loop_gpu(dims, W, ctx0, hid, steps, B, S, p, seed, shared, group):
                   torch.tensor(poss, dtype=torch.int32, device="cuda"), pool, n_pages, tab, bt)
         ctx = [ctx[b] + int(a[b]) + 1 for b in range(bt)]
     torch.cuda.synchronize()
-    return dict(acc=np.array(accs), tok=np.array(toks), ctx=ctx, pool=pool, table=table, n_pages=n_pages, dr=dr)
+    return dict(acc=np.array(accs), tok=toks, ctx=ctx, pool=pool, table=table, n_pages=n_pages, dr=dr,
+                blocks=blocks)
 
 
 def run_loop_oracle(dims, Wn, ctx0, hid_np, steps, B, S, p, seed, only=None, gpu=None):
@@ -235,7 +246,7 @@ def run_loop_oracle(dims, Wn, ctx0, hid_np, steps, B, S, p, seed, only=None, gpu
     subset of sequences (independent of the others).
 
     With `gpu` (the GPU loop's result) each draft reads the pool the GPU injected, so both
-    drafts see identical inputs.  Pool entries of positions below a sequence's length never
+    drafts see identical inputs, and each step drafts with the block size the GPU loop used.  Pool entries of positions below a sequence's length never
     change once injected, so the final GPU pool's prefix is the pool of every earlier step.
     The oracle's own injection is kept alongside and checked against that prefix within the
     bf16 flip tolerance.  A sequence whose trajectory left the GPU's falls back to its own
@@ -256,7 +267,8 @@ def run_loop_oracle(dims, Wn, ctx0, hid_np, steps, B, S, p, seed, only=None, gpu
                 draft_pools.append((gkv[b][0][:, :ctx[b]], gkv[b][1][:, :ctx[b]]))
             else:
                 draft_pools.append(pools[b])
-        res = oracle.draft_block(dims, Wn, draft_pools, [ctx[b] for b in idx], B, S, want_logits=False)
+        Bt = int(gpu["blocks"][st]) if gpu is not None else int(B)
+        res = oracle.draft_block(dims, Wn, draft_pools, [ctx[b] for b in idx], Bt, S, want_logits=False)
         tok = res["tokens"]
         flag = np.zeros(len(idx), dtype=bool)
         for r in range(len(idx)):
@@ -264,7 +276,7 @@ def run_loop_oracle(dims, Wn, ctx0, hid_np, steps, B, S, p, seed, only=None, gpu
                 now = np.nonzero(res["committed_at"][r] == s_)[0]
                 if any(res["gap"][r, s_, i] < TIE for i in now) or (s_ < S - 1 and res["boundary_gap"][r, s_] < TIE):
                     flag[r] = True
-        full = np.zeros((len(ctx0), B), dtype=np.int64)
+        full = np.zeros((len(ctx0), Bt), dtype=np.int64)
         full[idx] = tok
         zt = target_logits_for(torch.from_numpy(full), dims.vocab, p, seed, st).numpy()[idx]
         acc, _ = oracle.verify_greedy(zt, tok)
@@ -284,7 +296,7 @@ def run_loop_oracle(dims, Wn, ctx0, hid_np, steps, B, S, p, seed, only=None, gpu
                 T = ctx[b]
                 for name, own, got in (("K", pools[b][0], gkv[b][0]), ("V", pools[b][1], gkv[b][1])):
                     compare_pool_entries(got[:, :T], own[:, :T], dims.dtype, f"seq {b} {name}")
-    return dict(acc=np.array(accs), tok=np.array(toks), flags=np.array(flags), idx=idx)
+    return dict(acc=np.array(accs), tok=toks, flags=np.array(flags), idx=idx)
 
 
 def compare_loops(g, o, log_every=16):
@@ -330,6 +342,51 @@ def test_incremental_loop_small_model_all_sequences():
     # every divergence happened at a flagged near-tie (asserted in compare_loops); most
     # (step, sequence) pairs are still compared bit-exactly before one occurs
     assert out["pairs_compared"] >= out["pairs_total"] // 4
+
+
+def test_incremental_loop_adaptive_block_size():
+    """The step loop with the block size changing between steps: three fixed steps at
+    16, 4 and 8, then dflash_adaptive_block_size's choice from the acceptances so far
+    (step times in the ratio the 8B-shaped batch-32 draft measures at 4/8/16).  Every
+    step is checked against the oracle drafting with the same block size, and the pool
+    after the loop must equal a one-shot injection of every final prefix bit for bit."""
+    dims = synth.small_dims()
+    S, p, seed, steps = 2, 0.75, 43, 16
+    rng = np.random.default_rng(seed)
+    ctx0 = rng.integers(40, 200, size=12).tolist()
+    cands, times = [4, 8, 16], [3.87, 4.49, 6.03]
+
+    def policy(st, accs, blocks):
+        if st < 3:
+            return [16, 4, 8][st]
+        a = np.concatenate(accs)
+        bl = np.concatenate([np.full(len(x), b) for x, b in zip(accs, blocks)])
+        return Bn.dflash_adaptive_block_size(a.tolist(), bl.tolist(), cands, times)[0]
+
+    W = synth.make_weights(dims, seed, "cuda")
+    hid = loop_hiddens(dims, ctx0, (steps + 1) * 17, 0, 1, seed, "cuda")
+    g = run_loop_gpu(dims, W, ctx0, hid, steps, policy, S, p, seed, 0, 1, max_block=16)
+    log(f"adaptive blocks {g['blocks']}")
+    assert g["blocks"][:3] == [16, 4, 8] and set(g["blocks"]) <= set(cands)
+    for st, b in enumerate(g["blocks"]):
+        assert np.all((g["acc"][st] >= 0) & (g["acc"][st] <= b))
+    Wn = np_weights32(W)
+    o = run_loop_oracle(dims, Wn, ctx0, [f64(h) for h in hid], steps, None, S, p, seed, gpu=g)
+    out = compare_loops(g, o)
+    log(f"adaptive loop: {out}")
+    assert out["pairs_compared"] >= out["pairs_total"] // 4
+    n_pages, table = g["n_pages"], g["table"]
+    fresh = alloc_pool(dims, n_pages)
+    seqs = [b for b, c in enumerate(g["ctx"]) for _ in range(c)]
+    poss = [t for c in g["ctx"] for t in range(c)]
+    g["dr"].inject(torch.cat([hid[b][:c] for b, c in enumerate(g["ctx"])]),
+                   torch.tensor(seqs, dtype=torch.int32, device="cuda"),
+                   torch.tensor(poss, dtype=torch.int32, device="cuda"), fresh, n_pages,
+                   torch.from_numpy(table).cuda(), len(ctx0))
+    torch.cuda.synchronize()
+    used = np.unique(table[table >= 0])
+    assert torch.equal(g["pool"].view(n_pages, -1)[used].view(torch.int16),
+                       fresh.view(n_pages, -1)[used].view(torch.int16))
 
 
 def test_incremental_loop_8b_shape():
