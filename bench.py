@@ -425,6 +425,23 @@ def main():
         torch.cuda.synchronize()
         res["repredict_schedule"] = {"draft_ms": round(e0.elapsed_time(e1) / nd, 4),
                                      "note": "same batch and pool; every step re-predicts every position"}
+        # the same draft with QK-norm layers (unit gains; timing only, the pool was injected without it)
+        from dataclasses import replace as _replace
+        dims_qk = _replace(dims, qk_norm=True)
+        W_qk = dict(W, q_norm=[torch.ones(dims.head_dim, device=dev) for _ in range(dims.n_layers)],
+                    k_norm=[torch.ones(dims.head_dim, device=dev) for _ in range(dims.n_layers)])
+        cfg_qk, w_qk = Bn.make_config(dims_qk), Bn.Weights(W_qk)
+        for _ in range(2):
+            Bn.dflash_draft_block(cfg_qk, w_qk, pool, n_pages, table, pages_per, ctx_dev, max_ctx, bt, B, S, 0.0, 0,
+                                  tok, None, None, ws, ws_bytes)
+        e0.record(stream)
+        for _ in range(nd):
+            Bn.dflash_draft_block(cfg_qk, w_qk, pool, n_pages, table, pages_per, ctx_dev, max_ctx, bt, B, S, 0.0, 0,
+                                  tok, None, None, ws, ws_bytes)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        res["qk_norm"] = {"draft_ms": round(e0.elapsed_time(e1) / nd, 4),
+                          "note": "same batch and pool with per-head RMSNorm of queries and keys (query prep)"}
     if a.cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(dims, W, wl, B, S, int(ctx_before[0]))
     res["setup_s"] = round(setup_s, 1)

@@ -32,7 +32,7 @@ class dflash_config(ctypes.Structure):
         "hidden", "n_layers", "n_q_heads", "n_kv_heads", "head_dim", "intermediate", "vocab", "n_fuse",
         "target_hidden", "page_size", "mask_token_id")] + [
         ("rope_base", ctypes.c_float), ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32),
-        ("denoise_schedule", ctypes.c_int32)]
+        ("denoise_schedule", ctypes.c_int32), ("qk_norm", ctypes.c_int32)]
 
 
 _PP = ctypes.POINTER(ctypes.c_void_p)
@@ -42,7 +42,7 @@ class dflash_weights(ctypes.Structure):
     _fields_ = [("w_fc", ctypes.c_void_p), ("w_kv", ctypes.c_void_p), ("embed", ctypes.c_void_p),
                 ("final_norm", ctypes.c_void_p), ("lm_head", ctypes.c_void_p),
                 ("attn_norm", _PP), ("w_q", _PP), ("w_o", _PP), ("mlp_norm", _PP),
-                ("w_gate", _PP), ("w_up", _PP), ("w_down", _PP)]
+                ("w_gate", _PP), ("w_up", _PP), ("w_down", _PP), ("q_norm", _PP), ("k_norm", _PP)]
 
 
 _lib = None
@@ -111,7 +111,8 @@ def make_config(dims, schedule="progressive"):
     return dflash_config(dims.hidden, dims.n_layers, dims.n_q_heads, dims.n_kv_heads, dims.head_dim,
                          dims.intermediate, dims.vocab, dims.n_fuse, dims.target_hidden, dims.page_size,
                          dims.mask_token_id, float(dims.rope_base), float(dims.rms_eps),
-                         DFLASH_BF16 if dims.dtype == "bf16" else DFLASH_F32, SCHEDULES[schedule])
+                         DFLASH_BF16 if dims.dtype == "bf16" else DFLASH_F32, SCHEDULES[schedule],
+                         1 if getattr(dims, "qk_norm", False) else 0)
 
 
 class Weights:
@@ -122,14 +123,16 @@ class Weights:
         L = len(W["w_q"])
         arr = ctypes.c_void_p * L
         self._arrays = {k: arr(*[t.data_ptr() for t in W[k]]) for k in
-                        ("attn_norm", "w_q", "w_o", "mlp_norm", "w_gate", "w_up", "w_down")}
+                        ("attn_norm", "w_q", "w_o", "mlp_norm", "w_gate", "w_up", "w_down", "q_norm", "k_norm")
+                        if k in W}
         a = self._arrays
+        qk = {k: ctypes.cast(a[k], _PP) if k in a else None for k in ("q_norm", "k_norm")}
         self.c = dflash_weights(W["w_fc"].data_ptr(), W["w_kv"].data_ptr(), W["embed"].data_ptr(),
                                 W["final_norm"].data_ptr(), W["lm_head"].data_ptr(),
                                 ctypes.cast(a["attn_norm"], _PP), ctypes.cast(a["w_q"], _PP),
                                 ctypes.cast(a["w_o"], _PP), ctypes.cast(a["mlp_norm"], _PP),
                                 ctypes.cast(a["w_gate"], _PP), ctypes.cast(a["w_up"], _PP),
-                                ctypes.cast(a["w_down"], _PP))
+                                ctypes.cast(a["w_down"], _PP), qk["q_norm"], qk["k_norm"])
 
 
 def dflash_workspace_size(cfg, max_batch, block_size, max_inject_tokens, max_ctx_len):

@@ -70,6 +70,8 @@ dflash_status check_cfg(const dflash_config* c) {
   if (c->mask_token_id < 0 || c->mask_token_id >= c->vocab) return DFLASH_EINVAL;
   if (c->denoise_schedule != DFLASH_SCHEDULE_PROGRESSIVE && c->denoise_schedule != DFLASH_SCHEDULE_REPREDICT)
     return DFLASH_EINVAL;
+  if (c->qk_norm != 0 && c->qk_norm != 1) return DFLASH_EINVAL;
+  if (c->qk_norm && c->n_layers > kMaxQkLayers) return DFLASH_ECAPACITY;
   if (!(c->rope_base > 0.f) || !(c->rms_eps >= 0.f)) return DFLASH_EINVAL;
   return DFLASH_OK;
 }
@@ -77,6 +79,11 @@ dflash_status check_cfg(const dflash_config* c) {
 dflash_status check_weights(const dflash_config* c, const dflash_weights* w, bool draft) {
   if (!w) return DFLASH_EINVAL;
   if (!ptr_ok(w->w_fc) || !ptr_ok(w->w_kv)) return DFLASH_EINVAL;
+  if (c->qk_norm) {
+    if (!w->k_norm || (draft && !w->q_norm)) return DFLASH_EINVAL;
+    for (int l = 0; l < c->n_layers; ++l)
+      if (!w->k_norm[l] || (draft && !w->q_norm[l])) return DFLASH_EINVAL;
+  }
   if (!draft) return DFLASH_OK;
   if (!ptr_ok(w->embed) || !ptr_ok(w->final_norm) || !ptr_ok(w->lm_head)) return DFLASH_EINVAL;
   const void* const* arrs[7] = {(const void* const*)w->attn_norm, w->w_q, w->w_o, (const void* const*)w->mlp_norm,
@@ -311,6 +318,9 @@ dflash_status dflash_inject_kv(const dflash_config* cfg, const dflash_weights* w
     k.e.n_layers = cfg->n_layers;
     k.e.n_kv = nkv;
     k.e.head_dim = d;
+    k.e.k_norm_on = cfg->qk_norm;
+    k.e.rms_eps = cfg->rms_eps;
+    for (int l = 0; cfg->qk_norm && l < cfg->n_layers; ++l) k.e.k_gain[l] = w->k_norm[l];
     HIP_TRY(gemm(DFLASH_PROF_INJECT_KV, k, stream));
   }
   return DFLASH_OK;
@@ -415,7 +425,14 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
       const int ks_qkv = g.defer_reduce ? gemm_ksplit(g) : 1;
       ap.qkv_part = ks_qkv > 1 ? gpart : nullptr;
       ap.qkv_ks = ks_qkv;
+      // QK-norm: the query prep applies it (bf16, head_dim 128); otherwise it runs in
+      // place on the finished q/k rows before the attention kernels read them
+      ap.q_gain = cfg->qk_norm ? w->q_norm[l] : nullptr;
+      ap.k_gain = cfg->qk_norm ? w->k_norm[l] : nullptr;
+      ap.rms_eps = cfg->rms_eps;
       HIP_TRY(gemm(DFLASH_PROF_GEMM_QKV, g, stream));
+      if (cfg->qk_norm && !g.defer_reduce)
+        HIP_TRY(launch_qk_norm(qkv, M, nq, nkv, d, ap.q_gain, ap.k_gain, cfg->rms_eps, stream));
 
       ap.layer = l;
       HIP_TRY(launch_attention(ap, bf, stream, g_prof.cls == DFLASH_PROF_ATTN ? prof_attn : nullptr));

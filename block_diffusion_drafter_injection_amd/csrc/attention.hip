@@ -103,6 +103,20 @@ __device__ __forceinline__ void rope4(const float4& x0, const float4& x1, const 
                    x1.w * c23.z + x0.w * c23.w);
 }
 
+// QK-norm of one head row spread over TPR consecutive lanes (dims 4e..4e+3 in
+// x0 and their rotate-half partners in x1): x * gain / rms(x).
+template <int TPR, int D>
+__device__ __forceinline__ void head_rmsnorm(float4& x0, float4& x1, const float* gain, int e, float eps) {
+  float ss = x0.x * x0.x + x0.y * x0.y + x0.z * x0.z + x0.w * x0.w + x1.x * x1.x + x1.y * x1.y + x1.z * x1.z +
+             x1.w * x1.w;
+#pragma unroll
+  for (int o = 1; o < TPR; o <<= 1) ss += __shfl_xor(ss, o, kWave);
+  const float inv = 1.f / sqrtf(ss / (float)D + eps);
+  const float4 g0 = *(const float4*)(gain + 4 * e), g1 = *(const float4*)(gain + D / 2 + 4 * e);
+  x0 = make_float4(x0.x * inv * g0.x, x0.y * inv * g0.y, x0.z * inv * g0.z, x0.w * inv * g0.w);
+  x1 = make_float4(x1.x * inv * g1.x, x1.y * inv * g1.y, x1.z * inv * g1.z, x1.w * inv * g1.w);
+}
+
 template <int D>
 __global__ __launch_bounds__(256) void attn_qprep_kernel(AttnParams p) {
   // D/8 threads per row; thread e covers dims 4e .. 4e+3 and their
@@ -119,7 +133,8 @@ __global__ __launch_bounds__(256) void attn_qprep_kernel(AttnParams p) {
     const float qscale = p.scale * 1.4426950408889634f;   // scores come out in base-2 units
     const int r = u, j = r / p.B, i = r - j * p.B, row = b * p.B + i, n = m * g + j;
     const size_t off = (size_t)row * ldq + n * D + 4 * e;
-    const float4 x0 = qkv_quad(p, off, plane), x1 = qkv_quad(p, off + h, plane);
+    float4 x0 = qkv_quad(p, off, plane), x1 = qkv_quad(p, off + h, plane);
+    if (p.q_gain) head_rmsnorm<TPR, D>(x0, x1, p.q_gain, e, p.rms_eps);
     const float4* cs = (const float4*)(p.cs + (size_t)row * h + 4 * e);   // (cos, sin) of dims 4e .. 4e+3
     float4 y0, y1;
     rope4(x0, x1, cs[0], cs[1], y0, y1);
@@ -139,9 +154,10 @@ __global__ __launch_bounds__(256) void attn_qprep_kernel(AttnParams p) {
   const int r = is_k ? u - R : u - R - p.B;   // block position
   const int krow = b * p.B + r;
   const size_t off = (size_t)krow * ldq + (p.nq + (is_k ? 0 : p.nkv)) * D + m * D + 4 * e;
-  const float4 x0 = qkv_quad(p, off, plane), x1 = qkv_quad(p, off + h, plane);
+  float4 x0 = qkv_quad(p, off, plane), x1 = qkv_quad(p, off + h, plane);
   const size_t o = (((size_t)b * p.nkv + m) * p.B + r) * D + 4 * e;
-  if (is_k) {   // rotated key
+  if (is_k) {   // rotated key (QK-normed first when asked)
+    if (p.k_gain) head_rmsnorm<TPR, D>(x0, x1, p.k_gain, e, p.rms_eps);
     const float4* cs = (const float4*)(p.cs + (size_t)krow * h + 4 * e);
     float4 y0, y1;
     rope4(x0, x1, cs[0], cs[1], y0, y1);

@@ -12,6 +12,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));   // 16-byte reg
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWave = 64;
+constexpr int kMaxQkLayers = 16;   // layers whose QK-norm key gains one injection launch carries
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef float f32x2_t __attribute__((ext_vector_type(2)));

@@ -222,6 +222,42 @@ hipError_t launch_rope_table_tokens(const int* tok_pos, int n, int d, double bas
   return hipGetLastError();
 }
 
+// QK-norm in place, one wave per (row, query-or-key head) of qkv
+// [M, (nq + 2 nkv) d] (head_dim <= 128: two values per lane at most).
+__global__ __launch_bounds__(256) void qk_norm_kernel(float* qkv, int M, int nq, int nkv, int d,
+                                                     const float* q_gain, const float* k_gain, float eps) {
+  const int wave = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int heads = nq + nkv;
+  if (wave >= M * heads) return;   // the whole wave leaves together
+  const int row = wave / heads, hh = wave - row * heads;
+  float* x = qkv + (size_t)row * (nq + 2 * nkv) * d + (size_t)hh * d;
+  const float* g = hh < nq ? q_gain : k_gain;
+  float v[2], ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = lane + 64 * k;
+    v[k] = c < d ? x[c] : 0.f;
+    ss = fmaf(v[k], v[k], ss);
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) ss += __shfl_xor(ss, o, kWave);
+  const float inv = 1.f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int c = lane + 64 * k;
+    if (c < d) x[c] = v[k] * inv * g[c];
+  }
+}
+
+hipError_t launch_qk_norm(float* qkv, int M, int nq, int nkv, int d, const float* q_gain, const float* k_gain,
+                          float eps, hipStream_t s) {
+  const int waves = M * (nq + nkv);
+  if (waves <= 0) return hipSuccess;
+  if (d > 128 || !q_gain || !k_gain) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(qk_norm_kernel, dim3((waves + 3) / 4), dim3(256), 0, s, qkv, M, nq, nkv, d, q_gain, k_gain, eps);
+  return hipGetLastError();
+}
+
 hipError_t launch_block_init(int* tau, int* committed, int M, int mask_id, hipStream_t s) {
   hipLaunchKernelGGL(block_init_kernel, dim3((M + 255) / 256), dim3(256), 0, s, tau, committed, M, mask_id);
   return hipGetLastError();

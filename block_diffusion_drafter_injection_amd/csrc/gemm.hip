@@ -185,6 +185,19 @@ __device__ __forceinline__ void run_epilogue(const float* Cs, int ldc, int m0, i
   } else if constexpr (KIND == EPI_KVSCATTER) {
     const int d = e.head_dim, hd = d / 2, nkv = e.n_kv;
     const int hpt = BN / d;  // heads per tile
+    // QK-norm: 1 / rms of every (row, head) of the tile (head_dim >= 64, so at
+    // most BN / 64 heads per row); only the K heads use it
+    __shared__ float kinv[BM * (BN / 64)];
+    if (e.k_norm_on) {
+      for (int idx = tid; idx < BM * hpt; idx += NT) {
+        const int r = idx / hpt, hb = idx - r * hpt;
+        const float* x = Cs + r * ldc + hb * d;
+        float ss = 0.f;
+        for (int c = 0; c < d; ++c) ss = fmaf(x[c], x[c], ss);
+        kinv[idx] = 1.f / sqrtf(ss / (float)d + e.rms_eps);
+      }
+      __syncthreads();
+    }
     for (int idx = tid; idx < BM * hpt * hd; idx += NT) {
       const int r = idx / (hpt * hd);
       const int rem = idx - r * hpt * hd;
@@ -199,9 +212,15 @@ __device__ __forceinline__ void run_epilogue(const float* Cs, int ldc, int m0, i
       if (lp >= e.max_pages) continue;
       const int phys = e.block_table[(size_t)b * e.max_pages + lp];
       if (phys < 0 || phys >= e.n_pages) continue;
-      const float x0 = Cs[r * ldc + hb * d + j], x1 = Cs[r * ldc + hb * d + j + hd];
+      float x0 = Cs[r * ldc + hb * d + j], x1 = Cs[r * ldc + hb * d + j + hd];
       TP* chunk = (TP*)e.pool + ((((size_t)phys * L + l) * 2 + kv) * nkv + m) * (size_t)(16 * d);
       if (kv == 0) {
+        if (e.k_norm_on) {
+          const float sc = kinv[r * hpt + hb];
+          const float* gk = e.k_gain[l];
+          x0 = x0 * sc * gk[j];
+          x1 = x1 * sc * gk[j + hd];
+        }
         const float2 cs = e.rope_cs[(size_t)row * hd + j];
         const float y0 = x0 * cs.x - x1 * cs.y, y1 = x1 * cs.x + x0 * cs.y;
         if constexpr (sizeof(TP) == 2) {

@@ -47,6 +47,11 @@ struct EpiParams {
   int n_seqs, max_pages, n_pages;
   const float2* rope_cs;  // [M, d/2]
   int n_layers, n_kv, head_dim;
+  // EPI_KVSCATTER with QK-norm: each K head is RMS-normalised over head_dim
+  // with layer l's gains k_gain[l] before the rotation
+  int k_norm_on;
+  float rms_eps;
+  const float* k_gain[kMaxQkLayers];
 };
 
 struct GemmArgs {
@@ -93,6 +98,9 @@ struct AttnParams {
   float* vblk;            // [batch, nkv, B, d] block values, fp32 (bf16 pools)
   const float* qkv_part;  // [qkv_ks, M, (nq + 2 nkv) d] K-split partials of qkv, or null
   int qkv_ks;             // number of partials (the query prep sums them in split order)
+  const float* q_gain;    // QK-norm gains of this layer [d], or null (no QK-norm)
+  const float* k_gain;
+  float rms_eps;
 };
 // Context splits -> partials (no launch when there is no context).
 hipError_t launch_attention(const AttnParams& p, int wdtype, hipStream_t s, void (*mark)(int, hipStream_t));
@@ -105,6 +113,9 @@ hipError_t launch_rope_table_block(const int* ctx_len, int ctx_cap, int batch, i
 hipError_t launch_rope_table_tokens(const int* tok_pos, int n, int d, double base, float2* cs,
                                     hipStream_t s);
 hipError_t launch_block_init(int* tau, int* committed, int M, int mask_id, hipStream_t s);
+// QK-norm in place on the query and key heads of qkv [M, (nq + 2 nkv) d] (before RoPE).
+hipError_t launch_qk_norm(float* qkv, int M, int nq, int nkv, int d, const float* q_gain, const float* k_gain,
+                          float eps, hipStream_t s);
 hipError_t launch_embed(const int* tau, const void* embed, int wdtype, int vocab, float* h, int M,
                         int H, hipStream_t s);
 // With part != null, h += sum over the ksplit partials [ksplit][part_rows][H]

@@ -35,6 +35,7 @@ class ModelDims:
     dtype: str = "bf16"          # 'bf16' or 'fp32': storage type of weights, inputs and KV pool
     rms_eps: float = 1e-6
     page_size: int = 16
+    qk_norm: bool = False        # per-head RMSNorm of queries and keys before RoPE (Qwen3 layers)
 
     @property
     def mask_token_id(self):
@@ -128,6 +129,9 @@ def make_weights(d: ModelDims, seed, device="cpu", std=0.02):
         lm_head=mat(d.vocab, H),
         attn_norm=[], w_q=[], w_o=[], mlp_norm=[], w_gate=[], w_up=[], w_down=[],
     )
+    if d.qk_norm:
+        W["q_norm"] = [gain(hd) for _ in range(L)]
+        W["k_norm"] = [gain(hd) for _ in range(L)]
     for _ in range(L):
         W["attn_norm"].append(gain(H))
         W["w_q"].append(mat(nq * hd, H))

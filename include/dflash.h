@@ -97,6 +97,10 @@ typedef struct {
   float rms_eps;
   int32_t dtype;          /* dflash_dtype */
   int32_t denoise_schedule; /* dflash_schedule */
+  int32_t qk_norm;        /* 1: every query and key head is RMS-normalised over head_dim
+                           * (gains q_norm / k_norm, epsilon rms_eps) before the rotary
+                           * embedding, the injected context keys included (the Qwen3 layer);
+                           * 0: no QK-norm.  With 1, n_layers <= 16. */
 } dflash_config;
 
 /* Draft weights (all device pointers; per-layer entries are host arrays of
@@ -121,6 +125,8 @@ typedef struct {
   const void* const* w_gate;
   const void* const* w_up;
   const void* const* w_down;
+  const float* const* q_norm;  /* per layer [head_dim] fp32 gains; required iff qk_norm */
+  const float* const* k_norm;  /* per layer [head_dim] fp32 gains; required iff qk_norm */
 } dflash_weights;
 
 /* Bytes of workspace the three calls need for the given maxima (a call

@@ -37,6 +37,12 @@ What the pages fix, and the readings taken where they are silent:
 * Draft layer: RMSNorm, grouped-query attention (head n uses kv head
   n // (n_q/n_kv)), residual, RMSNorm, SwiGLU MLP, residual; final RMSNorm,
   LM head.  The mask token is id V-1 and argmax runs over the whole vocab.
+* QK-norm (optional, ``cfg.qk_norm``): the pages name the target family
+  (Qwen3) but not the drafter's layer internals; the Qwen3 layer normalises
+  every query and key head by RMSNorm over head_dim (gains q_norm[l] /
+  k_norm[l] of length d) before the rotary embedding.  With it on, the same
+  key normalisation applies to the injected context keys, since they are
+  keys of the same layer.
 """
 import numpy as np
 
@@ -54,6 +60,10 @@ def _lin(x, w):
     return np.asarray(x, F64) @ np.asarray(w, F64).T
 
 
+def _qk_norm(cfg):
+    return bool(getattr(cfg, "qk_norm", False))
+
+
 def inject(cfg, W, x, pos):
     """Context features -> per-layer K/V for the KV pool.
 
@@ -66,7 +76,10 @@ def inject(cfg, W, x, pos):
     kv = _lin(f, W["w_kv"])                      # all layers at once [n, L*2*nkv*d]
     kv = kv.reshape(-1, L, 2, nkv, d)
     pos = np.asarray(pos)
-    K = rope(kv[:, :, 0], pos[:, None, None], cfg.rope_base)
+    k = kv[:, :, 0]
+    if _qk_norm(cfg):
+        k = np.stack([rmsnorm(k[:, l], W["k_norm"][l], cfg.rms_eps) for l in range(L)], axis=1)
+    K = rope(k, pos[:, None, None], cfg.rope_base)
     V = kv[:, :, 1]
     return _store(cfg, K.transpose(1, 0, 2, 3)), _store(cfg, V.transpose(1, 0, 2, 3))
 
@@ -97,10 +110,14 @@ def forward_hidden(cfg, W, pools, ctx_len, tau):
     for l in range(L):
         u = rmsnorm(h, W["attn_norm"][l], cfg.rms_eps)
         q = _lin(u, W["w_q"][l]).reshape(bt, B, nq, d)
-        q = rope(q, pos[:, :, None], cfg.rope_base)
         kvw = W["w_kv"][l * 2 * nkvd:(l + 1) * 2 * nkvd]
         kv = _lin(u, kvw)
-        k = rope(kv[..., :nkvd].reshape(bt, B, nkv, d), pos[:, :, None], cfg.rope_base)
+        k = kv[..., :nkvd].reshape(bt, B, nkv, d)
+        if _qk_norm(cfg):
+            q = rmsnorm(q, W["q_norm"][l], cfg.rms_eps)
+            k = rmsnorm(k, W["k_norm"][l], cfg.rms_eps)
+        q = rope(q, pos[:, :, None], cfg.rope_base)
+        k = rope(k, pos[:, :, None], cfg.rope_base)
         v = kv[..., nkvd:].reshape(bt, B, nkv, d)
         o = np.empty((bt, B, nq, d), F64)
         for b in range(bt):

@@ -41,6 +41,15 @@ def _rms(x, gain, eps):
     return [x[c] / s * float(gain[c]) for c in range(len(x))]
 
 
+def _kn(cfg, W, l, head):
+    """Per-head key RMSNorm when the config asks for QK-norm."""
+    return _rms(head, W["k_norm"][l], cfg.rms_eps) if getattr(cfg, "qk_norm", False) else head
+
+
+def _qn(cfg, W, l, head):
+    return _rms(head, W["q_norm"][l], cfg.rms_eps) if getattr(cfg, "qk_norm", False) else head
+
+
 def inject(cfg, W, x_rows, positions):
     """-> K[l][t][m][e], V[l][t][m][e] as nested lists."""
     L, nkv, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
@@ -51,7 +60,8 @@ def inject(cfg, W, x_rows, positions):
         kv = _matvec(W["w_kv"], f)
         for l in range(L):
             base = l * 2 * nkv * d
-            K[l][t] = [[_store(cfg, v) for v in _rot(kv[base + m * d: base + (m + 1) * d], p, cfg.rope_base)]
+            K[l][t] = [[_store(cfg, v) for v in _rot(_kn(cfg, W, l, kv[base + m * d: base + (m + 1) * d]), p,
+                                                      cfg.rope_base)]
                        for m in range(nkv)]
             V[l][t] = [[_store(cfg, kv[base + nkv * d + m * d + e]) for e in range(d)] for m in range(nkv)]
     return K, V
@@ -74,10 +84,10 @@ def forward(cfg, W, pools, ctx_len, tau):
             for i in range(B):
                 p = T + i
                 qi = _matvec(W["w_q"][l], u[i])
-                q.append([_rot(qi[n * d:(n + 1) * d], p, cfg.rope_base) for n in range(nq)])
+                q.append([_rot(_qn(cfg, W, l, qi[n * d:(n + 1) * d]), p, cfg.rope_base) for n in range(nq)])
                 rows = W["w_kv"][l * 2 * nkv * d:(l + 1) * 2 * nkv * d]
                 kvi = _matvec(rows, u[i])
-                k.append([_rot(kvi[m * d:(m + 1) * d], p, cfg.rope_base) for m in range(nkv)])
+                k.append([_rot(_kn(cfg, W, l, kvi[m * d:(m + 1) * d]), p, cfg.rope_base) for m in range(nkv)])
                 v.append([kvi[nkv * d + m * d: nkv * d + (m + 1) * d] for m in range(nkv)])
             o = [[None] * nq for _ in range(B)]
             for m in range(nkv):

@@ -19,17 +19,31 @@ def _dims(name):
     return {"tiny": synth.TINY, "small": SMALL}[name]
 
 
+def _with_qk(dims, W, seed):
+    """QK-norm on, with random (non-unit) gains so a misplaced gain shows."""
+    from dataclasses import replace
+    dims = replace(dims, qk_norm=True)
+    g = torch.Generator(device="cpu").manual_seed(seed)
+    W = dict(W)
+    for k in ("q_norm", "k_norm"):
+        W[k] = [(1.0 + 0.3 * torch.randn(dims.head_dim, generator=g)).float().cuda() for _ in range(dims.n_layers)]
+    return dims, W
+
+
 def _tokens(ctx, device="cuda"):
     seq = np.concatenate([np.full(c, b) for b, c in enumerate(ctx)]).astype(np.int32)
     pos = np.concatenate([np.arange(c) for c in ctx]).astype(np.int32)
     return torch.from_numpy(seq).to(device), torch.from_numpy(pos).to(device)
 
 
-@pytest.mark.parametrize("name,ctx,chunk", [("tiny", [64], 4096), ("small", [37, 0, 70, 131], 64),
-                                            ("small", [5, 300], 4096)])
-def test_inject_matches_oracle(name, ctx, chunk):
+@pytest.mark.parametrize("name,ctx,chunk,qk", [("tiny", [64], 4096, False), ("small", [37, 0, 70, 131], 64, False),
+                                               ("small", [5, 300], 4096, False), ("tiny", [64, 20], 4096, True),
+                                               ("small", [37, 150], 64, True)])
+def test_inject_matches_oracle(name, ctx, chunk, qk):
     dims = _dims(name)
     W = synth.make_weights(dims, 7, "cuda")
+    if qk:
+        dims, W = _with_qk(dims, W, 70)
     table, n_pages = page_plan(ctx, 0, seed=3)
     tab = torch.from_numpy(table).cuda()
     pool = alloc_pool(dims, n_pages)
@@ -72,8 +86,10 @@ def test_incremental_injection_is_bitwise_one_shot():
     assert torch.equal(one.view(torch.int16), inc.view(torch.int16))
 
 
-def _draft_case(dims, ctx, B, S, T, seed, want_logits=True, schedule="progressive"):
+def _draft_case(dims, ctx, B, S, T, seed, want_logits=True, schedule="progressive", qk=False):
     W = synth.make_weights(dims, seed, "cuda")
+    if qk:
+        dims, W = _with_qk(dims, W, seed + 5)
     table, n_pages = page_plan(ctx, 0, seed=seed + 1)
     tab = torch.from_numpy(table).cuda()
     pool = alloc_pool(dims, n_pages)
@@ -124,6 +140,39 @@ def test_draft_repredict_matches_oracle(name, ctx, B, S, T):
     out = compare_draft(dims, S, res, tok, lg, cf, schedule="repredict")
     print(f"draft (re-predict) {name} ctx={ctx} B={B} S={S} T={T}: {out}")
     assert out["compared"] >= tok.size // 2
+
+
+@pytest.mark.parametrize("name,ctx,B,S,d", [
+    ("tiny", [64, 9], 4, 2, 64),          # fp32: in-place QK-norm, VALU attention
+    ("small", [0, 37, 300], 8, 2, 128),   # bf16, head_dim 128: QK-norm in the query prep, MFMA attention
+    ("small", [130, 16], 16, 2, 64),      # bf16, head_dim 64: in-place QK-norm, VALU attention
+])
+def test_draft_qk_norm_matches_oracle(name, ctx, B, S, d):
+    from dataclasses import replace
+    dims = _dims(name)
+    if d != dims.head_dim:
+        dims = replace(dims, head_dim=d)
+    res, tok, lg, cf, _ = _draft_case(dims, ctx, B, S, 0.0, seed=80 + B, qk=True)
+    out = compare_draft(dims, S, res, tok, lg, cf)
+    print(f"draft (QK-norm) {name} d={d} ctx={ctx} B={B} S={S}: {out}")
+    assert out["compared"] >= tok.size // 2
+
+
+def test_incremental_injection_with_qk_norm_is_bitwise_one_shot():
+    dims, W = _with_qk(SMALL, synth.make_weights(SMALL, 9, "cuda"), 90)
+    ctx = [150, 97]
+    table, n_pages = page_plan(ctx, 0, seed=4)
+    tab = torch.from_numpy(table).cuda()
+    hid = synth.make_hiddens(dims, sum(ctx), 10, "cuda")
+    seq, pos = _tokens(ctx)
+    dr = Drafter(dims, W, max_batch=2, block_size=8, max_ctx=150, max_inject=4096)
+    one = alloc_pool(dims, n_pages)
+    dr.inject(hid, seq, pos, one, n_pages, tab, 2)
+    inc = alloc_pool(dims, n_pages)
+    for a, b in [(0, 3), (3, 100), (100, seq.numel())]:
+        dr.inject(hid[a:b].contiguous(), seq[a:b].contiguous(), pos[a:b].contiguous(), inc, n_pages, tab, 2)
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int16), inc.view(torch.int16))
 
 
 def test_draft_is_deterministic():

@@ -35,10 +35,21 @@ def rand_pool(dims, T, seed, scale=1.0):
     return K.float().numpy().astype(np.float64), V.float().numpy().astype(np.float64)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_inject_matches_brute(dtype):
-    dims = replace(TINY, dtype=dtype)
+def with_qk_gains(dims, W, seed):
+    """Random (non-unit) QK-norm gains, so a swapped or misplaced gain changes the result."""
+    rng = np.random.default_rng(seed)
+    W = dict(W)
+    W["q_norm"] = [1.0 + 0.3 * rng.standard_normal(dims.head_dim) for _ in range(dims.n_layers)]
+    W["k_norm"] = [1.0 + 0.3 * rng.standard_normal(dims.head_dim) for _ in range(dims.n_layers)]
+    return W
+
+
+@pytest.mark.parametrize("dtype,qk", [("bf16", False), ("fp32", False), ("bf16", True), ("fp32", True)])
+def test_inject_matches_brute(dtype, qk):
+    dims = replace(TINY, dtype=dtype, qk_norm=qk)
     W = np_weights(dims, 11, std=0.3)
+    if qk:
+        W = with_qk_gains(dims, W, 111)
     x = np_hiddens(dims, 6, 12)
     pos = np.array([0, 1, 5, 16, 17, 300])
     K, V = oracle.inject(dims, W, x, pos)
@@ -47,6 +58,27 @@ def test_inject_matches_brute(dtype):
     assert np.allclose(V, np.array(Vb), rtol=1e-12, atol=1e-12)
     if dtype == "bf16":
         assert np.array_equal(bf16_round(K), K) and np.array_equal(bf16_round(V), V)
+
+
+def test_qk_norm_closed_forms():
+    # unit gains: every stored key head has rms 1 (RoPE is a rotation, so it keeps the norm)
+    dims = replace(TINY, dtype="fp32", qk_norm=True)
+    W = np_weights(dims, 17, std=0.3)
+    x = np_hiddens(dims, 9, 18)
+    K, V = oracle.inject(dims, W, x, np.arange(100, 109))
+    rms = np.sqrt(np.mean(K * K, axis=-1))
+    # the fp64 head norm misses 1 only by the eps inside the root: rms = r / sqrt(r^2 + eps)
+    kv = (W["w_kv"] @ (W["w_fc"] @ x.T)).T.reshape(9, dims.n_layers, 2, dims.n_kv_heads, dims.head_dim)
+    r2 = np.mean(kv[:, :, 0] ** 2, axis=-1).transpose(1, 0, 2)
+    assert np.allclose(rms, np.sqrt(r2 / (r2 + dims.rms_eps)), rtol=1e-12)
+    # values are untouched by QK-norm
+    _, V0 = oracle.inject(replace(dims, qk_norm=False), W, x, np.arange(100, 109))
+    assert np.array_equal(V, V0)
+    # query and key scaled by any positive factor give the same normalised head (up to eps)
+    Wq = dict(W)
+    Wq["w_kv"] = W["w_kv"] * 4.0
+    K4, _ = oracle.inject(dims, Wq, x, np.arange(100, 109))
+    assert np.allclose(K4, K, rtol=1e-6, atol=1e-9)
 
 
 def test_incremental_injection_equals_one_shot():
@@ -87,10 +119,12 @@ def test_attention_closed_forms():
     assert np.allclose(oracle.attention_group(q, keys[perm], vals[perm], 0.25), o, rtol=1e-13)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
-def test_forward_matches_brute(dtype):
-    dims = replace(TINY, dtype=dtype)
+@pytest.mark.parametrize("dtype,qk", [("bf16", False), ("fp32", False), ("bf16", True), ("fp32", True)])
+def test_forward_matches_brute(dtype, qk):
+    dims = replace(TINY, dtype=dtype, qk_norm=qk)
     W = np_weights(dims, 21, std=0.3)
+    if qk:
+        W = with_qk_gains(dims, W, 121)
     ctx = [0, 5, 11]
     pools = [rand_pool(dims, T, 30 + T, scale=2.0) for T in ctx]
     rng = np.random.default_rng(22)
