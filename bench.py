@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="turn rocprofv3 csv output into profiles/ summaries and exit")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--batch1", type=int, default=1,
+                    help="also time the draft call of the Qwen3-4B-shaped batch-1 block-8 workload")
     ap.add_argument("--ceilings", type=int, default=1,
                     help="measure the vendor GEMM rate and a device copy's HBM rate on this GPU, and price "
                          "the draft's executed work against them")
@@ -442,10 +444,52 @@ def main():
         torch.cuda.synchronize()
         res["qk_norm"] = {"draft_ms": round(e0.elapsed_time(e1) / nd, 4),
                           "note": "same batch and pool with per-head RMSNorm of queries and keys (query prep)"}
+    if a.batch1 and a.workload != "qwen3_4b_shape_b8":
+        res["batch1_block8"] = batch1_latency(Bn, nd)
     if a.cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(dims, W, wl, B, S, int(ctx_before[0]))
     res["setup_s"] = round(setup_s, 1)
     print(json.dumps(res))
+
+
+def batch1_latency(Bn, nd):
+    """Draft-call latency of the Qwen3-4B-shaped workload (one sequence, block 8, two denoise
+    steps, context 2048) on its own weights and pool, with the roofline of that call."""
+    import torch
+    from block_diffusion_drafter_injection_amd import synth
+    wl = synth.WORKLOADS["qwen3_4b_shape_b8"]
+    dims, B, S, dev = wl.dims, wl.block_size, wl.n_steps, "cuda"
+    ctx = int(synth.context_lengths(wl)[0])
+    W = synth.make_weights(dims, wl.seed, dev)
+    cfg, w = Bn.make_config(dims), Bn.Weights(W)
+    n_pages = (ctx + B + 15) // 16
+    table = torch.arange(n_pages, dtype=torch.int32, device=dev).view(1, -1)
+    pool = torch.zeros(Bn.pool_elems(dims, n_pages), dtype=dims.torch_dtype, device=dev)
+    ws_bytes = Bn.dflash_workspace_size(cfg, 1, B, ctx, ctx)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    hid = synth.make_hiddens(dims, ctx, wl.seed * 1000, dev)
+    Bn.dflash_inject_kv(cfg, w, hid, torch.zeros(ctx, dtype=torch.int32, device=dev),
+                        torch.arange(ctx, dtype=torch.int32, device=dev), ctx, pool, n_pages, table, 1, n_pages, ws,
+                        ws_bytes)
+    ctx_dev = torch.tensor([ctx], dtype=torch.int32, device=dev)
+    tok = torch.empty(1, B, dtype=torch.int32, device=dev)
+    for _ in range(3):
+        Bn.dflash_draft_block(cfg, w, pool, n_pages, table, n_pages, ctx_dev, ctx, 1, B, S, 0.0, 0, tok, None, None,
+                              ws, ws_bytes)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(nd * 4):
+        Bn.dflash_draft_block(cfg, w, pool, n_pages, table, n_pages, ctx_dev, ctx, 1, B, S, 0.0, 0, tok, None, None,
+                              ws, ws_bytes)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / (nd * 4)
+    t_roof = draft_roofline_ms(dims, 1, B, S, [ctx])
+    del W, w, pool, ws, hid
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "batch": 1, "block": B, "ctx": ctx, "draft_ms": round(ms, 4),
+            "drafted_tok_s": round(B / (ms / 1e3), 1), "t_roof_ms": round(t_roof, 4), "frac": round(t_roof / ms, 4),
+            "note": "weight streaming bound (M = 8 rows); the call is a chain of about a hundred small kernels"}
 
 
 def device_loop(a, Bn, cfg, w, dims, bt, B, S, pool, n_pages, table, pages_per, max_ctx, ctx_dev, acc, tok, outt,
@@ -559,7 +603,7 @@ def summarize(trace_dir, fetch_dir, write_dir):
     lines = [f"# rocprofv3 kernel statistics, {wl_name}", "",
              "Command (run from the repository root, output csv):", "",
              "    rocprofv3 --kernel-trace --stats --output-format csv -d <TRACE_DIR> -o run -- "
-             "python bench.py --steps 5 --warmup 2 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0", "",
+             "python bench.py --steps 5 --warmup 2 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0", "",
              f"Kernel sources hash: {h}", "",
              "| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:20]:
@@ -572,9 +616,9 @@ def summarize(trace_dir, fetch_dir, write_dir):
     tl = [f"# HBM traffic per launch, {wl_name}", "",
           "Commands (repository root, csv output):", "",
           "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -o p -- "
-          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --copy-calibration 1",
+          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0 --copy-calibration 1",
           "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -o p -- "
-          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --copy-calibration 1",
+          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0 --copy-calibration 1",
           "    python bench.py --summarize <TRACE_DIR> <FETCH_DIR> <WRITE_DIR>", "",
           f"Calibration: a {COPY_BYTES >> 20} MiB device copy (`{big[0][:60]}`) reads FETCH_SIZE = "
           f"{big[1]:.0f} KiB -> fetch scale {fetch_scale:.4f}; WRITE_SIZE scale "

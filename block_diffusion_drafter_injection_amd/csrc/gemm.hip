@@ -706,6 +706,98 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_fl_kernel(ActIn a, BRo
   }
 }
 
+// ---------------------------------------------------------------------------
+// GEMM for at most 16 rows (one or two sequences' blocks).  Each weight is used
+// by a single MFMA fragment, so nothing is staged in LDS: every lane loads its
+// 16-byte weight and activation operand fragments straight from global memory
+// into registers (the activation rows, a few KiB, stay in L1/L2), U k-steps at
+// a time so many loads are in flight per wave.  Eight waves of 16 columns make
+// a 128-column tile; the K range is split into ksplit parts (summed later in
+// split order), and with one part the tile goes through the usual epilogues.
+constexpr int kSkinnyBN = 128;
+
+template <int NP, int KIND>
+__global__ __launch_bounds__(512) void gemm_skinny_kernel(ActIn a, BRows<bf16_t> b, int M, int N, int K,
+                                                          int ksplit, float* part, EpiParams e) {
+  constexpr int BN = kSkinnyBN, LDC = BN + 4, U = 8;
+  // activation fragments of one batch, in fragment order [plane][step][lane] (16 B each),
+  // double-buffered; each of the NP * U fragments is one 1 KiB direct load
+  constexpr int AFRAG = NP * U, ABYTES = AFRAG * 1024;
+  static_assert(AFRAG % 8 == 0, "fragments per wave");
+  __shared__ __attribute__((aligned(1024))) unsigned char abuf[2 * ABYTES];
+  __shared__ __attribute__((aligned(16))) float Cs[16 * LDC];
+  const int ntn = (N + BN - 1) / BN;
+  const int tn = blockIdx.x % ntn, ks = blockIdx.x / ntn;
+  if (ks >= ksplit) return;
+  const int n0 = tn * BN;
+  const int nkt = K / 32;
+  const int kt0 = (int)((long long)ks * nkt / ksplit), kt1 = (int)((long long)(ks + 1) * nkt / ksplit);
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  const int lr = lane & 15, lq = lane >> 4;
+  // weight row n of this lane (clamped; columns past N are never stored)
+  const bf16_t* brow = b.row(min(n0 + wid * 16 + lr, N - 1), BN) + 8 * lq;
+  // activation fragments this wave copies: f = wid * (AFRAG / 8) + t, plane f / U,
+  // step f % U, from row lr (clamped; rows past M are never stored)
+  const int ar = min(lr, M - 1);
+  const bf16_t* asrc[AFRAG / 8];
+  int astep[AFRAG / 8];
+#pragma unroll
+  for (int t = 0; t < AFRAG / 8; ++t) {
+    const int f = wid * (AFRAG / 8) + t, p = f / U;
+    asrc[t] = (const bf16_t*)(p == 0 ? a.p0 : a.p1) + (size_t)ar * a.ld + 8 * lq;
+    astep[t] = f - p * U;
+  }
+  const uint32_t abase = (uint32_t)(size_t)abuf;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  int buf = 0;
+  for (int kt = kt0; kt < kt1; kt += U, buf ^= 1) {
+    // a batch of U steps; steps past the range read the last step again and
+    // contribute an exact zero (their activation fragment is zeroed)
+    bf16x8 bf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) bf[u] = as_bf16x8(*(const u32x4*)(brow + min(kt + u, kt1 - 1) * 32));
+#pragma unroll
+    for (int t = 0; t < AFRAG / 8; ++t) {
+      const int k = min(kt + astep[t], kt1 - 1);
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(asrc[t] + k * 32),
+          (__attribute__((address_space(3))) void*)(size_t)(abase + buf * ABYTES +
+                                                            (wid * (AFRAG / 8) + t) * 1024),
+          16, 0, 0);
+    }
+    wait_vmcnt<0>();
+    // the batch's activation fragments are in LDS for every wave; buffer buf was
+    // last read in the batch before the previous one, finished before that barrier
+    stage_barrier();
+    const unsigned char* ab = abuf + buf * ABYTES + lane * 16;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      bf16x8 af[NP];
+#pragma unroll
+      for (int p = 0; p < NP; ++p) af[p] = as_bf16x8(*(const u32x4*)(ab + (p * U + u) * 1024));
+      if (kt + u >= kt1) {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) af[p] = as_bf16x8(u32x4{0u, 0u, 0u, 0u});
+      }
+#pragma unroll
+      for (int p = 0; p < NP; ++p) acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[p], bf[u], acc, 0, 0, 0);
+    }
+  }
+  // lane (lq, lr) holds rows 4 lq + q of column 16 wid + lr
+#pragma unroll
+  for (int q = 0; q < 4; ++q) Cs[(4 * lq + q) * LDC + wid * 16 + lr] = acc[q];
+  __syncthreads();
+  if (ksplit > 1) {
+    float* dst = part + (size_t)ks * M * N;
+    for (int idx = threadIdx.x; idx < 16 * (BN / 4); idx += 512) {
+      const int r = idx / (BN / 4), c = (idx - r * (BN / 4)) * 4;
+      if (r < M && n0 + c < N) *(float4*)(dst + (size_t)r * N + n0 + c) = *(const float4*)(Cs + r * LDC + c);
+    }
+    return;
+  }
+  run_epilogue<KIND, 16, BN, 512, bf16_t>(Cs, LDC, 0, n0, M, N, e);
+}
+
 // Sum of the split-K partials of RB rows x BN columns (a row slice of one GEMM
 // tile: every epilogue is row-independent), in split order, then the epilogue.
 template <int RB, int BN, int KIND, typename TP>
@@ -817,6 +909,9 @@ int gemm_bn(int wdtype, int K) { return wdtype && K % 32 == 0 && tile_bn(DFLASH_
 // Tile configuration and K split of one GEMM (the table above).  A split is
 // used only when the tiles alone leave CUs idle; with fixed_split the split
 // depends on N and K only (injection must give the same bits for any M).
+#ifndef DFLASH_SKINNY
+#define DFLASH_SKINNY 1
+#endif
 #ifndef DFLASH_KS_TARGET
 #define DFLASH_KS_TARGET 256
 #endif
@@ -834,6 +929,15 @@ GemmPlan gemm_plan(int wdtype, int a_mode, int M, int N, int K, int kind, bool f
     if (cfg >= 10 && K % 64 != 0) cfg = 2;
     // SwiGLU tiles hold BN/2 gate and BN/2 up columns of the same rows
     if (kind == EPI_SWIGLU && (N / 2) % (tile_bn(cfg) / 2) != 0) cfg = (N / 2) % 128 == 0 && K % 64 == 0 ? 12 : 2;
+  }
+  // at most 16 rows: weights streamed straight into registers (gemm_skinny_kernel);
+  // the K split gives each wave about two batches of eight 32-deep steps (at most
+  // eight parts, so the consumer folds few partials) and depends on K only
+  if (!fixed_split && M <= 16 && K % 32 == 0 && kind != EPI_KVSCATTER && DFLASH_SKINNY) {
+    p.cfg = 20;
+    const int nkt = K / 32;
+    p.ksplit = kind == EPI_LMHEAD ? 1 : std::max(1, std::min({(nkt + 15) / 16, 8, nkt}));
+    return p;
   }
   p.cfg = cfg;
   if (cfg == 2) {
@@ -905,9 +1009,23 @@ static hipError_t go_fl(const GemmArgs& g, int ksplit, hipStream_t s) {
 }
 
 template <int NP, int KIND>
+static hipError_t go_skinny(const GemmArgs& g, int ksplit, hipStream_t s) {
+  const int ntn = (g.N + kSkinnyBN - 1) / kSkinnyBN;
+  BRows<bf16_t> b{(const bf16_t*)g.b.b0, (const bf16_t*)g.b.b1, g.b.ldb, g.b.split, g.b.mode};
+  hipLaunchKernelGGL((gemm_skinny_kernel<NP, KIND>), dim3(ntn * ksplit), dim3(512), 0, s, g.a, b, g.M, g.N, g.K,
+                     ksplit, g.part, g.e);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || ksplit == 1 || (g.defer_reduce && (KIND == EPI_ADD || KIND == EPI_STORE))) return err;
+  hipLaunchKernelGGL((splitk_reduce_kernel<16, kSkinnyBN, KIND, bf16_t>), dim3((g.M + 15) / 16 * ntn), dim3(256), 0,
+                     s, g.part, ksplit, g.M, g.N, g.e);
+  return hipGetLastError();
+}
+
+template <int NP, int KIND>
 static hipError_t go_bf16(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
   constexpr bool scatter = KIND == EPI_KVSCATTER;
   switch (p.cfg) {
+    case 20: if constexpr (!scatter) return go_skinny<NP, KIND>(g, p.ksplit, s); break;
     case 2: return go_dma<NP, KIND>(g, p.ksplit, s);
     case 10: if constexpr (!scatter) return go_fl<128, 384, 2, 4, NP, KIND>(g, p.ksplit, s); break;
     case 11: if constexpr (NP == 1 && !scatter) return go_fl<256, 256, 4, 2, 1, KIND>(g, p.ksplit, s); break;
