@@ -47,7 +47,8 @@ class dflash_weights(ctypes.Structure):
 
 _lib = None
 EXPORTS = ["dflash_workspace_size", "dflash_inject_kv", "dflash_draft_block", "dflash_verify_workspace_size",
-           "dflash_verify_block", "dflash_advance_context", "dflash_adaptive_block_size", "dflash_status_string",
+           "dflash_verify_block", "dflash_advance_context", "dflash_adaptive_block_size", "dflash_target_forward",
+           "dflash_status_string",
            "dflash_prof_select", "dflash_prof_collect"]
 
 
@@ -74,6 +75,9 @@ def lib():
     L.dflash_verify_block.restype = i32
     L.dflash_advance_context.argtypes = [i32, i32, vp, vp, vp, vp, vp]
     L.dflash_advance_context.restype = i32
+    L.dflash_target_forward.argtypes = [cfgp, wp, vp, i32, vp, i32, vp, i32, i32, i32, vp,
+                                        ctypes.POINTER(i32), i32, vp, vp, vp, sz, vp]
+    L.dflash_target_forward.restype = i32
     ip, fp = ctypes.POINTER(i32), ctypes.POINTER(f32)
     L.dflash_adaptive_block_size.argtypes = [ip, ip, i32, ip, fp, i32, f32, f32, fp]
     L.dflash_adaptive_block_size.restype = i32
@@ -173,6 +177,16 @@ def dflash_advance_context(batch, block_size, accept_len, ctx_len, tok_seq, tok_
     code = lib().dflash_advance_context(batch, block_size, _ptr(accept_len), _ptr(ctx_len), _ptr(tok_seq),
                                         _ptr(tok_pos), _stream(stream))
     _check("dflash_advance_context", code)
+
+
+def dflash_target_forward(cfg, weights, kv_pool, n_pages, block_table, max_pages, ctx_len, max_ctx_len, batch,
+                          n_tok, tokens, capture_layers, out_logits, out_hidden, workspace, ws_bytes, stream=None):
+    caps = (ctypes.c_int32 * max(len(capture_layers), 1))(*[int(x) for x in capture_layers])
+    code = lib().dflash_target_forward(ctypes.byref(cfg), ctypes.byref(weights.c), _ptr(kv_pool), n_pages,
+                                       _ptr(block_table), max_pages, _ptr(ctx_len), max_ctx_len, batch, n_tok,
+                                       _ptr(tokens), caps, len(capture_layers), _ptr(out_logits), _ptr(out_hidden),
+                                       _ptr(workspace), ws_bytes, _stream(stream))
+    _check("dflash_target_forward", code)
 
 
 def dflash_adaptive_block_size(accept_len, block_of, cand_block, step_time, prior_a=1.0, prior_b=1.0):

@@ -326,6 +326,119 @@ dflash_status dflash_inject_kv(const dflash_config* cfg, const dflash_weights* w
   return DFLASH_OK;
 }
 
+// Activation buffers of one forward (all in the workspace).
+struct FwdBufs {
+  float* h;      // residual stream [M, H] fp32
+  ActOut u, o, act;
+  float* qkv;
+  float* gpart;  // split-K partials
+};
+
+// Every layer of the model over the rows h [M, H] (M = batch * B tokens at
+// positions ctx_len[b] + i): RMSNorm, q/k/v, attention of the block over the
+// context pool plus the block keys (causal or not, ap.causal), O + residual,
+// RMSNorm, SwiGLU, down + residual.  pending_ks returns the K split of the
+// last down projection, whose partials the caller's final norm folds in.
+// append_pool: also write each layer's block K/V into that pool (bf16, head_dim
+// 128).  caps: per layer, where to store that layer's output (null p0: not
+// stored); the last layer's output is stored by the caller's final norm.
+static dflash_status run_layers(const dflash_config* cfg, const dflash_weights* w, AttnParams& ap,
+                                const FwdBufs& fb, int M, int B, void* append_pool, const ActOut* caps,
+                                int& pending_ks, hipStream_t stream) {
+  const int bf = cfg->dtype == DFLASH_BF16;
+  const int H = cfg->hidden, I = cfg->intermediate, d = cfg->head_dim, nq = cfg->n_q_heads, nkv = cfg->n_kv_heads;
+  const int Nqkv = (nq + 2 * nkv) * d;
+  float* h = fb.h;
+  const ActOut u = fb.u, o = fb.o, act = fb.act;
+  float* qkv = fb.qkv;
+  float* gpart = fb.gpart;
+  pending_ks = 0;   // K splits of a down projection whose partials the next norm folds in
+  for (int l = 0; l < cfg->n_layers; ++l) {
+    // the previous layer's down projection left its K-split partials to this norm
+    // (and, when asked, stores that finished output of layer l-1)
+    const ActOut* cap = (caps && l > 0 && caps[l - 1].p0) ? &caps[l - 1] : nullptr;
+    HIP_TRY(launch_rmsnorm(h, w->attn_norm[l], u, M, H, cfg->rms_eps, nullptr, B, 0, nullptr, stream,
+                           pending_ks > 1 ? gpart : nullptr, pending_ks, 0, cap));
+    pending_ks = 0;
+    GemmArgs g{};
+    g.wdtype = bf;
+    g.a = act_in(u);
+    g.b = BRowsArgs{w->w_q[l], (const char*)w->w_kv + (size_t)l * 2 * nkv * d * H * (bf ? 2 : 4), H, nq * d, 1};
+    g.M = M;
+    g.N = Nqkv;
+    g.part = gpart;
+    g.K = H;
+    g.kind = EPI_STORE;
+    g.e.out = ActOut{qkv, nullptr, Nqkv, ACT_F32};
+    // the query prep (bf16 pools, head_dim 128) sums a K split itself
+    g.defer_reduce = bf && d == 128;
+    const int ks_qkv = g.defer_reduce ? gemm_ksplit(g) : 1;
+    ap.qkv_part = ks_qkv > 1 ? gpart : nullptr;
+    ap.qkv_ks = ks_qkv;
+    // QK-norm: the query prep applies it (bf16, head_dim 128); otherwise it runs in
+    // place on the finished q/k rows before the attention kernels read them
+    ap.q_gain = cfg->qk_norm ? w->q_norm[l] : nullptr;
+    ap.k_gain = cfg->qk_norm ? w->k_norm[l] : nullptr;
+    ap.rms_eps = cfg->rms_eps;
+    HIP_TRY(gemm(DFLASH_PROF_GEMM_QKV, g, stream));
+    if (cfg->qk_norm && !g.defer_reduce)
+      HIP_TRY(launch_qk_norm(qkv, M, nq, nkv, d, ap.q_gain, ap.k_gain, cfg->rms_eps, stream));
+
+    ap.layer = l;
+    HIP_TRY(launch_attention(ap, bf, stream, g_prof.cls == DFLASH_PROF_ATTN ? prof_attn : nullptr));
+    // target forward: this layer's block K/V (from the query prep) join the target's own cache
+    if (append_pool)
+      HIP_TRY(launch_kv_append(ap.kblk, ap.vblk, ap.ctx_len, ap.ctx_cap, append_pool, ap.n_pages, ap.block_table,
+                               ap.max_pages, ap.batch, B, nkv, d, cfg->n_layers, l, stream));
+    HIP_TRY(launch_attn_finish(ap, bf, o, stream));
+
+    GemmArgs go{};
+    go.wdtype = bf;
+    go.a = act_in(o);
+    go.b = BRowsArgs{w->w_o[l], nullptr, nq * d, 0, 0};
+    go.M = M;
+    go.N = H;
+    go.part = gpart;
+    go.K = nq * d;
+    go.kind = EPI_ADD;
+    go.e.resid = h;
+    go.e.ldr = H;
+    go.defer_reduce = true;   // folded into the MLP norm below
+    const int ks_o = gemm_ksplit(go);
+    HIP_TRY(gemm(DFLASH_PROF_GEMM_O, go, stream));
+
+    HIP_TRY(launch_rmsnorm(h, w->mlp_norm[l], u, M, H, cfg->rms_eps, nullptr, B, 0, nullptr, stream,
+                           ks_o > 1 ? gpart : nullptr, ks_o));
+    GemmArgs gu{};
+    gu.wdtype = bf;
+    gu.a = act_in(u);
+    gu.b = BRowsArgs{w->w_gate[l], w->w_up[l], H, 0, 2};
+    gu.M = M;
+    gu.N = 2 * I;
+    gu.part = gpart;
+    gu.K = H;
+    gu.kind = EPI_SWIGLU;
+    gu.e.out = act;
+    HIP_TRY(gemm(DFLASH_PROF_GEMM_GATEUP, gu, stream));
+
+    GemmArgs gd{};
+    gd.wdtype = bf;
+    gd.a = act_in(act);
+    gd.b = BRowsArgs{w->w_down[l], nullptr, I, 0, 0};
+    gd.M = M;
+    gd.N = H;
+    gd.part = gpart;
+    gd.K = I;
+    gd.kind = EPI_ADD;
+    gd.e.resid = h;
+    gd.e.ldr = H;
+    gd.defer_reduce = true;   // folded into the next attention norm, or the final norm
+    pending_ks = gemm_ksplit(gd);
+    HIP_TRY(gemm(DFLASH_PROF_GEMM_DOWN, gd, stream));
+  }
+  return DFLASH_OK;
+}
+
 dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, const void* kv_pool,
                                  int32_t n_pages, const int32_t* block_table, int32_t max_pages,
                                  const int32_t* ctx_len, int32_t max_ctx_len, int32_t batch, int32_t block_size,
@@ -367,6 +480,7 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
   float* conf = (float*)at(workspace, L.conf);
   float2* cs = (float2*)at(workspace, L.cs);
   float* gpart = (float*)at(workspace, L.gemm_part);
+  const FwdBufs fb{h, u, o, act, qkv, gpart};
 
   AttnParams ap{};
   ap.pool = kv_pool;
@@ -404,84 +518,8 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
     const int n_open = B - done;
     const int last = s == S - 1;
     HIP_TRY(launch_embed(tau, w->embed, bf, cfg->vocab, h, M, H, stream));
-    int pending_ks = 0;   // K splits of a down projection whose partials the next norm folds in
-    for (int l = 0; l < cfg->n_layers; ++l) {
-      // the previous layer's down projection left its K-split partials to this norm
-      HIP_TRY(launch_rmsnorm(h, w->attn_norm[l], u, M, H, cfg->rms_eps, nullptr, B, 0, nullptr, stream,
-                             pending_ks > 1 ? gpart : nullptr, pending_ks));
-      pending_ks = 0;
-      GemmArgs g{};
-      g.wdtype = bf;
-      g.a = act_in(u);
-      g.b = BRowsArgs{w->w_q[l], (const char*)w->w_kv + (size_t)l * 2 * nkv * d * H * (bf ? 2 : 4), H, nq * d, 1};
-      g.M = M;
-      g.N = Nqkv;
-      g.part = gpart;
-      g.K = H;
-      g.kind = EPI_STORE;
-      g.e.out = ActOut{qkv, nullptr, Nqkv, ACT_F32};
-      // the query prep (bf16 pools, head_dim 128) sums a K split itself
-      g.defer_reduce = bf && d == 128;
-      const int ks_qkv = g.defer_reduce ? gemm_ksplit(g) : 1;
-      ap.qkv_part = ks_qkv > 1 ? gpart : nullptr;
-      ap.qkv_ks = ks_qkv;
-      // QK-norm: the query prep applies it (bf16, head_dim 128); otherwise it runs in
-      // place on the finished q/k rows before the attention kernels read them
-      ap.q_gain = cfg->qk_norm ? w->q_norm[l] : nullptr;
-      ap.k_gain = cfg->qk_norm ? w->k_norm[l] : nullptr;
-      ap.rms_eps = cfg->rms_eps;
-      HIP_TRY(gemm(DFLASH_PROF_GEMM_QKV, g, stream));
-      if (cfg->qk_norm && !g.defer_reduce)
-        HIP_TRY(launch_qk_norm(qkv, M, nq, nkv, d, ap.q_gain, ap.k_gain, cfg->rms_eps, stream));
-
-      ap.layer = l;
-      HIP_TRY(launch_attention(ap, bf, stream, g_prof.cls == DFLASH_PROF_ATTN ? prof_attn : nullptr));
-      HIP_TRY(launch_attn_finish(ap, bf, o, stream));
-
-      GemmArgs go{};
-      go.wdtype = bf;
-      go.a = act_in(o);
-      go.b = BRowsArgs{w->w_o[l], nullptr, nq * d, 0, 0};
-      go.M = M;
-      go.N = H;
-      go.part = gpart;
-      go.K = nq * d;
-      go.kind = EPI_ADD;
-      go.e.resid = h;
-      go.e.ldr = H;
-      go.defer_reduce = true;   // folded into the MLP norm below
-      const int ks_o = gemm_ksplit(go);
-      HIP_TRY(gemm(DFLASH_PROF_GEMM_O, go, stream));
-
-      HIP_TRY(launch_rmsnorm(h, w->mlp_norm[l], u, M, H, cfg->rms_eps, nullptr, B, 0, nullptr, stream,
-                             ks_o > 1 ? gpart : nullptr, ks_o));
-      GemmArgs gu{};
-      gu.wdtype = bf;
-      gu.a = act_in(u);
-      gu.b = BRowsArgs{w->w_gate[l], w->w_up[l], H, 0, 2};
-      gu.M = M;
-      gu.N = 2 * I;
-      gu.part = gpart;
-      gu.K = H;
-      gu.kind = EPI_SWIGLU;
-      gu.e.out = act;
-      HIP_TRY(gemm(DFLASH_PROF_GEMM_GATEUP, gu, stream));
-
-      GemmArgs gd{};
-      gd.wdtype = bf;
-      gd.a = act_in(act);
-      gd.b = BRowsArgs{w->w_down[l], nullptr, I, 0, 0};
-      gd.M = M;
-      gd.N = H;
-      gd.part = gpart;
-      gd.K = I;
-      gd.kind = EPI_ADD;
-      gd.e.resid = h;
-      gd.e.ldr = H;
-      gd.defer_reduce = true;   // folded into the next attention norm, or the final norm
-      pending_ks = gemm_ksplit(gd);
-      HIP_TRY(gemm(DFLASH_PROF_GEMM_DOWN, gd, stream));
-    }
+    int pending_ks = 0;   // K splits of the last down projection, folded by the final norm
+    HIP_TRY(run_layers(cfg, w, ap, fb, M, B, nullptr, nullptr, pending_ks, stream));
     const int Ms = batch * n_open;
     HIP_TRY(launch_rmsnorm(h, w->final_norm, y, Ms, H, cfg->rms_eps, committed, B, n_open, row_map, stream,
                            pending_ks > 1 ? gpart : nullptr, pending_ks, M));
@@ -509,6 +547,108 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
                           stream));
     if (!repredict) done += k_s;
   }
+  return DFLASH_OK;
+}
+
+dflash_status dflash_target_forward(const dflash_config* cfg, const dflash_weights* w, void* kv_pool,
+                                    int32_t n_pages, const int32_t* block_table, int32_t max_pages,
+                                    const int32_t* ctx_len, int32_t max_ctx_len, int32_t batch, int32_t n_tok,
+                                    const int32_t* tokens, const int32_t* capture_layers, int32_t n_capture,
+                                    float* out_logits, void* out_hidden, void* workspace, size_t ws_bytes,
+                                    hipStream_t stream) {
+  dflash_status st = check_cfg(cfg);
+  if (st != DFLASH_OK) return st;
+  if (cfg->dtype != DFLASH_BF16 || cfg->head_dim != 128) return DFLASH_ESHAPE;
+  if (!w || !w->w_kv || !w->embed || !w->final_norm || !w->lm_head) return DFLASH_EINVAL;
+  {
+    const void* const* arrs[7] = {(const void* const*)w->attn_norm, w->w_q, w->w_o,
+                                  (const void* const*)w->mlp_norm, w->w_gate, w->w_up, w->w_down};
+    for (auto a : arrs) {
+      if (!a) return DFLASH_EINVAL;
+      for (int l = 0; l < cfg->n_layers; ++l)
+        if (!a[l]) return DFLASH_EINVAL;
+    }
+    if (cfg->qk_norm) {
+      if (!w->q_norm || !w->k_norm) return DFLASH_EINVAL;
+      for (int l = 0; l < cfg->n_layers; ++l)
+        if (!w->q_norm[l] || !w->k_norm[l]) return DFLASH_EINVAL;
+    }
+  }
+  if (batch < 0 || n_pages < 0 || max_pages < 0 || max_ctx_len < 0 || n_capture < 0) return DFLASH_EINVAL;
+  if (n_tok < 1 || n_tok > 16) return DFLASH_ECAPACITY;
+  if (n_capture > 0 && (!capture_layers || !out_hidden)) return DFLASH_EINVAL;
+  std::vector<ActOut> caps(cfg->n_layers);
+  for (int f = 0; f < n_capture; ++f) {
+    const int l = capture_layers[f];
+    if (l < 0 || l >= cfg->n_layers || caps[l].p0) return DFLASH_EINVAL;   // out of range or repeated
+    caps[l] = ActOut{(bf16_t*)out_hidden + (size_t)f * cfg->hidden, nullptr, n_capture * cfg->hidden, ACT_BF16};
+  }
+  if (batch == 0) return DFLASH_OK;
+  if (!ctx_len || !tokens || !out_logits || !block_table || !kv_pool) return DFLASH_EINVAL;
+  if (!workspace || ((uintptr_t)workspace & 255)) return DFLASH_EWORKSPACE;
+  const int ctx_cap = n_pages > 0 ? (int)std::min<long long>(max_ctx_len, (long long)max_pages * 16) : 0;
+  const int B = n_tok, M = batch * B;
+  const DraftWS L = draft_layout(cfg, batch, B, ctx_cap);
+  if (L.total > ws_bytes) return DFLASH_EWORKSPACE;
+  const int H = cfg->hidden, d = cfg->head_dim, nq = cfg->n_q_heads, nkv = cfg->n_kv_heads;
+  float* h = (float*)at(workspace, L.h);
+  const FwdBufs fb{h, act_out(cfg, at(workspace, L.u_hi), at(workspace, L.u_lo), H),
+                   act_out(cfg, at(workspace, L.o_hi), at(workspace, L.o_lo), nq * d),
+                   act_out(cfg, at(workspace, L.act_hi), at(workspace, L.act_lo), cfg->intermediate),
+                   (float*)at(workspace, L.qkv), (float*)at(workspace, L.gemm_part)};
+  int* row_map = (int*)at(workspace, L.row_map);
+  float2* cs = (float2*)at(workspace, L.cs);
+
+  AttnParams ap{};
+  ap.pool = kv_pool;
+  ap.n_pages = n_pages;
+  ap.block_table = block_table;
+  ap.max_pages = max_pages;
+  ap.ctx_len = ctx_len;
+  ap.ctx_cap = ctx_cap;
+  ap.qkv = fb.qkv;
+  ap.cs = cs;
+  ap.batch = batch;
+  ap.B = B;
+  ap.nq = nq;
+  ap.nkv = nkv;
+  ap.d = d;
+  ap.n_layers = cfg->n_layers;
+  ap.scale = 1.0f / sqrtf((float)d);
+  ap.n_splits = L.ns;
+  ap.pps = L.pps;
+  ap.part_o = (float*)at(workspace, L.att_o);
+  ap.part_lse = (float*)at(workspace, L.att_lse);
+  ap.q_hi = (bf16_t*)at(workspace, L.q_hi);
+  ap.q_lo = (bf16_t*)at(workspace, L.q_lo);
+  ap.kblk = (float*)at(workspace, L.kblk);
+  ap.vblk = (float*)at(workspace, L.vblk);
+  ap.causal = 1;
+
+  HIP_TRY(launch_rope_table_block(ctx_len, ctx_cap, batch, B, d, (double)cfg->rope_base, cs, stream));
+  HIP_TRY(launch_embed(tokens, w->embed, 1, cfg->vocab, h, M, H, stream));
+  int pending_ks = 0;
+  HIP_TRY(run_layers(cfg, w, ap, fb, M, B, kv_pool, caps.data(), pending_ks, stream));
+  ActOut y{at(workspace, L.y), nullptr, H, ACT_BF16};
+  const ActOut* last_cap = caps[cfg->n_layers - 1].p0 ? &caps[cfg->n_layers - 1] : nullptr;
+  HIP_TRY(launch_rmsnorm(h, w->final_norm, y, M, H, cfg->rms_eps, nullptr, B, 0, row_map, stream,
+                         pending_ks > 1 ? fb.gpart : nullptr, pending_ks, M, last_cap));
+  GemmArgs gl{};
+  gl.wdtype = 1;
+  gl.a = ActIn{y.p0, nullptr, H, ACT_BF16};
+  gl.b = BRowsArgs{w->lm_head, nullptr, H, 0, 0};
+  gl.M = M;
+  gl.N = cfg->vocab;
+  gl.K = H;
+  gl.kind = EPI_LMHEAD;
+  gl.e.part_f = (float4*)at(workspace, L.part_f);
+  gl.e.part_i = (int*)at(workspace, L.part_i);
+  gl.e.ntiles = L.ntiles;
+  gl.e.row_map = row_map;
+  gl.e.logits = out_logits;
+  gl.e.block = B;
+  gl.e.temperature = 0.f;
+  HIP_TRY(gemm(DFLASH_PROF_LMHEAD, gl, stream));
   return DFLASH_OK;
 }
 

@@ -659,7 +659,7 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
     a += dpp_mov<0x4E>(a);
     a += dpp_mov<0x124>(a);   // row_ror:4
     a += dpp_mov<0x128>(a);   // row_ror:8
-    sc[k] = k < p.B ? a : -INFINITY;
+    sc[k] = (k < p.B && (!p.causal || k <= i)) ? a : -INFINITY;
     mx = fmaxf(mx, sc[k]);
   }
   float sum = 0.f;

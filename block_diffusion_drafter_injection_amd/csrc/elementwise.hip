@@ -60,7 +60,8 @@ constexpr int kRmsVec = 8;   // float4 per thread: rows up to 8192 wide
 
 __global__ __launch_bounds__(256) void rmsnorm_kernel(float* h, const float* gain, ActOut out, int H,
                                                       float eps, const int* committed, int B, int n_open,
-                                                      int* row_map, const float* part, int ksplit, int Mp) {
+                                                      int* row_map, const float* part, int ksplit, int Mp,
+                                                      ActOut cap) {
   __shared__ double red[4];
   __shared__ int src_s;
   const int r = blockIdx.x, tid = threadIdx.x;
@@ -77,6 +78,8 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* h, const float* gai
         }
       }
       row_map[r] = src;
+    } else if (row_map) {
+      row_map[r] = r;
     }
     src_s = src;
   }
@@ -102,6 +105,8 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* h, const float* gai
       v[k].x += a.x; v[k].y += a.y; v[k].z += a.z; v[k].w += a.w;
       *(float4*)(x + c) = v[k];
     }
+    // the finished residual row (a layer's output hidden state), in the storage type
+    if (cap.p0 && c < H) act_store4(cap, src_s, c, v[k]);
     ss += v[k].x * v[k].x + v[k].y * v[k].y + v[k].z * v[k].z + v[k].w * v[k].w;
   }
   double sd = ss;
@@ -274,10 +279,51 @@ hipError_t launch_embed(const int* tau, const void* embed, int wdtype, int vocab
 
 hipError_t launch_rmsnorm(float* h, const float* gain, ActOut out, int M, int H, float eps,
                           const int* committed, int B, int n_open, int* row_map, hipStream_t s,
-                          const float* part, int ksplit, int part_rows) {
+                          const float* part, int ksplit, int part_rows, const ActOut* capture) {
   if (M <= 0) return hipSuccess;
+  ActOut cap{};
+  if (capture) cap = *capture;
   hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(256), 0, s, h, gain, out, H, eps, committed, B, n_open,
-                     row_map, part, part ? ksplit : 0, part_rows > 0 ? part_rows : M);
+                     row_map, part, part ? ksplit : 0, part_rows > 0 ? part_rows : M, cap);
+  return hipGetLastError();
+}
+
+// Block K (rotated, fp32) and V of n_tok tokens per sequence, for one layer,
+// into the paged pool at positions ctx_len[b] + j: K chunk rows are
+// token-major [slot][d], V chunks dimension-major [d][slot].  Positions
+// outside the block table or unmapped pages are skipped.
+__global__ __launch_bounds__(256) void kv_append_kernel(const float* kblk, const float* vblk, const int* ctx_len,
+                                                        int ctx_cap, bf16_t* pool, int n_pages,
+                                                        const int* block_table, int max_pages, int batch, int n_tok,
+                                                        int nkv, int d, int n_layers, int layer) {
+  const size_t total = (size_t)batch * nkv * n_tok * d;
+  const size_t t = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= total) return;
+  const int e = (int)(t % d);
+  const size_t r = t / d;
+  const int j = (int)(r % n_tok);
+  const int m = (int)((r / n_tok) % nkv);
+  const int b = (int)(r / ((size_t)n_tok * nkv));
+  const int pos = min(max(ctx_len[b], 0), ctx_cap) + j;
+  const int lp = pos >> 4, slot = pos & 15;
+  if (lp >= max_pages) return;
+  const int phys = block_table[(size_t)b * max_pages + lp];
+  if (phys < 0 || phys >= n_pages) return;
+  const size_t src = (((size_t)b * nkv + m) * n_tok + j) * d + e;
+  const size_t chunk = (size_t)16 * d;
+  bf16_t* kc = pool + ((((size_t)phys * n_layers + layer) * 2 + 0) * nkv + m) * chunk;
+  bf16_t* vc = pool + ((((size_t)phys * n_layers + layer) * 2 + 1) * nkv + m) * chunk;
+  kc[slot * d + e] = f2bf(kblk[src]);
+  vc[e * 16 + slot] = f2bf(vblk[src]);
+}
+
+hipError_t launch_kv_append(const float* kblk, const float* vblk, const int* ctx_len, int ctx_cap, void* pool,
+                            int n_pages, const int* block_table, int max_pages, int batch, int n_tok, int nkv, int d,
+                            int n_layers, int layer, hipStream_t s) {
+  const size_t total = (size_t)batch * nkv * n_tok * d;
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(kv_append_kernel, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, s, kblk, vblk, ctx_len,
+                     ctx_cap, (bf16_t*)pool, n_pages, block_table, max_pages, batch, n_tok, nkv, d, n_layers, layer);
   return hipGetLastError();
 }
 

@@ -101,6 +101,7 @@ struct AttnParams {
   const float* q_gain;    // QK-norm gains of this layer [d], or null (no QK-norm)
   const float* k_gain;
   float rms_eps;
+  int causal;             // 1: block query i sees block keys j <= i only (target forward)
 };
 // Context splits -> partials (no launch when there is no context).
 hipError_t launch_attention(const AttnParams& p, int wdtype, hipStream_t s, void (*mark)(int, hipStream_t));
@@ -121,9 +122,18 @@ hipError_t launch_embed(const int* tau, const void* embed, int wdtype, int vocab
 // With part != null, h += sum over the ksplit partials [ksplit][part_rows][H]
 // (in split order, part_rows = M when 0) first, and the rows read are written
 // back to h.
+// With capture != null, the finished residual row (after the fold) is also
+// stored there in its storage type (a layer's output hidden state).  Without
+// committed, row_map (if given) receives the identity.
 hipError_t launch_rmsnorm(float* h, const float* gain, ActOut out, int M, int H, float eps,
                           const int* committed, int B, int n_open, int* row_map, hipStream_t s,
-                          const float* part = nullptr, int ksplit = 0, int part_rows = 0);
+                          const float* part = nullptr, int ksplit = 0, int part_rows = 0,
+                          const ActOut* capture = nullptr);
+// Rotated block K and block V of one layer (the query prep's kblk / vblk) into
+// the paged bf16 pool at positions ctx_len[b] + j.
+hipError_t launch_kv_append(const float* kblk, const float* vblk, const int* ctx_len, int ctx_cap, void* pool,
+                            int n_pages, const int* block_table, int max_pages, int batch, int n_tok, int nkv, int d,
+                            int n_layers, int layer, hipStream_t s);
 // Injection rows of the tokens a verification committed, and ctx_len += a + 1.
 hipError_t launch_advance_context(int batch, int B, const int* accept_len, int* ctx_len, int* tok_seq,
                                   int* tok_pos, hipStream_t s);

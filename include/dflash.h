@@ -190,6 +190,31 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
                                  float* out_conf, void* workspace, size_t ws_bytes,
                                  hipStream_t stream);
 
+/* Target-side verify forward ([Blog] 2. Flash Verification: the target checks
+ * the whole block in one forward; [Note] 三大核心创新 §1: the drafter is fed
+ * hidden states taken from several target layers).  The target model has the
+ * draft's layer structure (cfg and w describe the target; w_fc is unused).
+ * Sequence b runs n_tok tokens at positions ctx_len[b] .. ctx_len[b]+n_tok-1
+ * (the last committed token and the draft block): token j attends to the
+ * sequence's cached context (positions < ctx_len[b], read from kv_pool) and
+ * causally to tokens 0..j.  Outputs:
+ *   out_logits (device) [batch, n_tok, vocab] fp32: row j scores the token
+ *              at position ctx_len[b] + j + 1 (the rows dflash_verify_block takes)
+ *   out_hidden (device) [batch, n_tok, n_capture * hidden] bf16: the residual
+ *              stream after each layer capture_layers[f] (host, distinct, in
+ *              [0, n_layers)), slot f; the input of dflash_inject_kv
+ * and every layer's K (rotated) and V of the n_tok tokens are written into
+ * kv_pool at their positions (the target's own paged cache, the same layout
+ * as the draft's), so accepted tokens need no further pass.
+ * Limits: bf16 weights and head_dim 128; 1 <= n_tok <= 16; the workspace is
+ * dflash_workspace_size(cfg, max_batch, n_tok, 0, max_ctx_len). */
+dflash_status dflash_target_forward(const dflash_config* cfg, const dflash_weights* w, void* kv_pool,
+                                    int32_t n_pages, const int32_t* block_table, int32_t max_pages,
+                                    const int32_t* ctx_len, int32_t max_ctx_len, int32_t batch, int32_t n_tok,
+                                    const int32_t* tokens, const int32_t* capture_layers, int32_t n_capture,
+                                    float* out_logits, void* out_hidden, void* workspace, size_t ws_bytes,
+                                    hipStream_t stream);
+
 /* Device-side bookkeeping between two drafter steps, so that inject -> draft
  * -> verify -> advance repeats with no host round trip and can be captured
  * in a HIP graph (host work between steps leaves the GPU idle: [Deep] 3.2

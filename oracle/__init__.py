@@ -31,12 +31,13 @@ worked example.
 from .numerics import bf16_round, rope, rmsnorm, silu, log_softmax, logsumexp, split_hilo
 from .philox import philox4x32_10, gumbel_noise, uniform24
 from .model import (inject, forward_hidden, lm_head_logits, draft_block, attention_group,
-                    commit_counts)
+                    commit_counts, target_forward)
 from .verify import verify_greedy, verify_sampled, inverse_cdf
 
 __all__ = [
     "bf16_round", "rope", "rmsnorm", "silu", "log_softmax", "logsumexp", "split_hilo",
     "philox4x32_10", "gumbel_noise", "uniform24",
     "inject", "forward_hidden", "lm_head_logits", "draft_block", "attention_group", "commit_counts",
+    "target_forward",
     "verify_greedy", "verify_sampled", "inverse_cdf",
 ]

@@ -67,8 +67,9 @@ def inject(cfg, W, x_rows, positions):
     return K, V
 
 
-def forward(cfg, W, pools, ctx_len, tau):
-    """LM-head input y[b][i][c] of one draft forward, by explicit loops."""
+def forward(cfg, W, pools, ctx_len, tau, causal=False):
+    """LM-head input y[b][i][c] of one draft forward, by explicit loops (causal:
+    block token i sees block tokens 0..i only)."""
     H, L = cfg.hidden, cfg.n_layers
     nq, nkv, d = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim
     group = nq // nkv
@@ -93,8 +94,9 @@ def forward(cfg, W, pools, ctx_len, tau):
             for m in range(nkv):
                 for n in range(m * group, (m + 1) * group):
                     for i in range(B):
-                        keys = [[float(e) for e in Kc[l][t][m]] for t in range(T)] + [k[j][m] for j in range(B)]
-                        vals = [[float(e) for e in Vc[l][t][m]] for t in range(T)] + [v[j][m] for j in range(B)]
+                        seen = range(i + 1) if causal else range(B)
+                        keys = [[float(e) for e in Kc[l][t][m]] for t in range(T)] + [k[j][m] for j in seen]
+                        vals = [[float(e) for e in Vc[l][t][m]] for t in range(T)] + [v[j][m] for j in seen]
                         sc = [sum(q[i][n][e] * kk[e] for e in range(d)) / math.sqrt(d) for kk in keys]
                         mx = max(sc)
                         w = [math.exp(s - mx) for s in sc]

@@ -6,6 +6,7 @@ import pytest
 import torch
 
 import oracle
+from block_diffusion_drafter_injection_amd import binding as Bn
 from block_diffusion_drafter_injection_amd import synth
 from gpu_util import (Drafter, alloc_pool, compare_draft, compare_pool_entries, ctx_tensor, f64, np_weights,
                       pack_pool, page_plan, unpack_pool, verify)
@@ -211,3 +212,62 @@ def test_sampled_verify_matches_oracle(bt, B, V, T):
     assert np.array_equal(acc.cpu().numpy()[keep], acc_o[keep])
     assert np.array_equal(out.cpu().numpy()[keep], out_o[keep])
     print(f"sampled verify bt={bt} B={B}: mean accept {acc_o.mean():.2f}, excluded {int((~keep).sum())}")
+
+
+def test_target_forward_matches_oracle():
+    """Target-side verify forward (causal block over the target's own cache): logits, the
+    captured layer outputs and the K/V it appends to the pool, against the oracle; then
+    the same call on a prefix of the tokens reproduces the earlier rows (causality)."""
+    from dataclasses import replace
+    dims = replace(SMALL, n_layers=3)
+    W = synth.make_weights(dims, 95, "cuda")
+    ctx, n, caps = [37, 130, 0], 5, [0, 2]
+    bt = len(ctx)
+    table, n_pages = page_plan(ctx, n, seed=96)
+    tab = torch.from_numpy(table).cuda()
+    K, V = synth.make_pool_values(dims, sum(ctx), 97, "cuda")
+    pools, off = [], 0
+    pool = alloc_pool(dims, n_pages)
+    for b, c in enumerate(ctx):
+        Kb, Vb = K[:, off:off + c], V[:, off:off + c]
+        if c:
+            pack_pool(dims, pool, n_pages, table, b, Kb, Vb)
+        pools.append((f64(Kb), f64(Vb)))
+        off += c
+    g = torch.Generator(device="cuda").manual_seed(98)
+    tokens = torch.randint(0, dims.vocab, (bt, n), generator=g, device="cuda", dtype=torch.int32)
+    cfg, w = Bn.make_config(dims), Bn.Weights(W)
+    ws_bytes = Bn.dflash_workspace_size(cfg, bt, n, 0, max(ctx))
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+
+    def run(pool_, ntok):
+        z = torch.empty(bt, ntok, dims.vocab, dtype=torch.float32, device="cuda")
+        hid = torch.empty(bt, ntok, len(caps) * dims.hidden, dtype=torch.bfloat16, device="cuda")
+        Bn.dflash_target_forward(cfg, w, pool_, n_pages, tab, table.shape[1], ctx_tensor(ctx), max(ctx), bt, ntok,
+                                tokens[:, :ntok].contiguous(), caps, z, hid, ws, ws_bytes)
+        return z, hid
+
+    pool0 = pool.clone()
+    z, hid = run(pool, n)
+    torch.cuda.synchronize()
+    zo, ho, Ko, Vo = oracle.target_forward(dims, np_weights(W), pools, ctx, tokens.cpu().numpy(), capture_layers=caps)
+    zg = f64(z)
+    rel = np.max(np.abs(zg - zo), axis=-1) / np.max(np.abs(zo), axis=-1)
+    print(f"target forward: logits max rel err {rel.max():.2e}")
+    assert rel.max() <= 2e-2
+    # argmax rows (what greedy verification reads) agree away from near-ties
+    top2 = np.sort(zo, axis=-1)[..., -2:]
+    clear = (top2[..., 1] - top2[..., 0]) > 1e-3
+    assert np.array_equal(np.argmax(zg, -1)[clear], np.argmax(zo, -1)[clear])
+    compare_pool_entries(f64(hid), ho, dims.dtype, "captured hidden")
+    for b, c in enumerate(ctx):
+        Kg, Vg = unpack_pool(dims, pool, n_pages, table, b, c + n)
+        compare_pool_entries(Kg[:, c:], Ko[:, b], dims.dtype, f"appended K b={b}")
+        compare_pool_entries(Vg[:, c:], Vo[:, b], dims.dtype, f"appended V b={b}")
+        Kc, Vc = unpack_pool(dims, pool, n_pages, table, b, c)
+        assert np.array_equal(Kc, pools[b][0]) and np.array_equal(Vc, pools[b][1])   # context untouched
+    # causality: the first three tokens alone give the same first three rows
+    z3, hid3 = run(pool0, 3)
+    torch.cuda.synchronize()
+    rel3 = np.max(np.abs(f64(z3) - zg[:, :3]), axis=-1) / np.max(np.abs(zo[:, :3]), axis=-1)
+    assert rel3.max() <= 1e-3, rel3.max()

@@ -262,6 +262,50 @@ def test_repredict_special_cases():
         oracle.draft_block(TINY, W, pools, ctx, block_size=6, n_steps=1, schedule="other")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_target_forward_matches_brute(dtype):
+    dims = replace(TINY, dtype=dtype)
+    W = np_weights(dims, 31, std=0.3)
+    ctx = [0, 7]
+    pools = [rand_pool(dims, T, 90 + T, scale=2.0) for T in ctx]
+    tok = np.random.default_rng(32).integers(0, dims.vocab, size=(2, 5))
+    z, _, _, _ = oracle.target_forward(dims, W, pools, ctx, tok)
+    yb = np.array(brute.forward(dims, W, pools, ctx, tok.tolist(), causal=True))
+    zb = yb @ W["lm_head"].T
+    scale = np.max(np.abs(zb), axis=-1, keepdims=True)
+    # the LM-head input is rounded to bf16 on both sides; a rounding-boundary case may differ by one ulp
+    assert np.max(np.abs(z - zb) / scale) < (2e-2 if dtype == "bf16" else 1e-10)
+
+
+def test_target_forward_causality_and_closed_forms():
+    dims = replace(TINY, dtype="fp32")
+    W = np_weights(dims, 33, std=0.3)
+    ctx = [3, 12]
+    pools = [rand_pool(dims, T, 95 + T, scale=2.0) for T in ctx]
+    tok = np.random.default_rng(34).integers(0, dims.vocab, size=(2, 6))
+    L = dims.n_layers
+    z, hid, K, V = oracle.target_forward(dims, W, pools, ctx, tok, capture_layers=(0, L - 1))
+    # causal: dropping later tokens leaves the earlier rows unchanged
+    z3, hid3, K3, V3 = oracle.target_forward(dims, W, pools, ctx, tok[:, :3], capture_layers=(0, L - 1))
+    for a, b in ((z3, z[:, :3]), (hid3, hid[:, :3]), (K3, K[:, :, :3]), (V3, V[:, :, :3])):
+        assert np.allclose(a, b, rtol=1e-11, atol=1e-12)
+    # one token: causal and bidirectional attention coincide
+    y1 = oracle.forward_hidden(dims, W, pools, ctx, tok[:, :1])
+    assert np.allclose(z[:, :1], y1 @ W["lm_head"].T, rtol=1e-10, atol=1e-12)
+    # the last captured layer is the residual the final norm reads
+    H = dims.hidden
+    assert np.allclose(rmsnorm(hid[..., H:], W["final_norm"], dims.rms_eps) @ W["lm_head"].T, z, rtol=1e-9,
+                       atol=1e-10)
+    # layer-0 keys and values come straight from the embedding: RoPE(Wk RMSNorm(E[t])), Wv RMSNorm(E[t])
+    nkv, d = dims.n_kv_heads, dims.head_dim
+    u = rmsnorm(W["embed"][tok], W["attn_norm"][0], dims.rms_eps)
+    kv0 = u @ W["w_kv"][:2 * nkv * d].T
+    pos = np.array(ctx)[:, None] + np.arange(6)[None, :]
+    k0 = rope(kv0[..., :nkv * d].reshape(2, 6, nkv, d), pos[:, :, None], dims.rope_base)
+    assert np.allclose(K[0], k0, rtol=1e-11, atol=1e-12)
+    assert np.allclose(V[0], kv0[..., nkv * d:].reshape(2, 6, nkv, d), rtol=1e-11, atol=1e-12)
+
+
 def test_lm_head_ties_pick_lowest_index():
     W = np_weights(TINY, 27, std=0.3)
     W["lm_head"][9] = W["lm_head"][30]
