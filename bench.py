@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="turn rocprofv3 csv output into profiles/ summaries and exit")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--target", type=int, default=1,
+                    help="also time the target-side verify forward of a Qwen3-8B-shaped 36-layer target")
     ap.add_argument("--batch1", type=int, default=1,
                     help="also time the draft call of the Qwen3-4B-shaped batch-1 block-8 workload")
     ap.add_argument("--ceilings", type=int, default=1,
@@ -446,10 +448,64 @@ def main():
                           "note": "same batch and pool with per-head RMSNorm of queries and keys (query prep)"}
     if a.batch1 and a.workload != "qwen3_4b_shape_b8":
         res["batch1_block8"] = batch1_latency(Bn, nd)
+    if a.target:
+        res["target_forward"] = target_forward_bench(Bn, nd)
     if a.cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(dims, W, wl, B, S, int(ctx_before[0]))
     res["setup_s"] = round(setup_s, 1)
     print(json.dumps(res))
+
+
+def target_forward_bench(Bn, nd):
+    """dflash_target_forward of a random-init Qwen3-8B-shaped target (36 layers) over batch 32
+    x 17 tokens (the last committed token and a block of 16) at context 4096, capturing five
+    layers' outputs, with its roofline (weights once, every context K/V once per layer)."""
+    import torch
+    from dataclasses import replace
+    from block_diffusion_drafter_injection_amd import synth
+    dims = replace(synth.QWEN3_8B_SHAPE, n_layers=36)
+    bt, n, ctx, dev = 32, 17, 4096, "cuda"
+    caps = [1, 9, 17, 25, 33]
+    W = synth.make_weights(dims, 7, dev)
+    cfg, w = Bn.make_config(dims), Bn.Weights(W)
+    pages_per = (ctx + n + 15) // 16
+    n_pages = bt * pages_per
+    table = torch.arange(n_pages, dtype=torch.int32, device=dev).view(bt, pages_per)
+    pool = torch.randn(Bn.pool_elems(dims, n_pages), device=dev, dtype=torch.bfloat16).mul_(3.6)
+    ws_bytes = Bn.dflash_workspace_size(cfg, bt, n, 0, ctx)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ctx_dev = torch.full((bt,), ctx, dtype=torch.int32, device=dev)
+    tokens = torch.randint(0, dims.vocab, (bt, n), device=dev, dtype=torch.int32)
+    z = torch.empty(bt, n, dims.vocab, dtype=torch.float32, device=dev)
+    hid = torch.empty(bt, n, len(caps) * dims.hidden, dtype=torch.bfloat16, device=dev)
+
+    def call():
+        Bn.dflash_target_forward(cfg, w, pool, n_pages, table, pages_per, ctx_dev, ctx, bt, n, tokens, caps, z, hid,
+                                 ws, ws_bytes)
+    for _ in range(2):
+        call()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(nd):
+        call()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / nd
+    # roofline of one causal forward of bt*n rows (the LM head over every row)
+    H, L, I, V = dims.hidden, dims.n_layers, dims.intermediate, dims.vocab
+    nq, nkv, d = dims.n_q_heads, dims.n_kv_heads, dims.head_dim
+    M = bt * n
+    t = 0.0
+    for N, K in [((nq + 2 * nkv) * d, H), (H, nq * d), (2 * I, H), (H, I)]:
+        t += L * max(2.0 * M * N * K / PEAK_BF16, N * K * 2 / PEAK_HBM)
+    t += L * float(bt * ctx) * nkv * d * 2 * 2 / PEAK_HBM
+    t += max(2.0 * M * V * H / PEAK_BF16, V * H * 2 / PEAK_HBM)
+    del W, w, pool, ws, z, hid
+    torch.cuda.empty_cache()
+    return {"layers": L, "batch": bt, "n_tok": n, "ctx": ctx, "captured_layers": caps, "ms": round(ms, 4),
+            "t_roof_ms": round(t * 1e3, 4), "frac": round(t * 1e3 / ms, 4),
+            "note": "random-init Qwen3-8B-shaped target, causal over the 17 verified positions, full logits, "
+                    "K/V appended to its own cache"}
 
 
 def batch1_latency(Bn, nd):
@@ -603,7 +659,7 @@ def summarize(trace_dir, fetch_dir, write_dir):
     lines = [f"# rocprofv3 kernel statistics, {wl_name}", "",
              "Command (run from the repository root, output csv):", "",
              "    rocprofv3 --kernel-trace --stats --output-format csv -d <TRACE_DIR> -o run -- "
-             "python bench.py --steps 5 --warmup 2 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0", "",
+             "python bench.py --steps 5 --warmup 2 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0 --target 0", "",
              f"Kernel sources hash: {h}", "",
              "| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:20]:
@@ -616,9 +672,9 @@ def summarize(trace_dir, fetch_dir, write_dir):
     tl = [f"# HBM traffic per launch, {wl_name}", "",
           "Commands (repository root, csv output):", "",
           "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -o p -- "
-          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0 --copy-calibration 1",
+          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0 --target 0 --copy-calibration 1",
           "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -o p -- "
-          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0 --copy-calibration 1",
+          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0 --target 0 --copy-calibration 1",
           "    python bench.py --summarize <TRACE_DIR> <FETCH_DIR> <WRITE_DIR>", "",
           f"Calibration: a {COPY_BYTES >> 20} MiB device copy (`{big[0][:60]}`) reads FETCH_SIZE = "
           f"{big[1]:.0f} KiB -> fetch scale {fetch_scale:.4f}; WRITE_SIZE scale "

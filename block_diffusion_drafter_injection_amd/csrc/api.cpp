@@ -252,7 +252,7 @@ const char* dflash_status_string(dflash_status s) {
 
 size_t dflash_workspace_size(const dflash_config* cfg, int32_t max_batch, int32_t block_size,
                              int32_t max_inject_tokens, int32_t max_ctx_len) {
-  if (check_cfg(cfg) != DFLASH_OK || max_batch < 0 || block_size < 1 || block_size > 16 || max_inject_tokens < 0 ||
+  if (check_cfg(cfg) != DFLASH_OK || max_batch < 0 || block_size < 1 || block_size > 32 || max_inject_tokens < 0 ||
       max_ctx_len < 0)
     return 0;
   size_t need = 256;
@@ -575,7 +575,7 @@ dflash_status dflash_target_forward(const dflash_config* cfg, const dflash_weigh
     }
   }
   if (batch < 0 || n_pages < 0 || max_pages < 0 || max_ctx_len < 0 || n_capture < 0) return DFLASH_EINVAL;
-  if (n_tok < 1 || n_tok > 16) return DFLASH_ECAPACITY;
+  if (n_tok < 1 || n_tok > 32) return DFLASH_ECAPACITY;
   if (n_capture > 0 && (!capture_layers || !out_hidden)) return DFLASH_EINVAL;
   std::vector<ActOut> caps(cfg->n_layers);
   for (int f = 0; f < n_capture; ++f) {

@@ -565,12 +565,13 @@ __device__ __forceinline__ float dpp_mov(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
 }
 
-template <int D, bool PREP>
+template <int D, bool PREP, int NK = 16>
 __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut out) {
+  // NK: block keys held (16 for a draft block; 32 for a target forward of up to 32 tokens)
   constexpr int QR = 16, DPT = D / 16;   // 16 threads per query row, DPT dims each
   static_assert(DPT % 4 == 0, "dims per thread");
-  __shared__ __attribute__((aligned(16))) float kb[16][D];
-  __shared__ __attribute__((aligned(16))) float vb[16][D];
+  __shared__ __attribute__((aligned(16))) float kb[NK][D];
+  __shared__ __attribute__((aligned(16))) float vb[NK][D];
   const int g = p.nq / p.nkv, R = g * p.B, h = D / 2;
   const int qg = blockIdx.x, m = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
@@ -578,7 +579,7 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
   // Every global read is unconditional and four wide: block rows past B and
   // query rows past the group are clamped to a valid row (and masked or
   // dropped later), so all reads are in flight before the first use.
-  constexpr int KV4 = 16 * D / 4 / 256;   // float4 of K (and of V) per thread
+  constexpr int KV4 = NK * D / 4 / 256;   // float4 of K (and of V) per thread
 #pragma unroll
   for (int k = 0; k < KV4; ++k) {
     const int c4 = tid + 256 * k, jb = (4 * c4) / D, e = 4 * c4 - jb * D;
@@ -642,10 +643,10 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
   __syncthreads();
   // scores in base-2 units: partial dot over this thread's dims, summed over
   // the row's sixteen lanes (DPP: lane ^ 1, lane ^ 2, then rotations by 4, 8)
-  float sc[16];
+  float sc[NK];
   float mx = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
+  for (int k = 0; k < NK; ++k) {
     float a = 0.f;
 #pragma unroll
     for (int e = 0; e < DPT; e += 4) {
@@ -664,7 +665,7 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
   }
   float sum = 0.f;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
+  for (int k = 0; k < NK; ++k) {
     sc[k] = k < p.B ? __builtin_amdgcn_exp2f(sc[k] - mx) : 0.f;
     sum += sc[k];
   }
@@ -674,7 +675,7 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
 #pragma unroll
   for (int e = 0; e < DPT; ++e) ob[e] = 0.f;
 #pragma unroll
-  for (int k = 0; k < 16; ++k) {
+  for (int k = 0; k < NK; ++k) {
     const float w = sc[k] * rs;
 #pragma unroll
     for (int e = 0; e < DPT; e += 4) {
@@ -761,7 +762,10 @@ hipError_t launch_attn_finish(const AttnParams& p, int wdtype, ActOut out, hipSt
   const int R = (p.nq / p.nkv) * p.B;
   const dim3 grid((R + 15) / 16, p.nkv, p.batch);
   if (wdtype == 1 && p.d == 128)   // the query prep ran: prepared queries, block keys and values
-    hipLaunchKernelGGL((attn_finish_kernel<128, true>), grid, dim3(256), 0, s, p, out);
+    if (p.B > 16)
+      hipLaunchKernelGGL((attn_finish_kernel<128, true, 32>), grid, dim3(256), 0, s, p, out);
+    else
+      hipLaunchKernelGGL((attn_finish_kernel<128, true>), grid, dim3(256), 0, s, p, out);
   else if (p.d == 128)
     hipLaunchKernelGGL((attn_finish_kernel<128, false>), grid, dim3(256), 0, s, p, out);
   else

@@ -129,8 +129,9 @@ typedef struct {
   const float* const* k_norm;  /* per layer [head_dim] fp32 gains; required iff qk_norm */
 } dflash_weights;
 
-/* Bytes of workspace the three calls need for the given maxima (a call
- * checks its own arguments against ws_bytes).  max_inject_tokens bounds the
+/* Bytes of workspace the calls need for the given maxima (a call checks its
+ * own arguments against ws_bytes).  block_size is the draft block (at most
+ * 16) or a target forward's n_tok (at most 32).  max_inject_tokens bounds the
  * chunk size of one injection pass (larger injections are processed in
  * chunks of that size); max_ctx_len bounds the context any draft call
  * attends to.  Returns 0 if the configuration is invalid. */
@@ -206,7 +207,8 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
  * and every layer's K (rotated) and V of the n_tok tokens are written into
  * kv_pool at their positions (the target's own paged cache, the same layout
  * as the draft's), so accepted tokens need no further pass.
- * Limits: bf16 weights and head_dim 128; 1 <= n_tok <= 16; the workspace is
+ * Limits: bf16 weights and head_dim 128; 1 <= n_tok <= 32 (a block of up to 31
+ * and the token before it); the workspace is
  * dflash_workspace_size(cfg, max_batch, n_tok, 0, max_ctx_len). */
 dflash_status dflash_target_forward(const dflash_config* cfg, const dflash_weights* w, void* kv_pool,
                                     int32_t n_pages, const int32_t* block_table, int32_t max_pages,

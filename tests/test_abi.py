@@ -54,7 +54,8 @@ def test_workspace_size_rejects_bad_configs(L):
     assert B.dflash_workspace_size(_cfg(n_kv_heads=3), 4, 8, 64, 512) == 0
     assert B.dflash_workspace_size(_cfg(page_size=32), 4, 8, 64, 512) == 0
     assert B.dflash_workspace_size(_cfg(dtype=7), 4, 8, 64, 512) == 0
-    assert B.dflash_workspace_size(_cfg(), 4, 17, 64, 512) == 0
+    assert B.dflash_workspace_size(_cfg(), 4, 17, 64, 512) > 0    # a target forward of 17 tokens
+    assert B.dflash_workspace_size(_cfg(), 4, 33, 64, 512) == 0
     assert B.dflash_workspace_size(_cfg(hidden=500), 4, 8, 64, 512) == 0
     assert B.dflash_workspace_size(_cfg(hidden=8256), 4, 8, 64, 512) == 0   # rows wider than 8192
     assert B.dflash_workspace_size(_cfg(denoise_schedule=1), 4, 8, 64, 512) > 0

@@ -214,7 +214,8 @@ def test_sampled_verify_matches_oracle(bt, B, V, T):
     print(f"sampled verify bt={bt} B={B}: mean accept {acc_o.mean():.2f}, excluded {int((~keep).sum())}")
 
 
-def test_target_forward_matches_oracle():
+@pytest.mark.parametrize("n_tok_case", [0, 17])
+def test_target_forward_matches_oracle(n_tok_case):
     """Target-side verify forward (causal block over the target's own cache): logits, the
     captured layer outputs and the K/V it appends to the pool, against the oracle; then
     the same call on a prefix of the tokens reproduces the earlier rows (causality)."""
@@ -222,6 +223,8 @@ def test_target_forward_matches_oracle():
     dims = replace(SMALL, n_layers=3)
     W = synth.make_weights(dims, 95, "cuda")
     ctx, n, caps = [37, 130, 0], 5, [0, 2]
+    if n_tok_case:
+        n = n_tok_case
     bt = len(ctx)
     table, n_pages = page_plan(ctx, n, seed=96)
     tab = torch.from_numpy(table).cuda()
