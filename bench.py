@@ -374,6 +374,14 @@ def main():
         t_ex = draft_roofline_ms(dims, bt, B, S, ctx_before, peak=c["mfma_bf16_tflops"] * 1e12,
                                  hbm=c["hbm_copy_gbs"] * 1e9, executed=True)
         res["measured_ceilings"] = c
+        # the roofline kernel against what this GPU sustains on library work, with the
+        # hi/lo layer GEMMs' second MFMA counted as executed work
+        if roof["unit"] == "TFLOP/s":
+            ex = roof["achieved"] * (2.0 if cls in ("gemm_qkv", "gemm_o", "gemm_gateup", "gemm_down") else 1.0)
+            roof["executed"] = round(ex, 2)
+            roof["frac_executed_of_measured"] = round(ex / c["mfma_bf16_tflops"], 4)
+        else:
+            roof["frac_of_measured"] = round(roof["achieved"] / c["hbm_copy_gbs"], 4)
         res["draft_roofline"]["measured"] = {
             "t_roof_ms": round(t_ex, 4), "frac": round(t_ex / draft_ms, 4),
             "definition": "sum over the draft's kernels of max(executed flops (hi/lo counted twice) / the "
