@@ -110,6 +110,35 @@ def test_draft_argument_errors_return_before_launch(L):
     assert _draft(L, cfg, w2) == -1                             # a missing per-layer weight
 
 
+def _target(L, cfg, w, **kw):
+    args = dict(pool=8, n_pages=4, table=8, max_pages=4, ctx=8, max_ctx=16, batch=2, n=17, tokens=8, caps=[0],
+                logits=8, hidden=8, ws=256, ws_bytes=1 << 40)
+    args.update(kw)
+    caps = (ctypes.c_int32 * max(len(args["caps"]), 1))(*args["caps"])
+    return L.dflash_target_forward(ctypes.byref(cfg), ctypes.byref(w), args["pool"], args["n_pages"], args["table"],
+                                   args["max_pages"], args["ctx"], args["max_ctx"], args["batch"], args["n"],
+                                   args["tokens"], caps, len(args["caps"]), args["logits"], args["hidden"],
+                                   args["ws"], args["ws_bytes"], None)
+
+
+def test_target_forward_argument_errors_return_before_launch(L):
+    cfg = _cfg()
+    w, keep = _weights_stub(cfg.n_layers)
+    assert _target(L, cfg, w, n=0) == -4
+    assert _target(L, cfg, w, n=33) == -4
+    assert _target(L, _cfg(dtype=0), w) == -2                   # fp32 target: not supported
+    assert _target(L, _cfg(head_dim=64), w) == -2               # head_dim 64: not supported
+    assert _target(L, cfg, w, caps=[cfg.n_layers]) == -1       # capture layer out of range
+    assert _target(L, cfg, w, caps=[0, 0]) == -1               # repeated capture layer
+    assert _target(L, cfg, w, hidden=None) == -1               # captures without an output
+    assert _target(L, cfg, w, tokens=None) == -1
+    assert _target(L, cfg, w, logits=None) == -1
+    assert _target(L, cfg, w, ws=300) == -5
+    assert _target(L, cfg, w, ws_bytes=1024) == -5
+    assert _target(L, cfg, w, batch=0) == 0                     # nothing to do
+    assert _target(L, cfg, w, batch=0, caps=[]) == 0
+
+
 def test_verify_and_inject_argument_errors(L):
     f = L.dflash_verify_block
     assert f(2, 17, 100, 8, 8, 0.0, None, None, 8, 8, 256, 1 << 30, None) == -4
