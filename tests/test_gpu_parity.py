@@ -131,6 +131,7 @@ def test_draft_matches_oracle(name, ctx, B, S, T):
 
 @pytest.mark.parametrize("name,ctx,B,S,T", [
     ("tiny", [64, 5], 4, 2, 0.0),
+    ("small", [77], 8, 2, 0.0),           # one sequence: the skinny (at most 16 rows) GEMMs
     ("small", [0, 37, 300], 8, 2, 0.0),
     ("small", [130, 16], 16, 3, 0.0),
     ("small", [77, 8], 8, 2, 1.0),
@@ -146,6 +147,7 @@ def test_draft_repredict_matches_oracle(name, ctx, B, S, T):
 @pytest.mark.parametrize("name,ctx,B,S,d", [
     ("tiny", [64, 9], 4, 2, 64),          # fp32: in-place QK-norm, VALU attention
     ("small", [0, 37, 300], 8, 2, 128),   # bf16, head_dim 128: QK-norm in the query prep, MFMA attention
+    ("small", [150], 16, 2, 128),         # one sequence: skinny GEMMs feeding the query prep
     ("small", [130, 16], 16, 2, 64),      # bf16, head_dim 64: in-place QK-norm, VALU attention
 ])
 def test_draft_qk_norm_matches_oracle(name, ctx, B, S, d):
