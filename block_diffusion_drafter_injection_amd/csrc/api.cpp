@@ -71,7 +71,6 @@ dflash_status check_cfg(const dflash_config* c) {
   if (c->denoise_schedule != DFLASH_SCHEDULE_PROGRESSIVE && c->denoise_schedule != DFLASH_SCHEDULE_REPREDICT)
     return DFLASH_EINVAL;
   if (c->qk_norm != 0 && c->qk_norm != 1) return DFLASH_EINVAL;
-  if (c->qk_norm && c->n_layers > kMaxQkLayers) return DFLASH_ECAPACITY;
   if (!(c->rope_base > 0.f) || !(c->rms_eps >= 0.f)) return DFLASH_EINVAL;
   return DFLASH_OK;
 }
@@ -268,6 +267,8 @@ dflash_status dflash_inject_kv(const dflash_config* cfg, const dflash_weights* w
   dflash_status st = check_cfg(cfg);
   if (st != DFLASH_OK) return st;
   if ((st = check_weights(cfg, w, false)) != DFLASH_OK) return st;
+  // one injection launch carries every layer's QK-norm key gains
+  if (cfg->qk_norm && cfg->n_layers > kMaxQkLayers) return DFLASH_ECAPACITY;
   if (n_tok < 0 || n_pages < 0 || n_seqs < 0 || max_pages < 0) return DFLASH_EINVAL;
   if (n_tok == 0) return DFLASH_OK;
   if (!target_hidden || !tok_seq || !tok_pos || !kv_pool || !block_table) return DFLASH_EINVAL;

@@ -100,7 +100,8 @@ typedef struct {
   int32_t qk_norm;        /* 1: every query and key head is RMS-normalised over head_dim
                            * (gains q_norm / k_norm, epsilon rms_eps) before the rotary
                            * embedding, the injected context keys included (the Qwen3 layer);
-                           * 0: no QK-norm.  With 1, n_layers <= 16. */
+                           * 0: no QK-norm.  dflash_inject_kv supports QK-norm for at
+                           * most 16 layers (ECAPACITY beyond). */
 } dflash_config;
 
 /* Draft weights (all device pointers; per-layer entries are host arrays of

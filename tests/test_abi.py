@@ -137,6 +137,14 @@ def test_target_forward_argument_errors_return_before_launch(L):
     assert _target(L, cfg, w, ws_bytes=1024) == -5
     assert _target(L, cfg, w, batch=0) == 0                     # nothing to do
     assert _target(L, cfg, w, batch=0, caps=[]) == 0
+    # QK-norm targets are not limited to 16 layers (only injection is)
+    qk = _cfg(qk_norm=1, n_layers=36)
+    w36, keep36 = _weights_stub(36)
+    w36.q_norm = w36.w_q
+    w36.k_norm = w36.w_q
+    assert _target(L, qk, w36, batch=0) == 0
+    assert L.dflash_inject_kv(ctypes.byref(qk), ctypes.byref(w36), 8, 8, 8, 1, 8, 4, 8, 1, 4, 256, 1 << 40,
+                              None) == -4
 
 
 def test_verify_and_inject_argument_errors(L):

@@ -216,14 +216,16 @@ def test_sampled_verify_matches_oracle(bt, B, V, T):
     print(f"sampled verify bt={bt} B={B}: mean accept {acc_o.mean():.2f}, excluded {int((~keep).sum())}")
 
 
-@pytest.mark.parametrize("n_tok_case", [0, 17])
-def test_target_forward_matches_oracle(n_tok_case):
+@pytest.mark.parametrize("n_tok_case,qk", [(0, False), (17, False), (9, True)])
+def test_target_forward_matches_oracle(n_tok_case, qk):
     """Target-side verify forward (causal block over the target's own cache): logits, the
     captured layer outputs and the K/V it appends to the pool, against the oracle; then
     the same call on a prefix of the tokens reproduces the earlier rows (causality)."""
     from dataclasses import replace
     dims = replace(SMALL, n_layers=3)
     W = synth.make_weights(dims, 95, "cuda")
+    if qk:   # a Qwen3-style target: QK-norm with random gains
+        dims, W = _with_qk(dims, W, 99)
     ctx, n, caps = [37, 130, 0], 5, [0, 2]
     if n_tok_case:
         n = n_tok_case
