@@ -520,7 +520,10 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
     const int last = s == S - 1;
     HIP_TRY(launch_embed(tau, w->embed, bf, cfg->vocab, h, M, H, stream));
     int pending_ks = 0;   // K splits of the last down projection, folded by the final norm
-    HIP_TRY(run_layers(cfg, w, ap, fb, M, B, nullptr, nullptr, pending_ks, stream));
+    {
+      const dflash_status rs = run_layers(cfg, w, ap, fb, M, B, nullptr, nullptr, pending_ks, stream);
+      if (rs != DFLASH_OK) return rs;
+    }
     const int Ms = batch * n_open;
     HIP_TRY(launch_rmsnorm(h, w->final_norm, y, Ms, H, cfg->rms_eps, committed, B, n_open, row_map, stream,
                            pending_ks > 1 ? gpart : nullptr, pending_ks, M));
@@ -629,7 +632,10 @@ dflash_status dflash_target_forward(const dflash_config* cfg, const dflash_weigh
   HIP_TRY(launch_rope_table_block(ctx_len, ctx_cap, batch, B, d, (double)cfg->rope_base, cs, stream));
   HIP_TRY(launch_embed(tokens, w->embed, 1, cfg->vocab, h, M, H, stream));
   int pending_ks = 0;
-  HIP_TRY(run_layers(cfg, w, ap, fb, M, B, kv_pool, caps.data(), pending_ks, stream));
+  {
+    const dflash_status rs = run_layers(cfg, w, ap, fb, M, B, kv_pool, caps.data(), pending_ks, stream);
+    if (rs != DFLASH_OK) return rs;
+  }
   ActOut y{at(workspace, L.y), nullptr, H, ACT_BF16};
   const ActOut* last_cap = caps[cfg->n_layers - 1].p0 ? &caps[cfg->n_layers - 1] : nullptr;
   HIP_TRY(launch_rmsnorm(h, w->final_norm, y, M, H, cfg->rms_eps, nullptr, B, 0, row_map, stream,

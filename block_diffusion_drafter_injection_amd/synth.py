@@ -36,7 +36,6 @@ class ModelDims:
     rms_eps: float = 1e-6
     page_size: int = 16
     qk_norm: bool = False        # per-head RMSNorm of queries and keys before RoPE (Qwen3 layers)
-    act: str = "split"           # bf16 models: projection inputs as hi/lo pairs ('split') or rounded to bf16 ('bf16')
 
     @property
     def mask_token_id(self):

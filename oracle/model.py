@@ -37,14 +37,6 @@ What the pages fix, and the readings taken where they are silent:
 * Draft layer: RMSNorm, grouped-query attention (head n uses kv head
   n // (n_q/n_kv)), residual, RMSNorm, SwiGLU MLP, residual; final RMSNorm,
   LM head.  The mask token is id V-1 and argmax runs over the whole vocab.
-* GEMM activation operands (``cfg.act``, bf16 models only): the pages run
-  the drafter as a bf16 model and say nothing finer.  With act = 'bf16' the
-  input of every projection (the fused features entering the K/V
-  projection, the RMSNorm outputs entering q/k/v and gate/up, the attention
-  output entering the O projection and the SwiGLU output entering the down
-  projection) is rounded to bf16, as a bf16 model stores its activations;
-  products and sums stay exact.  With act = 'split' (the default) those
-  operands keep full precision.  The LM-head input is rounded in both.
 * QK-norm (optional, ``cfg.qk_norm``): the pages name the target family
   (Qwen3) but not the drafter's layer internals; the Qwen3 layer normalises
   every query and key head by RMSNorm over head_dim (gains q_norm[l] /
@@ -61,14 +53,6 @@ from .philox import gumbel_noise
 def _store(cfg, x):
     """Round to the storage type of the KV pool / LM-head input."""
     return bf16_round(x) if cfg.dtype == "bf16" else np.asarray(x, F64)
-
-
-def _act(cfg, x):
-    """A projection's activation operand: rounded to bf16 when the config
-    stores activations as bf16, else kept exact."""
-    if cfg.dtype == "bf16" and getattr(cfg, "act", "split") == "bf16":
-        return bf16_round(x)
-    return np.asarray(x, F64)
 
 
 def _lin(x, w):
@@ -89,7 +73,7 @@ def inject(cfg, W, x, pos):
     """
     L, nkv, d = cfg.n_layers, cfg.n_kv_heads, cfg.head_dim
     f = _lin(x, W["w_fc"])                       # fused context features [n, H]
-    kv = _lin(_act(cfg, f), W["w_kv"])           # all layers at once [n, L*2*nkv*d]
+    kv = _lin(f, W["w_kv"])                      # all layers at once [n, L*2*nkv*d]
     kv = kv.reshape(-1, L, 2, nkv, d)
     pos = np.asarray(pos)
     k = kv[:, :, 0]
@@ -147,7 +131,7 @@ def _forward(cfg, W, pools, ctx_len, tau, causal=False, capture=()):
     Kn = np.empty((L, bt, B, nkv, d), F64)
     Vn = np.empty((L, bt, B, nkv, d), F64)
     for l in range(L):
-        u = _act(cfg, rmsnorm(h, W["attn_norm"][l], cfg.rms_eps))
+        u = rmsnorm(h, W["attn_norm"][l], cfg.rms_eps)
         q = _lin(u, W["w_q"][l]).reshape(bt, B, nq, d)
         kvw = W["w_kv"][l * 2 * nkvd:(l + 1) * 2 * nkvd]
         kv = _lin(u, kvw)
@@ -175,10 +159,10 @@ def _forward(cfg, W, pools, ctx_len, tau, causal=False, capture=()):
                 vals = np.concatenate([Vc[l, :T, m], v[b, :, m]], axis=0)
                 qm = q[b, :, m * g:(m + 1) * g].reshape(B * g, d)
                 o[b, :, m * g:(m + 1) * g] = attention_group(qm, keys, vals, scale).reshape(B, g, d)
-        h = h + _lin(_act(cfg, o.reshape(bt, B, nq * d)), W["w_o"][l])
-        u = _act(cfg, rmsnorm(h, W["mlp_norm"][l], cfg.rms_eps))
+        h = h + _lin(o.reshape(bt, B, nq * d), W["w_o"][l])
+        u = rmsnorm(h, W["mlp_norm"][l], cfg.rms_eps)
         a = silu(_lin(u, W["w_gate"][l])) * _lin(u, W["w_up"][l])
-        h = h + _lin(_act(cfg, a), W["w_down"][l])
+        h = h + _lin(a, W["w_down"][l])
         if l in capture:
             outs[l] = h.copy()
     y = rmsnorm(h, W["final_norm"], cfg.rms_eps)

@@ -22,13 +22,6 @@ def _store(cfg, x):
     return _bf16(x) if cfg.dtype == "bf16" else x
 
 
-def _a(cfg, vec):
-    """A projection input as the config stores activations (bf16 or exact)."""
-    if cfg.dtype == "bf16" and getattr(cfg, "act", "split") == "bf16":
-        return [_bf16(v) for v in vec]
-    return vec
-
-
 def _rot(vec, p, base):
     d = len(vec)
     out = [0.0] * d
@@ -64,7 +57,7 @@ def inject(cfg, W, x_rows, positions):
     V = [[None] * len(x_rows) for _ in range(L)]
     for t, (x, p) in enumerate(zip(x_rows, positions)):
         f = _matvec(W["w_fc"], [float(v) for v in x])
-        kv = _matvec(W["w_kv"], _a(cfg, f))
+        kv = _matvec(W["w_kv"], f)
         for l in range(L):
             base = l * 2 * nkv * d
             K[l][t] = [[_store(cfg, v) for v in _rot(_kn(cfg, W, l, kv[base + m * d: base + (m + 1) * d]), p,
@@ -87,7 +80,7 @@ def forward(cfg, W, pools, ctx_len, tau, causal=False):
         Kc, Vc = pools[b]
         h = [[float(W["embed"][tok][c]) for c in range(H)] for tok in toks]
         for l in range(L):
-            u = [_a(cfg, _rms(h[i], W["attn_norm"][l], cfg.rms_eps)) for i in range(B)]
+            u = [_rms(h[i], W["attn_norm"][l], cfg.rms_eps) for i in range(B)]
             q, k, v = [], [], []
             for i in range(B):
                 p = T + i
@@ -111,14 +104,14 @@ def forward(cfg, W, pools, ctx_len, tau, causal=False):
                         o[i][n] = [sum(w[t] * vals[t][e] for t in range(len(keys))) / tot for e in range(d)]
             for i in range(B):
                 flat = [o[i][n][e] for n in range(nq) for e in range(d)]
-                ao = _matvec(W["w_o"][l], _a(cfg, flat))
+                ao = _matvec(W["w_o"][l], flat)
                 h[i] = [h[i][c] + ao[c] for c in range(H)]
             for i in range(B):
-                u2 = _a(cfg, _rms(h[i], W["mlp_norm"][l], cfg.rms_eps))
+                u2 = _rms(h[i], W["mlp_norm"][l], cfg.rms_eps)
                 gt = _matvec(W["w_gate"][l], u2)
                 up = _matvec(W["w_up"][l], u2)
                 a = [gt[r] / (1.0 + math.exp(-gt[r])) * up[r] for r in range(len(gt))]
-                dn = _matvec(W["w_down"][l], _a(cfg, a))
+                dn = _matvec(W["w_down"][l], a)
                 h[i] = [h[i][c] + dn[c] for c in range(H)]
         out.append([[_store(cfg, e) for e in _rms(h[i], W["final_norm"], cfg.rms_eps)] for i in range(B)])
     return out
