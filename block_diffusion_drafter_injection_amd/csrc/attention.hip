@@ -690,7 +690,14 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
   float mxl = blse;
 #pragma unroll
   for (int k = 0; k < NPF; ++k) mxl = fmaxf(mxl, pl[k]);
-  for (int sp = NPF; sp < p.n_splits; ++sp) mxl = fmaxf(mxl, p.part_lse[sp * Mq + qrow]);
+  // the remaining split maxima, eight loads in flight at a time
+  for (int s0 = NPF; s0 < p.n_splits; s0 += 8) {
+    float l8[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) l8[k] = s0 + k < p.n_splits ? p.part_lse[(s0 + k) * Mq + qrow] : -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) mxl = fmaxf(mxl, l8[k]);
+  }
   float tot = 0.f, acc[DPT];
 #pragma unroll
   for (int e = 0; e < DPT; ++e) acc[e] = 0.f;
@@ -708,19 +715,31 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
       acc[e + 3] = fmaf(w, v.w, acc[e + 3]);
     }
   }
-#pragma unroll 4
-  for (int sp = NPF; sp < p.n_splits; ++sp) {
-    const float l = p.part_lse[sp * Mq + qrow];
-    const float w = expf(l - mxl);
-    tot += w;
-    const float* src = p.part_o + (sp * Mq + qrow) * D + d0;
+  // the remaining splits in split order, four splits' loads in flight at a time; a
+  // split past the end reads as (lse -inf, o 0) and adds exactly nothing
+  for (int s0 = NPF; s0 < p.n_splits; s0 += 4) {
+    float l4[4];
+    float4 v4[4][DPT / 4];
 #pragma unroll
-    for (int e = 0; e < DPT; e += 4) {
-      const float4 v = *(const float4*)(src + e);
-      acc[e] = fmaf(w, v.x, acc[e]);
-      acc[e + 1] = fmaf(w, v.y, acc[e + 1]);
-      acc[e + 2] = fmaf(w, v.z, acc[e + 2]);
-      acc[e + 3] = fmaf(w, v.w, acc[e + 3]);
+    for (int k = 0; k < 4; ++k) {
+      const bool ok = s0 + k < p.n_splits;
+      l4[k] = ok ? p.part_lse[(s0 + k) * Mq + qrow] : -INFINITY;
+      const float* src = p.part_o + ((s0 + k) * Mq + qrow) * D + d0;
+#pragma unroll
+      for (int e = 0; e < DPT; e += 4) v4[k][e / 4] = ok ? *(const float4*)(src + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float w = expf(l4[k] - mxl);
+      tot += w;
+#pragma unroll
+      for (int e = 0; e < DPT; e += 4) {
+        const float4 v = v4[k][e / 4];
+        acc[e] = fmaf(w, v.x, acc[e]);
+        acc[e + 1] = fmaf(w, v.y, acc[e + 1]);
+        acc[e + 2] = fmaf(w, v.z, acc[e + 2]);
+        acc[e + 3] = fmaf(w, v.w, acc[e + 3]);
+      }
     }
   }
   {

@@ -56,13 +56,17 @@ __global__ void embed_kernel(const int* tau, const T* embed, int vocab, float* h
 // sequence) and row_map receives b*B + i for each.  With part != null the
 // source row first takes the sum of its K-split partials ([ksplit][Mp][H],
 // indexed by the source row), which is also written back to h.
-constexpr int kRmsVec = 8;   // float4 per thread: rows up to 8192 wide
+constexpr int kRmsMaxH = 8192;   // widest row
+constexpr int kRmsMaxSplit = 8;   // K-split partials folded with all loads in flight (more: one at a time)
 
-__global__ __launch_bounds__(256) void rmsnorm_kernel(float* h, const float* gain, ActOut out, int H,
+// NT threads per row: 256, or 1024 when there are few rows (more loads in flight per row).
+template <int NT>
+__global__ __launch_bounds__(NT) void rmsnorm_kernel(float* h, const float* gain, ActOut out, int H,
                                                       float eps, const int* committed, int B, int n_open,
                                                       int* row_map, const float* part, int ksplit, int Mp,
                                                       ActOut cap) {
-  __shared__ double red[4];
+  constexpr int kRmsVec = kRmsMaxH / (4 * NT);   // float4 per thread
+  __shared__ double red[NT / 64];
   __shared__ int src_s;
   const int r = blockIdx.x, tid = threadIdx.x;
   if (tid == 0) {
@@ -84,7 +88,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* h, const float* gai
     src_s = src;
   }
   __syncthreads();
-  // the row is read once into registers (H <= 256 * 4 * kRmsVec); squares are
+  // the row is read once into registers (H <= NT * 4 * kRmsVec); squares are
   // summed in fp32 per thread (at most 4 * kRmsVec terms) and in double across
   // threads
   float* x = h + (size_t)src_s * H;
@@ -92,15 +96,29 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* h, const float* gai
   float ss = 0.f;
 #pragma unroll
   for (int k = 0; k < kRmsVec; ++k) {
-    const int c = tid * 4 + 1024 * k;
+    const int c = tid * 4 + 4 * NT * k;
     v[k] = c < H ? *(const float4*)(x + c) : make_float4(0.f, 0.f, 0.f, 0.f);
     if (part && c < H) {
       // residual += sum of the split-K partials, in split order (the same sums
-      // the split-K reduce would form)
+      // the split-K reduce would form).  Up to kRmsMaxSplit partials are loaded
+      // before the first add, so their loads are in flight together.
+      const float* pp = part + (size_t)src_s * H + c;
+      const size_t stride = (size_t)Mp * H;
       float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int sp = 0; sp < ksplit; ++sp) {
-        const float4 pv = *(const float4*)(part + ((size_t)sp * Mp + src_s) * H + c);
-        a.x += pv.x; a.y += pv.y; a.z += pv.z; a.w += pv.w;
+      if (ksplit <= kRmsMaxSplit) {
+        float4 pv[kRmsMaxSplit];
+#pragma unroll
+        for (int sp = 0; sp < kRmsMaxSplit; ++sp)
+          pv[sp] = sp < ksplit ? *(const float4*)(pp + sp * stride) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int sp = 0; sp < kRmsMaxSplit; ++sp) {
+          if (sp < ksplit) { a.x += pv[sp].x; a.y += pv[sp].y; a.z += pv[sp].z; a.w += pv[sp].w; }
+        }
+      } else {
+        for (int sp = 0; sp < ksplit; ++sp) {
+          const float4 pv = *(const float4*)(pp + sp * stride);
+          a.x += pv.x; a.y += pv.y; a.z += pv.z; a.w += pv.w;
+        }
       }
       v[k].x += a.x; v[k].y += a.y; v[k].z += a.z; v[k].w += a.w;
       *(float4*)(x + c) = v[k];
@@ -114,11 +132,13 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(float* h, const float* gai
   for (int o = 32; o > 0; o >>= 1) sd += __shfl_xor(sd, o, kWave);
   if ((tid & 63) == 0) red[tid >> 6] = sd;
   __syncthreads();
-  const double tot = red[0] + red[1] + red[2] + red[3];
+  double tot = 0.0;
+#pragma unroll
+  for (int w = 0; w < NT / 64; ++w) tot += red[w];
   const float rs = (float)(1.0 / sqrt(tot / (double)H + (double)eps));
 #pragma unroll
   for (int k = 0; k < kRmsVec; ++k) {
-    const int c = tid * 4 + 1024 * k;
+    const int c = tid * 4 + 4 * NT * k;
     if (c < H) {
       const float4 gg = *(const float4*)(gain + c);
       act_store4(out, r, c, make_float4(v[k].x * rs * gg.x, v[k].y * rs * gg.y, v[k].z * rs * gg.z, v[k].w * rs * gg.w));
@@ -283,8 +303,13 @@ hipError_t launch_rmsnorm(float* h, const float* gain, ActOut out, int M, int H,
   if (M <= 0) return hipSuccess;
   ActOut cap{};
   if (capture) cap = *capture;
-  hipLaunchKernelGGL(rmsnorm_kernel, dim3(M), dim3(256), 0, s, h, gain, out, H, eps, committed, B, n_open,
-                     row_map, part, part ? ksplit : 0, part_rows > 0 ? part_rows : M, cap);
+  const int ks = part ? ksplit : 0, mp = part_rows > 0 ? part_rows : M;
+  if (M < 128)
+    hipLaunchKernelGGL(rmsnorm_kernel<1024>, dim3(M), dim3(1024), 0, s, h, gain, out, H, eps, committed, B, n_open,
+                       row_map, part, ks, mp, cap);
+  else
+    hipLaunchKernelGGL(rmsnorm_kernel<256>, dim3(M), dim3(256), 0, s, h, gain, out, H, eps, committed, B, n_open,
+                       row_map, part, ks, mp, cap);
   return hipGetLastError();
 }
 
