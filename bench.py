@@ -758,7 +758,7 @@ def summarize(trace_dir, fetch_dir, write_dir):
     lines = [f"# rocprofv3 kernel statistics, {wl_name}", "",
              "Command (run from the repository root, output csv):", "",
              "    rocprofv3 --kernel-trace --stats --output-format csv -d <TRACE_DIR> -o run -- "
-             "python bench.py --steps 5 --warmup 2 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0 --target 0", "",
+             "python bench.py --steps 5 --warmup 2 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0 --target 0 --longctx 0", "",
              f"Kernel sources hash: {h}", "",
              "| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:20]:
@@ -771,9 +771,9 @@ def summarize(trace_dir, fetch_dir, write_dir):
     tl = [f"# HBM traffic per launch, {wl_name}", "",
           "Commands (repository root, csv output):", "",
           "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -o p -- "
-          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0 --target 0 --copy-calibration 1",
+          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0 --target 0 --longctx 0 --copy-calibration 1",
           "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -o p -- "
-          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0 --target 0 --copy-calibration 1",
+          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0 --target 0 --longctx 0 --copy-calibration 1",
           "    python bench.py --summarize <TRACE_DIR> <FETCH_DIR> <WRITE_DIR>", "",
           f"Calibration: a {COPY_BYTES >> 20} MiB device copy (`{big[0][:60]}`) reads FETCH_SIZE = "
           f"{big[1]:.0f} KiB -> fetch scale {fetch_scale:.4f}; WRITE_SIZE scale "
