@@ -216,6 +216,46 @@ def test_sampled_verify_matches_oracle(bt, B, V, T):
     print(f"sampled verify bt={bt} B={B}: mean accept {acc_o.mean():.2f}, excluded {int((~keep).sum())}")
 
 
+@pytest.mark.parametrize("case", ["v1", "v64_peaked", "v100_flat", "equal", "last_index", "v5003_b1"])
+def test_sampled_verify_edge_cases(case):
+    """Sampled verification at the edges of its draw: a one-token vocabulary, vocabularies
+    smaller than one draw segment, very peaked and very flat distributions, p = q (every
+    draft token accepted, bonus drawn from p), and residual mass only at the last index."""
+    bt, B, V, T = {"v1": (3, 4, 1, 1.0), "v64_peaked": (4, 16, 64, 0.05), "v100_flat": (5, 8, 100, 4.0),
+                   "equal": (4, 8, 777, 1.0), "last_index": (4, 6, 5003, 1.0), "v5003_b1": (7, 1, 5003, 1.0)}[case]
+    zd, zt = synth.make_sampled_logits(bt, B, V, seed=7 * V + B, device="cuda")
+    draft = synth.sample_tokens(zd, T, seed=bt + B)
+    if case == "equal":
+        zt = torch.cat([zd, zt[:, B:]], dim=1).contiguous()
+    if case == "last_index":
+        # the draft puts its mass on token 0 and drafts it; the target prefers token V-1, so
+        # the first test rejects (u q < p fails for u >= p/q) and max(0, p - q) sits at V-1
+        zd = torch.full((bt, B, V), -30.0, device="cuda")
+        zd[:, :, 0] = 30.0
+        zt = torch.full((bt, B + 1, V), -30.0, device="cuda")
+        zt[:, :, V - 1] = 30.0
+        draft = torch.zeros(bt, B, dtype=torch.int32, device="cuda")
+    U = synth.make_uniforms(bt, B, seed=V + B, device="cuda")
+    acc, out = verify(zt, draft, T, zd, U)
+    torch.cuda.synchronize()
+    acc_o, out_o, margin = oracle.verify_sampled(zt.cpu().numpy(), zd.cpu().numpy(), draft.cpu().numpy(),
+                                                 U.cpu().numpy(), T)
+    keep = margin > 1e-9
+    assert keep.sum() >= bt - 1
+    assert np.array_equal(acc.cpu().numpy()[keep], acc_o[keep])
+    assert np.array_equal(out.cpu().numpy()[keep], out_o[keep])
+    a = acc.cpu().numpy()
+    o = out.cpu().numpy()
+    assert np.all((a >= 0) & (a <= B))
+    assert np.all((o[np.arange(bt), a] >= 0) & (o[np.arange(bt), a] < V))
+    if case == "v1":
+        assert np.all(a == B) and np.all(o == 0)
+    if case == "equal":
+        assert np.all(a == B)
+    if case == "last_index":
+        assert np.all(a == 0) and np.all(o[:, 0] == V - 1)
+
+
 @pytest.mark.parametrize("n_tok_case,qk", [(0, False), (17, False), (9, True)])
 def test_target_forward_matches_oracle(n_tok_case, qk):
     """Target-side verify forward (causal block over the target's own cache): logits, the
