@@ -185,8 +185,8 @@ def main():
         summarize(*a.summarize)
         return
     if a.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; multi-GPU runs are not part of it "
-                                   "(the draft step shards by sequence with no exchange)", "n_gpus": a.gpus}))
+        print(json.dumps({"error": "bench.py measures one GPU only; it has no multi-GPU mode "
+                                   "(the draft step would shard by sequence with no exchange)", "n_gpus": a.gpus}))
         sys.exit(2)
     import numpy as np
     import torch
