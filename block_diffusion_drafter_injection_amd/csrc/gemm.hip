@@ -915,6 +915,25 @@ int gemm_bn(int wdtype, int K) { return wdtype && K % 32 == 0 && tile_bn(DFLASH_
 #ifndef DFLASH_KS_TARGET
 #define DFLASH_KS_TARGET 256
 #endif
+// Estimated time (us) of a SwiGLU GEMM on tile config c with its best K split
+// (returned in ks): whole rounds of one tile per CU at the sustained per-CU
+// MFMA rate (about 5 TFLOP/s of executed work), plus, for a split, the reduce
+// pass over the fp32 partials at HBM speed (about 5 TB/s).
+static double swiglu_split_us(int c, int np, int M, int N, int K, int& ks_out) {
+  const int bm = tile_bm(c), bn = tile_bn(c), cus = 256;
+  const int tiles = ((M + bm - 1) / bm) * ((N + bn - 1) / bn);
+  const double tile_us = 2.0 * np * bm * bn * (double)K / 5.1e12 * 1e6;
+  const int cap = std::min(8, std::max(1, K / 32 / 16));
+  double best = 1e30;
+  for (int ks = 1; ks <= cap; ++ks) {
+    const double rounds = (double)((tiles * ks + cus - 1) / cus);
+    const double reduce_us = ks > 1 ? (ks + 0.5) * (double)M * N * 4.0 / 5e12 * 1e6 : 0.0;
+    const double us = rounds * tile_us / ks + reduce_us;
+    if (us < best - 1e-9) { best = us; ks_out = ks; }
+  }
+  return best;
+}
+
 GemmPlan gemm_plan(int wdtype, int a_mode, int M, int N, int K, int kind, bool fixed_split) {
   GemmPlan p{0, 1};
   if (wdtype == 0) return p;
@@ -949,6 +968,24 @@ GemmPlan gemm_plan(int wdtype, int a_mode, int M, int N, int K, int kind, bool f
     ks = std::max(ks, 1);
     if (kind == EPI_LMHEAD) ks = 1;
     p.ksplit = ks;
+    return p;
+  }
+  if (kind == EPI_SWIGLU && (cfg == 10 || cfg == 12)) {
+    // SwiGLU partials need a reduce pass of their own (the activation is not
+    // linear), so the split is priced with it, and the 128x384 and 128x256
+    // tiles are compared: with 544 rows the wide tile leaves a fifth row of
+    // tiles that only a four-way split (and its reduce) packs into whole rounds
+    int best_cfg = cfg, best_ks = 1;
+    double best_us = 1e30;
+    const int np = a_mode == ACT_HILO ? 2 : 1;
+    for (int c : {10, 12}) {
+      if ((N / 2) % (tile_bn(c) / 2) != 0 || K % 64 != 0) continue;
+      int ks = 1;
+      const double us = swiglu_split_us(c, np, M, N, K, ks);
+      if (us < best_us - 1e-9) { best_us = us; best_cfg = c; best_ks = ks; }
+    }
+    p.cfg = best_cfg;
+    p.ksplit = best_ks;
     return p;
   }
   // one workgroup per CU: pick the split that minimises rounds per unit of work

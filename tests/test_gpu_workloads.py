@@ -4,6 +4,7 @@ sampled sequences (the sequences of a batch are independent); loops check
 every step.  Near-ties (top-2 or commit-boundary gap below 1e-3) are excluded
 and counted, never hidden."""
 import time
+from dataclasses import replace
 
 import numpy as np
 import pytest
@@ -12,7 +13,8 @@ import torch
 import oracle
 from block_diffusion_drafter_injection_amd import binding as Bn
 from block_diffusion_drafter_injection_amd import synth
-from gpu_util import (TIE, Drafter, alloc_pool, compare_draft, compare_pool_entries, ctx_tensor, f64, pack_pool,
+from gpu_util import (TIE, Drafter, alloc_pool, compare_draft, compare_forward_outputs, compare_pool_entries,
+                      ctx_tensor, f64, pack_pool,
                       page_plan, unpack_pool, verify)
 
 pytestmark = pytest.mark.gpu
@@ -135,6 +137,58 @@ def test_qwen3_8b_shape_injection_sampled():
     K, V = unpack_pool(d, pool, n_pages, readable, 0, p0 + n)
     compare_pool_entries(K[:, p0:], Ko, "bf16", "K")
     compare_pool_entries(V[:, p0:], Vo, "bf16", "V")
+
+
+def test_target_forward_8b_shape_sampled():
+    """The target forward at the Qwen3-8B layer shape over batch 32 x 17 tokens (544 GEMM
+    rows, as the benchmark runs it; 4 layers instead of 36 to keep the oracle short), context
+    4096 each: logits, captured layer outputs and appended K/V of two sampled sequences
+    against the oracle."""
+    d = replace(synth.QWEN3_8B_SHAPE, n_layers=4)
+    bt, n, ctx, caps = 32, 17, 4096, [1, 3]
+    t0 = time.time()
+    W = synth.make_weights(d, 13, "cuda")
+    pages_per = (ctx + n + 15) // 16
+    n_pages = bt * pages_per + 1
+    pool = alloc_pool(d, n_pages)
+    table = np.zeros((bt, pages_per), dtype=np.int32)
+    sample = [4, 29]
+    host_pools = {}
+    for b in range(bt):
+        first = 1 + b * pages_per
+        table[b] = np.arange(first, first + pages_per)
+        K, V = synth.make_pool_values(d, ctx, 500 + b, "cuda")
+        pack_contiguous(d, pool, n_pages, first, K, V)
+        if b in sample:
+            host_pools[b] = (f64(K), f64(V))
+        del K, V
+    tab = torch.from_numpy(table).cuda()
+    g = torch.Generator(device="cuda").manual_seed(14)
+    tokens = torch.randint(0, d.vocab, (bt, n), generator=g, device="cuda", dtype=torch.int32)
+    cfg, w = Bn.make_config(d), Bn.Weights(W)
+    ws_bytes = Bn.dflash_workspace_size(cfg, bt, n, 0, ctx)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    z = torch.empty(bt, n, d.vocab, dtype=torch.float32, device="cuda")
+    hid = torch.empty(bt, n, len(caps) * d.hidden, dtype=torch.bfloat16, device="cuda")
+    Bn.dflash_target_forward(cfg, w, pool, n_pages, tab, pages_per, ctx_tensor([ctx] * bt), ctx, bt, n, tokens, caps,
+                             z, hid, ws, ws_bytes)
+    torch.cuda.synchronize()
+    log(f"gpu target forward done {time.time() - t0:.1f}s")
+    Wn = np_weights32(W)
+    zo, ho, Ko, Vo = oracle.target_forward(d, Wn, [host_pools[b] for b in sample], [ctx] * len(sample),
+                                           tokens.cpu().numpy()[sample], capture_layers=caps)
+    zg = f64(z[sample])
+    rel = np.max(np.abs(zg - zo), axis=-1) / np.max(np.abs(zo), axis=-1)
+    log(f"target forward 8B shape: logits max rel err {rel.max():.2e} {time.time() - t0:.1f}s")
+    assert rel.max() <= 2e-2
+    top2 = np.sort(zo, axis=-1)[..., -2:]
+    clear = (top2[..., 1] - top2[..., 0]) > 1e-3
+    assert np.array_equal(np.argmax(zg, -1)[clear], np.argmax(zo, -1)[clear])
+    compare_forward_outputs(f64(hid[sample]), ho, "captured hidden")
+    for k, b in enumerate(sample):
+        Kg, Vg = unpack_pool(d, pool, n_pages, table, b, ctx + n)
+        compare_forward_outputs(Kg[:, ctx:], Ko[:, k], f"appended K b={b}")
+        compare_forward_outputs(Vg[:, ctx:], Vo[:, k], f"appended V b={b}")
 
 
 def test_longctx_temperature1_sampled():
