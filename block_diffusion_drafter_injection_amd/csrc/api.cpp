@@ -116,7 +116,20 @@ void attn_split(int bt, int nkv, int nqg, int ctx_cap, int& ns, int& pps) {
 #ifndef DFLASH_ATT_WG_TARGET
 #define DFLASH_ATT_WG_TARGET 512
 #endif
-  const int want = (DFLASH_ATT_WG_TARGET + pairs - 1) / pairs;
+#ifndef DFLASH_ATT_MAX_PPS
+#define DFLASH_ATT_MAX_PPS 132
+#endif
+#ifndef DFLASH_ATT_BALANCE_NS
+#define DFLASH_ATT_BALANCE_NS 4
+#endif
+  // enough splits for DFLASH_ATT_WG_TARGET workgroups; and, up to
+  // DFLASH_ATT_BALANCE_NS splits, at most about DFLASH_ATT_MAX_PPS pages per
+  // split, so that in a batch of mixed lengths the longest sequence is spread
+  // over several workgroups (splits past a shorter sequence's end exit at once).
+  // Beyond that the partials each split writes cost more than the balance gains
+  // (measured on contexts of 16k-32k tokens).
+  const int by_len = std::min(DFLASH_ATT_BALANCE_NS, (pages + DFLASH_ATT_MAX_PPS - 1) / DFLASH_ATT_MAX_PPS);
+  const int want = std::max((DFLASH_ATT_WG_TARGET + pairs - 1) / pairs, by_len);
   const int max_ns = std::max(1, pages / 8);   // at least four 32-token tiles per split
   const int min_ns = (pages + 511) / 512;   // the context kernel stages at most 512 page ids
   ns = std::max(min_ns, std::max(1, std::min(want, max_ns)));
