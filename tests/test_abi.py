@@ -153,6 +153,11 @@ def test_verify_and_inject_argument_errors(L):
     assert f(2, 8, 100, 8, 8, 1.0, None, None, 8, 8, 256, 1 << 30, None) == -1   # T > 0 needs draft logits
     assert f(2, 8, 100, None, 8, 0.0, None, None, 8, 8, 256, 1 << 30, None) == -1
     assert f(2, 8, 100, 8, 8, 0.0, None, None, 8, 8, 256, 8, None) == -5
+    # one byte short of the documented size is refused before any launch (sampled path too)
+    need = L.dflash_verify_workspace_size(32, 16, 151936)
+    assert need > 32 * 33 * 19 * 16                 # chunk pairs alone are not enough
+    assert f(32, 16, 151936, 8, 8, 1.0, 8, 8, 8, 8, 256, need - 1, None) == -5
+    assert f(32, 16, 151936, 8, 8, 0.0, None, None, 8, 8, 256, need - 1, None) == -5
     assert f(0, 8, 100, None, None, 0.0, None, None, None, None, None, 0, None) == 0
     cfg = _cfg()
     w, keep = _weights_stub(cfg.n_layers)
