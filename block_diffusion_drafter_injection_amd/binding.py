@@ -12,6 +12,8 @@ import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("DFLASH_LIB") or os.path.join(_PKG, "libdflash.so")
+# the same kernels behind a host layer that checks device-resident indices first
+DEBUG_LIB_PATH = os.path.join(_PKG, "libdflash_debug.so")
 
 DFLASH_F32, DFLASH_BF16 = 0, 1
 SCHEDULES = {"progressive": 0, "repredict": 1}   # dflash_schedule
@@ -45,7 +47,7 @@ class dflash_weights(ctypes.Structure):
                 ("w_gate", _PP), ("w_up", _PP), ("w_down", _PP), ("q_norm", _PP), ("k_norm", _PP)]
 
 
-_lib = None
+_libs = {}
 EXPORTS = ["dflash_workspace_size", "dflash_inject_kv", "dflash_draft_block", "dflash_verify_workspace_size",
            "dflash_verify_block", "dflash_advance_context", "dflash_adaptive_block_size", "dflash_target_forward",
            "dflash_status_string",
@@ -54,12 +56,20 @@ EXPORTS = ["dflash_workspace_size", "dflash_inject_kv", "dflash_draft_block", "d
 
 def lib():
     """Load libdflash.so (raises if it is missing)."""
-    global _lib
-    if _lib is not None:
-        return _lib
-    if not os.path.exists(LIB_PATH):
-        raise RuntimeError(f"{LIB_PATH} is not built; run python -m block_diffusion_drafter_injection_amd.build")
-    L = ctypes.CDLL(LIB_PATH)
+    return _load(LIB_PATH)
+
+
+def debug_lib():
+    """Load libdflash_debug.so, the variant that checks device indices on the host."""
+    return _load(DEBUG_LIB_PATH)
+
+
+def _load(path):
+    if path in _libs:
+        return _libs[path]
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run python -m block_diffusion_drafter_injection_amd.build")
+    L = ctypes.CDLL(path)
     vp, i32, sz, f32, u64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c_float, ctypes.c_uint64
     cfgp, wp = ctypes.POINTER(dflash_config), ctypes.POINTER(dflash_weights)
     L.dflash_workspace_size.argtypes = [cfgp, i32, i32, i32, i32]
@@ -67,7 +77,7 @@ def lib():
     L.dflash_inject_kv.argtypes = [cfgp, wp, vp, vp, vp, i32, vp, i32, vp, i32, i32, vp, sz, vp]
     L.dflash_inject_kv.restype = i32
     L.dflash_draft_block.argtypes = [cfgp, wp, vp, i32, vp, i32, vp, i32, i32, i32, i32, f32, u64, vp, vp, vp,
-                                     vp, sz, vp]
+                                     vp, vp, sz, vp]
     L.dflash_draft_block.restype = i32
     L.dflash_verify_workspace_size.argtypes = [i32, i32, i32]
     L.dflash_verify_workspace_size.restype = sz
@@ -87,7 +97,7 @@ def lib():
     L.dflash_prof_select.restype = i32
     L.dflash_prof_collect.argtypes = [ctypes.POINTER(f32), ctypes.POINTER(i32)]
     L.dflash_prof_collect.restype = i32
-    _lib = L
+    _libs[path] = L
     return L
 
 
@@ -157,11 +167,12 @@ def dflash_inject_kv(cfg, weights, target_hidden, tok_seq, tok_pos, n_tok, kv_po
 
 def dflash_draft_block(cfg, weights, kv_pool, n_pages, block_table, max_pages, ctx_len, max_ctx_len, batch,
                        block_size, n_steps, temperature, seed, out_tokens, out_logits, out_conf, workspace,
-                       ws_bytes, stream=None):
+                       ws_bytes, stream=None, anchor=None):
+    """anchor: optional device int32 [batch], the token block position 0 starts from."""
     code = lib().dflash_draft_block(ctypes.byref(cfg), ctypes.byref(weights.c), _ptr(kv_pool), n_pages,
                                     _ptr(block_table), max_pages, _ptr(ctx_len), max_ctx_len, batch, block_size,
-                                    n_steps, float(temperature), int(seed), _ptr(out_tokens), _ptr(out_logits),
-                                    _ptr(out_conf), _ptr(workspace), ws_bytes, _stream(stream))
+                                    n_steps, float(temperature), int(seed), _ptr(anchor), _ptr(out_tokens),
+                                    _ptr(out_logits), _ptr(out_conf), _ptr(workspace), ws_bytes, _stream(stream))
     _check("dflash_draft_block", code)
 
 

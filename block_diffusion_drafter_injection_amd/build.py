@@ -36,14 +36,21 @@ def compile_flags():
             "-Wno-unused-result"]
 
 
-def build(jobs=5, verbose=False, defines=(), out=None, objdir=None):
+DEBUG_LIB = os.path.join(PKG, "libdflash_debug.so")
+
+
+def build(jobs=5, verbose=False, defines=(), out=None, objdir=None, debug_variant=True):
+    """Compile every source and link libdflash.so; with debug_variant also link
+    libdflash_debug.so, whose host layer (api.cpp built with DFLASH_DEBUG)
+    checks device-resident indices before launching the same kernels."""
     cc = hipcc()
     objdir = objdir or os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
 
-    def one(src):
-        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
-        cmd = [cc, *compile_flags(), *FILE_FLAGS.get(src, []), *[f"-D{d}" for d in defines], "-c",
+    def one(job):
+        src, extra, stem = job
+        obj = os.path.join(objdir, stem + ".o")
+        cmd = [cc, *compile_flags(), *FILE_FLAGS.get(src, []), *[f"-D{d}" for d in defines], *extra, "-c",
                os.path.join(CSRC, src), "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
@@ -54,15 +61,25 @@ def build(jobs=5, verbose=False, defines=(), out=None, objdir=None):
                 print(err)
         return obj
 
+    jobs_list = [(src, [], os.path.splitext(src)[0]) for src in SOURCES]
+    if debug_variant:
+        jobs_list.append(("api.cpp", ["-DDFLASH_DEBUG"], "api_debug"))
     with ThreadPoolExecutor(max_workers=jobs) as ex:
-        objs = list(ex.map(one, SOURCES))
+        objs = list(ex.map(one, jobs_list))
+
+    def link(lib, parts):
+        tmp = lib + ".tmp"
+        cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *parts]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"link failed:\n{r.stderr[-6000:]}")
+        os.replace(tmp, lib)
+
     lib = out or LIB
-    tmp = lib + ".tmp"
-    cmd = [cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"link failed:\n{r.stderr[-6000:]}")
-    os.replace(tmp, lib)
+    kernels = objs[1:len(SOURCES)]
+    link(lib, [objs[0], *kernels])
+    if debug_variant:
+        link(DEBUG_LIB, [objs[-1], *kernels])
     return lib
 
 

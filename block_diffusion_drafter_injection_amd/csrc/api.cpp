@@ -3,7 +3,10 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
+#include <climits>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "dflash.h"
@@ -14,8 +17,12 @@ using namespace dflash;
 namespace {
 
 // ---------------------------------------------------------------- timing hooks
+// The only state the library keeps: measurement hooks (dflash_prof_*) that,
+// when a kernel class is selected, bracket that class's launches with HIP
+// events.  Off by default; guarded by a mutex.
 struct Prof {
-  int cls = DFLASH_PROF_NONE;
+  std::atomic<int> cls{DFLASH_PROF_NONE};
+  std::mutex mu;
   std::vector<hipEvent_t> pool;  // reusable events
   std::vector<std::pair<hipEvent_t, hipEvent_t>> recorded;
   hipEvent_t open = nullptr;
@@ -32,7 +39,9 @@ hipEvent_t prof_event() {
 }
 
 void prof_mark(int cls, int phase, hipStream_t s) {
-  if (g_prof.cls == DFLASH_PROF_NONE || g_prof.cls != cls) return;
+  const int sel = g_prof.cls.load(std::memory_order_relaxed);
+  if (sel == DFLASH_PROF_NONE || sel != cls) return;
+  std::lock_guard<std::mutex> lock(g_prof.mu);
   hipEvent_t e = prof_event();
   if (!e) return;
   if (hipEventRecord(e, s) != hipSuccess) return;
@@ -113,23 +122,15 @@ void attn_split(int bt, int nkv, int nqg, int ctx_cap, int& ns, int& pps) {
     return;
   }
   const int pairs = std::max(1, bt * nkv * nqg);
-#ifndef DFLASH_ATT_WG_TARGET
-#define DFLASH_ATT_WG_TARGET 512
-#endif
-#ifndef DFLASH_ATT_MAX_PPS
-#define DFLASH_ATT_MAX_PPS 132
-#endif
-#ifndef DFLASH_ATT_BALANCE_NS
-#define DFLASH_ATT_BALANCE_NS 4
-#endif
-  // enough splits for DFLASH_ATT_WG_TARGET workgroups; and, up to
-  // DFLASH_ATT_BALANCE_NS splits, at most about DFLASH_ATT_MAX_PPS pages per
-  // split, so that in a batch of mixed lengths the longest sequence is spread
-  // over several workgroups (splits past a shorter sequence's end exit at once).
-  // Beyond that the partials each split writes cost more than the balance gains
-  // (measured on contexts of 16k-32k tokens).
-  const int by_len = std::min(DFLASH_ATT_BALANCE_NS, (pages + DFLASH_ATT_MAX_PPS - 1) / DFLASH_ATT_MAX_PPS);
-  const int want = std::max((DFLASH_ATT_WG_TARGET + pairs - 1) / pairs, by_len);
+  // enough splits for kAttWgTarget workgroups; and, up to kAttBalanceSplits
+  // splits, at most about kAttMaxPps pages per split, so that in a batch of
+  // mixed lengths the longest sequence is spread over several workgroups
+  // (splits past a shorter sequence's end exit at once).  Beyond that the
+  // partials each split writes cost more than the balance gains (measured on
+  // contexts of 16k-32k tokens).
+  constexpr int kAttWgTarget = 512, kAttMaxPps = 132, kAttBalanceSplits = 4;
+  const int by_len = std::min(kAttBalanceSplits, (pages + kAttMaxPps - 1) / kAttMaxPps);
+  const int want = std::max((kAttWgTarget + pairs - 1) / pairs, by_len);
   const int max_ns = std::max(1, pages / 8);   // at least four 32-token tiles per split
   const int min_ns = (pages + 511) / 512;   // the context kernel stages at most 512 page ids
   ns = std::max(min_ns, std::max(1, std::min(want, max_ns)));
@@ -240,6 +241,74 @@ ActOut act_out(const dflash_config* c, void* hi, void* lo, int ld) {
 }
 ActIn act_in(const ActOut& o) { return ActIn{o.p0, o.p1, o.ld, o.mode}; }
 
+// ---------------------------------------------------------------- debug build
+// Built with DFLASH_DEBUG, every call copies its device-resident indices to the
+// host (on the call's stream, then synchronised) and checks them before
+// anything is launched: a value outside its documented range returns
+// DFLASH_EINVAL.  The release build trusts the caller (its kernels clamp or skip
+// such values, so a bad index gives wrong numbers rather than a fault).
+#ifdef DFLASH_DEBUG
+bool dbg_fetch(std::vector<int32_t>& v, const int32_t* src, size_t n, hipStream_t s) {
+  v.resize(n);
+  if (n == 0) return true;
+  if (hipMemcpyAsync(v.data(), src, n * sizeof(int32_t), hipMemcpyDeviceToHost, s) != hipSuccess) return false;
+  return hipStreamSynchronize(s) == hipSuccess;
+}
+
+// ctx_len[b] in [0, ctx_cap]; the pages of positions [0, ctx_len[b] + extra) mapped
+// to a physical page in [0, n_pages).
+dflash_status dbg_context(const int32_t* ctx_len, int batch, int ctx_cap, int extra, const int32_t* table,
+                          int max_pages, int n_pages, hipStream_t s) {
+  std::vector<int32_t> c, t;
+  if (!dbg_fetch(c, ctx_len, batch, s) || !dbg_fetch(t, table, (size_t)batch * max_pages, s)) return DFLASH_EHIP;
+  for (int b = 0; b < batch; ++b) {
+    if (c[b] < 0 || c[b] > ctx_cap) return DFLASH_EINVAL;
+    const int pages = (c[b] + extra + 15) / 16;
+    if (pages > max_pages) return DFLASH_EINVAL;
+    for (int lp = 0; lp < pages; ++lp) {
+      const int ph = t[(size_t)b * max_pages + lp];
+      if (ph < 0 || ph >= n_pages) return DFLASH_EINVAL;
+    }
+  }
+  return DFLASH_OK;
+}
+
+// Injection rows: tok_seq -1 (skip) or a sequence in [0, n_seqs) whose page of
+// tok_pos is mapped to a physical page in [0, n_pages).
+dflash_status dbg_inject(const int32_t* tok_seq, const int32_t* tok_pos, int n_tok, const int32_t* table,
+                         int n_seqs, int max_pages, int n_pages, hipStream_t s) {
+  std::vector<int32_t> q, p, t;
+  if (!dbg_fetch(q, tok_seq, n_tok, s) || !dbg_fetch(p, tok_pos, n_tok, s) ||
+      !dbg_fetch(t, table, (size_t)n_seqs * max_pages, s))
+    return DFLASH_EHIP;
+  for (int i = 0; i < n_tok; ++i) {
+    if (q[i] == -1) continue;
+    if (q[i] < 0 || q[i] >= n_seqs || p[i] < 0 || p[i] / 16 >= max_pages) return DFLASH_EINVAL;
+    const int ph = t[(size_t)q[i] * max_pages + p[i] / 16];
+    if (ph < 0 || ph >= n_pages) return DFLASH_EINVAL;
+  }
+  return DFLASH_OK;
+}
+
+// Every entry of a device int32 array in [lo, hi].
+dflash_status dbg_range(const int32_t* v, size_t n, int lo, int hi, hipStream_t s) {
+  std::vector<int32_t> h;
+  if (!dbg_fetch(h, v, n, s)) return DFLASH_EHIP;
+  for (int32_t x : h)
+    if (x < lo || x > hi) return DFLASH_EINVAL;
+  return DFLASH_OK;
+}
+#define DBG_CHECK(x)                                  \
+  do {                                                \
+    const dflash_status dbg_st_ = (x);                \
+    if (dbg_st_ != DFLASH_OK) return dbg_st_;         \
+  } while (0)
+#else
+#define DBG_CHECK(x) \
+  do {               \
+  } while (0)
+#endif
+
 #define HIP_TRY(x)                              \
   do {                                          \
     if ((x) != hipSuccess) return DFLASH_EHIP;  \
@@ -288,6 +357,7 @@ dflash_status dflash_inject_kv(const dflash_config* cfg, const dflash_weights* w
   if (!workspace || ((uintptr_t)workspace & 255)) return DFLASH_EWORKSPACE;
   const int chunk = inject_chunk_capacity(cfg, ws_bytes);
   if (chunk < 1) return DFLASH_EWORKSPACE;
+  DBG_CHECK(dbg_inject(tok_seq, tok_pos, n_tok, block_table, n_seqs, max_pages, n_pages, stream));
   const InjectWS L = inject_layout(cfg, chunk);
   const int bf = cfg->dtype == DFLASH_BF16;
   const size_t el = bf ? 2 : 4;
@@ -456,15 +526,17 @@ static dflash_status run_layers(const dflash_config* cfg, const dflash_weights* 
 dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights* w, const void* kv_pool,
                                  int32_t n_pages, const int32_t* block_table, int32_t max_pages,
                                  const int32_t* ctx_len, int32_t max_ctx_len, int32_t batch, int32_t block_size,
-                                 int32_t n_steps, float temperature, uint64_t seed, int32_t* out_tokens,
-                                 float* out_logits, float* out_conf, void* workspace, size_t ws_bytes,
-                                 hipStream_t stream) {
+                                 int32_t n_steps, float temperature, uint64_t seed, const int32_t* anchor_tokens,
+                                 int32_t* out_tokens, float* out_logits, float* out_conf, void* workspace,
+                                 size_t ws_bytes, hipStream_t stream) {
   dflash_status st = check_cfg(cfg);
   if (st != DFLASH_OK) return st;
   if ((st = check_weights(cfg, w, true)) != DFLASH_OK) return st;
   if (batch < 0 || n_pages < 0 || max_pages < 0 || max_ctx_len < 0) return DFLASH_EINVAL;
   if (block_size < 1 || block_size > 16) return DFLASH_ECAPACITY;
-  if (n_steps < 1 || n_steps > block_size) return DFLASH_EINVAL;
+  // an anchor takes block position 0, so B - 1 positions are left to denoise
+  const int given = anchor_tokens ? 1 : 0;
+  if (n_steps < 1 || n_steps > block_size - given) return DFLASH_EINVAL;
   if (!(temperature >= 0.f)) return DFLASH_EINVAL;
   if (batch == 0) return DFLASH_OK;
   if (!ctx_len || !out_tokens || !block_table || (!kv_pool && max_ctx_len > 0)) return DFLASH_EINVAL;
@@ -472,6 +544,8 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
   const int ctx_cap = n_pages > 0 ? (int)std::min<long long>(max_ctx_len, (long long)max_pages * 16) : 0;
   const DraftWS L = draft_layout(cfg, batch, block_size, ctx_cap);
   if (L.total > ws_bytes) return DFLASH_EWORKSPACE;
+  DBG_CHECK(dbg_context(ctx_len, batch, ctx_cap, 0, block_table, max_pages, n_pages, stream));
+  if (anchor_tokens) DBG_CHECK(dbg_range(anchor_tokens, (size_t)batch, 0, cfg->vocab - 1, stream));
 
   const int bf = cfg->dtype == DFLASH_BF16;
   const int B = block_size, M = batch * B, S = n_steps;
@@ -522,13 +596,14 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
   ap.vblk = (float*)at(workspace, L.vblk);
 
   HIP_TRY(launch_rope_table_block(ctx_len, ctx_cap, batch, B, d, (double)cfg->rope_base, cs, stream));
-  HIP_TRY(launch_block_init(tau, committed, M, cfg->mask_token_id, stream));
+  HIP_TRY(launch_block_init(tau, committed, M, B, cfg->mask_token_id, anchor_tokens, stream));
 
-  // re-predict schedule: every position stays open and takes its candidate at every step
+  // re-predict schedule: every open position takes its candidate at every step
   const bool repredict = cfg->denoise_schedule == DFLASH_SCHEDULE_REPREDICT;
-  int done = 0;
+  const int Bo = B - given;   // positions the steps denoise
+  int done = given;
   for (int s = 0; s < S; ++s) {
-    const int k_s = repredict ? B : ((s + 1) * B) / S - (s * B) / S;
+    const int k_s = repredict ? Bo : ((s + 1) * Bo) / S - (s * Bo) / S;
     const int n_open = B - done;
     const int last = s == S - 1;
     HIP_TRY(launch_embed(tau, w->embed, bf, cfg->vocab, h, M, H, stream));
@@ -607,6 +682,8 @@ dflash_status dflash_target_forward(const dflash_config* cfg, const dflash_weigh
   const int B = n_tok, M = batch * B;
   const DraftWS L = draft_layout(cfg, batch, B, ctx_cap);
   if (L.total > ws_bytes) return DFLASH_EWORKSPACE;
+  DBG_CHECK(dbg_context(ctx_len, batch, ctx_cap, n_tok, block_table, max_pages, n_pages, stream));
+  DBG_CHECK(dbg_range(tokens, (size_t)batch * n_tok, 0, cfg->vocab - 1, stream));
   const int H = cfg->hidden, d = cfg->head_dim, nq = cfg->n_q_heads, nkv = cfg->n_kv_heads;
   float* h = (float*)at(workspace, L.h);
   const FwdBufs fb{h, act_out(cfg, at(workspace, L.u_hi), at(workspace, L.u_lo), H),
@@ -689,6 +766,7 @@ dflash_status dflash_verify_block(int32_t batch, int32_t block_size, int32_t voc
   if (temperature > 0.f && (!draft_logits || !uniforms)) return DFLASH_EINVAL;
   if (!workspace || ((uintptr_t)workspace & 255)) return DFLASH_EWORKSPACE;
   if (ws_bytes < verify_ws_bytes(batch, block_size, vocab)) return DFLASH_EWORKSPACE;
+  DBG_CHECK(dbg_range(draft_tokens, (size_t)batch * block_size, 0, vocab - 1, stream));
   hipError_t e;
   prof_mark(DFLASH_PROF_VERIFY, 0, stream);
   if (temperature > 0.f)
@@ -744,6 +822,8 @@ dflash_status dflash_advance_context(int32_t batch, int32_t block_size, const in
   if (block_size < 1 || block_size > 16) return DFLASH_ECAPACITY;
   if (batch == 0) return DFLASH_OK;
   if (!accept_len || !ctx_len || !tok_seq || !tok_pos) return DFLASH_EINVAL;
+  DBG_CHECK(dbg_range(accept_len, (size_t)batch, 0, block_size, stream));
+  DBG_CHECK(dbg_range(ctx_len, (size_t)batch, 0, INT32_MAX - block_size - 1, stream));
   return launch_advance_context(batch, block_size, accept_len, ctx_len, tok_seq, tok_pos, stream) == hipSuccess
              ? DFLASH_OK
              : DFLASH_EHIP;
@@ -751,12 +831,13 @@ dflash_status dflash_advance_context(int32_t batch, int32_t block_size, const in
 
 dflash_status dflash_prof_select(int32_t kernel_class) {
   if (kernel_class < DFLASH_PROF_NONE || kernel_class > DFLASH_PROF_VERIFY) return DFLASH_EINVAL;
-  g_prof.cls = kernel_class;
+  g_prof.cls.store(kernel_class, std::memory_order_relaxed);
   return DFLASH_OK;
 }
 
 dflash_status dflash_prof_collect(float* total_ms, int32_t* n_launches) {
   if (!total_ms || !n_launches) return DFLASH_EINVAL;
+  std::lock_guard<std::mutex> lock(g_prof.mu);
   double tot = 0.0;
   for (auto& pr : g_prof.recorded) {
     if (hipEventSynchronize(pr.second) != hipSuccess) return DFLASH_EHIP;

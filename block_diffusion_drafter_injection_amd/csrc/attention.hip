@@ -50,10 +50,7 @@ __device__ __forceinline__ void split_pages(const AttnParams& p, int npages, int
 
 // ---------------------------------------------------------------------------
 constexpr int kMaxPPS = 512;   // pages per context split (bounded by the host)
-#ifndef DFLASH_ATT_STAGES
-#define DFLASH_ATT_STAGES 4
-#endif
-constexpr int kAttStages = DFLASH_ATT_STAGES;  // 32-token tiles resident per workgroup
+constexpr int kAttStages = 4;   // 32-token tiles resident per workgroup
 
 // s_waitcnt on the vector-memory counter only, through the builtin so that
 // the compiler's own wait insertion knows which loads have completed
@@ -278,6 +275,12 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
     int ph = pp < pg1 ? ptab[pp - pg0] : first_ph;
     return ph >= 0 ? ph : first_ph;
   };
+  // page q (0, 1) of tile t lies in the split but has no valid physical page:
+  // its tokens are skipped (scores masked, values zeroed), as the VALU path does
+  auto unmapped = [&](int t, int q) __attribute__((always_inline)) {
+    const int pp = pg0 + 2 * t + q;
+    return pp < pg1 && ptab[pp - pg0] < 0;
+  };
   auto issue = [&](int ph, int st) __attribute__((always_inline)) {
     const char* base = (const char*)(srcbase + (size_t)__builtin_amdgcn_readfirstlane(ph) * page_stride);
 #pragma unroll
@@ -308,14 +311,16 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
   const int tl = 8 * (lane >> 4);   // first of this lane's 8 tokens in a tile
 
   // V slots at or past the context end may hold anything (a page never
-  // written); in the last tile they are zeroed so that P = 0 meets V = 0.
+  // written), and so may the stand-in page read for an unmapped one; they are
+  // zeroed so that P = 0 meets V = 0.
   auto zero_tail = [&](int t) __attribute__((always_inline)) {
     const int tok0 = (pg0 + 2 * t) * 16;
-    if (tok0 + 32 > ctx) {
+    const bool bad0 = unmapped(t, 0), bad1 = unmapped(t, 1);
+    if (tok0 + 32 > ctx || bad0 || bad1) {
       unsigned char* vt = lds + (t % kAttStages) * TILE + KBYTES;
       for (int c = tid; c < 2 * D * 16; c += 256) {
         const int pg = c / (D * 16), rem = c - pg * D * 16, d = rem >> 4, slot = rem & 15;
-        if (tok0 + pg * 16 + slot >= ctx) {
+        if (tok0 + pg * 16 + slot >= ctx || (pg ? bad1 : bad0)) {
           const int lh = (slot >> 3) ^ ((d >> 3) & 1);
           *(bf16_t*)(vt + pg * (D * 32) + d * 32 + lh * 16 + (slot & 7) * 2) = 0;
         }
@@ -406,10 +411,13 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
         stn[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf[1][kk], ql[kk], stn[1], 0, 0, 0);
       }
       const int tok0 = (pg0 + 2 * it) * 16;
-      // lane owns query (lane & 15) and tokens tok0 + tl + 4t + e, scores in
-      // base-2 units (the queries carry scale * log2 e)
+      // lane owns query (lane & 15) and tokens tok0 + tl + 4t + e, all on page
+      // lane >> 5 of the tile; scores in base-2 units (the queries carry
+      // scale * log2 e)
+      const bool bad0 = unmapped(it, 0), bad1 = unmapped(it, 1);
+      const bool page_ok = !((lane >> 5) ? bad1 : bad0);
       float s[8];
-      if (tok0 + 32 <= tok_end) {
+      if (tok0 + 32 <= tok_end && !bad0 && !bad1) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -418,7 +426,8 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) s[t * 4 + e] = tok0 + tl + 4 * t + e < tok_end ? stc[t][e] : -INFINITY;
+          for (int e = 0; e < 4; ++e)
+            s[t * 4 + e] = (page_ok && tok0 + tl + 4 * t + e < tok_end) ? stc[t][e] : -INFINITY;
       }
       // row maximum over the four lanes holding this query's 32 tokens
       const float mx = row_max4(fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])),

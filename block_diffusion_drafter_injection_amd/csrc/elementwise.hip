@@ -35,11 +35,12 @@ __global__ void rope_tokens_kernel(const int* tok_pos, int n, int d, double base
   cs[idx] = rope_cs(tok_pos[row], j, d, base);
 }
 
-__global__ void block_init_kernel(int* tau, int* committed, int M, int mask_id) {
+__global__ void block_init_kernel(int* tau, int* committed, int M, int B, int mask_id, const int* anchor) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i < M) {
-    tau[i] = mask_id;
-    committed[i] = 0;
+    const bool given = anchor && i % B == 0;
+    tau[i] = given ? anchor[i / B] : mask_id;
+    committed[i] = given ? 1 : 0;
   }
 }
 
@@ -217,7 +218,7 @@ __global__ __launch_bounds__(64) void commit_kernel(const int* cand, const float
   if (i < B) {
     if (out_conf) out_conf[((size_t)b * S + step) * B + i] = open[i] ? cs[i] : __int_as_float(0x7fc00000);
     if (repredict) {
-      tau[row] = cand[row];
+      if (open[i]) tau[row] = cand[row];   // a given anchor stays
     } else if (open[i]) {
       int rank = 0;
       for (int k = 0; k < B; ++k)
@@ -283,8 +284,10 @@ hipError_t launch_qk_norm(float* qkv, int M, int nq, int nkv, int d, const float
   return hipGetLastError();
 }
 
-hipError_t launch_block_init(int* tau, int* committed, int M, int mask_id, hipStream_t s) {
-  hipLaunchKernelGGL(block_init_kernel, dim3((M + 255) / 256), dim3(256), 0, s, tau, committed, M, mask_id);
+hipError_t launch_block_init(int* tau, int* committed, int M, int B, int mask_id, const int* anchor,
+                             hipStream_t s) {
+  hipLaunchKernelGGL(block_init_kernel, dim3((M + 255) / 256), dim3(256), 0, s, tau, committed, M, B, mask_id,
+                     anchor);
   return hipGetLastError();
 }
 

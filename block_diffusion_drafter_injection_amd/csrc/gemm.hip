@@ -883,38 +883,22 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(ActIn a, BRows<float> b, 
 //   10: 128x384, eight 64x96 waves     11: 256x256, eight 64x128 waves (one plane)
 //   12: 128x256, eight 64x64 waves     13: 64x256, eight 64x32 waves (one plane, at most 64 rows)
 //   (gemm_fl_kernel, one workgroup per CU, two for 13)
-#ifndef DFLASH_T_SWIGLU
-#define DFLASH_T_SWIGLU 10
-#endif
-#ifndef DFLASH_T_LMHEAD
-#define DFLASH_T_LMHEAD 11
-#endif
-#ifndef DFLASH_T_LMHEAD_SMALL   // LM head with at most 256 rows (fewer idle CUs in the last round)
-#define DFLASH_T_LMHEAD_SMALL 11
-#endif
-#ifndef DFLASH_T_ADD
-#define DFLASH_T_ADD 12
-#endif
-#ifndef DFLASH_T_STORE
-#define DFLASH_T_STORE 10
-#endif
+constexpr int kCfgSwiglu = 10;       // gate/up + SwiGLU
+constexpr int kCfgLmhead = 11;       // LM head (one bf16 plane)
+constexpr int kCfgAdd = 12;          // O and down + residual
+constexpr int kCfgStore = 10;        // q/k/v
 static int tile_bn(int cfg) {
   return cfg == 10 ? 384 : cfg >= 11 ? 256 : 128;
 }
 static int tile_bm(int cfg) { return cfg == 11 ? 256 : cfg == 13 ? 64 : 128; }
 
 // LM-head partials cover 128 columns each, or 64 when the tile width is not a multiple of 128
-int gemm_bn(int wdtype, int K) { return wdtype && K % 32 == 0 && tile_bn(DFLASH_T_LMHEAD) % 128 ? 64 : 128; }
+int gemm_bn(int wdtype, int K) { return wdtype && K % 32 == 0 && tile_bn(kCfgLmhead) % 128 ? 64 : 128; }
 
 // Tile configuration and K split of one GEMM (the table above).  A split is
 // used only when the tiles alone leave CUs idle; with fixed_split the split
 // depends on N and K only (injection must give the same bits for any M).
-#ifndef DFLASH_SKINNY
-#define DFLASH_SKINNY 1
-#endif
-#ifndef DFLASH_KS_TARGET
-#define DFLASH_KS_TARGET 256
-#endif
+constexpr int kInjectWgTarget = 256;   // workgroups the injection's fixed K split aims for
 // Estimated time (us) of a SwiGLU GEMM on tile config c with its best K split
 // (returned in ks): whole rounds of one tile per CU at the sustained per-CU
 // MFMA rate (about 5 TFLOP/s of executed work), plus, for a split, the reduce
@@ -939,10 +923,10 @@ GemmPlan gemm_plan(int wdtype, int a_mode, int M, int N, int K, int kind, bool f
   if (wdtype == 0) return p;
   int cfg = 2;
   if (!fixed_split && K % 32 == 0) {
-    if (kind == EPI_SWIGLU) cfg = DFLASH_T_SWIGLU;
-    else if (kind == EPI_LMHEAD) cfg = M > 256 ? DFLASH_T_LMHEAD : M > 64 ? DFLASH_T_LMHEAD_SMALL : 13;
-    else if (kind == EPI_ADD) cfg = DFLASH_T_ADD;
-    else if (kind == EPI_STORE) cfg = DFLASH_T_STORE;
+    if (kind == EPI_SWIGLU) cfg = kCfgSwiglu;
+    else if (kind == EPI_LMHEAD) cfg = M > 64 ? kCfgLmhead : 13;
+    else if (kind == EPI_ADD) cfg = kCfgAdd;
+    else if (kind == EPI_STORE) cfg = kCfgStore;
     const bool one_plane = a_mode != ACT_HILO;
     if ((cfg == 11 || cfg == 13) && !one_plane) cfg = 12;
     if (cfg >= 10 && K % 64 != 0) cfg = 2;
@@ -952,7 +936,7 @@ GemmPlan gemm_plan(int wdtype, int a_mode, int M, int N, int K, int kind, bool f
   // at most 16 rows: weights streamed straight into registers (gemm_skinny_kernel);
   // the K split gives each wave about two batches of eight 32-deep steps (at most
   // eight parts, so the consumer folds few partials) and depends on K only
-  if (!fixed_split && M <= 16 && K % 32 == 0 && kind != EPI_KVSCATTER && DFLASH_SKINNY) {
+  if (!fixed_split && M <= 16 && K % 32 == 0 && kind != EPI_KVSCATTER) {
     p.cfg = 20;
     const int nkt = K / 32;
     p.ksplit = kind == EPI_LMHEAD ? 1 : std::max(1, std::min({(nkt + 15) / 16, 8, nkt}));
@@ -963,7 +947,7 @@ GemmPlan gemm_plan(int wdtype, int a_mode, int M, int N, int K, int kind, bool f
     const int nkt = K / 32;
     const int tn = (N + 127) / 128;
     const int tiles = (fixed_split ? 1 : (M + 127) / 128) * tn;
-    int ks = (DFLASH_KS_TARGET + tiles - 1) / tiles;
+    int ks = (kInjectWgTarget + tiles - 1) / tiles;
     ks = std::min(ks, std::max(1, nkt / 4));
     ks = std::max(ks, 1);
     if (kind == EPI_LMHEAD) ks = 1;

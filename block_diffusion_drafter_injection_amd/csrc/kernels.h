@@ -113,7 +113,10 @@ hipError_t launch_rope_table_block(const int* ctx_len, int ctx_cap, int batch, i
                                    double base, float2* cs, hipStream_t s);
 hipError_t launch_rope_table_tokens(const int* tok_pos, int n, int d, double base, float2* cs,
                                     hipStream_t s);
-hipError_t launch_block_init(int* tau, int* committed, int M, int mask_id, hipStream_t s);
+// tau = mask_id, nothing committed; with anchor != null, position 0 of each block
+// of B takes anchor[b] and is committed from the start.
+hipError_t launch_block_init(int* tau, int* committed, int M, int B, int mask_id, const int* anchor,
+                             hipStream_t s);
 // QK-norm in place on the query and key heads of qkv [M, (nq + 2 nkv) d] (before RoPE).
 hipError_t launch_qk_norm(float* qkv, int M, int nq, int nkv, int d, const float* q_gain, const float* k_gain,
                           float eps, hipStream_t s);

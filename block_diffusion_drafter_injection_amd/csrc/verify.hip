@@ -30,14 +30,15 @@ size_t verify_ws_bytes(int batch, int B, int V) {
   return rows * nc * 16 + rows * 8 + (size_t)batch * kSeg * 8 + 256;
 }
 
-__global__ __launch_bounds__(256) void greedy_rows_kernel(const float* z, int V, float* pval, int* pidx) {
+// vec4: V % 4 == 0 and a 16-byte aligned base (checked by the host), so every
+// row and chunk starts on a 16-byte boundary and takes 128-bit loads.
+__global__ __launch_bounds__(256) void greedy_rows_kernel(const float* z, int V, int vec4, float* pval, int* pidx) {
   const int ch = blockIdx.x, row = blockIdx.y, nc = gridDim.x;
   const int v0 = ch * kVChunk, v1 = min(V, v0 + kVChunk);
   const float* zr = z + (size_t)row * V;
   float best = -INFINITY;
   int bi = -1;
-  const bool vec = (V & 3) == 0;
-  if (vec) {
+  if (vec4) {
     for (int v = v0 + threadIdx.x * 4; v < v1; v += 1024) {
       const float4 x = *(const float4*)(zr + v);
       if (x.x > best || bi < 0) { best = x.x; bi = v; }
@@ -354,7 +355,8 @@ hipError_t launch_verify_greedy(int batch, int B, int V, const float* zt, const 
   const int rows = batch * (B + 1);
   float* pval = (float*)ws;
   int* pidx = (int*)(pval + (size_t)rows * nc);
-  hipLaunchKernelGGL(greedy_rows_kernel, dim3(nc, rows), dim3(256), 0, s, zt, V, pval, pidx);
+  const int vec4 = (V % 4 == 0) && ((uintptr_t)zt % 16 == 0);
+  hipLaunchKernelGGL(greedy_rows_kernel, dim3(nc, rows), dim3(256), 0, s, zt, V, vec4, pval, pidx);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(greedy_accept_kernel, dim3(batch), dim3(64), 0, s, B, nc, pval, pidx, draft, accept_len,

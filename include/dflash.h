@@ -22,7 +22,15 @@
  *   failed launch returns DFLASH_EHIP.  Device-resident indices (block
  *   tables, positions, context lengths, tokens) are the caller's contract;
  *   kernels clamp or skip out-of-range values instead of reading or writing
- *   outside the buffers, so a wrong index gives wrong numbers, not a fault.
+ *   outside the buffers, so a wrong index gives wrong numbers, not a fault
+ *   (context tokens on a page the block table leaves unmapped, -1, are left
+ *   out of the attention).  A library built with DFLASH_DEBUG (the build's
+ *   debug variant, libdflash_debug.so) copies those indices to the host before
+ *   launching anything, synchronising the stream, and returns DFLASH_EINVAL
+ *   for any outside its documented range: a context length above the call's
+ *   bound, an unmapped or out-of-range page under a context or an injected
+ *   position, a sequence index outside [-1, n_seqs), a token outside the
+ *   vocabulary, an acceptance length outside [0, block_size].
  * - Matrices are row-major.  A weight W of shape [out, in] maps x to W x.
  * - dtype DFLASH_BF16: weights, embeddings, target hidden states and the KV
  *   pool are bfloat16; RMSNorm gains are float32; activations are float32
@@ -182,14 +190,24 @@ dflash_status dflash_inject_kv(const dflash_config* cfg, const dflash_weights* w
  *   out_conf (device, optional) [batch, n_steps, block_size] fp32: confidence of each
  *              open position at each step, NaN where the position was already committed
  *              (re-predict: every position is open at every step)
- * Limits: 1 <= block_size <= 16; 1 <= n_steps <= block_size; temperature >= 0. */
+ *   anchor_tokens (device, optional) [batch]: NULL for the pages' all-[MASK] block.
+ *              Otherwise block position 0 of sequence b holds anchor_tokens[b] from
+ *              the start, given rather than drafted, and the schedule above runs over
+ *              the other block_size-1 positions.  This is the last committed token of
+ *              a closed loop: its target hidden state arrives only with the next
+ *              verify forward, so it cannot be injected before this call, and the
+ *              context (ctx_len[b] tokens) holds everything before it.  Its
+ *              out_tokens entry is the anchor, its out_logits row is not written, its
+ *              out_conf entries are NaN.
+ * Limits: 1 <= block_size <= 16; 1 <= n_steps <= block_size (block_size - 1 with an
+ * anchor); temperature >= 0. */
 dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights* w,
                                  const void* kv_pool, int32_t n_pages,
                                  const int32_t* block_table, int32_t max_pages,
                                  const int32_t* ctx_len, int32_t max_ctx_len, int32_t batch,
                                  int32_t block_size, int32_t n_steps, float temperature,
-                                 uint64_t seed, int32_t* out_tokens, float* out_logits,
-                                 float* out_conf, void* workspace, size_t ws_bytes,
+                                 uint64_t seed, const int32_t* anchor_tokens, int32_t* out_tokens,
+                                 float* out_logits, float* out_conf, void* workspace, size_t ws_bytes,
                                  hipStream_t stream);
 
 /* Target-side verify forward ([Blog] 2. Flash Verification: the target checks
@@ -296,11 +314,15 @@ int32_t dflash_adaptive_block_size(const int32_t* accept_len, const int32_t* blo
 /* Human-readable name of a status code (static string). */
 const char* dflash_status_string(dflash_status s);
 
-/* Kernel timing for measurement.  dflash_prof_select(k) makes every later
- * launch of kernel class k (see dflash_kernel_class) record a HIP event pair
- * on the launch stream; dflash_prof_collect waits for the recorded events,
- * returns the summed duration in ms and the launch count, and clears them.
- * k = DFLASH_PROF_NONE turns recording off.  Not thread-safe. */
+/* Kernel timing for measurement (the benchmark's live per-kernel rates).
+ * dflash_prof_select(k) makes every later launch of kernel class k (see
+ * dflash_kernel_class) record a HIP event pair on the launch stream;
+ * dflash_prof_collect waits for the recorded events (the one place the library
+ * blocks on the GPU), returns the summed duration in ms and the launch count,
+ * and clears them.  k = DFLASH_PROF_NONE (the default) turns recording off;
+ * then no call touches this state.  The event list is the library's only
+ * mutable state; it is guarded by a mutex, but interleaving calls on several
+ * streams while recording mixes their events. */
 typedef enum {
   DFLASH_PROF_NONE = 0,
   DFLASH_PROF_ATTN = 1,       /* paged context attention (all layers, all steps) */

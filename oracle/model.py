@@ -194,7 +194,7 @@ def _top2_gap(x):
 
 
 def draft_block(cfg, W, pools, ctx_len, block_size, n_steps, temperature=0.0, seed=0,
-                want_logits=True, seq_ids=None, schedule="progressive"):
+                want_logits=True, seq_ids=None, schedule="progressive", anchor=None):
     """Denoise one [MASK] block per sequence in n_steps forwards.
 
     The pages ("DFLASH + Spec V2 深度解析", 2.3 块扩散) say only that a few
@@ -209,12 +209,21 @@ def draft_block(cfg, W, pools, ctx_len, block_size, n_steps, temperature=0.0, se
     seq_ids: batch index of each row in the Philox counter (default 0..bt-1),
     so a subset of a batch can be redrawn with the noise it had in the batch.
 
+    anchor: optional [bt] token ids.  The pages' block is all [MASK]; in a closed
+    loop the last committed token's target hidden state only arrives with the next
+    verify forward ("DFlash：用“块扩散”魔法…", 2. Flash Verification: one target
+    forward checks the block), so that token cannot be injected before the draft
+    runs.  Reading taken: it then sits at block position 0 (position ctx_len[b], the
+    context holding everything before it) as a known, committed token, and the
+    other B-1 positions are denoised: the schedule above runs over those B-1.
+
     Returns a dict with
       tokens [bt, B]            committed tokens,
       logits [bt, B, V]         each position's logits at its commit step (if want_logits),
       conf [bt, S, B]           confidence of every still-open position at each step (nan otherwise),
       cand [bt, S, B]           candidate token of every open position at each step (-1 otherwise),
       committed_at [bt, B]      step index (0-based) at which each position was committed
+                                (-1 for an anchor, which is given, not committed)
                                 (re-predict: the last step),
       gap [bt, S, B]            top-1 minus top-2 of the score the candidate maximises
                                 (logits at T=0, logits/T + Gumbel at T>0),
@@ -228,12 +237,17 @@ def draft_block(cfg, W, pools, ctx_len, block_size, n_steps, temperature=0.0, se
     tau = np.full((bt, B), cfg.mask_token_id, dtype=np.int64)
     committed = np.zeros((bt, B), dtype=bool)
     committed_at = np.full((bt, B), -1, dtype=np.int64)
+    n_given = 0
+    if anchor is not None:
+        tau[:, 0] = np.asarray(anchor, dtype=np.int64)
+        committed[:, 0] = True                  # given, never predicted (committed_at stays -1)
+        n_given = 1
     conf = np.full((bt, S, B), np.nan)
     cand = np.full((bt, S, B), -1, dtype=np.int64)
     gap = np.full((bt, S, B), np.nan)
     boundary = np.full((bt, S), np.inf)
     logits = np.zeros((bt, B, V), F64) if want_logits else None
-    ks = commit_counts(B, S)
+    ks = commit_counts(B - n_given, S)
     for s in range(S):
         y = forward_hidden(cfg, W, pools, ctx_len, tau)
         rows = [(b, i) for b in range(bt) for i in range(B) if not committed[b, i]]
@@ -255,8 +269,8 @@ def draft_block(cfg, W, pools, ctx_len, block_size, n_steps, temperature=0.0, se
             if want_logits:
                 logits[b, i] = zr
         if schedule == "repredict":
-            tau = cand[:, s].copy()
-            committed_at[:] = s
+            tau[:, n_given:] = cand[:, s, n_given:]
+            committed_at[:, n_given:] = s
             continue
         for b in range(bt):
             open_i = np.nonzero(~committed[b])[0]

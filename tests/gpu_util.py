@@ -196,8 +196,9 @@ def compare_draft(dims, S, res, tokens, logits, conf, tie=TIE, logit_tol=None, s
     scale = np.max(np.abs(res["logits"]), axis=-1) if res["logits"] is not None else np.ones((bt, Bk))
     if logits is not None:
         zo = res["logits"]
-        rel = np.max(np.abs(logits - zo), axis=-1) / scale
-        out["max_rel"] = float(np.max(rel[compare])) if compare.any() else 0.0
+        drafted = compare & (at >= 0)        # a given anchor has no logits row
+        rel = np.max(np.abs(logits - zo), axis=-1) / np.where(drafted, scale, 1.0)
+        out["max_rel"] = float(np.max(rel[drafted])) if drafted.any() else 0.0
         assert out["max_rel"] <= tol, f"logit rel err {out['max_rel']} > {tol}"
     if conf is not None:
         co = res["conf"]
@@ -235,14 +236,15 @@ class Drafter:
                            n_seqs, table.shape[1], self.ws, self.ws_bytes)
 
     def draft(self, pool, n_pages, table, ctx_len, max_ctx, block_size, n_steps, temperature=0.0, seed=0,
-              want_logits=True):
+              want_logits=True, anchor=None):
         bt = int(ctx_len.numel())
         dev = ctx_len.device
         tok = torch.empty(bt, block_size, dtype=torch.int32, device=dev)
         lg = torch.empty(bt, block_size, self.dims.vocab, dtype=torch.float32, device=dev) if want_logits else None
         cf = torch.empty(bt, n_steps, block_size, dtype=torch.float32, device=dev)
         B.dflash_draft_block(self.cfg, self.w, pool, n_pages, table, table.shape[1], ctx_len, max_ctx, bt,
-                             block_size, n_steps, temperature, seed, tok, lg, cf, self.ws, self.ws_bytes)
+                             block_size, n_steps, temperature, seed, tok, lg, cf, self.ws, self.ws_bytes,
+                             anchor=anchor)
         return tok, lg, cf
 
 

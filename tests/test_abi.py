@@ -79,12 +79,12 @@ def _weights_stub(n_layers):
 
 def _draft(L, cfg, w, **kw):
     args = dict(pool=8, n_pages=4, table=8, max_pages=4, ctx=8, max_ctx=16, batch=2, B=8, S=2, T=0.0,
-                tok=8, ws=256, ws_bytes=1 << 40)
+                anchor=None, tok=8, ws=256, ws_bytes=1 << 40)
     args.update(kw)
     return L.dflash_draft_block(ctypes.byref(cfg), ctypes.byref(w), args["pool"], args["n_pages"], args["table"],
                                 args["max_pages"], args["ctx"], args["max_ctx"], args["batch"], args["B"],
-                                args["S"], args["T"], 0, args["tok"], None, None, args["ws"], args["ws_bytes"],
-                                None)
+                                args["S"], args["T"], 0, args["anchor"], args["tok"], None, None, args["ws"],
+                                args["ws_bytes"], None)
 
 
 def test_draft_argument_errors_return_before_launch(L):
@@ -105,6 +105,8 @@ def test_draft_argument_errors_return_before_launch(L):
     assert _draft(L, _cfg(denoise_schedule=2), w) == -1         # unknown schedule
     assert _draft(L, _cfg(denoise_schedule=-1), w) == -1
     assert _draft(L, cfg, w, batch=0) == 0                      # nothing to do
+    assert _draft(L, cfg, w, S=8, anchor=8) == -1               # an anchor leaves B - 1 positions to denoise
+    assert _draft(L, cfg, w, B=1, S=1, anchor=8) == -1          # nothing left to draft
     w2, keep2 = _weights_stub(cfg.n_layers)
     keep2[1] = None
     assert _draft(L, cfg, w2) == -1                             # a missing per-layer weight
@@ -181,3 +183,12 @@ def test_advance_context_argument_errors(L):
 def test_profiler_select_validates_class(L):
     assert L.dflash_prof_select(99) == -1
     assert L.dflash_prof_select(0) == 0
+
+
+def test_debug_variant_exports_the_same_symbols():
+    if not os.path.exists(B.DEBUG_LIB_PATH):
+        from block_diffusion_drafter_injection_amd import build
+        build.build()
+    D = B.debug_lib()
+    for n in declared_functions():
+        assert hasattr(D, n), n

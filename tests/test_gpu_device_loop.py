@@ -1,17 +1,21 @@
 """Device-side step loop: dflash_advance_context against its definition, and a
 loop of draft -> verify -> advance -> inject that never returns to the host,
 run eagerly and as a replayed HIP graph, against the loop whose injection
-lists the host builds from the acceptance lengths (the one the oracle pins
-in the incremental-loop tests).  Tokens, acceptance lengths and the final
-pool must be identical bit for bit: the injection GEMMs split K by N and K
-only, so a row's K/V do not depend on how many rows share the call."""
+lists the host builds from the acceptance lengths.  Tokens, acceptance
+lengths and the final pool must be identical bit for bit: the injection GEMMs
+split K by N and K only, so a row's K/V do not depend on how many rows share
+the call.  The oracle then replays the same trajectory step by step (draft on
+the pool the GPU had injected by then, verification against the same target
+logits, its own injection of the committed rows), so the device loop is pinned
+to the fp64 definition and not only to the host-driven loop."""
 import numpy as np
 import pytest
 import torch
 
+import oracle
 from block_diffusion_drafter_injection_amd import binding as B
 from block_diffusion_drafter_injection_amd import synth
-from gpu_util import Drafter, alloc_pool, page_plan
+from gpu_util import TIE, Drafter, alloc_pool, compare_pool_entries, f64, np_weights, page_plan, unpack_pool
 
 pytestmark = pytest.mark.gpu
 
@@ -167,3 +171,55 @@ def test_device_loop_and_graph_replay_match_host_loop():
     for other, name in ((dev, "device loop"), (gl, "graph replay")):
         assert torch.equal(other.pool.view(n_pages, -1)[used].view(torch.int16), pa), f"{name} pool differs"
     log(f"graph replay equals the host loop over {K} steps; pools bitwise equal")
+
+    # The oracle along the same trajectory.  Positions below a sequence's length never
+    # change once injected, so the prefix of the final pool is the pool of every earlier
+    # step: each oracle draft reads exactly what the GPU draft read.
+    Wn = np_weights(W)
+    final = [int(c) for c in gl.ctx.cpu().tolist()]
+    gkv = [unpack_pool(dims, gl.pool, n_pages, table_np, b, final[b]) for b in range(bt)]
+    hid0 = f64(synth.make_hiddens(dims, sum(ctx0), 33, "cuda"))
+    own, off = [], 0
+    for c in ctx0:
+        own.append(oracle.inject(dims, Wn, hid0[off:off + c], np.arange(c)))
+        off += c
+    zc, zmaxc, zminc = f64(z), f64(zmax), f64(zmin)
+    ctx = list(ctx0)
+    alive = np.ones(bt, dtype=bool)
+    pairs = 0
+    for k in range(K):
+        pools = [(gkv[b][0][:, :ctx[b]], gkv[b][1][:, :ctx[b]]) for b in range(bt)]
+        res = oracle.draft_block(dims, Wn, pools, ctx, Bk, S, want_logits=False)
+        tok_o = res["tokens"]
+        coin = coins[k].cpu().numpy()
+        zk = zc.copy()
+        for b in range(bt):
+            for i in range(Bk):
+                zk[b, i, tok_o[b, i]] = zmaxc[b, i] if coin[b, i] else zminc[b, i]
+        a_o, out_o = oracle.verify_greedy(zk, tok_o)
+        tok_g, acc_g, out_g = ref[k]
+        for b in range(bt):
+            if not alive[b]:
+                continue
+            same = np.array_equal(tok_g[b], tok_o[b]) and acc_g[b] == a_o[b] and np.array_equal(out_g[b], out_o[b])
+            if not same:
+                near = any(res["gap"][b, s, i] < TIE for s in range(S) for i in range(Bk)
+                           if res["committed_at"][b, i] == s) or np.any(res["boundary_gap"][b, :S - 1] < TIE)
+                assert near, f"step {k} seq {b}: GPU {tok_g[b]} a={acc_g[b]} oracle {tok_o[b]} a={a_o[b]}"
+                alive[b] = False
+                continue
+            pairs += 1
+        hk = f64(hid[k])
+        for b in range(bt):
+            n = int(a_o[b]) + 1
+            Kn, Vn = oracle.inject(dims, Wn, hk[b * (Bk + 1):b * (Bk + 1) + n], np.arange(ctx[b], ctx[b] + n))
+            own[b] = (np.concatenate([own[b][0], Kn], 1), np.concatenate([own[b][1], Vn], 1))
+            ctx[b] += n
+    log(f"oracle replay of the device loop: {pairs} of {K * bt} (step, sequence) pairs bit-exact, "
+        f"{int((~alive).sum())} dropped after a near-tie")
+    assert pairs >= (K * bt) // 2
+    for b in range(bt):
+        if alive[b]:
+            assert ctx[b] == final[b]
+            compare_pool_entries(gkv[b][0], own[b][0], dims.dtype, f"seq {b} K")
+            compare_pool_entries(gkv[b][1], own[b][1], dims.dtype, f"seq {b} V")

@@ -87,7 +87,7 @@ def test_incremental_injection_is_bitwise_one_shot():
     assert torch.equal(one.view(torch.int16), inc.view(torch.int16))
 
 
-def _draft_case(dims, ctx, B, S, T, seed, want_logits=True, schedule="progressive", qk=False):
+def _draft_case(dims, ctx, B, S, T, seed, want_logits=True, schedule="progressive", qk=False, anchor=None):
     W = synth.make_weights(dims, seed, "cuda")
     if qk:
         dims, W = _with_qk(dims, W, seed + 5)
@@ -104,11 +104,12 @@ def _draft_case(dims, ctx, B, S, T, seed, want_logits=True, schedule="progressiv
         pools.append((f64(Kb), f64(Vb)))
         off += c
     dr = Drafter(dims, W, max_batch=len(ctx), block_size=B, max_ctx=max(ctx), schedule=schedule)
+    anc = None if anchor is None else torch.tensor(anchor, dtype=torch.int32, device="cuda")
     tok, lg, cf = dr.draft(pool, n_pages, tab, ctx_tensor(ctx), max(ctx), B, S, T, seed=1234 + seed,
-                           want_logits=want_logits)
+                           want_logits=want_logits, anchor=anc)
     torch.cuda.synchronize()
     res = oracle.draft_block(dims, np_weights(W), pools, ctx, B, S, temperature=T, seed=1234 + seed,
-                             schedule=schedule)
+                             schedule=schedule, anchor=anchor)
     return res, tok.cpu().numpy(), (f64(lg) if lg is not None else None), f64(cf), (dr, pool, n_pages, tab)
 
 
@@ -158,6 +159,29 @@ def test_draft_qk_norm_matches_oracle(name, ctx, B, S, d):
     res, tok, lg, cf, _ = _draft_case(dims, ctx, B, S, 0.0, seed=80 + B, qk=True)
     out = compare_draft(dims, S, res, tok, lg, cf)
     print(f"draft (QK-norm) {name} d={d} ctx={ctx} B={B} S={S}: {out}")
+    assert out["compared"] >= tok.size // 2
+
+
+@pytest.mark.parametrize("name,ctx,B,S,T,schedule", [
+    ("tiny", [64, 3], 4, 2, 0.0, "progressive"),
+    ("small", [0, 37, 300], 8, 2, 0.0, "progressive"),
+    ("small", [130, 16], 16, 3, 0.0, "progressive"),
+    ("small", [77], 16, 2, 0.0, "progressive"),       # one sequence: the skinny GEMMs
+    ("small", [77, 8], 8, 2, 1.0, "progressive"),
+    ("small", [45, 200], 8, 2, 0.0, "repredict"),
+    ("small", [9, 40], 2, 1, 0.0, "progressive"),     # one drafted position
+])
+def test_draft_with_anchor_matches_oracle(name, ctx, B, S, T, schedule):
+    """Block position 0 given (the last committed token of a closed loop), the other
+    B-1 positions denoised: tokens, logits and confidences against the oracle."""
+    dims = _dims(name)
+    rng = np.random.default_rng(B * 7 + S)
+    anchor = rng.integers(0, dims.vocab, size=len(ctx)).tolist()
+    res, tok, lg, cf, _ = _draft_case(dims, ctx, B, S, T, seed=110 + B + S, schedule=schedule, anchor=anchor)
+    assert np.array_equal(tok[:, 0], anchor)
+    assert np.all(np.isnan(cf[:, :, 0]))
+    out = compare_draft(dims, S, res, tok, lg, cf, schedule=schedule)
+    print(f"anchored draft {name} ctx={ctx} B={B} S={S} T={T} {schedule}: {out}")
     assert out["compared"] >= tok.size // 2
 
 
@@ -318,3 +342,63 @@ def test_target_forward_matches_oracle(n_tok_case, qk):
     torch.cuda.synchronize()
     rel3 = np.max(np.abs(f64(z3) - zg[:, :3]), axis=-1) / np.max(np.abs(zo[:, :3]), axis=-1)
     assert rel3.max() <= 1e-3, rel3.max()
+
+
+def test_unmapped_context_pages_are_left_out():
+    """Context pages the block table leaves unmapped (-1) are skipped by the MFMA context
+    kernel, as by the VALU one: the draft equals the oracle's over the context with those
+    tokens removed (block positions still ctx_len + i).  Physical page 0 is kept unused and
+    NaN-poisoned, so the page read in place of an unmapped first page holds NaN: its
+    scores must be masked and its values zeroed, or the output turns NaN."""
+    dims = SMALL
+    ctx, B, S = [100, 70], 8, 2
+    unmapped = {0: [0, 3], 1: [2]}
+    W = synth.make_weights(dims, 51, "cuda")
+    pages = [(c + 15) // 16 for c in ctx]
+    n_pages = 1 + sum(pages)
+    table = np.zeros((len(ctx), max(pages)), dtype=np.int32)
+    nxt = 1
+    for b, npg in enumerate(pages):
+        table[b, :npg] = np.arange(nxt, nxt + npg)
+        nxt += npg
+    pool = alloc_pool(dims, n_pages)          # NaN everywhere, physical page 0 stays so
+    K, V = synth.make_pool_values(dims, sum(ctx), 52, "cuda")
+    pools, off = [], 0
+    for b, c in enumerate(ctx):
+        Kb, Vb = K[:, off:off + c], V[:, off:off + c]
+        pack_pool(dims, pool, n_pages, table, b, Kb, Vb)
+        keep = np.ones(c, dtype=bool)
+        for lp in unmapped[b]:
+            keep[16 * lp:16 * lp + 16] = False
+            table[b, lp] = -1
+        # the oracle slices the first ctx_len tokens of what it is given: the kept ones
+        pools.append((f64(Kb)[:, keep], f64(Vb)[:, keep]))
+        off += c
+    tab = torch.from_numpy(table).cuda()
+    dr = Drafter(dims, W, max_batch=len(ctx), block_size=B, max_ctx=max(ctx))
+    tok, lg, cf = dr.draft(pool, n_pages, tab, ctx_tensor(ctx), max(ctx), B, S)
+    torch.cuda.synchronize()
+    assert torch.isfinite(lg).all()
+    res = oracle.draft_block(dims, np_weights(W), pools, ctx, B, S)
+    out = compare_draft(dims, S, res, tok.cpu().numpy(), f64(lg), f64(cf))
+    print(f"unmapped pages {unmapped}: {out}")
+    assert out["compared"] >= tok.numel() // 2
+
+
+@pytest.mark.parametrize("V", [4096, 5003])
+def test_greedy_verify_misaligned_logits(V):
+    """Target logits at a base that is 4- but not 16-byte aligned (an offset view): the
+    row kernel must not take its 128-bit path, and the result equals the oracle's."""
+    bt, B = 5, 8
+    g = torch.Generator(device="cuda").manual_seed(V)
+    draft = torch.randint(0, V, (bt, B), generator=g, device="cuda", dtype=torch.int32)
+    zt = synth.make_greedy_target_logits(draft, V, 0.7, seed=V, device="cuda")
+    buf = torch.empty(zt.numel() + 1, dtype=torch.float32, device="cuda")
+    zo = buf[1:].view(zt.shape)
+    zo.copy_(zt)
+    assert zo.data_ptr() % 16 != 0
+    acc, out = verify(zo, draft)
+    torch.cuda.synchronize()
+    acc_o, out_o = oracle.verify_greedy(zt.cpu().numpy(), draft.cpu().numpy())
+    assert np.array_equal(acc.cpu().numpy(), acc_o)
+    assert np.array_equal(out.cpu().numpy(), out_o)

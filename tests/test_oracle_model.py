@@ -351,3 +351,98 @@ def test_synthetic_match_rate_gives_truncated_geometric_acceptance():
     expect = p * (1 - p ** B) / (1 - p)
     sd = np.std(acc) / np.sqrt(n)
     assert abs(acc.mean() - expect) < 4 * sd
+
+
+@pytest.mark.parametrize("chunk", [1, 7, 16, 36, 37, 100])
+def test_lm_head_chunks_match_explicit_dots(chunk):
+    """The LM head is computed over vocabulary chunks; every column of every row, whatever
+    the chunk size (one column, ragged last chunk, one chunk, larger than the vocabulary),
+    equals the plain dot product of the row with that vocabulary row, summed by a loop."""
+    W = np_weights(TINY, 29, std=0.3)
+    rng = np.random.default_rng(31)
+    y = rng.standard_normal((3, TINY.hidden))
+    z = oracle.lm_head_logits(TINY, W, y, chunk=chunk)
+    assert z.shape == (3, TINY.vocab)
+    for r in range(3):
+        for v in range(TINY.vocab):
+            ref = 0.0
+            for c in range(TINY.hidden):
+                ref += float(y[r, c]) * float(W["lm_head"][v, c])
+            assert abs(z[r, v] - ref) <= 1e-12 * max(1.0, abs(ref)), (r, v, chunk)
+
+
+def test_lm_head_default_chunks_over_a_large_vocabulary():
+    """A vocabulary spanning three default chunks (16384 columns each, ragged last one):
+    the chunked product equals one whole-matrix product, and the columns on both sides of
+    each chunk edge equal their explicit dot products."""
+    dims = replace(TINY, hidden=8, vocab=2 * 16384 + 5)
+    rng = np.random.default_rng(32)
+    W = {"lm_head": rng.standard_normal((dims.vocab, dims.hidden))}
+    y = rng.standard_normal((4, dims.hidden))
+    z = oracle.lm_head_logits(dims, W, y)
+    assert np.allclose(z, y @ W["lm_head"].T, rtol=1e-13, atol=1e-13)
+    for v in (0, 16383, 16384, 16385, 32767, 32768, dims.vocab - 1):
+        for r in range(4):
+            ref = sum(float(y[r, c]) * float(W["lm_head"][v, c]) for c in range(dims.hidden))
+            assert abs(z[r, v] - ref) <= 1e-12 * max(1.0, abs(ref)), (r, v)
+
+
+def test_anchored_single_step_is_forward_plus_argmax():
+    """With an anchor, block position 0 holds the given token from the start: one step
+    equals the brute-force forward of [anchor, MASK, ...] plus argmax on positions 1..B-1,
+    and position 0 keeps the anchor."""
+    W = np_weights(TINY, 33, std=0.3)
+    ctx = [4, 13]
+    pools = [rand_pool(TINY, T, 90 + T) for T in ctx]
+    anchor = np.array([5, 17])
+    B = 5
+    r = oracle.draft_block(TINY, W, pools, ctx, block_size=B, n_steps=1, anchor=anchor)
+    tau0 = np.full((2, B), TINY.mask_token_id)
+    tau0[:, 0] = anchor
+    y = np.array(brute.forward(TINY, W, pools, ctx, tau0.tolist()))
+    z = y @ W["lm_head"].T
+    assert np.array_equal(r["tokens"][:, 0], anchor)
+    assert np.array_equal(r["tokens"][:, 1:], np.argmax(z[:, 1:], -1))
+    assert np.all(r["committed_at"][:, 0] == -1) and np.all(r["committed_at"][:, 1:] == 0)
+    assert np.all(np.isnan(r["conf"][:, 0, 0])) and np.all(r["cand"][:, 0, 0] == -1)
+
+
+@pytest.mark.parametrize("B,S", [(8, 2), (5, 2), (16, 3), (4, 3)])
+def test_anchored_progressive_schedule_commits_over_the_open_positions(B, S):
+    W = np_weights(TINY, 34, std=0.3)
+    ctx = [0, 7, 21]
+    pools = [rand_pool(TINY, T, 95 + T) for T in ctx]
+    anchor = np.array([1, 36, 12])
+    r = oracle.draft_block(TINY, W, pools, ctx, block_size=B, n_steps=S, anchor=anchor)
+    want = oracle.commit_counts(B - 1, S)
+    assert sum(want) == B - 1
+    for b in range(3):
+        assert r["tokens"][b, 0] == anchor[b] and r["committed_at"][b, 0] == -1
+        got = [int(np.sum(r["committed_at"][b] == s)) for s in range(S)]
+        assert got == want
+        for s in range(S):
+            assert np.isnan(r["conf"][b, s, 0])            # the anchor is never open
+            done = r["committed_at"][b] < s
+            done[0] = True
+            assert np.all(np.isnan(r["conf"][b, s][done]))
+            assert not np.any(np.isnan(r["conf"][b, s][~done]))
+
+
+def test_anchored_repredict_keeps_the_anchor():
+    W = np_weights(TINY, 35, std=0.3)
+    ctx = [3, 9]
+    pools = [rand_pool(TINY, T, 97 + T) for T in ctx]
+    anchor = np.array([2, 30])
+    r1 = oracle.draft_block(TINY, W, pools, ctx, block_size=6, n_steps=1, anchor=anchor, schedule="repredict")
+    p1 = oracle.draft_block(TINY, W, pools, ctx, block_size=6, n_steps=1, anchor=anchor)
+    assert np.array_equal(r1["tokens"], p1["tokens"])
+    r3 = oracle.draft_block(TINY, W, pools, ctx, block_size=6, n_steps=3, anchor=anchor, schedule="repredict")
+    assert np.array_equal(r3["tokens"][:, 0], anchor)
+    # each step re-predicts positions 1.. from the previous step's block, the anchor kept
+    tau = np.full((2, 6), TINY.mask_token_id)
+    tau[:, 0] = anchor
+    for s in range(3):
+        y = np.array(brute.forward(TINY, W, pools, ctx, tau.tolist()))
+        tau[:, 1:] = np.argmax(y @ W["lm_head"].T, -1)[:, 1:]
+        assert np.array_equal(r3["cand"][:, s, 1:], tau[:, 1:])
+    assert np.array_equal(r3["tokens"], tau)
