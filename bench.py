@@ -54,6 +54,11 @@ def parse():
                     help="also time the step loop kept on the GPU (dflash_advance_context, HIP graph replay)")
     ap.add_argument("--block-sweep", type=int, default=1,
                     help="also time the draft call alone at block sizes 4, 8 and 16 on the same batch and pool")
+    ap.add_argument("--incremental", type=int, default=1,
+                    help="also time the incremental workload (block 8, lognormal contexts, shared prefixes)")
+    ap.add_argument("--tiny", type=int, default=1, help="also time the tiny fp32 workload (absolute latency)")
+    ap.add_argument("--closed", type=int, default=1,
+                    help="also time the closed step with a 36-layer Qwen3-8B-shaped target in the loop")
     return ap.parse_args()
 
 
@@ -460,12 +465,300 @@ def main():
         res["batch1_block8"] = batch1_latency(Bn, nd)
     if a.longctx and a.workload == "qwen3_8b_shape_b16_bs32":
         res["longctx_sampled"] = longctx_bench(Bn, nd, W)
+    if a.incremental and a.workload == "qwen3_8b_shape_b16_bs32":
+        res["incremental_b8"] = incremental_bench(a, Bn, W)
+    if a.tiny:
+        res["tiny_fp32_b4"] = tiny_bench(a, Bn)
     if a.target:
         res["target_forward"] = target_forward_bench(Bn, nd)
+    if a.closed and a.workload == "qwen3_8b_shape_b16_bs32":
+        res["closed_step"] = closed_step_bench(a, Bn, W)
     if a.cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(dims, W, wl, B, S, int(ctx_before[0]))
     res["setup_s"] = round(setup_s, 1)
     print(json.dumps(res))
+
+
+def host_step_loop(Bn, cfg, w, dims, bt, B, S, pool, n_pages, table, max_pages, max_ctx, ctx0, new_hid, ws,
+                   ws_bytes, p_match, steps, warmup, seed):
+    """The drafter step driven from the host, as the main measurement runs it: inject the
+    previous step's a+1 accepted tokens of every sequence (their rows of new_hid), draft a
+    block, verify it greedily against target logits that agree with each draft token with
+    probability p_match (the stand-in for the target model, outside the timed intervals).
+    Returns ms per step (inject + draft + verify, HIP events on the stream), the draft-only
+    time on the final state, and the accepted tokens (a+1 summed over sequences) per step."""
+    import numpy as np
+    import torch
+    dev = "cuda"
+    stream = torch.cuda.current_stream()
+    g = torch.Generator(device=dev).manual_seed(seed)
+    z0 = torch.randn(bt, B + 1, dims.vocab, generator=g, device=dev, dtype=torch.float32)
+    zmax = z0[:, :B].amax(-1) + 1.0
+    zmin = z0[:, :B].amin(-1) - 1.0
+    ctx = np.asarray(ctx0, dtype=np.int64).copy()
+    ctx_dev = torch.tensor(ctx, dtype=torch.int32, device=dev)
+    tok = torch.empty(bt, B, dtype=torch.int32, device=dev)
+    acc = torch.empty(bt, dtype=torch.int32, device=dev)
+    outt = torch.empty(bt, B + 1, dtype=torch.int32, device=dev)
+    vws_bytes = Bn.dflash_verify_workspace_size(bt, B, dims.vocab)
+    vws = torch.empty(vws_bytes, dtype=torch.uint8, device=dev)
+    pin_seq = torch.empty(bt * (B + 1), dtype=torch.int32, pin_memory=True)
+    pin_pos = torch.empty(bt * (B + 1), dtype=torch.int32, pin_memory=True)
+    dev_seq = torch.empty(bt * (B + 1), dtype=torch.int32, device=dev)
+    dev_pos = torch.empty(bt * (B + 1), dtype=torch.int32, device=dev)
+    last = None
+    hot, accs = [], []
+    for i in range(warmup + steps):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        n_new = 0
+        if last is not None:
+            seqs = np.concatenate([np.full(int(x) + 1, b) for b, x in enumerate(last)])
+            poss = np.concatenate([np.arange(ctx[b], ctx[b] + int(x) + 1) for b, x in enumerate(last)])
+            n_new = len(seqs)
+            pin_seq[:n_new] = torch.from_numpy(seqs.astype(np.int32))
+            pin_pos[:n_new] = torch.from_numpy(poss.astype(np.int32))
+            dev_seq[:n_new].copy_(pin_seq[:n_new], non_blocking=True)
+            dev_pos[:n_new].copy_(pin_pos[:n_new], non_blocking=True)
+            ctx = ctx + last + 1
+            ctx_dev.copy_(torch.from_numpy(ctx.astype(np.int32)), non_blocking=True)
+        ev[0].record(stream)
+        if n_new:
+            Bn.dflash_inject_kv(cfg, w, new_hid, dev_seq, dev_pos, n_new, pool, n_pages, table, bt, max_pages, ws,
+                                ws_bytes)
+        Bn.dflash_draft_block(cfg, w, pool, n_pages, table, max_pages, ctx_dev, max_ctx, bt, B, S, 0.0, 0, tok, None,
+                              None, ws, ws_bytes)
+        ev[1].record(stream)
+        coin = torch.rand(bt, B, generator=g, device=dev) < p_match
+        idx = tok.long().unsqueeze(-1)
+        keep = z0[:, :B].gather(-1, idx)
+        z0[:, :B].scatter_(-1, idx, torch.where(coin, zmax, zmin).unsqueeze(-1))
+        ev[2].record(stream)
+        Bn.dflash_verify_block(bt, B, dims.vocab, z0, tok, 0.0, None, None, acc, outt, vws, vws_bytes)
+        ev[3].record(stream)
+        z0[:, :B].scatter_(-1, idx, keep)
+        last = acc.cpu().numpy().astype(np.int64)     # the scheduler needs the acceptance
+        torch.cuda.synchronize()
+        if i >= warmup:
+            hot.append(ev[0].elapsed_time(ev[1]) + ev[2].elapsed_time(ev[3]))
+            accs.append(int(np.sum(last + 1)))
+    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    nd = 5
+    d0.record(stream)
+    for _ in range(nd):
+        Bn.dflash_draft_block(cfg, w, pool, n_pages, table, max_pages, ctx_dev, max_ctx, bt, B, S, 0.0, 0, tok, None,
+                              None, ws, ws_bytes)
+    d1.record(stream)
+    torch.cuda.synchronize()
+    return float(np.mean(hot)), d0.elapsed_time(d1) / nd, accs, ctx
+
+
+def incremental_bench(a, Bn, W):
+    """The incremental workload: batch 32, block 8, two denoise steps, contexts lognormal
+    (median 2048, clamped to [512, 8192]) in the paged pool, eight groups of four sequences
+    sharing a 512-token prefix (32 physical pages named by four block-table rows, injected
+    once); every step injects only the a+1 tokens the previous verification committed, then
+    drafts and verifies.  Same Qwen3-8B-shaped weights as the main measurement."""
+    import numpy as np
+    import torch
+    from block_diffusion_drafter_injection_amd import synth
+    wl = synth.WORKLOADS["incremental_8b_shape_b8_bs32"]
+    dims, bt, B, S, dev = wl.dims, wl.batch, wl.block_size, wl.n_steps, "cuda"
+    cfg, w = Bn.make_config(dims), Bn.Weights(W)
+    ctx0 = synth.context_lengths(wl).numpy().astype(np.int64)
+    steps, warm = a.steps, a.warmup
+    grow = (steps + warm + 2) * (B + 1)
+    shared_pages, group = wl.shared_prefix // 16, wl.group_size
+    need = [(int(c) + grow + 15) // 16 for c in ctx0]
+    max_pages = max(need)
+    table = np.full((bt, max_pages), -1, dtype=np.int32)
+    nxt = 0
+    for g0 in range(0, bt, group):
+        table[g0:g0 + group, :shared_pages] = np.arange(nxt, nxt + shared_pages)
+        nxt += shared_pages
+    for b in range(bt):
+        table[b, shared_pages:need[b]] = np.arange(nxt, nxt + need[b] - shared_pages)
+        nxt += need[b] - shared_pages
+    n_pages = nxt
+    tab = torch.from_numpy(table).to(dev)
+    pool = torch.zeros(Bn.pool_elems(dims, n_pages), dtype=dims.torch_dtype, device=dev)
+    max_ctx = int(ctx0.max()) + grow
+    ws_bytes = Bn.dflash_workspace_size(cfg, bt, B, 8192, max_ctx)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    # initial contexts (setup, untimed): each shared prefix injected once, by the group's first sequence
+    for b in range(bt):
+        start = wl.shared_prefix if b % group else 0
+        c = int(ctx0[b])
+        hid = synth.make_hiddens(dims, c - start, wl.seed * 1000 + b, dev)
+        Bn.dflash_inject_kv(cfg, w, hid, torch.full((c - start,), b, dtype=torch.int32, device=dev),
+                            torch.arange(start, c, dtype=torch.int32, device=dev), c - start, pool, n_pages, tab, bt,
+                            max_pages, ws, ws_bytes)
+        del hid
+    new_hid = synth.make_hiddens(dims, bt * (B + 1), wl.seed + 77, dev)
+    torch.cuda.synchronize()
+    ms, draft_ms, accs, ctx_end = host_step_loop(Bn, cfg, w, dims, bt, B, S, pool, n_pages, tab, max_pages, max_ctx,
+                                                 ctx0, new_hid, ws, ws_bytes, wl.p_match, steps, warm, 3000 + wl.seed)
+    accepted = float(np.mean(accs))
+    t_roof = draft_roofline_ms(dims, bt, B, S, ctx_end)
+    unique_pages = float(np.sum(ctx_end)) - (bt - bt // group) * wl.shared_prefix
+    del pool, ws, new_hid
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "batch": bt, "block": B, "denoise_steps": S, "ctx_min": int(ctx0.min()),
+            "ctx_max": int(ctx0.max()), "ctx_mean": round(float(ctx0.mean()), 1), "shared_prefix": wl.shared_prefix,
+            "group_size": group, "steps": steps,
+            "ms_per_step": round(ms, 4), "accepted_tok_s": round(accepted / (ms / 1e3), 1),
+            "mean_accept_plus_bonus": round(accepted / bt, 3),
+            "draft_ms": round(draft_ms, 4), "drafted_tok_s": round(bt * B / (draft_ms / 1e3), 1),
+            "t_roof_ms": round(t_roof, 4), "frac": round(t_roof / draft_ms, 4),
+            "note": "step = inject a+1 committed tokens per sequence + draft + greedy verify; the roofline "
+                    "counts every sequence's context K/V once per layer and forward (shared prefix pages too), "
+                    f"the pool holding {int(unique_pages)} distinct tokens"}
+
+
+def tiny_bench(a, Bn):
+    """The tiny fp32 workload (hidden 256, 2 layers, vocab 1024, block 4, two denoise steps,
+    batch 1, context 64): absolute latencies, since its work is far below any roofline (the
+    call is a chain of short kernels, so launch latency sets its time)."""
+    import numpy as np
+    import torch
+    from block_diffusion_drafter_injection_amd import synth
+    wl = synth.WORKLOADS["tiny_fp32_b4"]
+    dims, bt, B, S, dev = wl.dims, wl.batch, wl.block_size, wl.n_steps, "cuda"
+    ctx0 = synth.context_lengths(wl).numpy().astype(np.int64)
+    W = synth.make_weights(dims, wl.seed, dev)
+    cfg, w = Bn.make_config(dims), Bn.Weights(W)
+    steps, warm = max(a.steps, 20), max(a.warmup, 3)
+    grow = (steps + warm + 2) * (B + 1)
+    max_ctx = int(ctx0.max()) + grow
+    max_pages = (max_ctx + 15) // 16
+    tab = torch.arange(max_pages, dtype=torch.int32, device=dev).view(1, -1)
+    pool = torch.zeros(Bn.pool_elems(dims, max_pages), dtype=dims.torch_dtype, device=dev)
+    ws_bytes = Bn.dflash_workspace_size(cfg, bt, B, 256, max_ctx)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    c = int(ctx0[0])
+    Bn.dflash_inject_kv(cfg, w, synth.make_hiddens(dims, c, wl.seed * 1000, dev),
+                        torch.zeros(c, dtype=torch.int32, device=dev), torch.arange(c, dtype=torch.int32, device=dev),
+                        c, pool, max_pages, tab, 1, max_pages, ws, ws_bytes)
+    new_hid = synth.make_hiddens(dims, bt * (B + 1), wl.seed + 77, dev)
+    torch.cuda.synchronize()
+    ms, draft_ms, accs, _ = host_step_loop(Bn, cfg, w, dims, bt, B, S, pool, max_pages, tab, max_pages, max_ctx, ctx0,
+                                           new_hid, ws, ws_bytes, wl.p_match, steps, warm, 3000 + wl.seed)
+    accepted = float(np.mean(accs))
+    del pool, ws, W, w
+    torch.cuda.empty_cache()
+    return {"workload": wl.name, "dtype": "f32", "batch": bt, "block": B, "ctx": c, "steps": steps,
+            "draft_ms": round(draft_ms, 4), "ms_per_step": round(ms, 4),
+            "accepted_tok_s": round(accepted / (ms / 1e3), 1), "mean_accept_plus_bonus": round(accepted / bt, 3),
+            "note": "absolute latency (fp32 VALU kernels; far below every roofline)"}
+
+
+def closed_step_bench(a, Bn, W):
+    """The drafter step with a target model in the loop: the Qwen3-8B-shaped draft (block 16:
+    the last committed token as anchor plus 15 drafted positions) and a random-init
+    Qwen3-8B-shaped 36-layer target, batch 32, contexts 4096.  One step: draft ->
+    dflash_target_forward over the block (full logits, five captured layers, K/V appended to
+    the target's cache) -> greedy verification of the 15 drafted tokens ->
+    dflash_advance_context -> injection of the captured states of the a+1 processed tokens ->
+    the bonus token becomes the next anchor.  Everything on the device, timed with events.
+    Random-init draft and target agree on almost no token, so a is about 0 and each step
+    commits about one token per sequence: the figure is the step's time, not a speed-up."""
+    import numpy as np
+    import torch
+    from dataclasses import replace
+    from block_diffusion_drafter_injection_amd import synth
+    dd = synth.QWEN3_8B_SHAPE
+    td = replace(synth.QWEN3_8B_SHAPE, n_layers=36, n_fuse=1)
+    caps = [1, 9, 17, 25, 33]
+    bt, Bk, S, ctx, dev = 32, 16, 2, 4096, "cuda"
+    steps, warm = a.steps, a.warmup
+    Wt = synth.make_weights(td, 7, dev)
+    dcfg, dw = Bn.make_config(dd), Bn.Weights(W)
+    tcfg, tw = Bn.make_config(td), Bn.Weights(Wt)
+    inj = ctx - 1
+    grow = (steps + warm + 2) * Bk
+    pages_per = (inj + grow + 15) // 16
+    n_pages = bt * pages_per
+    table = torch.arange(n_pages, dtype=torch.int32, device=dev).view(bt, pages_per)
+    # both caches filled directly (values of the spread injection produces; setup, untimed)
+    pool_d = torch.empty(Bn.pool_elems(dd, n_pages), dtype=torch.bfloat16, device=dev).normal_(0.0, 3.6)
+    pool_t = torch.empty(Bn.pool_elems(td, n_pages), dtype=torch.bfloat16, device=dev).normal_(0.0, 3.6)
+    max_ctx = inj + grow
+    dws_bytes = Bn.dflash_workspace_size(dcfg, bt, Bk, bt * Bk, max_ctx)
+    dws = torch.empty(dws_bytes, dtype=torch.uint8, device=dev)
+    tws_bytes = Bn.dflash_workspace_size(tcfg, bt, Bk, 0, max_ctx)
+    tws = torch.empty(tws_bytes, dtype=torch.uint8, device=dev)
+    vws_bytes = Bn.dflash_verify_workspace_size(bt, Bk - 1, td.vocab)
+    vws = torch.empty(vws_bytes, dtype=torch.uint8, device=dev)
+    ctx_dev = torch.full((bt,), inj, dtype=torch.int32, device=dev)
+    anchor = torch.randint(0, dd.vocab, (bt,), device=dev, dtype=torch.int32)
+    tok = torch.empty(bt, Bk, dtype=torch.int32, device=dev)
+    drafted = torch.empty(bt, Bk - 1, dtype=torch.int32, device=dev)
+    z = torch.empty(bt, Bk, td.vocab, dtype=torch.float32, device=dev)
+    hid = torch.empty(bt, Bk, len(caps) * td.hidden, dtype=torch.bfloat16, device=dev)
+    acc = torch.empty(bt, dtype=torch.int32, device=dev)
+    out = torch.empty(bt, Bk, dtype=torch.int32, device=dev)
+    seq = torch.empty(bt * Bk, dtype=torch.int32, device=dev)
+    pos = torch.empty_like(seq)
+    F = len(caps)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev:
+            ev[0].record(stream)
+        Bn.dflash_draft_block(dcfg, dw, pool_d, n_pages, table, pages_per, ctx_dev, max_ctx, bt, Bk, S, 0.0, 0, tok,
+                              None, None, dws, dws_bytes, anchor=anchor)
+        if ev:
+            ev[1].record(stream)
+        Bn.dflash_target_forward(tcfg, tw, pool_t, n_pages, table, pages_per, ctx_dev, max_ctx, bt, Bk, tok, caps, z,
+                                 hid, tws, tws_bytes)
+        if ev:
+            ev[2].record(stream)
+        drafted.copy_(tok[:, 1:])
+        Bn.dflash_verify_block(bt, Bk - 1, td.vocab, z, drafted, 0.0, None, None, acc, out, vws, vws_bytes)
+        Bn.dflash_advance_context(bt, Bk - 1, acc, ctx_dev, seq, pos)
+        Bn.dflash_inject_kv(dcfg, dw, hid.view(bt * Bk, F * td.hidden), seq, pos, bt * Bk, pool_d, n_pages, table, bt,
+                            pages_per, dws, dws_bytes)
+        anchor.copy_(out.gather(1, acc.long().unsqueeze(1)).squeeze(1))
+        if ev:
+            ev[3].record(stream)
+
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    ctx_start = int(ctx_dev.min().item())
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+    tot = torch.zeros(bt, dtype=torch.int64, device=dev)
+    for i in range(steps):
+        step(evs[i])
+        tot += acc.long() + 1
+    torch.cuda.synchronize()
+    ms = [e[0].elapsed_time(e[3]) for e in evs]
+    d_ms = [e[0].elapsed_time(e[1]) for e in evs]
+    t_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    committed = float(tot.sum().item()) / steps
+    # rooflines: the draft's, and one causal target forward of bt*Bk rows (weights once,
+    # every context K/V once per layer, the LM head over every row)
+    H, L, I, V = td.hidden, td.n_layers, td.intermediate, td.vocab
+    nq, nkv, d = td.n_q_heads, td.n_kv_heads, td.head_dim
+    M = bt * Bk
+    tt = 0.0
+    for N, K in [((nq + 2 * nkv) * d, H), (H, nq * d), (2 * I, H), (H, I)]:
+        tt += L * max(2.0 * M * N * K / PEAK_BF16, N * K * 2 / PEAK_HBM)
+    tt += L * float(bt * ctx_start) * nkv * d * 2 * 2 / PEAK_HBM
+    tt += max(2.0 * M * V * H / PEAK_BF16, V * H * 2 / PEAK_HBM)
+    td_roof = draft_roofline_ms(dd, bt, Bk, S, [ctx_start] * bt)
+    del Wt, tw, pool_d, pool_t, dws, tws, z, hid
+    torch.cuda.empty_cache()
+    return {"batch": bt, "block": Bk, "anchor": True, "drafted_per_seq": Bk - 1, "ctx_start": ctx_start + 1,
+            "target_layers": L, "captured_layers": caps, "steps": steps,
+            "ms_per_step": round(float(np.mean(ms)), 4), "draft_ms": round(float(np.mean(d_ms)), 4),
+            "target_forward_ms": round(float(np.mean(t_ms)), 4),
+            "verify_advance_inject_ms": round(float(np.mean(ms)) - float(np.mean(d_ms)) - float(np.mean(t_ms)), 4),
+            "committed_tok_s": round(committed / (float(np.mean(ms)) / 1e3), 1),
+            "mean_accept_plus_bonus": round(committed / bt, 3),
+            "draft_t_roof_ms": round(td_roof, 4), "target_t_roof_ms": round(tt * 1e3, 4),
+            "step_frac": round((td_roof + tt * 1e3) / float(np.mean(ms)), 4),
+            "note": "random-init draft and target: acceptance about 0, so the committed rate is about one token "
+                    "per sequence per step; the step time is the figure"}
 
 
 def target_forward_bench(Bn, nd):

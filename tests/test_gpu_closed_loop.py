@@ -149,11 +149,13 @@ def check_oracle(dd, td, Wd, Wt, g, Bk, S, caps, sample, forward_rule):
 
 
 def test_closed_loop_small_shape():
-    """Draft: the small bf16 shape over a vocabulary of 16 (random-init models then agree
-    often enough for acceptances above 0).  Target: 4 random-init layers of width 384 (the
-    draft's fused-layer width), layers 0, 2, 3 captured.  Batch 6, block 8 (anchor + 7),
-    12 steps, every sequence checked every step."""
-    V = 16
+    """Draft: the small bf16 shape over a vocabulary of 4 (random-init models then agree
+    often enough for acceptances above 0; the LM head then has a single partial column
+    tile).  Target: 4 random-init layers of width 384 (the draft's fused-layer width),
+    layers 0, 2, 3 captured.  Batch 6, block 8 (anchor + 7), 12 steps, every sequence
+    checked every step.  Captured states and appended K/V come out of a multi-layer
+    forward, so they are held to the multi-layer rule."""
+    V = 4
     dd = synth.small_dims(vocab=V)
     td = synth.ModelDims(hidden=384, n_layers=4, n_q_heads=4, n_kv_heads=2, head_dim=128, intermediate=768,
                          vocab=V, n_fuse=1, target_hidden=384, rope_base=1e6)
@@ -168,7 +170,7 @@ def test_closed_loop_small_shape():
     assert np.all((accs >= 0) & (accs <= Bk - 1))
     assert np.array_equal(g["final"], np.array(ctx0) - 1 + (accs + 1).sum(0))
     stats = check_oracle(dd, td, np64(Wd), np64(Wt), g, Bk, S, caps, list(range(len(ctx0))),
-                         lambda got, ref, label: compare_pool_entries(got, ref, "bf16", label))
+                         compare_forward_outputs)
     log(f"closed loop vs oracle chain: {stats}")
     assert stats["pairs"] >= steps * len(ctx0) // 2
     assert accs.sum() > 0
