@@ -49,7 +49,8 @@ class dflash_weights(ctypes.Structure):
 
 _libs = {}
 EXPORTS = ["dflash_workspace_size", "dflash_inject_kv", "dflash_draft_block", "dflash_verify_workspace_size",
-           "dflash_verify_block", "dflash_advance_context", "dflash_adaptive_block_size", "dflash_target_forward",
+           "dflash_verify_block", "dflash_verify_block_static", "dflash_advance_context",
+           "dflash_adaptive_block_size", "dflash_target_forward",
            "dflash_status_string",
            "dflash_prof_select", "dflash_prof_collect"]
 
@@ -83,6 +84,8 @@ def _load(path):
     L.dflash_verify_workspace_size.restype = sz
     L.dflash_verify_block.argtypes = [i32, i32, i32, vp, vp, f32, vp, vp, vp, vp, vp, sz, vp]
     L.dflash_verify_block.restype = i32
+    L.dflash_verify_block_static.argtypes = [i32, i32, i32, vp, vp, f32, vp, vp, vp, vp, vp]
+    L.dflash_verify_block_static.restype = i32
     L.dflash_advance_context.argtypes = [i32, i32, vp, vp, vp, vp, vp]
     L.dflash_advance_context.restype = i32
     L.dflash_target_forward.argtypes = [cfgp, wp, vp, i32, vp, i32, vp, i32, i32, i32, vp,
@@ -182,6 +185,14 @@ def dflash_verify_block(batch, block_size, vocab, target_logits, draft_tokens, t
                                      float(temperature), _ptr(draft_logits), _ptr(uniforms), _ptr(accept_len),
                                      _ptr(out_tokens), _ptr(workspace), ws_bytes, _stream(stream))
     _check("dflash_verify_block", code)
+
+
+def dflash_verify_block_static(batch, block_size, vocab, target_logits, draft_tokens, temperature, draft_logits,
+                               uniforms, accept_len, out_tokens, stream=None):
+    code = lib().dflash_verify_block_static(batch, block_size, vocab, _ptr(target_logits), _ptr(draft_tokens),
+                                            float(temperature), _ptr(draft_logits), _ptr(uniforms), _ptr(accept_len),
+                                            _ptr(out_tokens), _stream(stream))
+    _check("dflash_verify_block_static", code)
 
 
 def dflash_advance_context(batch, block_size, accept_len, ctx_len, tok_seq, tok_pos, stream=None):

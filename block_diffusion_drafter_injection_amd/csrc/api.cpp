@@ -314,6 +314,65 @@ dflash_status dbg_range(const int32_t* v, size_t n, int lo, int hi, hipStream_t 
     if ((x) != hipSuccess) return DFLASH_EHIP;  \
   } while (0)
 
+// Block verification behind both verify entry points; prof: the timing hooks may
+// record events around it (never for the allocation-free variant).
+dflash_status verify_impl(int32_t batch, int32_t block_size, int32_t vocab, const float* target_logits,
+                          const int32_t* draft_tokens, float temperature, const float* draft_logits,
+                          const float* uniforms, int32_t* accept_len, int32_t* out_tokens, void* workspace,
+                          size_t ws_bytes, hipStream_t stream, bool prof) {
+  if (batch < 0 || vocab < 1) return DFLASH_EINVAL;
+  if (block_size < 1 || block_size > 16) return DFLASH_ECAPACITY;
+  if (!(temperature >= 0.f)) return DFLASH_EINVAL;
+  if (batch == 0) return DFLASH_OK;
+  if (!target_logits || !draft_tokens || !accept_len || !out_tokens) return DFLASH_EINVAL;
+  if (temperature > 0.f && (!draft_logits || !uniforms)) return DFLASH_EINVAL;
+  if (!workspace || ((uintptr_t)workspace & 255)) return DFLASH_EWORKSPACE;
+  if (ws_bytes < verify_ws_bytes(batch, block_size, vocab)) return DFLASH_EWORKSPACE;
+  DBG_CHECK(dbg_range(draft_tokens, (size_t)batch * block_size, 0, vocab - 1, stream));
+  hipError_t e;
+  if (prof) prof_mark(DFLASH_PROF_VERIFY, 0, stream);
+  if (temperature > 0.f)
+    e = launch_verify_sampled(batch, block_size, vocab, target_logits, draft_logits, draft_tokens, uniforms,
+                              temperature, accept_len, out_tokens, workspace, stream);
+  else
+    e = launch_verify_greedy(batch, block_size, vocab, target_logits, draft_tokens, accept_len, out_tokens,
+                             workspace, stream);
+  if (prof) prof_mark(DFLASH_PROF_VERIFY, 1, stream);
+  return e == hipSuccess ? DFLASH_OK : DFLASH_EHIP;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- static scratch
+// Scratch of dflash_verify_block_static, for callers that cannot allocate: one
+// array per GPU the library runs on, held until the process ends.  In host code
+// the array's name only stands in for it; its device address is looked up with
+// hipGetSymbolAddress once per device (with that device current) and that
+// address is what the kernels receive.  The verify kernels write every scratch
+// entry they read within the same call, so nothing needs clearing between calls.
+constexpr size_t kVerifyScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kVerifyScratchBytes];
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+
+// Device address of this process's scratch on the current device.
+hipError_t verify_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 }  // namespace
 
 extern "C" {
@@ -758,25 +817,21 @@ dflash_status dflash_verify_block(int32_t batch, int32_t block_size, int32_t voc
                                   const int32_t* draft_tokens, float temperature, const float* draft_logits,
                                   const float* uniforms, int32_t* accept_len, int32_t* out_tokens,
                                   void* workspace, size_t ws_bytes, hipStream_t stream) {
+  return verify_impl(batch, block_size, vocab, target_logits, draft_tokens, temperature, draft_logits, uniforms,
+                     accept_len, out_tokens, workspace, ws_bytes, stream, true);
+}
+
+dflash_status dflash_verify_block_static(int32_t batch, int32_t block_size, int32_t vocab,
+                                         const float* target_logits, const int32_t* draft_tokens, float temperature,
+                                         const float* draft_logits, const float* uniforms, int32_t* accept_len,
+                                         int32_t* out_tokens, hipStream_t stream) {
   if (batch < 0 || vocab < 1) return DFLASH_EINVAL;
   if (block_size < 1 || block_size > 16) return DFLASH_ECAPACITY;
-  if (!(temperature >= 0.f)) return DFLASH_EINVAL;
-  if (batch == 0) return DFLASH_OK;
-  if (!target_logits || !draft_tokens || !accept_len || !out_tokens) return DFLASH_EINVAL;
-  if (temperature > 0.f && (!draft_logits || !uniforms)) return DFLASH_EINVAL;
-  if (!workspace || ((uintptr_t)workspace & 255)) return DFLASH_EWORKSPACE;
-  if (ws_bytes < verify_ws_bytes(batch, block_size, vocab)) return DFLASH_EWORKSPACE;
-  DBG_CHECK(dbg_range(draft_tokens, (size_t)batch * block_size, 0, vocab - 1, stream));
-  hipError_t e;
-  prof_mark(DFLASH_PROF_VERIFY, 0, stream);
-  if (temperature > 0.f)
-    e = launch_verify_sampled(batch, block_size, vocab, target_logits, draft_logits, draft_tokens, uniforms,
-                              temperature, accept_len, out_tokens, workspace, stream);
-  else
-    e = launch_verify_greedy(batch, block_size, vocab, target_logits, draft_tokens, accept_len, out_tokens,
-                             workspace, stream);
-  prof_mark(DFLASH_PROF_VERIFY, 1, stream);
-  return e == hipSuccess ? DFLASH_OK : DFLASH_EHIP;
+  if (verify_ws_bytes(batch, block_size, vocab) > kVerifyScratchBytes) return DFLASH_ECAPACITY;
+  void* ws = nullptr;
+  if (verify_scratch(&ws) != hipSuccess) return DFLASH_EHIP;
+  return verify_impl(batch, block_size, vocab, target_logits, draft_tokens, temperature, draft_logits, uniforms,
+                     accept_len, out_tokens, ws, kVerifyScratchBytes, stream, false);
 }
 
 int32_t dflash_adaptive_block_size(const int32_t* accept_len, const int32_t* block_of, int32_t n_obs,

@@ -286,6 +286,24 @@ dflash_status dflash_verify_block(int32_t batch, int32_t block_size, int32_t voc
                                   int32_t* out_tokens, void* workspace, size_t ws_bytes,
                                   hipStream_t stream);
 
+/* dflash_verify_block for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * verification with the same arguments and results, but no workspace argument.
+ * Its scratch is a fixed 8 MiB array that the library holds on each GPU it runs on
+ * until the process ends; it is found once per device with hipGetSymbolAddress
+ * (the stream's device must be the calling thread's current device), and nothing
+ * is allocated or freed.  Capacity: dflash_verify_workspace_size(batch,
+ * block_size, vocab) <= 8 MiB (batch 32, block 16, vocabulary 151936 needs about
+ * 0.4 MiB); larger requests return DFLASH_ECAPACITY before anything is enqueued.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (several streams or threads at once) race on it and must be serialised by the
+ * caller.  Each call writes every scratch entry it reads, so no clearing is needed. */
+dflash_status dflash_verify_block_static(int32_t batch, int32_t block_size, int32_t vocab,
+                                         const float* target_logits, const int32_t* draft_tokens,
+                                         float temperature, const float* draft_logits,
+                                         const float* uniforms, int32_t* accept_len,
+                                         int32_t* out_tokens, hipStream_t stream);
+
 /* Block size for the next drafter step, chosen from the acceptance seen so
  * far.  The pages name block sizes that adapt to how hard the input is as a
  * direction ([Deep] 7.3 短期趋势) and note that too large a block wastes draft
