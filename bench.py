@@ -998,8 +998,9 @@ def device_loop(a, Bn, cfg, w, dims, bt, B, S, pool, n_pages, table, pages_per, 
     return {"graph": True, "steps": K, "ms_per_step": round(ms, 4), "wall_ms_per_step": round(wall * 1e3 / K, 4),
             "accepted_tok_s": round(accepted / K / (ms / 1e3), 1),
             "mean_accept_plus_bonus": round(accepted / K / bt, 3),
-            "note": "inject rows of all block+1 verified positions (uncommitted rows skipped), so the "
-                    "injection GEMMs run on batch*(block+1) rows; includes the target-logit stand-in kernels"}
+            "note": "injection rows of all block+1 verified positions, those past the accepted prefix "
+                    "marked -1 and packed out on the device, so the injection GEMMs run on the accepted "
+                    "rows only; includes the target-logit stand-in kernels"}
 
 
 def load_traffic(workload, cls):

@@ -194,7 +194,7 @@ DraftWS draft_layout(const dflash_config* c, int bt, int B, int ctx_cap) {
 }
 
 struct InjectWS {
-  size_t f_hi, f_lo, cs, gemm_part, total;
+  size_t f_hi, f_lo, cs, gemm_part, src, seq_c, pos_c, count, total;
 };
 
 // Split-K partial bytes per injected token (the fc and KV GEMMs run one after
@@ -216,6 +216,10 @@ InjectWS inject_layout(const dflash_config* c, int chunk) {
   w.f_lo = k.take((size_t)chunk * c->hidden * el);
   w.cs = k.take((size_t)chunk * (c->head_dim / 2) * 8);
   w.gemm_part = k.take((size_t)chunk * inject_part_per_token(c));
+  w.src = k.take((size_t)chunk * 4);
+  w.seq_c = k.take((size_t)chunk * 4);
+  w.pos_c = k.take((size_t)chunk * 4);
+  w.count = k.take(4);
   w.total = k.off;
   return w;
 }
@@ -223,7 +227,7 @@ InjectWS inject_layout(const dflash_config* c, int chunk) {
 // Injection chunk the workspace holds (rows of one fused-feature pass).
 int inject_chunk_capacity(const dflash_config* c, size_t ws_bytes) {
   const size_t el = c->dtype == DFLASH_BF16 ? 2 : 4;
-  const size_t per = 2 * c->hidden * el + (c->head_dim / 2) * 8 + inject_part_per_token(c);
+  const size_t per = 2 * c->hidden * el + (c->head_dim / 2) * 8 + inject_part_per_token(c) + 12;
   size_t n = ws_bytes / (per + 1);
   while (n > 0 && inject_layout(c, (int)std::min<size_t>(n, 1 << 30)).total > ws_bytes) n -= std::max<size_t>(1, n / 64);
   return (int)std::min<size_t>(n, 1 << 30);
@@ -424,11 +428,31 @@ dflash_status dflash_inject_kv(const dflash_config* cfg, const dflash_weights* w
   const int d = cfg->head_dim, nkv = cfg->n_kv_heads;
   for (int t0 = 0; t0 < n_tok; t0 += chunk) {
     const int n = std::min(chunk, n_tok - t0);
-    HIP_TRY(launch_rope_table_tokens(tok_pos + t0, n, d, (double)cfg->rope_base, (float2*)at(workspace, L.cs),
-                                     stream));
+    // bf16: the rows to write (tok_seq >= 0) are packed to the front on the
+    // device, and both GEMMs stop at their count, so rows that are skipped
+    // (a step loop's unaccepted block positions) cost no GEMM work.  Each row's
+    // result depends only on its own inputs (fixed K split), so packing leaves
+    // every written value unchanged.
+    const int* seq = tok_seq + t0;
+    const int* pos = tok_pos + t0;
+    const int* rows = nullptr;
+    const int* count = nullptr;
+    if (bf) {
+      int* src = (int*)at(workspace, L.src);
+      int* seq_c = (int*)at(workspace, L.seq_c);
+      int* pos_c = (int*)at(workspace, L.pos_c);
+      int* cnt = (int*)at(workspace, L.count);
+      HIP_TRY(launch_compact_rows(seq, pos, n, src, seq_c, pos_c, cnt, stream));
+      seq = seq_c;
+      pos = pos_c;
+      rows = src;
+      count = cnt;
+    }
+    HIP_TRY(launch_rope_table_tokens(pos, n, d, (double)cfg->rope_base, (float2*)at(workspace, L.cs), stream));
     GemmArgs g{};
     g.wdtype = bf;
-    g.a = ActIn{(const char*)target_hidden + (size_t)t0 * FH * el, nullptr, FH, bf ? ACT_BF16 : ACT_F32};
+    g.a = ActIn{(const char*)target_hidden + (size_t)t0 * FH * el, nullptr, FH, bf ? ACT_BF16 : ACT_F32, rows};
+    g.m_dev = count;
     g.b = BRowsArgs{w->w_fc, nullptr, FH, 0, 0};
     g.M = n;
     g.N = H;
@@ -449,10 +473,11 @@ dflash_status dflash_inject_kv(const dflash_config* cfg, const dflash_weights* w
     k.K = H;
     k.kind = EPI_KVSCATTER;
     k.fixed_split = true;
+    k.m_dev = count;
     k.part = (float*)at(workspace, L.gemm_part);
     k.e.pool = kv_pool;
-    k.e.tok_seq = tok_seq + t0;
-    k.e.tok_pos = tok_pos + t0;
+    k.e.tok_seq = seq;
+    k.e.tok_pos = pos;
     k.e.block_table = block_table;
     k.e.n_seqs = n_seqs;
     k.e.max_pages = max_pages;

@@ -63,6 +63,7 @@ struct ActIn {
   const void* p1;
   int ld;
   int mode;
+  const int* rows;   // optional gather: logical row r reads source row rows[r] (device)
 };
 
 __device__ __forceinline__ void act_store(const ActOut& o, int row, int col, float v) {

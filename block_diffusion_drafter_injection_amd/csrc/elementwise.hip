@@ -241,6 +241,54 @@ hipError_t launch_rope_table_block(const int* ctx_len, int ctx_cap, int batch, i
   return hipGetLastError();
 }
 
+// Stable compaction of injection rows: the rows r < n with tok_seq[r] >= 0
+// become rows 0..count-1 in their order (src[i] = r, seq_c[i] = tok_seq[r],
+// pos_c[i] = tok_pos[r]); rows count..n-1 get seq_c = -1 and pos_c = 0, which
+// the scatter skips.  One workgroup walks the rows 1024 at a time: a ballot
+// ranks the rows of each wave, the wave counts give each wave's offset, and a
+// running total carries over to the next 1024.
+__global__ __launch_bounds__(1024) void compact_rows_kernel(const int* tok_seq, const int* tok_pos, int n, int* src,
+                                                           int* seq_c, int* pos_c, int* count) {
+  __shared__ int wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int base = 0;
+  for (int r0 = 0; r0 < n; r0 += 1024) {
+    const int r = r0 + tid;
+    const int sq = r < n ? tok_seq[r] : -1;
+    const bool v = sq >= 0;
+    const unsigned long long m = __ballot(v);
+    if (lane == 0) wsum[w] = __popcll(m);
+    __syncthreads();
+    int off = base, tot = 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      off += k < w ? wsum[k] : 0;
+      tot += wsum[k];
+    }
+    if (v) {
+      const int i = off + __popcll(m & ((1ull << lane) - 1ull));
+      src[i] = r;
+      seq_c[i] = sq;
+      pos_c[i] = tok_pos[r];
+    }
+    base += tot;
+    __syncthreads();   // wsum is rewritten by the next block of rows
+  }
+  for (int i = base + tid; i < n; i += 1024) {
+    src[i] = 0;
+    seq_c[i] = -1;
+    pos_c[i] = 0;
+  }
+  if (tid == 0) *count = base;
+}
+
+hipError_t launch_compact_rows(const int* tok_seq, const int* tok_pos, int n, int* src, int* seq_c, int* pos_c,
+                               int* count, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(compact_rows_kernel, dim3(1), dim3(1024), 0, s, tok_seq, tok_pos, n, src, seq_c, pos_c, count);
+  return hipGetLastError();
+}
+
 hipError_t launch_rope_table_tokens(const int* tok_pos, int n, int d, double base, float2* cs, hipStream_t s) {
   const int t = n * (d / 2);
   if (t <= 0) return hipSuccess;

@@ -307,7 +307,7 @@ __device__ __forceinline__ void lds_reads_done_barrier() {
 
 template <int NP, int KIND>
 __global__ __launch_bounds__(256, 2) void gemm_dma_kernel(ActIn a, BRows<bf16_t> b, int M, int N, int K, int ksplit,
-                                                           float* part, EpiParams e) {
+                                                           float* part, EpiParams e, const int* m_dev) {
   using C = DmaCfg<NP>;
   constexpr int BM = C::BM, BN = C::BN, BK = C::BK, LPT = C::LPT;
   __shared__ __attribute__((aligned(1024))) unsigned char smem[C::SMEM];
@@ -321,6 +321,11 @@ __global__ __launch_bounds__(256, 2) void gemm_dma_kernel(ActIn a, BRows<bf16_t>
   }
   const int tm = t % ntm, tn = (t / ntm) % ntn, ks = t / (ntm * ntn);
   const int m0 = tm * BM, n0 = tn * BN;
+  // rows from the device count on are left alone: tiles wholly past it leave
+  // at once (the partial layout keeps the row stride of M)
+  const int Mp = M;
+  if (m_dev) M = min(M, max(*m_dev, 0));
+  if (m0 >= M) return;
   const int nkt = K / BK;
   const int kt0 = (int)((long long)ks * nkt / ksplit), kt1 = (int)((long long)(ks + 1) * nkt / ksplit);
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -336,7 +341,8 @@ __global__ __launch_bounds__(256, 2) void gemm_dma_kernel(ActIn a, BRows<bf16_t>
     const bf16_t* base;
     if (row < NP * BM) {
       const int p = row / BM, r = row - p * BM;
-      const int gr = min(m0 + r, M - 1);
+      int gr = min(m0 + r, M - 1);
+      if (a.rows) gr = a.rows[gr];
       base = (const bf16_t*)(p == 0 ? a.p0 : a.p1) + (size_t)gr * a.ld;
     } else {
       base = b.row(min(n0 + row - NP * BM, N - 1), BN);
@@ -405,7 +411,7 @@ __global__ __launch_bounds__(256, 2) void gemm_dma_kernel(ActIn a, BRows<bf16_t>
         Cs[(wm * 64 + 16 * i + 4 * (lane >> 4) + q) * C::LDC + wn * 64 + 16 * j + (lane & 15)] = acc[i][j][q];
   __syncthreads();
   if (ksplit > 1) {
-    float* dst = part + (size_t)ks * M * N;
+    float* dst = part + (size_t)ks * Mp * N;
     constexpr int C4 = BN / 4;
     for (int idx = tid; idx < BM * C4; idx += 256) {
       const int r = idx / C4, c = (idx - r * C4) * 4;
@@ -591,6 +597,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_fl_kernel(ActIn a, BRo
     if (ksplit == 1) {
       constexpr int OW = C::WN / 2, LDW = OW + 4;
       static_assert(C::NW * 64 * LDW * 4 <= C::SMEM, "per-wave output slices");
+      // the slices overlap the pipeline buffers: every wave is done reading
+      // them and every copy has landed before any slice is written
+      __syncthreads();
       float* wl = (float*)smem + wid * (64 * LDW);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -802,19 +811,22 @@ __global__ __launch_bounds__(512) void gemm_skinny_kernel(ActIn a, BRows<bf16_t>
 // tile: every epilogue is row-independent), in split order, then the epilogue.
 template <int RB, int BN, int KIND, typename TP>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* part, int ksplit, int M, int N,
-                                                             EpiParams e) {
+                                                             EpiParams e, const int* m_dev) {
   constexpr int LDC = BN + 4;
   __shared__ __attribute__((aligned(16))) float Cs[RB * LDC];
   const int nrb = (M + RB - 1) / RB;
   const int rb = blockIdx.x % nrb, tn = blockIdx.x / nrb;
   const int m0 = rb * RB, n0 = tn * BN;
+  const int Mp = M;   // row stride of the partials
+  if (m_dev) M = min(M, max(*m_dev, 0));
+  if (m0 >= M) return;
   constexpr int C4 = BN / 4;
   for (int idx = threadIdx.x; idx < RB * C4; idx += 256) {
     const int r = idx / C4, c = (idx - r * C4) * 4;
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     if (m0 + r < M && n0 + c < N) {
       for (int k = 0; k < ksplit; ++k) {
-        const float4 v = *(const float4*)(part + ((size_t)k * M + m0 + r) * N + n0 + c);
+        const float4 v = *(const float4*)(part + ((size_t)k * Mp + m0 + r) * N + n0 + c);
         acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
       }
     }
@@ -1006,11 +1018,11 @@ static hipError_t go_dma(const GemmArgs& g, int ksplit, hipStream_t s) {
   const int grid = (total + 7) / 8 * 8;
   BRows<bf16_t> b{(const bf16_t*)g.b.b0, (const bf16_t*)g.b.b1, g.b.ldb, g.b.split, g.b.mode};
   hipLaunchKernelGGL((gemm_dma_kernel<NP, KIND>), dim3(grid), dim3(256), 0, s, g.a, b, g.M, g.N, g.K, ksplit, g.part,
-                     g.e);
+                     g.e, g.m_dev);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || ksplit == 1 || (g.defer_reduce && (KIND == EPI_ADD || KIND == EPI_STORE))) return err;
   hipLaunchKernelGGL((splitk_reduce_kernel<16, 128, KIND, bf16_t>), dim3((g.M + 15) / 16 * ntn), dim3(256), 0, s,
-                     g.part, ksplit, g.M, g.N, g.e);
+                     g.part, ksplit, g.M, g.N, g.e, g.m_dev);
   return hipGetLastError();
 }
 
@@ -1025,7 +1037,7 @@ static hipError_t go_fl(const GemmArgs& g, int ksplit, hipStream_t s) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || ksplit == 1 || (g.defer_reduce && (KIND == EPI_ADD || KIND == EPI_STORE))) return err;
   hipLaunchKernelGGL((splitk_reduce_kernel<16, BN, KIND, bf16_t>), dim3((g.M + 15) / 16 * ntn), dim3(256), 0, s,
-                     g.part, ksplit, g.M, g.N, g.e);
+                     g.part, ksplit, g.M, g.N, g.e, nullptr);
   return hipGetLastError();
 }
 
@@ -1038,7 +1050,7 @@ static hipError_t go_skinny(const GemmArgs& g, int ksplit, hipStream_t s) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || ksplit == 1 || (g.defer_reduce && (KIND == EPI_ADD || KIND == EPI_STORE))) return err;
   hipLaunchKernelGGL((splitk_reduce_kernel<16, kSkinnyBN, KIND, bf16_t>), dim3((g.M + 15) / 16 * ntn), dim3(256), 0,
-                     s, g.part, ksplit, g.M, g.N, g.e);
+                     s, g.part, ksplit, g.M, g.N, g.e, nullptr);
   return hipGetLastError();
 }
 
@@ -1065,6 +1077,7 @@ int gemm_ksplit(const GemmArgs& g) {
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   if (g.wdtype == 0) {
+    if (g.m_dev || g.a.rows) return hipErrorInvalidValue;
     switch (g.kind) {
       case EPI_STORE: return go_f32<EPI_STORE>(g, s);
       case EPI_ADD: return go_f32<EPI_ADD>(g, s);
@@ -1076,6 +1089,8 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   }
   const GemmPlan p = gemm_plan(g.wdtype, g.a.mode, g.M, g.N, g.K, g.kind, g.fixed_split);
   if (p.ksplit > 1 && !g.part) return hipErrorInvalidValue;
+  // a device row count and a row gather are carried by tile configuration 2 only
+  if ((g.m_dev || g.a.rows) && p.cfg != 2) return hipErrorInvalidValue;
   if (g.a.mode == ACT_HILO) {
     switch (g.kind) {
       case EPI_STORE: return go_bf16<2, EPI_STORE>(g, p, s);

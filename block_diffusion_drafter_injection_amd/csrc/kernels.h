@@ -65,6 +65,8 @@ struct GemmArgs {
   float* part;           // split-K partials (gemm_partial_bytes of the plan), or null
   bool defer_reduce;     // EPI_ADD / EPI_STORE with a K split: leave the partials to the consumer
                          // (the next RMSNorm, or the query prep of the attention)
+  const int* m_dev;      // optional device row count <= M: rows from it on are neither computed
+                         // nor written (tile configuration 2 only, i.e. a fixed K split)
 };
 
 struct GemmPlan {
@@ -111,6 +113,10 @@ hipError_t launch_attn_finish(const AttnParams& p, int wdtype, ActOut out, hipSt
 // Elementwise and bookkeeping kernels.
 hipError_t launch_rope_table_block(const int* ctx_len, int ctx_cap, int batch, int B, int d,
                                    double base, float2* cs, hipStream_t s);
+// Injection rows with tok_seq >= 0 packed to the front, in order (the rest
+// marked -1); count = how many (device).
+hipError_t launch_compact_rows(const int* tok_seq, const int* tok_pos, int n, int* src, int* seq_c, int* pos_c,
+                               int* count, hipStream_t s);
 hipError_t launch_rope_table_tokens(const int* tok_pos, int n, int d, double base, float2* cs,
                                     hipStream_t s);
 // tau = mask_id, nothing committed; with anchor != null, position 0 of each block

@@ -87,6 +87,46 @@ def test_incremental_injection_is_bitwise_one_shot():
     assert torch.equal(one.view(torch.int16), inc.view(torch.int16))
 
 
+@pytest.mark.parametrize("ctx,n_decoy", [([150, 97], 120), ([700, 600], 900)])
+def test_injection_skips_marked_rows_bitwise(ctx, n_decoy):
+    """Rows with tok_seq = -1 are dropped before the GEMMs (packed out on the device):
+    the same rows with decoys marked -1 spread among them (decoys aim at positions the real
+    rows write, so a decoy that got through would change the pool) give the one-shot pool
+    bit for bit; a call whose rows are all marked leaves the pool untouched.  The larger
+    case has more than 1024 rows, so the packing runs over several blocks."""
+    dims = SMALL
+    W = synth.make_weights(dims, 11, "cuda")
+    table, n_pages = page_plan(ctx, 0, seed=6)
+    tab = torch.from_numpy(table).cuda()
+    hid = synth.make_hiddens(dims, sum(ctx), 12, "cuda")
+    seq, pos = _tokens(ctx)
+    n = seq.numel()
+    dr = Drafter(dims, W, max_batch=len(ctx), block_size=8, max_ctx=max(ctx), max_inject=n + n_decoy)
+    one = alloc_pool(dims, n_pages)
+    dr.inject(hid, seq, pos, one, n_pages, tab, len(ctx))
+    g = torch.Generator().manual_seed(n_decoy)
+    total = n + n_decoy
+    real_at = torch.sort(torch.randperm(total, generator=g)[:n]).values   # keeps the real rows' order
+    is_real = torch.zeros(total, dtype=torch.bool)
+    is_real[real_at] = True
+    mseq = torch.full((total,), -1, dtype=torch.int32)
+    mpos = pos.cpu()[torch.randint(0, n, (total,), generator=g)].to(torch.int32)
+    mhid = synth.make_hiddens(dims, total, 13, "cuda")
+    mseq[real_at] = seq.cpu()
+    mpos[real_at] = pos.cpu()
+    mhid[real_at.cuda()] = hid
+    assert (~is_real).sum().item() == n_decoy
+    mixed = alloc_pool(dims, n_pages)
+    dr.inject(mhid, mseq.cuda(), mpos.cuda(), mixed, n_pages, tab, len(ctx))
+    torch.cuda.synchronize()
+    assert torch.equal(one.view(torch.int16), mixed.view(torch.int16))
+    # every row marked: nothing is written
+    before = mixed.clone()
+    dr.inject(mhid, torch.full_like(mseq, -1).cuda(), mpos.cuda(), mixed, n_pages, tab, len(ctx))
+    torch.cuda.synchronize()
+    assert torch.equal(before.view(torch.int16), mixed.view(torch.int16))
+
+
 def _draft_case(dims, ctx, B, S, T, seed, want_logits=True, schedule="progressive", qk=False, anchor=None):
     W = synth.make_weights(dims, seed, "cuda")
     if qk:
