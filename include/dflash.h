@@ -160,8 +160,10 @@ size_t dflash_workspace_size(const dflash_config* cfg, int32_t max_batch, int32_
  *   kv_pool (device) pool of n_pages pages (layout above)
  *   block_table (device) [n_seqs, max_pages] physical page per logical page
  * Tokens whose sequence (tok_seq = -1, say), logical page or physical page
- * is out of range are skipped.  Tokens are processed in chunks of the rows
- * the workspace holds. */
+ * is out of range are skipped.  With bf16 weights, rows with tok_seq < 0 are
+ * packed out on the device before the products (their cost is a few bytes
+ * each, not a GEMM row), which leaves every written value unchanged.  Tokens
+ * are processed in chunks of the rows the workspace holds. */
 dflash_status dflash_inject_kv(const dflash_config* cfg, const dflash_weights* w,
                                const void* target_hidden, const int32_t* tok_seq,
                                const int32_t* tok_pos, int32_t n_tok, void* kv_pool,
@@ -245,9 +247,11 @@ dflash_status dflash_target_forward(const dflash_config* cfg, const dflash_weigh
  * j = 0..block_size this writes injection row r = b*(block_size+1) + j:
  *   tok_seq[r] = (j <= accept_len[b]) ? b : -1,  tok_pos[r] = ctx_len[b] + j
  * and then advances ctx_len[b] by accept_len[b] + 1.  dflash_inject_kv skips
- * rows with tok_seq = -1, so the next injection takes n_tok =
- * batch*(block_size+1) rows of target hidden states laid out [b][j] (the
- * target's states at the block_size+1 verified positions of each sequence).
+ * rows with tok_seq = -1 (and, with bf16 weights, packs them out before its
+ * products, so only the accepted rows cost GEMM work), so the next injection
+ * takes n_tok = batch*(block_size+1) rows of target hidden states laid out
+ * [b][j] (the target's states at the block_size+1 verified positions of each
+ * sequence).
  *   accept_len (device) [batch], as dflash_verify_block writes it (values
  *              are clamped to [0, block_size])
  *   ctx_len (device) [batch], read and advanced in place
