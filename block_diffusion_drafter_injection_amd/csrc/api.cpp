@@ -139,7 +139,11 @@ void attn_split(int bt, int nkv, int nqg, int ctx_cap, int& ns, int& pps) {
   ns = (pages + pps - 1) / pps;
 }
 
-int n_qgroups(const dflash_config* c, int B) { return ((c->n_q_heads / c->n_kv_heads) * B + 63) / 64; }
+int n_qgroups(const dflash_config* c, int B) {
+  const int R = (c->n_q_heads / c->n_kv_heads) * B;
+  const int qg = att_query_group(R, c->dtype == DFLASH_BF16 ? 1 : 0, c->head_dim);
+  return (R + qg - 1) / qg;
+}
 
 struct DraftWS {
   size_t h, u_hi, u_lo, qkv, o_hi, o_lo, act_hi, act_lo, y, row_map, part_f, part_i, att_o, att_lse, cs, tau,

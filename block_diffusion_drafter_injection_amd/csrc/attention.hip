@@ -51,7 +51,7 @@ __device__ __forceinline__ void split_pages(const AttnParams& p, int npages, int
 // ---------------------------------------------------------------------------
 constexpr int kMaxPPS = 512;   // pages per context split (bounded by the host)
 constexpr int kCachePolicyNT = 2;   // cache-policy operand of the direct loads: non-temporal
-constexpr int kAttStages = 5;   // 32-token tiles resident per workgroup (two workgroups fill the 160 KiB of LDS)
+constexpr int kAttStages = 5;   // 32-token tiles resident per four-wave workgroup (two fill the 160 KiB of LDS)
 
 // s_waitcnt on the vector-memory counter only, through the builtin so that
 // the compiler's own wait insertion knows which loads have completed
@@ -168,11 +168,15 @@ __global__ __launch_bounds__(256) void attn_qprep_kernel(AttnParams p) {
 }
 
 // Context part of the block attention, one (context split, kv head, sequence,
-// 64-query group) per workgroup of four waves.  Tiles of 32 tokens (two
-// pages: K 2 x 4 KiB, V 2 x 4 KiB) are copied global -> LDS by
+// query group) per workgroup of NW waves, 16 query rows per wave: four waves
+// (64 rows, two workgroups per CU, kAttStages tiles each) or, when a kv head
+// has more than 64 query rows (a target forward over a block and the token
+// before it), eight waves (128 rows, one workgroup per CU, twice the tiles),
+// so that the context is streamed once for all of them.  Tiles of 32 tokens
+// (two pages: K 2 x 4 KiB, V 2 x 4 KiB) are copied global -> LDS by
 // global_load_lds_dwordx4 (lane i of an instruction fills LDS bytes
-// base + 16 i), kAttStages deep; wave w copies page w & 1 of the tile, K for
-// w < 2 and V otherwise, so it needs one physical page per tile.  The split's
+// base + 16 i); wave w copies part w / 4 of page w & 1 of the tile, K for
+// w % 4 < 2 and V otherwise, so it needs one physical page per tile.  The split's
 // page ids come from the block table once, into registers (lane j holds tile
 // j + 64 r), and a lane read picks a tile's page at its issue; unmapped pages
 // become wave-uniform bit masks.  The loop has no LDS round trip besides the
@@ -197,20 +201,36 @@ __device__ __forceinline__ float row_max4(float x) {
 
 constexpr int kPidRegs = kMaxPPS / 128;   // page-id registers per wave (64 tiles of two pages each)
 
-template <int D>
-__global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
+// vmcnt wait for a tile with k later tiles of PT copies each still in flight
+template <int PT, int MAXK>
+__device__ __forceinline__ void att_wait_tiles(int k) {
+  if constexpr (MAXK == 0) {
+    att_wait_vmcnt<0>();
+  } else {
+    if (k >= MAXK) att_wait_vmcnt<MAXK * PT>();
+    else att_wait_tiles<PT, MAXK - 1>(k);
+  }
+}
+
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW) void attn_ctx_mfma_kernel(AttnParams p) {
   static_assert(D == 128, "context kernel is specialised for head_dim 128");
-  static_assert(kAttStages >= 2 && kAttStages <= 7, "wait table covers up to 5 tiles in flight");
+  static_assert(NW == 4 || NW == 8, "four or eight waves");
+  constexpr int STAGES = NW == 8 ? 2 * kAttStages : kAttStages;   // tiles resident (LDS of one CU either way)
+  constexpr int QG = 16 * NW;                 // query rows per workgroup
+  static_assert(STAGES >= 2 && STAGES <= 10, "stages");
   static_assert(kPidRegs == 4, "page-id register select");
   constexpr int KK = D / 32, NN = D / 16;
   constexpr int KBYTES = 32 * D * 2;          // K tile: 32 tokens x 256 B
   constexpr int VBYTES = 2 * D * 32;          // V tile: 2 pages x D rows x 32 B
   constexpr int TILE = KBYTES + VBYTES;       // 16 KiB
-  constexpr int PER_THREAD = TILE / 1024 / 4; // load instructions per wave per tile
-  __shared__ __attribute__((aligned(1024))) unsigned char lds[kAttStages * TILE];
+  constexpr int PER_THREAD = TILE / 1024 / NW; // load instructions per wave per tile
+  static_assert(STAGES * TILE <= 160 * 1024, "LDS");
+  static_assert((STAGES - 1) * PER_THREAD < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(1024))) unsigned char lds[STAGES * TILE];
 
   const int g = p.nq / p.nkv, R = g * p.B;
-  const int nqg = (R + 63) / 64;
+  const int nqg = (R + QG - 1) / QG;
   const int split = blockIdx.x / nqg, qg = blockIdx.x - split * nqg;
   const int m = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
@@ -220,9 +240,9 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
   split_pages(p, npages, split, pg0, pg1);
   const int ntiles = pg1 > pg0 ? (pg1 - pg0 + 1) >> 1 : 0;
 
-  const int r = qg * 64 + wid * 16 + (lane & 15);
+  const int r = qg * QG + wid * 16 + (lane & 15);
   const bool rvalid = r < R;
-  const bool wave_active = qg * 64 + wid * 16 < R;
+  const bool wave_active = qg * QG + wid * 16 < R;
   const int j = rvalid ? r / p.B : 0, i = rvalid ? r - (r / p.B) * p.B : 0;
   const int n = m * g + j, row = b * p.B + i;
 
@@ -238,7 +258,8 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
   }
   // page ids: page q (0, 1) of tile t = lane + 64 rr, -1 past the split or unmapped;
   // any_bad (wave-uniform): some page of the split has no valid physical page
-  const int wrole = __builtin_amdgcn_readfirstlane(wid);
+  const int wid_u = __builtin_amdgcn_readfirstlane(wid);
+  const int wrole = wid_u & 3, wpart = wid_u >> 2;   // copy role (K0, K1, V0, V1) and its part
   const int wpage = wrole & 1;
   int mypid[kPidRegs];
   int pid00 = -1;
@@ -273,18 +294,19 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
   const int first_ph = (ntiles && pid00 >= 0) ? pid00 : 0;
 
   // copy role of this wave and the per-lane byte offsets of its PER_THREAD
-  // loads within a page chunk (instruction ins = 4 wid + q fills LDS bytes
-  // ins * 1024 .. + 1023 of the tile)
+  // loads within a page chunk (instruction ins = 4 wrole + qq, qq = the
+  // wave's part * PER_THREAD + q, fills LDS bytes ins * 1024 .. + 1023 of the tile)
   const bf16_t* srcbase = wrole < 2 ? kbase : vbase;
   uint32_t loff[PER_THREAD];
 #pragma unroll
   for (int q = 0; q < PER_THREAD; ++q) {
+    const int qq = wpart * PER_THREAD + q;
     if (wrole < 2) {
-      const int krow = 16 * wpage + 4 * q + (lane >> 4);
+      const int krow = 16 * wpage + 4 * qq + (lane >> 4);
       const int lc = (lane & 15) ^ kswz(krow);
       loff[q] = (uint32_t)((krow & 15) * (D * 2) + lc * 16);
     } else {
-      const int d = 32 * q + (lane >> 1);
+      const int d = 32 * qq + (lane >> 1);
       const int lh = (lane & 1) ^ ((d >> 3) & 1);
       loff[q] = (uint32_t)(d * 32 + lh * 16);
     }
@@ -314,7 +336,7 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
     for (int q = 0; q < PER_THREAD; ++q)
       __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(base + loff[q]),
                                        (__attribute__((address_space(3))) void*)(size_t)(lds0 + st * TILE +
-                                                                                         (4 * wrole + q) * 1024),
+                                                     (4 * wrole + wpart * PER_THREAD + q) * 1024),
                                        16, 0, kCachePolicyNT);
   };
 
@@ -344,8 +366,8 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
     const int tok0 = (pg0 + 2 * t) * 16;
     const bool bad0 = unmapped(t, 0), bad1 = unmapped(t, 1);
     if (tok0 + 32 > ctx || bad0 || bad1) {
-      unsigned char* vt = lds + (t % kAttStages) * TILE + KBYTES;
-      for (int c = tid; c < 2 * D * 16; c += 256) {
+      unsigned char* vt = lds + (t % STAGES) * TILE + KBYTES;
+      for (int c = tid; c < 2 * D * 16; c += 64 * NW) {
         const int pg = c / (D * 16), rem = c - pg * D * 16, d = rem >> 4, slot = rem & 15;
         if (tok0 + pg * 16 + slot >= ctx || (pg ? bad1 : bad0)) {
           const int lh = (slot >> 3) ^ ((d >> 3) & 1);
@@ -357,7 +379,7 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
   };
 #define ATT_SCORES(T, O0, O1)                                                                                 \
   do {                                                                                                        \
-    const unsigned char* kt_ = lds + ((T) % kAttStages) * TILE;                                               \
+    const unsigned char* kt_ = lds + ((T) % STAGES) * TILE;                                                   \
     O0 = f32x4{0.f, 0.f, 0.f, 0.f};                                                                           \
     O1 = f32x4{0.f, 0.f, 0.f, 0.f};                                                                           \
     _Pragma("unroll") for (int kk = 0; kk < KK; ++kk) {                                                       \
@@ -371,7 +393,7 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
   } while (0)
 #define ATT_READ_V(T, VF)                                                                                     \
   do {                                                                                                        \
-    const unsigned char* vt_ = lds + ((T) % kAttStages) * TILE + KBYTES;                                      \
+    const unsigned char* vt_ = lds + ((T) % STAGES) * TILE + KBYTES;                                          \
     _Pragma("unroll") for (int nn = 0; nn < NN; ++nn) VF[nn] = as_bf16x8(*(const u32x4*)(vt_ + voff[nn]));    \
   } while (0)
 
@@ -384,17 +406,10 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
   // P V by then).
   int issued = 0;   // tiles issued so far
 #pragma unroll
-  for (int t = 0; t < kAttStages; ++t)
+  for (int t = 0; t < STAGES; ++t)
     if (t < ntiles) { issue(page_of(t), t); ++issued; }
   auto wait_tile = [&](int t) __attribute__((always_inline)) {
-    switch (min(issued - 1 - t, 5)) {   // tiles issued after tile t
-      case 0: att_wait_vmcnt<0>(); break;
-      case 1: att_wait_vmcnt<PER_THREAD>(); break;
-      case 2: att_wait_vmcnt<2 * PER_THREAD>(); break;
-      case 3: att_wait_vmcnt<3 * PER_THREAD>(); break;
-      case 4: att_wait_vmcnt<4 * PER_THREAD>(); break;
-      default: att_wait_vmcnt<5 * PER_THREAD>(); break;
-    }
+    att_wait_tiles<PER_THREAD, STAGES - 1>(issued - 1 - t);   // tiles issued after tile t
   };
 
   f32x4 stc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
@@ -414,7 +429,7 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
       wait_tile(it + 1);
       att_barrier();
       if (it >= 1 && issued < ntiles) {
-        issue(page_of(issued), (it - 1) % kAttStages);   // tile it+kAttStages-1 into tile it-1's buffer
+        issue(page_of(issued), (it - 1) % STAGES);   // tile it+STAGES-1 into tile it-1's buffer
         ++issued;
       }
       zero_tail(it + 1);
@@ -423,7 +438,7 @@ __global__ __launch_bounds__(256) void attn_ctx_mfma_kernel(AttnParams p) {
       // K of tile it+1 (stale and unused after the last tile)
       bf16x8 kf[2][KK];
       {
-        const unsigned char* kt = lds + ((it + 1) % kAttStages) * TILE;
+        const unsigned char* kt = lds + ((it + 1) % STAGES) * TILE;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
           kf[0][kk] = as_bf16x8(*(const u32x4*)(kt + koff[0][kk]));
@@ -797,8 +812,10 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
 }
 
 // ---------------------------------------------------------------------------
+int att_query_group(int R, int wdtype, int d) { return wdtype == 1 && d == 128 && R > 64 ? 128 : 64; }
+
 hipError_t launch_attention(const AttnParams& p, int wdtype, hipStream_t s, void (*mark)(int, hipStream_t)) {
-  const int g = p.nq / p.nkv, R = g * p.B, nqg = (R + 63) / 64;
+  const int g = p.nq / p.nkv, R = g * p.B, qgr = att_query_group(R, wdtype, p.d), nqg = (R + qgr - 1) / qgr;
   // the prepared queries and block keys also feed the finish kernel, with or
   // without context
   if (wdtype == 1 && p.d == 128) {
@@ -807,8 +824,10 @@ hipError_t launch_attention(const AttnParams& p, int wdtype, hipStream_t s, void
   if (p.n_splits <= 0) return hipGetLastError();
   const dim3 gctx(p.n_splits * nqg, p.nkv, p.batch);
   if (mark) mark(0, s);
-  if (wdtype == 1 && p.d == 128)
-    hipLaunchKernelGGL(attn_ctx_mfma_kernel<128>, gctx, dim3(256), 0, s, p);
+  if (wdtype == 1 && p.d == 128 && qgr == 128)
+    hipLaunchKernelGGL((attn_ctx_mfma_kernel<128, 8>), gctx, dim3(512), 0, s, p);
+  else if (wdtype == 1 && p.d == 128)
+    hipLaunchKernelGGL((attn_ctx_mfma_kernel<128, 4>), gctx, dim3(256), 0, s, p);
   else if (wdtype == 1)
     hipLaunchKernelGGL((attn_valu_kernel<bf16_t, 64, true>), gctx, dim3(256), 0, s, p);
   else if (p.d == 128)

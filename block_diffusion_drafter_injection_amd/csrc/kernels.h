@@ -106,6 +106,8 @@ struct AttnParams {
   int causal;             // 1: block query i sees block keys j <= i only (target forward)
 };
 // Context splits -> partials (no launch when there is no context).
+// Query rows per context workgroup for R query rows per kv head (64 or 128).
+int att_query_group(int R, int wdtype, int d);
 hipError_t launch_attention(const AttnParams& p, int wdtype, hipStream_t s, void (*mark)(int, hipStream_t));
 // In-block keys + merge with the partials -> attention output as GEMM operand.
 hipError_t launch_attn_finish(const AttnParams& p, int wdtype, ActOut out, hipStream_t s);
