@@ -97,33 +97,29 @@ __global__ __launch_bounds__(64) void greedy_accept_kernel(int B, int nc, const 
   }
 }
 
-// e^x in double for x <= 0 (the terms of a log-sum-exp below its maximum):
-// Cody-Waite reduction x = n ln2 + r with ln2 split in two (n ln2_hi exact),
-// |r| <= ln2 / 2, e^r by its Taylor series to degree 13 (truncation below
-// 2e-16 relative), scaled by 2^n.  Within about one ulp of e^x; terms below
-// 2^-1020 are returned as 0 (the sum they join is at least 1).
-__device__ __forceinline__ double exp_nonpos(double x) {
-  constexpr double kLog2e = 1.4426950408889634074, kLn2Hi = 6.93147180369123816490e-01,
-                   kLn2Lo = 1.90821492927058770002e-10;
-  const double t = x * kLog2e;
-  if (t < -1020.0) return 0.0;
-  const double n = rint(t);
-  const double r = fma(-n, kLn2Lo, fma(-n, kLn2Hi, x));
-  double p = 1.0 / 6227020800.0;   // 1/13!
-  p = fma(p, r, 1.0 / 479001600.0);
-  p = fma(p, r, 1.0 / 39916800.0);
-  p = fma(p, r, 1.0 / 3628800.0);
-  p = fma(p, r, 1.0 / 362880.0);
-  p = fma(p, r, 1.0 / 40320.0);
-  p = fma(p, r, 1.0 / 5040.0);
-  p = fma(p, r, 1.0 / 720.0);
+// e^x in double for x <= 0, table-driven (Tang's method): with n = rint(32 x / ln2),
+// x = n ln2/32 + r, |r| <= ln2/64 (Cody-Waite: ln2/32 split in two, n times the
+// high part exact), e^r by its Taylor series to degree 6 (truncation below 2e-17
+// relative), times 2^(j/32) (j = n mod 32, from tab) and 2^floor(n/32).  Within
+// about two ulps of e^x, with 15 double operations where a degree-13 series over
+// |r| <= ln2/2 takes 23; terms below 2^-1020 (the log-sum-exp they join is at
+// least 1) are returned as 0.
+__device__ __forceinline__ double exp_nonpos_tab(double x, const double* tab) {
+  constexpr double k32Log2e = 46.166241308446828384, kHi = 6.93147180369123816490e-01 / 32.0,
+                   kLo = 1.90821492927058770002e-10 / 32.0;
+  const double t = x * k32Log2e;
+  const double n = rint(fmax(t, -32.0 * 1021.0));
+  const double r = fma(-n, kLo, fma(-n, kHi, x));
+  double p = 1.0 / 720.0;
   p = fma(p, r, 1.0 / 120.0);
   p = fma(p, r, 1.0 / 24.0);
   p = fma(p, r, 1.0 / 6.0);
   p = fma(p, r, 0.5);
   p = fma(p, r, 1.0);
   p = fma(p, r, 1.0);
-  return ldexp(p, (int)n);
+  const int ni = (int)n;
+  const double e = ldexp(tab[ni & 31] * p, ni >> 5);
+  return t < -32.0 * 1020.0 ? 0.0 : e;
 }
 
 // (max, sum exp(x - max)) of x = z/T over one chunk, in double.  The chunk is
@@ -161,6 +157,8 @@ __global__ __launch_bounds__(256) void lse_rows_kernel(const float* zt, const fl
   for (int k = 0; k < kLsePer; ++k) mf = fmaxf(mf, x[k]);
   __shared__ float red[4];
   __shared__ double dred[4];
+  __shared__ double tab[32];   // 2^(j/32)
+  if (tid < 32) tab[tid] = exp2((double)tid / 32.0);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mf = fmaxf(mf, __shfl_xor(mf, o, kWave));
   if ((tid & 63) == 0) red[tid >> 6] = mf;
@@ -170,7 +168,7 @@ __global__ __launch_bounds__(256) void lse_rows_kernel(const float* zt, const fl
   double s = 0.0;
 #pragma unroll
   for (int k = 0; k < kLsePer; ++k)
-    if (x[k] != -INFINITY) s += exp_nonpos(fmin((double)x[k] * invT - mx, 0.0));
+    if (x[k] != -INFINITY) s += exp_nonpos_tab(fmin((double)x[k] * invT - mx, 0.0), tab);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, kWave);
   if ((tid & 63) == 0) dred[tid >> 6] = s;
