@@ -76,6 +76,13 @@ KERNEL_NAMES = {
 KERNEL_SOURCES = ["common.h", "kernels.h", "gemm.hip", "attention.hip", "elementwise.hip", "verify.hip", "api.cpp"]
 
 
+def pct(xs):
+    """median, p10 and p90 of a list of per-call times (ms)"""
+    import numpy as np
+    q = np.percentile(np.asarray(xs, dtype=np.float64), [50, 10, 90])
+    return {"median": round(float(q[0]), 4), "p10": round(float(q[1]), 4), "p90": round(float(q[2]), 4), "n": len(xs)}
+
+
 def source_hash():
     import hashlib
     h = hashlib.sha256()
@@ -312,16 +319,17 @@ def main():
                 best, cls = ms, c
         Bn.dflash_prof_select("none")
 
-    # draft-only latency (separate, a few calls on the current state)
-    d0, d1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    d0.record(stream)
-    nd = 5
-    for _ in range(nd):
+    # draft-only latency (separate, back-to-back calls on the current state, each between its own events)
+    nd = 20
+    dev_ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nd)]
+    for e0_, e1_ in dev_ev:
+        e0_.record(stream)
         Bn.dflash_draft_block(cfg, w, pool, n_pages, table, pages_per, ctx_dev, max_ctx, bt, B, S, 0.0, 0, tok, None,
                               None, ws, ws_bytes)
-    d1.record(stream)
+        e1_.record(stream)
     torch.cuda.synchronize()
-    draft_ms = d0.elapsed_time(d1) / nd
+    draft_calls = [e0_.elapsed_time(e1_) for e0_, e1_ in dev_ev]
+    draft_ms = float(np.mean(draft_calls))
 
     # timed region
     Bn.dflash_prof_select(cls)
@@ -368,6 +376,8 @@ def main():
                    "layers": dims.n_layers, "vocab": dims.vocab, "ctx_start": int(ctx0.mean()),
                    "p_match": wl.p_match},
         "draft_ms": round(draft_ms, 4),
+        "draft_latency_ms": pct(draft_calls),
+        "step_latency_ms": pct(hot),
         "drafted_tok_s": round(bt * B / (draft_ms / 1e3), 1),
         "mean_accept_plus_bonus": round(accepted / bt, 3),
         "wall_ms_per_step": round(wall * 1e3 / a.steps, 3),
