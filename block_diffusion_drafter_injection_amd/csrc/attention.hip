@@ -627,6 +627,10 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
   // NK: block keys held (16 for a draft block; 32 for a target forward of up to 32 tokens)
   constexpr int QR = 16, DPT = D / 16;   // 16 threads per query row, DPT dims each
   static_assert(DPT % 4 == 0, "dims per thread");
+  // a thread's dims are C chunks of four, chunk c at c * (D / C) + 4 * part: the
+  // sixteen threads of a row read each chunk as 256 contiguous bytes (no LDS
+  // bank conflicts, coalesced global reads and stores)
+  constexpr int C = DPT / 4;
   __shared__ __attribute__((aligned(16))) float kb[NK][D];
   __shared__ __attribute__((aligned(16))) float vb[NK][D];
   const int g = p.nq / p.nkv, R = g * p.B, h = D / 2;
@@ -661,7 +665,7 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
   const int rc = rv ? rr : R - 1;
   const int j = rc / p.B, i = rc - j * p.B;
   const int row = b * p.B + i, n = m * g + j;
-  const int d0 = part * DPT;   // this thread's dims d0 .. d0 + DPT - 1
+  auto dch = [&](int c) { return c * (D / C) + 4 * part; };   // first dim of chunk c
   // the first context partials of this row, loaded now so their latency
   // overlaps the in-block attention (the merge below uses them in split order)
   constexpr int NPF = 2;
@@ -674,18 +678,19 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
     pl[k] = k < p.n_splits ? p.part_lse[k * Mq + qrow] : -INFINITY;
 #pragma unroll
     for (int e = 0; e < DPT; e += 4)
-      po[k][e / 4] = k < p.n_splits ? *(const float4*)(p.part_o + (k * Mq + qrow) * D + d0 + e)
+      po[k][e / 4] = k < p.n_splits ? *(const float4*)(p.part_o + (k * Mq + qrow) * D + dch(e / 4))
                                     : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   float q[DPT];
   if constexpr (PREP) {
     // prepared rotated query (hi + lo), carrying scale * log2 e
-    const size_t qoff = (((size_t)b * p.nkv + m) * R + rc) * D + d0;
+    const size_t qoff = (((size_t)b * p.nkv + m) * R + rc) * D;
 #pragma unroll
     for (int k = 0; k < DPT; k += 4) {
       // a bf16 is the high half of an fp32: element 2t of a word is w << 16,
       // element 2t+1 is w & 0xffff0000
-      const u32x2 hv = *(const u32x2*)(p.q_hi + qoff + k), lv = *(const u32x2*)(p.q_lo + qoff + k);
+      const size_t o = qoff + dch(k / 4);
+      const u32x2 hv = *(const u32x2*)(p.q_hi + o), lv = *(const u32x2*)(p.q_lo + o);
       q[k] = __uint_as_float(hv.x << 16) + __uint_as_float(lv.x << 16);
       q[k + 1] = __uint_as_float(hv.x & 0xffff0000u) + __uint_as_float(lv.x & 0xffff0000u);
       q[k + 2] = __uint_as_float(hv.y << 16) + __uint_as_float(lv.y << 16);
@@ -695,7 +700,7 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
     const float* qv = p.qkv + (size_t)row * ldq + n * D;
     const float2* cs = p.cs + (size_t)row * h;
 #pragma unroll
-    for (int e = 0; e < DPT; ++e) q[e] = rope_elem(qv, cs, d0 + e, D) * p.scale * 1.4426950408889634f;
+    for (int e = 0; e < DPT; ++e) q[e] = rope_elem(qv, cs, dch(e / 4) + (e & 3), D) * p.scale * 1.4426950408889634f;
   }
   __syncthreads();
   // scores in base-2 units: partial dot over this thread's dims, summed over
@@ -707,7 +712,7 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
     float a = 0.f;
 #pragma unroll
     for (int e = 0; e < DPT; e += 4) {
-      const float4 kv = *(const float4*)&kb[k][d0 + e];
+      const float4 kv = *(const float4*)&kb[k][dch(e / 4)];
       a = fmaf(q[e], kv.x, a);
       a = fmaf(q[e + 1], kv.y, a);
       a = fmaf(q[e + 2], kv.z, a);
@@ -736,7 +741,7 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
     const float w = sc[k] * rs;
 #pragma unroll
     for (int e = 0; e < DPT; e += 4) {
-      const float4 vv = *(const float4*)&vb[k][d0 + e];
+      const float4 vv = *(const float4*)&vb[k][dch(e / 4)];
       ob[e] = fmaf(w, vv.x, ob[e]);
       ob[e + 1] = fmaf(w, vv.y, ob[e + 1]);
       ob[e + 2] = fmaf(w, vv.z, ob[e + 2]);
@@ -781,9 +786,10 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
     for (int k = 0; k < 4; ++k) {
       const bool ok = s0 + k < p.n_splits;
       l4[k] = ok ? p.part_lse[(s0 + k) * Mq + qrow] : -INFINITY;
-      const float* src = p.part_o + ((s0 + k) * Mq + qrow) * D + d0;
+      const float* src = p.part_o + ((s0 + k) * Mq + qrow) * D;
 #pragma unroll
-      for (int e = 0; e < DPT; e += 4) v4[k][e / 4] = ok ? *(const float4*)(src + e) : make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int e = 0; e < DPT; e += 4)
+        v4[k][e / 4] = ok ? *(const float4*)(src + dch(e / 4)) : make_float4(0.f, 0.f, 0.f, 0.f);
     }
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
@@ -808,7 +814,8 @@ __global__ __launch_bounds__(256) void attn_finish_kernel(AttnParams p, ActOut o
   const float inv = 1.f / tot;
 #pragma unroll
   for (int e = 0; e < DPT; e += 4)
-    act_store4(out, row, n * D + d0 + e, make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv));
+    act_store4(out, row, n * D + dch(e / 4),
+               make_float4(acc[e] * inv, acc[e + 1] * inv, acc[e + 2] * inv, acc[e + 3] * inv));
 }
 
 // ---------------------------------------------------------------------------
