@@ -38,6 +38,10 @@ def parse():
     ap.add_argument("--cpu-baseline", type=int, default=1, help="time the fp64 oracle on a bounded sample")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="after the timed steps, run one plain device copy of COPY_BYTES (for HBM counter scaling)")
+    ap.add_argument("--summarize-sq", nargs=3, metavar=("DIR1", "DIR2", "DIR3"),
+                    help="write profiles/sq_counters_*.md from the three shader-sequencer counter passes")
+    ap.add_argument("--summarize-verify", metavar="TRACE_DIR",
+                    help="write profiles/kernel_stats_sampled_verify_*.md from a --longctx 1 kernel trace")
     ap.add_argument("--summarize", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="turn rocprofv3 csv output into profiles/ summaries and exit")
     ap.add_argument("--seed", type=int, default=0)
@@ -193,6 +197,12 @@ def measured_ceilings(dims, bt, B):
 
 def main():
     a = parse()
+    if a.summarize_sq:
+        summarize_sq(*a.summarize_sq)
+        return
+    if a.summarize_verify:
+        summarize_verify(a.summarize_verify)
+        return
     if a.summarize:
         summarize(*a.summarize)
         return
@@ -1062,7 +1072,7 @@ def summarize(trace_dir, fetch_dir, write_dir):
     lines = [f"# rocprofv3 kernel statistics, {wl_name}", "",
              "Command (run from the repository root, output csv):", "",
              "    rocprofv3 --kernel-trace --stats --output-format csv -d <TRACE_DIR> -o run -- "
-             "python bench.py --steps 5 --warmup 2 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0 --target 0 --longctx 0", "",
+             "python bench.py --steps 5 --warmup 2 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0 --target 0 --longctx 0 --incremental 0 --tiny 0 --closed 0", "",
              f"Kernel sources hash: {h}", "",
              "| kernel | calls | avg us | total ms | % |", "|---|---|---|---|---|"]
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:20]:
@@ -1075,9 +1085,9 @@ def summarize(trace_dir, fetch_dir, write_dir):
     tl = [f"# HBM traffic per launch, {wl_name}", "",
           "Commands (repository root, csv output):", "",
           "    rocprofv3 --pmc FETCH_SIZE --output-format csv -d <FETCH_DIR> -o p -- "
-          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0 --target 0 --longctx 0 --copy-calibration 1",
+          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0 --target 0 --longctx 0 --incremental 0 --tiny 0 --closed 0 --copy-calibration 1",
           "    rocprofv3 --pmc WRITE_SIZE --output-format csv -d <WRITE_DIR> -o p -- "
-          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0 --target 0 --longctx 0 --copy-calibration 1",
+          "python bench.py --steps 2 --warmup 1 --cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0 --target 0 --longctx 0 --incremental 0 --tiny 0 --closed 0 --copy-calibration 1",
           "    python bench.py --summarize <TRACE_DIR> <FETCH_DIR> <WRITE_DIR>", "",
           f"Calibration: a {COPY_BYTES >> 20} MiB device copy (`{big[0][:60]}`) reads FETCH_SIZE = "
           f"{big[1]:.0f} KiB -> fetch scale {fetch_scale:.4f}; WRITE_SIZE scale "
@@ -1099,6 +1109,119 @@ def summarize(trace_dir, fetch_dir, write_dir):
     with open(os.path.join(ROOT, "profiles", f"hbm_traffic_{wl_name}.md"), "w") as fh:
         fh.write("\n".join(tl) + "\n")
     print("\n".join(lines + [""] + tl))
+
+
+PROFILE_OFF = ("--cpu-baseline 0 --device-loop 0 --block-sweep 0 --ceilings 0 --batch1 0 --target 0 --longctx 0 "
+               "--incremental 0 --tiny 0 --closed 0")
+SQ_PASSES = [
+    "SQ_LDS_BANK_CONFLICT SQ_LDS_IDX_ACTIVE SQ_VALU_MFMA_BUSY_CYCLES SQ_BUSY_CYCLES SQ_WAIT_INST_LDS SQ_INSTS_LDS "
+    "SQ_WAVE_CYCLES SQ_WAIT_ANY",
+    "SQ_INSTS_VALU SQ_INSTS_SALU SQ_INSTS_MFMA SQ_INSTS_LDS SQ_ACTIVE_INST_VALU SQ_WAIT_INST_ANY SQ_INSTS_VMEM "
+    "SQ_ACTIVE_INST_ANY",
+    "SQ_WAVES SQ_BUSY_CYCLES SQ_ACTIVE_INST_LDS SQ_ACTIVE_INST_SCA SQ_ACTIVE_INST_VMEM SQ_ACTIVE_INST_MISC "
+    "SQ_INST_CYCLES_SALU GRBM_GUI_ACTIVE",
+]
+SQ_CLASSES = [
+    ("LM head (`gemm_fl_kernel<256, 256, 4, 2, 1, 3>`, both denoise steps)", r"gemm_fl_kernel<256, 256, 4, 2, 1, 3>"),
+    ("gate/up (SwiGLU) (`gemm_fl_kernel<128, 384, 2, 4, 2, 2>`)", r"gemm_fl_kernel<128, 384, 2, 4, 2, 2>"),
+    ("O and down (residual) (`gemm_fl_kernel<128, 256, 2, 4, 2, 1>`)", r"gemm_fl_kernel<128, 256, 2, 4, 2, 1>"),
+    ("q/k/v (`gemm_fl_kernel<128, 384, 2, 4, 2, 0>`)", r"gemm_fl_kernel<128, 384, 2, 4, 2, 0>"),
+    ("attention context (`attn_ctx_mfma_kernel<128, 4>`)", r"attn_ctx_mfma_kernel<128, 4>"),
+    ("attention finish (`attn_finish_kernel`)", r"attn_finish_kernel"),
+    ("query prep (`attn_qprep_kernel`)", r"attn_qprep_kernel"),
+    ("RMSNorm (`rmsnorm_kernel`)", r"rmsnorm_kernel"),
+]
+
+
+def _counter_classes(d):
+    """Per kernel class, the mean over its dispatches of each counter (summed over the rows of a dispatch)."""
+    import collections
+    import glob
+    import numpy as np
+    per = collections.defaultdict(lambda: collections.defaultdict(float))
+    name = {}
+    for r in _read_csv(glob.glob(os.path.join(d, "*counter_collection.csv"))[0]):
+        per[r["Dispatch_Id"]][r["Counter_Name"]] += float(r["Counter_Value"])
+        name[r["Dispatch_Id"]] = r["Kernel_Name"]
+    cls = collections.defaultdict(lambda: collections.defaultdict(list))
+    for dd, c in per.items():
+        for label, pat in SQ_CLASSES:
+            if re.search(pat, name[dd]):
+                for k, v in c.items():
+                    cls[label][k].append(v)
+                break
+    return {l: {k: float(np.mean(v)) for k, v in c.items()} for l, c in cls.items()}
+
+
+def summarize_sq(d1, d2, d3):
+    """profiles/sq_counters_*.md from the three counter passes of SQ_PASSES."""
+    p1, p2, p3 = _counter_classes(d1), _counter_classes(d2), _counter_classes(d3)
+    wl_name = parse_workload_from(d1)
+    lines = [f"# Shader-sequencer counters per kernel, {wl_name}", "",
+             "Three counter passes over the same short benchmark run (repository root, csv output; each pass stays "
+             "within the per-block counter limits), then the summary:", ""]
+    for i, ctr in enumerate(SQ_PASSES, 1):
+        lines.append(f"    rocprofv3 --pmc {ctr} --output-format csv -d <DIR{i}> -o p -- python bench.py --steps 1 "
+                     f"--warmup 1 {PROFILE_OFF}")
+    lines += ["    python bench.py --summarize-sq <DIR1> <DIR2> <DIR3>", "",
+              f"Kernel sources hash: {source_hash()}", "",
+              "Derived per dispatch (each counter summed over the rows the tool reports for the dispatch), averaged "
+              "over the dispatches of each kernel. The GRBM_GUI_ACTIVE value is the sum over the 8 XCDs, so it is "
+              "divided by 8 to get the dispatch's cycles:", "",
+              "- MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / (cycles x 1024 SIMDs);",
+              "- LDS indexed busy % = SQ_LDS_IDX_ACTIVE / (cycles x 256 CUs) (ds_read/ds_write only; the direct "
+              "global->LDS copies are not indexed operations and are not in it);",
+              "- bank-conflict cycles % = SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE;",
+              "- wave time waiting % = SQ_WAIT_ANY / SQ_WAVE_CYCLES (both in quad-cycles);",
+              "- instructions per wave = SQ_INSTS_* / SQ_WAVES (\"other VALU\" excludes the MFMAs, which the VALU "
+              "count includes).", "",
+              "| kernel | cycles per XCD (µs at 2.1 GHz) | MFMA busy % | LDS indexed busy % | bank-conflict cycles % "
+              "of LDS | wave time waiting % | MFMA / wave | other VALU / wave | SALU / wave | LDS instr / wave |",
+              "|---|---|---|---|---|---|---|---|---|---|"]
+    for label, _ in SQ_CLASSES:
+        a, b, c = p1.get(label), p2.get(label), p3.get(label)
+        if not (a and b and c):
+            continue
+        cyc = c["GRBM_GUI_ACTIVE"] / 8
+        waves = max(c["SQ_WAVES"], 1.0)
+        lines.append(
+            f"| {label} | {cyc / 2100:.0f} | {100 * a['SQ_VALU_MFMA_BUSY_CYCLES'] / (cyc * 1024):.0f} | "
+            f"{100 * a['SQ_LDS_IDX_ACTIVE'] / (cyc * 256):.0f} | "
+            f"{100 * a['SQ_LDS_BANK_CONFLICT'] / max(a['SQ_LDS_IDX_ACTIVE'], 1):.0f} | "
+            f"{100 * a['SQ_WAIT_ANY'] / max(a['SQ_WAVE_CYCLES'], 1):.0f} | {b['SQ_INSTS_MFMA'] / waves:.0f} | "
+            f"{(b['SQ_INSTS_VALU'] - b['SQ_INSTS_MFMA']) / waves:.0f} | {b['SQ_INSTS_SALU'] / waves:.0f} | "
+            f"{b['SQ_INSTS_LDS'] / waves:.0f} |")
+    with open(os.path.join(ROOT, "profiles", f"sq_counters_{wl_name}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def summarize_verify(trace_dir):
+    """profiles/kernel_stats_sampled_verify_*.md: the sampled-verification kernels of a --longctx 1 trace."""
+    import glob
+    rows = _read_csv(glob.glob(os.path.join(trace_dir, "*kernel_stats.csv"))[0])
+    wl = "longctx_sampled_8b_shape_b16_bs32"
+    lines = [f"# rocprofv3 kernel statistics, sampled verification of {wl}", "",
+             "Command (run from the repository root, output csv), then the summary:", "",
+             "    rocprofv3 --kernel-trace --stats --output-format csv -d <TRACE_DIR> -o run -- python bench.py "
+             "--steps 2 --warmup 1 " + PROFILE_OFF.replace("--longctx 0", "--longctx 1"),
+             "    python bench.py --summarize-verify <TRACE_DIR>", "",
+             f"Kernel sources hash: {source_hash()}", "",
+             "The sampled-verification kernels run only in the `longctx_sampled` section of that command (batch 32, "
+             "block 16, vocabulary 151936, T = 1: 330 MB of target and 311 MB of draft logits per call); the rows "
+             "below are those kernels from `run_kernel_stats.csv`.", "",
+             "| kernel | calls | avg us | total ms |", "|---|---|---|---|"]
+    tot = 0.0
+    for w in ["lse_rows_kernel", "draw_select_kernel", "draw_segments_kernel", "lse_merge_kernel"]:
+        for r in rows:
+            if r["Name"].split("(")[0].endswith(w):
+                avg = float(r["AverageNs"]) / 1e3
+                tot += avg
+                lines.append(f"| `{w}` | {r['Calls']} | {avg:.1f} | {float(r['TotalDurationNs']) / 1e6:.2f} |")
+    lines += ["", f"Sum of the per-call averages: {tot:.1f} us per verification (641 MB of logits; 80 us at 8 TB/s)."]
+    with open(os.path.join(ROOT, "profiles", f"kernel_stats_sampled_verify_{wl}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def parse_workload_from(trace_dir):
