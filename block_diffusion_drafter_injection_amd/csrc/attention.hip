@@ -578,21 +578,31 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
     split_pages(p, npages, split, pg0, pg1);
     const TP* pool = (const TP*)p.pool;
     const size_t chunk = 16 * D;
+    // Each page's K and V chunks are staged in LDS by the whole workgroup (one
+    // coalesced pass, one memory round trip per page) and every query row then
+    // walks the page's tokens from LDS.
+    __shared__ float ks[16 * D], vs[16 * D];
     for (int pg = pg0; pg < pg1; ++pg) {
-      const int ph = phys_page(p, b, pg);
+      const int ph = phys_page(p, b, pg);   // the same for every thread of the workgroup
       if (ph < 0) continue;
       const TP* Kc = pool + (((size_t)ph * p.n_layers + p.layer) * 2 * p.nkv + m) * chunk;
       const TP* Vc = Kc + (size_t)p.nkv * chunk;
       const int ns = min(16, ctx - pg * 16);
+      __syncthreads();   // the previous page's reads are done
+      for (int i = tid; i < 16 * D; i += 256) {
+        ks[i] = ld_f(Kc, i);
+        vs[i] = ld_f(Vc, i);
+      }
+      __syncthreads();
       for (int slot = 0; slot < ns; ++slot) {
         float sd = 0.f;
 #pragma unroll
-        for (int e = 0; e < DQ; ++e) sd += q[e] * ld_f(Kc, (size_t)slot * D + q4 * DQ + e);
+        for (int e = 0; e < DQ; ++e) sd += q[e] * ks[slot * D + q4 * DQ + e];
         sd += __shfl_xor(sd, 1, kWave);
         sd += __shfl_xor(sd, 2, kWave);
         float vv[DQ];
 #pragma unroll
-        for (int e = 0; e < DQ; ++e) vv[e] = ld_f(Vc, (size_t)(q4 * DQ + e) * 16 + slot);
+        for (int e = 0; e < DQ; ++e) vv[e] = vs[(q4 * DQ + e) * 16 + slot];
         consume(sd, vv);
       }
     }

@@ -888,6 +888,72 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(ActIn a, BRows<float> b, 
   run_epilogue<KIND, BM, BN, NT, float>(Cs, LDC, m0, n0, M, N, e);
 }
 
+// fp32 GEMM for at most 16 rows (the fp32 workloads' draft forwards and step
+// injections, latency-bound): the rows' activations are staged in LDS once,
+// then each wave takes groups of G columns, loads every weight it needs for a
+// group at once (lanes across K: contiguous runs of the weight rows), forms
+// the row dot products in registers and sums them over the wave.  BN columns
+// per workgroup; the usual epilogues over the 16-row tile.
+constexpr int kF32RowsMaxK = 1024;
+template <int KIND, int BN>
+__global__ __launch_bounds__(256) void gemm_f32_rows_kernel(ActIn a, BRows<float> b, int M, int N, int K,
+                                                            EpiParams e) {
+  constexpr int LDC = BN + 4, KK = kF32RowsMaxK / 64, G = 4, GPW = BN / 4 / G;
+  static_assert(BN % (4 * G) == 0, "columns per wave");
+  __shared__ __attribute__((aligned(16))) float As[16 * kF32RowsMaxK];
+  __shared__ __attribute__((aligned(16))) float Cs[16 * LDC];
+  const int n0 = blockIdx.x * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const float* A = (const float*)a.p0;
+  for (int i = tid; i < M * K; i += 256) {
+    const int m = i / K, k = i - m * K;
+    As[m * kF32RowsMaxK + k] = A[(size_t)m * a.ld + k];
+  }
+  __syncthreads();
+  for (int gi = 0; gi < GPW; ++gi) {
+    const int c0 = (wid * GPW + gi) * G;
+    float w[G][KK];
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+      const float* br = b.row(min(n0 + c0 + j, N - 1), BN);
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int k = lane + 64 * kk;
+        w[j][kk] = k < K ? br[k] : 0.f;
+      }
+    }
+    float acc[G][16];
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int m = 0; m < 16; ++m) acc[j][m] = 0.f;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      const int k = lane + 64 * kk;
+      if (64 * kk >= K) break;
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        if (m >= M) break;
+        const float av = k < K ? As[m * kF32RowsMaxK + k] : 0.f;
+#pragma unroll
+        for (int j = 0; j < G; ++j) acc[j][m] = fmaf(av, w[j][kk], acc[j][m]);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < G; ++j)
+#pragma unroll
+      for (int m = 0; m < 16; ++m) {
+        if (m >= M) break;
+        float v = acc[j][m];
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+        if (lane == 0) Cs[m * LDC + c0 + j] = v;
+      }
+  }
+  __syncthreads();
+  run_epilogue<KIND, 16, BN, 256, float>(Cs, LDC, 0, n0, M, N, e);
+}
+
 // ---------------------------------------------------------------------------
 // Tile choice per GEMM kind (bf16 weights):
 //   2: 128x128, four 64x64 waves, two workgroups per CU (gemm_dma_kernel;
@@ -1004,6 +1070,14 @@ size_t gemm_partial_bytes(const GemmPlan& p, int M, int N) {
 
 template <int KIND>
 static hipError_t go_f32(const GemmArgs& g, hipStream_t s) {
+  if (g.M <= 16 && g.K <= kF32RowsMaxK) {
+    // LM-head partials and the KV scatter's rotated heads need 128-column tiles
+    constexpr int BN = (KIND == EPI_LMHEAD || KIND == EPI_KVSCATTER) ? 128 : 32;
+    BRows<float> b{(const float*)g.b.b0, (const float*)g.b.b1, g.b.ldb, g.b.split, g.b.mode};
+    hipLaunchKernelGGL((gemm_f32_rows_kernel<KIND, BN>), dim3((g.N + BN - 1) / BN), dim3(256), 0, s, g.a, b, g.M,
+                       g.N, g.K, g.e);
+    return hipGetLastError();
+  }
   const int total = ((g.M + 63) / 64) * ((g.N + 127) / 128);
   const int grid = (total + 7) / 8 * 8;
   BRows<float> b{(const float*)g.b.b0, (const float*)g.b.b1, g.b.ldb, g.b.split, g.b.mode};
