@@ -589,9 +589,16 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
       const TP* Vc = Kc + (size_t)p.nkv * chunk;
       const int ns = min(16, ctx - pg * 16);
       __syncthreads();   // the previous page's reads are done
-      for (int i = tid; i < 16 * D; i += 256) {
-        ks[i] = ld_f(Kc, i);
-        vs[i] = ld_f(Vc, i);
+      float kv[2][16 * D / 256];   // all of a thread's loads in flight before any LDS store
+#pragma unroll
+      for (int t = 0; t < 16 * D / 256; ++t) {
+        kv[0][t] = ld_f(Kc, tid + 256 * t);
+        kv[1][t] = ld_f(Vc, tid + 256 * t);
+      }
+#pragma unroll
+      for (int t = 0; t < 16 * D / 256; ++t) {
+        ks[tid + 256 * t] = kv[0][t];
+        vs[tid + 256 * t] = kv[1][t];
       }
       __syncthreads();
       for (int slot = 0; slot < ns; ++slot) {

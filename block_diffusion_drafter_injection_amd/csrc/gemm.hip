@@ -889,27 +889,42 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(ActIn a, BRows<float> b, 
 }
 
 // fp32 GEMM for at most 16 rows (the fp32 workloads' draft forwards and step
-// injections, latency-bound): the rows' activations are staged in LDS once,
-// then each wave takes groups of G columns, loads every weight it needs for a
-// group at once (lanes across K: contiguous runs of the weight rows), forms
-// the row dot products in registers and sums them over the wave.  BN columns
-// per workgroup; the usual epilogues over the 16-row tile.
+// injections, latency-bound): the rows' activations are copied to LDS once
+// (direct 16-byte loads, all in flight together), then each wave takes groups
+// of G columns, loads every weight it needs for a group at once (lanes across
+// K: contiguous runs of the weight rows) and, row by row, forms the dot
+// products in registers and sums them over the wave.  BN columns per
+// workgroup; the usual epilogues over the 16-row tile.  KK = K / 64 rounded up
+// to 4, 8 or 16; a group holds at most 64 weights per lane, so it has
+// min(64 / KK, 8) columns.  Rows are 16-byte aligned with K a multiple of 4
+// (checked by the host).
 constexpr int kF32RowsMaxK = 1024;
-template <int KIND, int BN>
+template <int KIND, int BN, int KK>
 __global__ __launch_bounds__(256) void gemm_f32_rows_kernel(ActIn a, BRows<float> b, int M, int N, int K,
                                                             EpiParams e) {
-  constexpr int LDC = BN + 4, KK = kF32RowsMaxK / 64, G = 4, GPW = BN / 4 / G;
-  static_assert(BN % (4 * G) == 0, "columns per wave");
-  __shared__ __attribute__((aligned(16))) float As[16 * kF32RowsMaxK];
+  constexpr int G0 = (64 / KK < BN / 4) ? 64 / KK : BN / 4, G = G0 < 8 ? G0 : 8, LDC = BN + 4, GPW = BN / 4 / G;
+  static_assert(BN % (4 * G) == 0 && KK * 64 <= kF32RowsMaxK, "columns per wave");
+  __shared__ __attribute__((aligned(1024))) float As[16 * kF32RowsMaxK];
   __shared__ __attribute__((aligned(16))) float Cs[16 * LDC];
   const int n0 = blockIdx.x * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wid = __builtin_amdgcn_readfirstlane(tid >> 6);
   const float* A = (const float*)a.p0;
-  for (int i = tid; i < M * K; i += 256) {
-    const int m = i / K, k = i - m * K;
-    As[m * kF32RowsMaxK + k] = A[(size_t)m * a.ld + k];
+  {
+    // 1 KiB blocks (256 floats of a row); lanes past the row's end read its last
+    // four values again (their LDS slots are never used)
+    const int nkb = (K + 255) / 256;
+    const uint32_t as0 = (uint32_t)(size_t)As;
+    for (int f = wid; f < M * nkb; f += 4) {
+      const int m = f / nkb, kb = f - m * nkb;
+      const int k = min(kb * 256 + lane * 4, K - 4);
+      __builtin_amdgcn_global_load_lds((const __attribute__((address_space(1))) void*)(A + (size_t)m * a.ld + k),
+                                       (__attribute__((address_space(3))) void*)(size_t)(
+                                           as0 + (uint32_t)(m * kF32RowsMaxK + kb * 256) * 4),
+                                       16, 0, 0);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
   }
-  __syncthreads();
   for (int gi = 0; gi < GPW; ++gi) {
     const int c0 = (wid * GPW + gi) * G;
     float w[G][KK];
@@ -922,33 +937,26 @@ __global__ __launch_bounds__(256) void gemm_f32_rows_kernel(ActIn a, BRows<float
         w[j][kk] = k < K ? br[k] : 0.f;
       }
     }
-    float acc[G][16];
+    // rows: a runtime loop (the arrays are indexed by unrolled constants only)
+    for (int m = 0; m < M; ++m) {
+      float acc[G];
 #pragma unroll
-    for (int j = 0; j < G; ++j)
+      for (int j = 0; j < G; ++j) acc[j] = 0.f;
 #pragma unroll
-      for (int m = 0; m < 16; ++m) acc[j][m] = 0.f;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      const int k = lane + 64 * kk;
-      if (64 * kk >= K) break;
-#pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        if (m >= M) break;
+      for (int kk = 0; kk < KK; ++kk) {
+        const int k = lane + 64 * kk;
         const float av = k < K ? As[m * kF32RowsMaxK + k] : 0.f;
 #pragma unroll
-        for (int j = 0; j < G; ++j) acc[j][m] = fmaf(av, w[j][kk], acc[j][m]);
+        for (int j = 0; j < G; ++j) acc[j] = fmaf(av, w[j][kk], acc[j]);
       }
-    }
 #pragma unroll
-    for (int j = 0; j < G; ++j)
-#pragma unroll
-      for (int m = 0; m < 16; ++m) {
-        if (m >= M) break;
-        float v = acc[j][m];
+      for (int j = 0; j < G; ++j) {
+        float v = acc[j];
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
         if (lane == 0) Cs[m * LDC + c0 + j] = v;
       }
+    }
   }
   __syncthreads();
   run_epilogue<KIND, 16, BN, 256, float>(Cs, LDC, 0, n0, M, N, e);
@@ -1070,12 +1078,18 @@ size_t gemm_partial_bytes(const GemmPlan& p, int M, int N) {
 
 template <int KIND>
 static hipError_t go_f32(const GemmArgs& g, hipStream_t s) {
-  if (g.M <= 16 && g.K <= kF32RowsMaxK) {
+  if (g.M <= 16 && g.K <= kF32RowsMaxK && g.K >= 4 && g.K % 4 == 0 && g.a.ld % 4 == 0 &&
+      (uintptr_t)g.a.p0 % 16 == 0) {
     // LM-head partials and the KV scatter's rotated heads need 128-column tiles
     constexpr int BN = (KIND == EPI_LMHEAD || KIND == EPI_KVSCATTER) ? 128 : 32;
     BRows<float> b{(const float*)g.b.b0, (const float*)g.b.b1, g.b.ldb, g.b.split, g.b.mode};
-    hipLaunchKernelGGL((gemm_f32_rows_kernel<KIND, BN>), dim3((g.N + BN - 1) / BN), dim3(256), 0, s, g.a, b, g.M,
-                       g.N, g.K, g.e);
+    const dim3 grid((g.N + BN - 1) / BN);
+    if (g.K <= 256)
+      hipLaunchKernelGGL((gemm_f32_rows_kernel<KIND, BN, 4>), grid, dim3(256), 0, s, g.a, b, g.M, g.N, g.K, g.e);
+    else if (g.K <= 512)
+      hipLaunchKernelGGL((gemm_f32_rows_kernel<KIND, BN, 8>), grid, dim3(256), 0, s, g.a, b, g.M, g.N, g.K, g.e);
+    else
+      hipLaunchKernelGGL((gemm_f32_rows_kernel<KIND, BN, 16>), grid, dim3(256), 0, s, g.a, b, g.M, g.N, g.K, g.e);
     return hipGetLastError();
   }
   const int total = ((g.M + 63) / 64) * ((g.N + 127) / 128);
