@@ -114,7 +114,7 @@ struct Carve {
   }
 };
 
-void attn_split(int bt, int nkv, int nqg, int ctx_cap, int& ns, int& pps) {
+void attn_split(int bt, int nkv, int nqg, int ctx_cap, bool valu, int& ns, int& pps) {
   const int pages = (ctx_cap + 15) / 16;
   if (pages <= 0) {
     ns = 0;
@@ -131,7 +131,10 @@ void attn_split(int bt, int nkv, int nqg, int ctx_cap, int& ns, int& pps) {
   constexpr int kAttWgTarget = 512, kAttMaxPps = 132, kAttBalanceSplits = 4;
   const int by_len = std::min(kAttBalanceSplits, (pages + kAttMaxPps - 1) / kAttMaxPps);
   const int want = std::max((kAttWgTarget + pairs - 1) / pairs, by_len);
-  const int max_ns = std::max(1, pages / 8);   // at least four 32-token tiles per split
+  // at least four 32-token tiles per split for the MFMA kernel (its pipeline
+  // fill); the VALU kernel (fp32 pools, head_dim 64) walks a split page by
+  // page and takes splits down to one tile
+  const int max_ns = valu ? std::max(1, (pages + 1) / 2) : std::max(1, pages / 8);
   const int min_ns = (pages + 511) / 512;   // the context kernel stages at most 512 page ids
   ns = std::max(min_ns, std::max(1, std::min(want, max_ns)));
   pps = (pages + ns - 1) / ns;
@@ -156,7 +159,7 @@ DraftWS draft_layout(const dflash_config* c, int bt, int B, int ctx_cap) {
   const size_t M = (size_t)bt * B;
   const size_t H = c->hidden, I = c->intermediate, d = c->head_dim, nq = c->n_q_heads, nkv = c->n_kv_heads;
   const size_t el = c->dtype == DFLASH_BF16 ? 2 : 4;  // one plane of an activation operand
-  attn_split(bt, (int)nkv, n_qgroups(c, B), ctx_cap, w.ns, w.pps);
+  attn_split(bt, (int)nkv, n_qgroups(c, B), ctx_cap, !(c->dtype == DFLASH_BF16 && c->head_dim == 128), w.ns, w.pps);
   w.ntiles = (c->vocab + gemm_bn(c->dtype, c->hidden) - 1) / gemm_bn(c->dtype, c->hidden);
   Carve k;
   w.h = k.take(M * H * 4);

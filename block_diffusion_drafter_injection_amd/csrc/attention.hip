@@ -553,18 +553,19 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
   {
     const float* qv = p.qkv + (size_t)row * ldq + n * D;
     const float2* cs = p.cs + (size_t)row * (D / 2);
+    // scores in base-2 units: the query carries scale * log2 e
+    const float qs = p.scale * 1.4426950408889634f;
 #pragma unroll
     for (int e = 0; e < DQ; ++e) {
-      q[e] = rvalid ? rope_elem(qv, cs, q4 * DQ + e, D) : 0.f;
+      q[e] = rvalid ? rope_elem(qv, cs, q4 * DQ + e, D) * qs : 0.f;
       o[e] = 0.f;
     }
   }
   float m_run = -INFINITY, l_run = 0.f;
-  auto consume = [&](float sdot, const float* vvals) {  // vvals may point to LDS
+  auto consume = [&](float sc, const float* vvals) {  // vvals may point to LDS
     // vvals: this lane's DQ value entries
-    const float sc = sdot * p.scale;
     const float m_new = fmaxf(m_run, sc);
-    const float alpha = expf(m_run - m_new), pw = expf(sc - m_new);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new), pw = __builtin_amdgcn_exp2f(sc - m_new);
     l_run = l_run * alpha + pw;
 #pragma unroll
     for (int e = 0; e < DQ; ++e) o[e] = o[e] * alpha + pw * vvals[e];
@@ -618,7 +619,9 @@ __global__ __launch_bounds__(256) void attn_valu_kernel(AttnParams p) {
   const size_t Mq = (size_t)p.batch * p.B * p.nq;
   const size_t qrow = (size_t)row * p.nq + n;
   const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
-  if (q4 == 0) p.part_lse[split * Mq + qrow] = l_run > 0.f ? m_run + logf(l_run) : -INFINITY;
+  // natural-log LSE, as the finish kernel merges it
+  if (q4 == 0)
+    p.part_lse[split * Mq + qrow] = l_run > 0.f ? (m_run + log2f(l_run)) * 0.6931471805599453f : -INFINITY;
   float* dst = p.part_o + (split * Mq + qrow) * D + q4 * DQ;
 #pragma unroll
   for (int e = 0; e < DQ; ++e) dst[e] = o[e] * inv;
