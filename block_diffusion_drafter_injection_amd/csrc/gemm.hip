@@ -446,7 +446,7 @@ __device__ __forceinline__ void mfma_read_interleave() {
 // read touches land on distinct bank groups).  The fragment pipeline runs in
 // 32-deep half stages: the reads of the next half overlap the MFMAs of the
 // current one, and the one barrier per stage sits between the two halves.
-template <int BM, int BN, int WGM, int WGN, int NP>
+template <int BM, int BN, int WGM, int WGN, int NP, int BS = 2>
 struct FlCfg {
   static constexpr int NT = 64 * WGM * WGN, NW = WGM * WGN, BK = 64;
   static constexpr int WM = BM / WGM, WN = BN / WGN, FM = WM / 16, FN = WN / 16;
@@ -455,7 +455,10 @@ struct FlCfg {
   static constexpr int BLOCKS = ROWS / 8;             // 1 KiB load instructions per stage
   static constexpr int LPT = BLOCKS / NW;             // per wave
   static constexpr int LDC = BN + 4;
-  static constexpr int SMEM_PIPE = 2 * STAGE_BYTES;
+  // BS = 3: activation rows in two slots, weight rows in three (weights run a stage further ahead)
+  static constexpr int A_BYTES = NP * BM * 128, B_BYTES = BN * 128, A_BLOCKS = NP * BM / 8;
+  static constexpr int SMEM_PIPE = BS == 2 ? 2 * STAGE_BYTES : 2 * A_BYTES + BS * B_BYTES;
+  static_assert(BS == 2 || (BS == 3 && A_BLOCKS % LPT == 0 && (NP * BM) % 16 == 0), "loader waves");
   static constexpr int SMEM_EPI = 64 * LDC * 4;
   static constexpr int SMEM = SMEM_PIPE > SMEM_EPI ? SMEM_PIPE : SMEM_EPI;
   static_assert(BLOCKS % NW == 0 && WM % 16 == 0 && WN % 16 == 0 && WM == 64, "tile shape");
@@ -463,10 +466,10 @@ struct FlCfg {
   static_assert(LPT <= 63, "vmcnt range");
 };
 
-template <int BM, int BN, int WGM, int WGN, int NP, int KIND>
+template <int BM, int BN, int WGM, int WGN, int NP, int KIND, int BS = 2>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_fl_kernel(ActIn a, BRows<bf16_t> b, int M, int N, int K,
                                                                      int ksplit, float* part, EpiParams e) {
-  using C = FlCfg<BM, BN, WGM, WGN, NP>;
+  using C = FlCfg<BM, BN, WGM, WGN, NP, BS>;
   constexpr int BK = C::BK, LPT = C::LPT, FM = C::FM, FN = C::FN, NT = C::NT;
   // SwiGLU tiles load gate and up rows interleaved per 32 columns, so each
   // wave holds both halves of its output columns
@@ -556,6 +559,84 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_fl_kernel(ActIn a, BRo
 
   const int nloc = kt1 - kt0;
   bf16x8 f0a[NP][FM], f0b[FN], f1a[NP][FM], f1b[FN];
+  if constexpr (BS == 3) {
+    // Activation rows in two slots, weight rows in three: a wave's load blocks
+    // are all activation rows or all weight rows, and the weight rows of stage
+    // it+3 are issued at the stage boundary after stage it, two stage-times
+    // before their use (the activation rows of stage it+2, one stage-time).
+    const bool a_wave = wid_u * LPT < C::A_BLOCKS;
+    const uint32_t dst0 = a_wave ? lds0 + (uint32_t)(wid_u * LPT) * 1024
+                                 : lds0 + 2 * C::A_BYTES + (uint32_t)(wid_u * LPT - C::A_BLOCKS) * 1024;
+    const uint32_t slot_bytes = a_wave ? C::A_BYTES : C::B_BYTES;
+#define FL3_ISSUE(KT, SLOT)                                                                                      \
+  do {                                                                                                           \
+    const uint32_t k0_ = (uint32_t)(KT) * (BK * 2);                                                              \
+    const uint32_t d_ = dst0 + (uint32_t)(SLOT) * slot_bytes;                                                    \
+    _Pragma("unroll") for (int q = 0; q < LPT; ++q) {                                                            \
+      __builtin_amdgcn_global_load_lds(                                                                          \
+          (const __attribute__((address_space(1))) void*)((const char*)bbase[q] + (size_t)(boff[q] + k0_)),      \
+          (__attribute__((address_space(3))) void*)(size_t)(d_ + q * 1024), 16, 0, 0);                           \
+    }                                                                                                            \
+  } while (0)
+#define FL3_LOAD(F, SA, SB, H)                                                                                 \
+  do {                                                                                                         \
+    const unsigned char* sa_ = smem + (SA) * C::A_BYTES;                                                       \
+    const unsigned char* sb_ = smem + 2 * C::A_BYTES + (SB) * C::B_BYTES;                                      \
+    const int lc_ = 4 * (H) + lq;                                                                              \
+    _Pragma("unroll") for (int p = 0; p < NP; ++p) _Pragma("unroll") for (int i = 0; i < FM; ++i) {            \
+      const int row = p * BM + wm * C::WM + 16 * i + lr;                                                       \
+      F##a[p][i] = as_bf16x8(*(const u32x4*)(sa_ + row * 128 + ((lc_ ^ ((row >> 1) & 7)) << 4)));             \
+    }                                                                                                          \
+    _Pragma("unroll") for (int j = 0; j < FN; ++j) {                                                           \
+      const int row = wn * C::WN + 16 * j + lr;                                                                \
+      F##b[j] = as_bf16x8(*(const u32x4*)(sb_ + row * 128 + ((lc_ ^ ((row >> 1) & 7)) << 4)));                \
+    }                                                                                                          \
+  } while (0)
+    if (nloc > 0) FL3_ISSUE(kt0, 0);
+    if (nloc > 1) FL3_ISSUE(kt0 + 1, 1);
+    if (!a_wave && nloc > 2) FL3_ISSUE(kt0 + 2, 2);
+    if (nloc > 0) {
+      // stage 0 landed: an activation wave may leave stage 1 in flight, a weight
+      // wave stages 1 and 2
+      if (a_wave) {
+        if (nloc > 1) wait_vmcnt<LPT>();
+        else wait_vmcnt<0>();
+      } else {
+        if (nloc > 2) wait_vmcnt<2 * LPT>();
+        else if (nloc > 1) wait_vmcnt<LPT>();
+        else wait_vmcnt<0>();
+      }
+      stage_barrier();
+      FL3_LOAD(f0, 0, 0, 0);
+    }
+    for (int it = 0; it < nloc; ++it) {
+      const int sa = it & 1, sb = it % 3, sb1 = sb == 2 ? 0 : sb + 1;
+      FL3_LOAD(f1, sa, sb, 1);
+      FL_MMA(f0);
+      mfma_read_interleave<NP * FM + FN, NP * FM * FN>();
+      if (it + 1 < nloc) {
+        // stage it+1 landed (a weight wave may still have stage it+2 in flight);
+        // every wave holds all of stage it, so its slots take stages it+2 / it+3
+        if (a_wave) {
+          wait_vmcnt<0>();
+        } else {
+          if (it + 2 < nloc) wait_vmcnt<LPT>();
+          else wait_vmcnt<0>();
+        }
+        lds_reads_done_barrier();
+        if (a_wave) {
+          if (it + 2 < nloc) FL3_ISSUE(kt0 + it + 2, sa);
+        } else {
+          if (it + 3 < nloc) FL3_ISSUE(kt0 + it + 3, sb);
+        }
+      }
+      FL3_LOAD(f0, sa ^ 1, sb1, 0);
+      FL_MMA(f1);
+      mfma_read_interleave<NP * FM + FN, NP * FM * FN>();
+    }
+#undef FL3_LOAD
+#undef FL3_ISSUE
+  } else {
   if (nloc > 0) FL_ISSUE(kt0, 0);
   if (nloc > 1) FL_ISSUE(kt0 + 1, 1);
   if (nloc > 0) {
@@ -583,6 +664,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_fl_kernel(ActIn a, BRo
     FL_LOAD(f0, cur ^ 1, 0);
     FL_MMA(f1);
     mfma_read_interleave<NP * FM + FN, NP * FM * FN>();
+  }
   }
 #undef FL_LOAD
 #undef FL_MMA
@@ -1114,13 +1196,13 @@ static hipError_t go_dma(const GemmArgs& g, int ksplit, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WGM, int WGN, int NP, int KIND>
+template <int BM, int BN, int WGM, int WGN, int NP, int KIND, int BS = 2>
 static hipError_t go_fl(const GemmArgs& g, int ksplit, hipStream_t s) {
   const int ntm = (g.M + BM - 1) / BM, ntn = (g.N + BN - 1) / BN;
   const int total = ntm * ntn * ksplit;
   const int grid = (total + 7) / 8 * 8;
   BRows<bf16_t> b{(const bf16_t*)g.b.b0, (const bf16_t*)g.b.b1, g.b.ldb, g.b.split, g.b.mode};
-  hipLaunchKernelGGL((gemm_fl_kernel<BM, BN, WGM, WGN, NP, KIND>), dim3(grid), dim3(64 * WGM * WGN), 0, s, g.a, b,
+  hipLaunchKernelGGL((gemm_fl_kernel<BM, BN, WGM, WGN, NP, KIND, BS>), dim3(grid), dim3(64 * WGM * WGN), 0, s, g.a, b,
                      g.M, g.N, g.K, ksplit, g.part, g.e);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || ksplit == 1 || (g.defer_reduce && (KIND == EPI_ADD || KIND == EPI_STORE))) return err;
@@ -1149,7 +1231,7 @@ static hipError_t go_bf16(const GemmArgs& g, const GemmPlan& p, hipStream_t s) {
     case 20: if constexpr (!scatter) return go_skinny<NP, KIND>(g, p.ksplit, s); break;
     case 2: return go_dma<NP, KIND>(g, p.ksplit, s);
     case 10: if constexpr (!scatter) return go_fl<128, 384, 2, 4, NP, KIND>(g, p.ksplit, s); break;
-    case 11: if constexpr (NP == 1 && !scatter) return go_fl<256, 256, 4, 2, 1, KIND>(g, p.ksplit, s); break;
+    case 11: if constexpr (NP == 1 && !scatter) return go_fl<256, 256, 4, 2, 1, KIND, 3>(g, p.ksplit, s); break;
     case 12: if constexpr (!scatter) return go_fl<128, 256, 2, 4, NP, KIND>(g, p.ksplit, s); break;
     case 13: if constexpr (NP == 1 && !scatter) return go_fl<64, 256, 1, 8, 1, KIND>(g, p.ksplit, s); break;
     default: break;

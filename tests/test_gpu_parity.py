@@ -161,6 +161,8 @@ def _draft_case(dims, ctx, B, S, T, seed, want_logits=True, schedule="progressiv
     ("small", [45, 200], 16, 3, 0.0),
     ("small", [77, 8], 8, 2, 1.0),
     ("tiny", [64], 4, 2, 0.7),
+    ("small", [200], 8, 2, 0.0),          # one sequence: K sliced inside the workgroup (at most 16 rows)
+    ("small", [31], 16, 2, 1.0),
 ])
 def test_draft_matches_oracle(name, ctx, B, S, T):
     dims = _dims(name)
