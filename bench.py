@@ -68,14 +68,15 @@ def parse():
 
 COPY_BYTES = 1 << 29          # 512 MiB read + 512 MiB written by the calibration copy
 # Kernel name patterns (regular expressions) of each timed class: GEMM kernels
-# end their template arguments with (operand planes, epilogue kind).
+# end their template arguments with (operand planes, epilogue kind), the
+# large-tile kernel then with its count of weight stages.
 KERNEL_NAMES = {
     "attn": r"attn_ctx_mfma_kernel",
-    "gemm_qkv": r"gemm_\w+_kernel<[^>]*, 2, 0>",
-    "gemm_o": r"gemm_\w+_kernel<[^>]*, 2, 1>",
-    "gemm_down": r"gemm_\w+_kernel<[^>]*, 2, 1>",
-    "gemm_gateup": r"gemm_\w+_kernel<[^>]*, 2, 2>",
-    "lmhead": r"gemm_\w+_kernel<[^>]*, 1, 3>",
+    "gemm_qkv": r"gemm_\w+_kernel<[^>]*, 2, 0(, \d)?>",
+    "gemm_o": r"gemm_\w+_kernel<[^>]*, 2, 1(, \d)?>",
+    "gemm_down": r"gemm_\w+_kernel<[^>]*, 2, 1(, \d)?>",
+    "gemm_gateup": r"gemm_\w+_kernel<[^>]*, 2, 2(, \d)?>",
+    "lmhead": r"gemm_\w+_kernel<[^>]*, 1, 3(, \d)?>",
 }
 KERNEL_SOURCES = ["common.h", "kernels.h", "gemm.hip", "attention.hip", "elementwise.hip", "verify.hip", "api.cpp"]
 
@@ -1122,10 +1123,10 @@ SQ_PASSES = [
     "SQ_INST_CYCLES_SALU GRBM_GUI_ACTIVE",
 ]
 SQ_CLASSES = [
-    ("LM head (`gemm_fl_kernel<256, 256, 4, 2, 1, 3>`, both denoise steps)", r"gemm_fl_kernel<256, 256, 4, 2, 1, 3>"),
-    ("gate/up (SwiGLU) (`gemm_fl_kernel<128, 384, 2, 4, 2, 2>`)", r"gemm_fl_kernel<128, 384, 2, 4, 2, 2>"),
-    ("O and down (residual) (`gemm_fl_kernel<128, 256, 2, 4, 2, 1>`)", r"gemm_fl_kernel<128, 256, 2, 4, 2, 1>"),
-    ("q/k/v (`gemm_fl_kernel<128, 384, 2, 4, 2, 0>`)", r"gemm_fl_kernel<128, 384, 2, 4, 2, 0>"),
+    ("LM head (`gemm_fl_kernel<256, 256, 4, 2, 1, 3, 3>`, both denoise steps)", r"gemm_fl_kernel<256, 256, 4, 2, 1, 3, 3>"),
+    ("gate/up (SwiGLU) (`gemm_fl_kernel<128, 384, 2, 4, 2, 2, 2>`)", r"gemm_fl_kernel<128, 384, 2, 4, 2, 2, 2>"),
+    ("O and down (residual) (`gemm_fl_kernel<128, 256, 2, 4, 2, 1, 2>`)", r"gemm_fl_kernel<128, 256, 2, 4, 2, 1, 2>"),
+    ("q/k/v (`gemm_fl_kernel<128, 384, 2, 4, 2, 0, 2>`)", r"gemm_fl_kernel<128, 384, 2, 4, 2, 0, 2>"),
     ("attention context (`attn_ctx_mfma_kernel<128, 4>`)", r"attn_ctx_mfma_kernel<128, 4>"),
     ("attention finish (`attn_finish_kernel`)", r"attn_finish_kernel"),
     ("query prep (`attn_qprep_kernel`)", r"attn_qprep_kernel"),
