@@ -151,6 +151,7 @@ int n_qgroups(const dflash_config* c, int B) {
 struct DraftWS {
   size_t h, u_hi, u_lo, qkv, o_hi, o_lo, act_hi, act_lo, y, row_map, part_f, part_i, att_o, att_lse, cs, tau,
       committed, cand, conf, gemm_part, q_hi, q_lo, kblk, vblk, total;
+  size_t gemm_part_bytes;
   int ns, pps, ntiles;
 };
 
@@ -194,7 +195,9 @@ DraftWS draft_layout(const dflash_config* c, int bt, int B, int ctx_cap) {
     pb = std::max(pb, gemm_partial_bytes(gemm_plan(wd, am, Mi, Hi, Nq, EPI_ADD, false), Mi, Hi));
     pb = std::max(pb, gemm_partial_bytes(gemm_plan(wd, am, Mi, 2 * Ii, Hi, EPI_SWIGLU, false), Mi, 2 * Ii));
     pb = std::max(pb, gemm_partial_bytes(gemm_plan(wd, am, Mi, Hi, Ii, EPI_ADD, false), Mi, Hi));
+    if (wd) pb = std::max(pb, gemm_lmhead_part_bytes(Mi, c->vocab));   // LM head's last round of tiles
     w.gemm_part = k.take(pb);
+    w.gemm_part_bytes = pb;
   }
   w.total = k.off;
   return w;
@@ -724,6 +727,8 @@ dflash_status dflash_draft_block(const dflash_config* cfg, const dflash_weights*
     gl.e.seed_lo = (uint32_t)(seed & 0xffffffffu);
     gl.e.seed_hi = (uint32_t)(seed >> 32);
     gl.e.step = s;
+    gl.part = gpart;
+    gl.part_cap = L.gemm_part_bytes;
     HIP_TRY(gemm(DFLASH_PROF_LMHEAD, gl, stream));
     HIP_TRY(launch_lm_combine(gl.e.part_f, gl.e.part_i, L.ntiles, Ms, row_map, cand, conf, stream));
     HIP_TRY(launch_commit(cand, conf, tau, committed, out_conf, out_tokens, batch, B, S, s, k_s, last, repredict,
@@ -836,6 +841,8 @@ dflash_status dflash_target_forward(const dflash_config* cfg, const dflash_weigh
   gl.e.logits = out_logits;
   gl.e.block = B;
   gl.e.temperature = 0.f;
+  gl.part = fb.gpart;
+  gl.part_cap = L.gemm_part_bytes;
   HIP_TRY(gemm(DFLASH_PROF_LMHEAD, gl, stream));
   return DFLASH_OK;
 }

@@ -116,7 +116,7 @@ __device__ __forceinline__ void run_epilogue(const float* Cs, int ldc, int m0, i
         const int r = idx / C4, c = (idx - r * C4) * 4;
         const int row = m0 + r;
         if (row >= M) continue;
-        const size_t base = (size_t)e.row_map[row] * N;
+        const size_t base = (size_t)e.row_map[row] * e.ldz + e.col0;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           if (n0 + c + q < N) e.logits[base + n0 + c + q] = Cs[r * ldc + c + q];
@@ -144,11 +144,12 @@ __device__ __forceinline__ void run_epilogue(const float* Cs, int ldc, int m0, i
       const int c0 = gq * GRP + q * CPT;
       if (rv) {
         for (int c = 0; c < CPT; c += 4) {
-          const int v0 = n0 + c0 + c;
+          const int v0 = n0 + c0 + c;   // launch column; vocabulary index e.col0 + v0
           uint4 w = make_uint4(0, 0, 0, 0);
           if (samp && v0 < N)
-            w = philox4x32_10(make_uint4((uint32_t)(v0 >> 2), (uint32_t)bi, (uint32_t)e.step, (uint32_t)bb),
-                              e.seed_lo, e.seed_hi);
+            w = philox4x32_10(
+                make_uint4((uint32_t)((e.col0 + v0) >> 2), (uint32_t)bi, (uint32_t)e.step, (uint32_t)bb),
+                e.seed_lo, e.seed_hi);
           const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
           for (int k = 0; k < 4; ++k) {
@@ -156,7 +157,7 @@ __device__ __forceinline__ void run_epilogue(const float* Cs, int ldc, int m0, i
             if (v >= N) break;
             const float zt = samp ? Cs[r * ldc + c0 + c + k] / T : Cs[r * ldc + c0 + c + k];
             const float sc = samp ? zt + gumbel_from_word(ww[k]) : zt;
-            if (sc > P.pmax || P.idx < 0) { P.pmax = sc; P.idx = v; P.zc = zt; }
+            if (sc > P.pmax || P.idx < 0) { P.pmax = sc; P.idx = e.col0 + v; P.zc = zt; }
             P.zmax = fmaxf(P.zmax, zt);
           }
         }
@@ -177,7 +178,7 @@ __device__ __forceinline__ void run_epilogue(const float* Cs, int ldc, int m0, i
         P = (q & o) ? lm_merge(Q, P) : lm_merge(P, Q);
       }
       if (rv && q == 0 && n0 + gq * GRP < N) {
-        const size_t pi = (size_t)row * e.ntiles + (n0 + gq * GRP) / GRP;
+        const size_t pi = (size_t)row * e.ntiles + (e.col0 + n0 + gq * GRP) / GRP;
         e.part_f[pi] = make_float4(P.pmax, P.zmax, P.zsum, P.zc);
         e.part_i[pi] = P.idx;
       }
@@ -729,7 +730,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_fl_kernel(ActIn a, BRo
             for (int j = 0; j < FN; ++j) {
               const int v = cbase + 16 * j + lr;
               const float z = acc[i][j][q];
-              if (v < N && (ix < 0 || z > mx)) { mx = z; ix = v; }
+              if (v < N && (ix < 0 || z > mx)) { mx = z; ix = e.col0 + v; }
             }
 #pragma unroll
             for (int o = 1; o < 16; o <<= 1) {
@@ -745,12 +746,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_fl_kernel(ActIn a, BRo
             for (int o = 1; o < 16; o <<= 1) sm += __shfl_xor(sm, o, kWave);
             if (r < M) {
               if (lr == 0) {
-                const size_t pi = (size_t)r * e.ntiles + cbase / 128;
+                const size_t pi = (size_t)r * e.ntiles + (e.col0 + cbase) / 128;
                 e.part_f[pi] = make_float4(mx, mx, sm, mx);
                 e.part_i[pi] = ix;
               }
               if (e.logits) {
-                const size_t base = (size_t)e.row_map[r] * N;
+                const size_t base = (size_t)e.row_map[r] * e.ldz + e.col0;
 #pragma unroll
                 for (int j = 0; j < FN; ++j)
                   if (cbase + 16 * j + lr < N) e.logits[base + cbase + 16 * j + lr] = acc[i][j][q];
@@ -1244,8 +1245,42 @@ int gemm_ksplit(const GemmArgs& g) {
   return gemm_plan(g.wdtype, g.a.mode, g.M, g.N, g.K, g.kind, g.fixed_split).ksplit;
 }
 
-hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
-  if (g.M <= 0 || g.N <= 0) return hipSuccess;
+// LM head on 256 x 256 tiles (one workgroup per CU): the column tiles of the
+// last, partly filled round run as a second launch with their K range split
+// ks ways (ks partial tiles of a third or a half of the work fill the CUs the
+// round would leave idle), and their partials are summed in split order before
+// the argmax / log-sum-exp epilogue.  The second denoise step's 256 rows make
+// 594 tiles: two whole rounds, then 82 tiles split three ways.  Returns the
+// columns of the whole rounds (0: no split) and ks.
+static int lmhead_split(int M, int N, int& ks) {
+  ks = 1;
+  if (N % 4) return 0;   // the partials are summed four columns at a time
+  const int cus = 256, ntm = (M + 255) / 256, ntn = (N + 255) / 256;
+  const int c = (ntm * ntn / cus) * cus / ntm;   // column tiles in whole rounds
+  const int rem = ntn - c;
+  ks = rem > 0 ? std::min(4, cus / (ntm * rem)) : 1;
+  return (c > 0 && ks >= 2) ? c * 256 : 0;
+}
+
+size_t gemm_lmhead_part_bytes(int M, int N) {
+  size_t best = 0;
+  for (int ntm = 1; ntm <= (M + 255) / 256; ++ntm) {
+    const int m = std::min(M, ntm * 256);
+    if (m <= 64) continue;   // at most 64 rows: 64 x 256 tiles, no split
+    int ks = 1;
+    const int cols = lmhead_split(m, N, ks);
+    if (cols > 0) best = std::max(best, (size_t)ks * m * (N - cols) * 4);
+  }
+  return best;
+}
+
+hipError_t launch_gemm(const GemmArgs& g_in, hipStream_t s) {
+  if (g_in.M <= 0 || g_in.N <= 0) return hipSuccess;
+  GemmArgs g = g_in;
+  if (g.kind == EPI_LMHEAD) {
+    g.e.col0 = 0;
+    g.e.ldz = g.N;
+  }
   if (g.wdtype == 0) {
     if (g.m_dev || g.a.rows) return hipErrorInvalidValue;
     switch (g.kind) {
@@ -1271,7 +1306,19 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t s) {
   } else {
     switch (g.kind) {
       case EPI_STORE: return go_bf16<1, EPI_STORE>(g, p, s);
-      case EPI_LMHEAD: return go_bf16<1, EPI_LMHEAD>(g, p, s);
+      case EPI_LMHEAD: {
+        int ks = 1;
+        const int cols = p.cfg == 11 && g.part ? lmhead_split(g.M, g.N, ks) : 0;
+        if (cols == 0 || (size_t)ks * g.M * (g.N - cols) * 4 > g.part_cap) return go_bf16<1, EPI_LMHEAD>(g, p, s);
+        GemmArgs g1 = g, g2 = g;
+        g1.N = cols;
+        g2.N = g.N - cols;
+        g2.b.b0 = (const bf16_t*)g.b.b0 + (size_t)cols * g.b.ldb;
+        g2.e.col0 = cols;
+        const hipError_t err = go_fl<256, 256, 4, 2, 1, EPI_LMHEAD, 3>(g1, 1, s);
+        if (err != hipSuccess) return err;
+        return go_fl<256, 256, 4, 2, 1, EPI_LMHEAD, 3>(g2, ks, s);
+      }
     }
   }
   return hipErrorInvalidValue;

@@ -35,6 +35,8 @@ struct EpiParams {
   int ntiles;
   const int* row_map;    // compact row -> b*B + i
   float* logits;         // [bt*B, V] or null
+  int col0;              // vocabulary index of the launch's column 0 (set by launch_gemm)
+  int ldz;               // vocabulary size: logits row stride (set by launch_gemm)
   int block;             // B
   float temperature;
   uint32_t seed_lo, seed_hi;
@@ -67,6 +69,8 @@ struct GemmArgs {
                          // (the next RMSNorm, or the query prep of the attention)
   const int* m_dev;      // optional device row count <= M: rows from it on are neither computed
                          // nor written (tile configuration 2 only, i.e. a fixed K split)
+  size_t part_cap;       // EPI_LMHEAD: bytes at part (0: none); the last round of tiles is K-split
+                         // into it when gemm_lmhead_part_bytes(M, N) fit
 };
 
 struct GemmPlan {
@@ -75,6 +79,9 @@ struct GemmPlan {
 };
 GemmPlan gemm_plan(int wdtype, int a_mode, int M, int N, int K, int kind, bool fixed_split);
 size_t gemm_partial_bytes(const GemmPlan& p, int M, int N);
+// Partial bytes the bf16 LM head over at most M rows (N columns, one activation
+// plane) uses for the K split of its last, partly filled round of tiles.
+size_t gemm_lmhead_part_bytes(int M, int N);
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t s);
 int gemm_ksplit(const GemmArgs& g);   // K split launch_gemm uses for g
 int gemm_bn(int wdtype, int K);  // columns per LM-head partial (partial count = ceil(N / bn))
