@@ -172,6 +172,19 @@ def test_draft_matches_oracle(name, ctx, B, S, T):
     assert out["compared"] >= tok.size // 2
 
 
+@pytest.mark.parametrize("inter,T", [(4608, 0.0), (5120, 1.0)])
+def test_draft_one_sequence_long_down_projection(inter, T):
+    """One sequence with an MLP wide enough that each of the down projection's eight
+    K splits is longer than two batches of eight 32-deep steps (the at-most-16-row GEMM
+    that copies the split's activation fragments to LDS once)."""
+    from dataclasses import replace
+    dims = replace(SMALL, intermediate=inter)
+    res, tok, lg, cf, _ = _draft_case(dims, [90], 8, 2, T, seed=140 + inter % 7)
+    out = compare_draft(dims, 2, res, tok, lg, cf)
+    print(f"draft one sequence, intermediate {inter}, T={T}: {out}")
+    assert out["compared"] >= tok.size // 2
+
+
 @pytest.mark.parametrize("name,ctx,B,S,T", [
     ("tiny", [64, 5], 4, 2, 0.0),
     ("small", [77], 8, 2, 0.0),           # one sequence: the skinny (at most 16 rows) GEMMs
