@@ -186,8 +186,11 @@ __global__ __launch_bounds__(256) void attn_qprep_kernel(AttnParams p) {
 // 8(r / 4) + 4t + (r % 4), r = 0..15: lane (gq, q) then holds the scores of
 // tokens 8 gq .. 8 gq + 7 in order, which are also the 8 consecutive tokens
 // its V^T operand needs (one 16-byte read of a V row).  K rows (256 B) keep
-// chunk c at c ^ kswz(row), V rows (32 B) keep half h at h ^ ((d >> 3) & 1):
-// the sixteen rows one operand read touches land on distinct bank groups.
+// chunk c at c ^ kswz(row), so the sixteen rows one operand read touches land
+// on distinct bank groups; V rows (32 B) keep their two halves in place: a
+// probe of the shader sequencer's bank-conflict counter finds the 16-row V
+// read conflict-free laid out so, and 2-way conflicted when the halves of rows
+// d and d + 8 are swapped.
 __device__ __forceinline__ int kswz(int krow) { return (krow & 15) ^ (((krow >> 4) & 1) << 2); }
 
 // Maximum over lanes l, l ^ 16, l ^ 32 and l ^ 48 (lane swaps across the
@@ -307,7 +310,7 @@ __global__ __launch_bounds__(64 * NW) void attn_ctx_mfma_kernel(AttnParams p) {
       loff[q] = (uint32_t)((krow & 15) * (D * 2) + lc * 16);
     } else {
       const int d = 32 * qq + (lane >> 1);
-      const int lh = (lane & 1) ^ ((d >> 3) & 1);
+      const int lh = lane & 1;
       loff[q] = (uint32_t)(d * 32 + lh * 16);
     }
   }
@@ -353,7 +356,7 @@ __global__ __launch_bounds__(64 * NW) void attn_ctx_mfma_kernel(AttnParams p) {
 #pragma unroll
     for (int nn = 0; nn < NN; ++nn) {
       const int d = 16 * nn + rr;
-      voff[nn] = (gq >> 1) * (D * 32) + d * 32 + (((gq & 1) ^ ((d >> 3) & 1)) << 4);
+      voff[nn] = (gq >> 1) * (D * 32) + d * 32 + ((gq & 1) << 4);
     }
   }
   const int tok_end = min(ctx, pg1 * 16);
@@ -370,7 +373,7 @@ __global__ __launch_bounds__(64 * NW) void attn_ctx_mfma_kernel(AttnParams p) {
       for (int c = tid; c < 2 * D * 16; c += 64 * NW) {
         const int pg = c / (D * 16), rem = c - pg * D * 16, d = rem >> 4, slot = rem & 15;
         if (tok0 + pg * 16 + slot >= ctx || (pg ? bad1 : bad0)) {
-          const int lh = (slot >> 3) ^ ((d >> 3) & 1);
+          const int lh = slot >> 3;
           *(bf16_t*)(vt + pg * (D * 32) + d * 32 + lh * 16 + (slot & 7) * 2) = 0;
         }
       }
