@@ -326,7 +326,7 @@ def run_loop_oracle(dims, Wn, ctx0, hid_np, steps, B, S, p, seed, only=None, gpu
             gkv[b] = unpack_pool(dims, gpu["pool"], gpu["n_pages"], gpu["table"], b, int(gpu["ctx"][b]))
     same_path = {b: gpu is not None for b in idx}
     ctx = {b: ctx0[b] for b in idx}
-    accs, toks, flags = [], [], []
+    accs, toks, flags, gaps = [], [], [], []
     t_start = time.time()
     for st in range(steps):
         if st % 8 == 0:
@@ -341,9 +341,13 @@ def run_loop_oracle(dims, Wn, ctx0, hid_np, steps, B, S, p, seed, only=None, gpu
         res = oracle.draft_block(dims, Wn, draft_pools, [ctx[b] for b in idx], Bt, S, want_logits=False)
         tok = res["tokens"]
         flag = np.zeros(len(idx), dtype=bool)
+        mgap = np.full(len(idx), np.inf)   # smallest decisive gap of the step (reported on a divergence)
         for r in range(len(idx)):
             for s_ in range(S):
                 now = np.nonzero(res["committed_at"][r] == s_)[0]
+                cand = [res["gap"][r, s_, i] for i in now] + ([res["boundary_gap"][r, s_]] if s_ < S - 1 else [])
+                if cand:
+                    mgap[r] = min(mgap[r], float(np.min(cand)))
                 if any(res["gap"][r, s_, i] < TIE for i in now) or (s_ < S - 1 and res["boundary_gap"][r, s_] < TIE):
                     flag[r] = True
         full = np.zeros((len(ctx0), Bt), dtype=np.int64)
@@ -353,6 +357,7 @@ def run_loop_oracle(dims, Wn, ctx0, hid_np, steps, B, S, p, seed, only=None, gpu
         accs.append(acc)
         toks.append(tok)
         flags.append(flag)
+        gaps.append(mgap)
         for r, b in enumerate(idx):
             if same_path[b] and not (np.array_equal(gpu["tok"][st][b], tok[r]) and gpu["acc"][st][b] == acc[r]):
                 same_path[b] = False
@@ -366,7 +371,7 @@ def run_loop_oracle(dims, Wn, ctx0, hid_np, steps, B, S, p, seed, only=None, gpu
                 T = ctx[b]
                 for name, own, got in (("K", pools[b][0], gkv[b][0]), ("V", pools[b][1], gkv[b][1])):
                     compare_pool_entries(got[:, :T], own[:, :T], dims.dtype, f"seq {b} {name}")
-    return dict(acc=np.array(accs), tok=toks, flags=np.array(flags), idx=idx)
+    return dict(acc=np.array(accs), tok=toks, flags=np.array(flags), gaps=np.array(gaps), idx=idx)
 
 
 def compare_loops(g, o, log_every=16):
@@ -383,7 +388,8 @@ def compare_loops(g, o, log_every=16):
             same = np.array_equal(g["tok"][st][b], o["tok"][st][r]) and g["acc"][st][b] == o["acc"][st][r]
             if not same:
                 assert o["flags"][st][r], f"step {st} seq {b}: GPU {g['tok'][st][b]} a={g['acc'][st][b]} " \
-                                          f"oracle {o['tok'][st][r]} a={o['acc'][st][r]} without a near-tie"
+                                          f"oracle {o['tok'][st][r]} a={o['acc'][st][r]} without a near-tie " \
+                                          f"(smallest oracle gap of the step {o['gaps'][st][r]:.3e})"
                 alive[r] = False
                 dropped += 1
     return dict(steps=int(o["acc"].shape[0]), seqs=len(idx), pairs_compared=compared,
