@@ -60,65 +60,86 @@ __global__ void embed_kernel(const int* tau, const T* embed, int vocab, float* h
 constexpr int kRmsMaxH = 8192;   // widest row
 constexpr int kRmsMaxSplit = 8;   // K-split partials folded with all loads in flight (more: one at a time)
 
-// NT threads per row: 256, or 1024 when there are few rows (more loads in flight per row).
-template <int NT>
+// NT threads per row (1024 when there are few rows, so more loads are in
+// flight per row), VEC float4 of the row per thread.  Every global read of a
+// row -- the residual and up to kRmsMaxSplit partials of each of the thread's
+// VEC quads -- is issued before the first add or store, so a row costs one
+// memory round trip (a store between the quads would keep the later loads
+// behind it: h and the partials may alias as far as the compiler knows).
+template <int NT, int VEC>
 __global__ __launch_bounds__(NT) void rmsnorm_kernel(float* h, const float* gain, ActOut out, int H,
                                                       float eps, const int* committed, int B, int n_open,
                                                       int* row_map, const float* part, int ksplit, int Mp,
                                                       ActOut cap) {
-  constexpr int kRmsVec = kRmsMaxH / (4 * NT);   // float4 per thread
   __shared__ double red[NT / 64];
   __shared__ int src_s;
   const int r = blockIdx.x, tid = threadIdx.x;
-  if (tid == 0) {
-    int src = r;
+  if (tid < 64) {
+    // source row: r itself, or the (r mod n_open)-th still-open position of its
+    // sequence (a ballot ranks up to 64 positions per pass)
     if (committed) {
       const int b = r / n_open, jj = r - b * n_open;
+      bool found = false;
       int seen = 0;
-      src = b * B;
-      for (int i = 0; i < B; ++i) {
-        if (!committed[b * B + i]) {
-          if (seen == jj) { src = b * B + i; break; }
-          ++seen;
+      for (int base = 0; base < B && !found; base += 64) {
+        const int i = base + tid;
+        const bool open = i < B && !committed[b * B + i];
+        const unsigned long long m = __ballot(open);
+        const int cnt = __popcll(m);
+        if (jj < seen + cnt) {
+          if (open && __popcll(m & ((1ull << tid) - 1ull)) == jj - seen) {
+            src_s = b * B + i;
+            row_map[r] = b * B + i;
+          }
+          found = true;
         }
+        seen += cnt;
       }
-      row_map[r] = src;
-    } else if (row_map) {
-      row_map[r] = r;
+      if (!found && tid == 0) {
+        src_s = b * B;
+        row_map[r] = b * B;
+      }
+    } else if (tid == 0) {
+      src_s = r;
+      if (row_map) row_map[r] = r;
     }
-    src_s = src;
   }
   __syncthreads();
-  // the row is read once into registers (H <= NT * 4 * kRmsVec); squares are
-  // summed in fp32 per thread (at most 4 * kRmsVec terms) and in double across
+  // the row is read once into registers (H <= NT * 4 * VEC); squares are
+  // summed in fp32 per thread (at most 4 * VEC terms) and in double across
   // threads
   float* x = h + (size_t)src_s * H;
-  float4 v[kRmsVec];
-  float ss = 0.f;
+  const bool fold = part && ksplit <= kRmsMaxSplit;
+  const size_t stride = (size_t)Mp * H;
+  float4 v[VEC];
+  float4 pv[VEC][kRmsMaxSplit];
 #pragma unroll
-  for (int k = 0; k < kRmsVec; ++k) {
+  for (int k = 0; k < VEC; ++k) {
     const int c = tid * 4 + 4 * NT * k;
     v[k] = c < H ? *(const float4*)(x + c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float* pp = part + (size_t)src_s * H + c;
+#pragma unroll
+    for (int sp = 0; sp < kRmsMaxSplit; ++sp)
+      pv[k][sp] = (fold && sp < ksplit && c < H) ? *(const float4*)(pp + sp * stride) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float ss = 0.f;
+#pragma unroll
+  for (int k = 0; k < VEC; ++k) {
+    const int c = tid * 4 + 4 * NT * k;
     if (part && c < H) {
       // residual += sum of the split-K partials, in split order (the same sums
-      // the split-K reduce would form).  Up to kRmsMaxSplit partials are loaded
-      // before the first add, so their loads are in flight together.
-      const float* pp = part + (size_t)src_s * H + c;
-      const size_t stride = (size_t)Mp * H;
+      // the split-K reduce would form)
       float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (ksplit <= kRmsMaxSplit) {
-        float4 pv[kRmsMaxSplit];
-#pragma unroll
-        for (int sp = 0; sp < kRmsMaxSplit; ++sp)
-          pv[sp] = sp < ksplit ? *(const float4*)(pp + sp * stride) : make_float4(0.f, 0.f, 0.f, 0.f);
+      if (fold) {
 #pragma unroll
         for (int sp = 0; sp < kRmsMaxSplit; ++sp) {
-          if (sp < ksplit) { a.x += pv[sp].x; a.y += pv[sp].y; a.z += pv[sp].z; a.w += pv[sp].w; }
+          if (sp < ksplit) { a.x += pv[k][sp].x; a.y += pv[k][sp].y; a.z += pv[k][sp].z; a.w += pv[k][sp].w; }
         }
       } else {
+        const float* pp = part + (size_t)src_s * H + c;
         for (int sp = 0; sp < ksplit; ++sp) {
-          const float4 pv = *(const float4*)(pp + sp * stride);
-          a.x += pv.x; a.y += pv.y; a.z += pv.z; a.w += pv.w;
+          const float4 q = *(const float4*)(pp + sp * stride);
+          a.x += q.x; a.y += q.y; a.z += q.z; a.w += q.w;
         }
       }
       v[k].x += a.x; v[k].y += a.y; v[k].z += a.z; v[k].w += a.w;
@@ -138,7 +159,7 @@ __global__ __launch_bounds__(NT) void rmsnorm_kernel(float* h, const float* gain
   for (int w = 0; w < NT / 64; ++w) tot += red[w];
   const float rs = (float)(1.0 / sqrt(tot / (double)H + (double)eps));
 #pragma unroll
-  for (int k = 0; k < kRmsVec; ++k) {
+  for (int k = 0; k < VEC; ++k) {
     const int c = tid * 4 + 4 * NT * k;
     if (c < H) {
       const float4 gg = *(const float4*)(gain + c);
@@ -354,13 +375,26 @@ hipError_t launch_rmsnorm(float* h, const float* gain, ActOut out, int M, int H,
   if (M <= 0) return hipSuccess;
   ActOut cap{};
   if (capture) cap = *capture;
+  if (H <= 0 || H > kRmsMaxH || H % 4) return hipErrorInvalidValue;
   const int ks = part ? ksplit : 0, mp = part_rows > 0 ? part_rows : M;
-  if (M < 128)
-    hipLaunchKernelGGL(rmsnorm_kernel<1024>, dim3(M), dim3(1024), 0, s, h, gain, out, H, eps, committed, B, n_open,
-                       row_map, part, ks, mp, cap);
-  else
-    hipLaunchKernelGGL(rmsnorm_kernel<256>, dim3(M), dim3(256), 0, s, h, gain, out, H, eps, committed, B, n_open,
-                       row_map, part, ks, mp, cap);
+#define RMS_GO(NT, VEC)                                                                                        \
+  hipLaunchKernelGGL((rmsnorm_kernel<NT, VEC>), dim3(M), dim3(NT), 0, s, h, gain, out, H, eps, committed, B, n_open, \
+                     row_map, part, ks, mp, cap)
+  // threads per row and quads per thread: the row in one pass, at most four
+  // quads (and their partials) in registers per thread
+  if (M < 128) {
+    if (H <= 4096) RMS_GO(1024, 1);
+    else RMS_GO(1024, 2);
+  } else if (H <= 1024) {
+    RMS_GO(256, 1);
+  } else if (H <= 2048) {
+    RMS_GO(256, 2);
+  } else if (H <= 4096) {
+    RMS_GO(256, 4);
+  } else {
+    RMS_GO(512, 4);
+  }
+#undef RMS_GO
   return hipGetLastError();
 }
 
