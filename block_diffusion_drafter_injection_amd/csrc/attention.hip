@@ -78,17 +78,45 @@ __device__ __forceinline__ void att_barrier() {
 // (fp32) are written too, [b][kv head][i][d], for the in-block part of the
 // attention.  When the q/k/v projection left K-split partials, they are
 // summed here in split order (the sums a separate reduction would form).
-__device__ __forceinline__ float4 qkv_quad(const AttnParams& p, size_t off, size_t plane) {
-  if (p.qkv_ks <= 1) return *(const float4*)(p.qkv + off);
-  float4 a = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int s = 0; s < p.qkv_ks; ++s) {
-    const float4 v = *(const float4*)(p.qkv_part + s * plane + off);
+// The quads of a head row at off (dims 4e ..) and off + h (their rotate-half
+// partners), each summed over the K-split partials in split order.  Up to
+// kQkvMaxSplit partials of both quads are loaded before the first add, so
+// their loads are in flight together; more are folded one at a time.
+constexpr int kQkvMaxSplit = 8;
+__device__ __forceinline__ void qkv_quads(const AttnParams& p, size_t off, size_t h, size_t plane, float4& x0,
+                                          float4& x1) {
+  if (p.qkv_ks <= 1) {
+    x0 = *(const float4*)(p.qkv + off);
+    x1 = *(const float4*)(p.qkv + off + h);
+    return;
+  }
+  x0 = make_float4(0.f, 0.f, 0.f, 0.f);
+  x1 = x0;
+  auto add = [](float4& a, const float4& v) {
     a.x += v.x;
     a.y += v.y;
     a.z += v.z;
     a.w += v.w;
+  };
+  if (p.qkv_ks <= kQkvMaxSplit) {
+    float4 v0[kQkvMaxSplit], v1[kQkvMaxSplit];
+#pragma unroll
+    for (int s = 0; s < kQkvMaxSplit; ++s) {
+      v0[s] = s < p.qkv_ks ? *(const float4*)(p.qkv_part + s * plane + off) : make_float4(0.f, 0.f, 0.f, 0.f);
+      v1[s] = s < p.qkv_ks ? *(const float4*)(p.qkv_part + s * plane + off + h) : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+#pragma unroll
+    for (int s = 0; s < kQkvMaxSplit; ++s)
+      if (s < p.qkv_ks) {
+        add(x0, v0[s]);
+        add(x1, v1[s]);
+      }
+    return;
   }
-  return a;
+  for (int s = 0; s < p.qkv_ks; ++s) {
+    add(x0, *(const float4*)(p.qkv_part + s * plane + off));
+    add(x1, *(const float4*)(p.qkv_part + s * plane + off + h));
+  }
 }
 
 // Rotate-half RoPE of four consecutive first-half dims x0 (4e .. 4e+3) and
@@ -131,7 +159,8 @@ __global__ __launch_bounds__(256) void attn_qprep_kernel(AttnParams p) {
     const float qscale = p.scale * 1.4426950408889634f;   // scores come out in base-2 units
     const int r = u, j = r / p.B, i = r - j * p.B, row = b * p.B + i, n = m * g + j;
     const size_t off = (size_t)row * ldq + n * D + 4 * e;
-    float4 x0 = qkv_quad(p, off, plane), x1 = qkv_quad(p, off + h, plane);
+    float4 x0, x1;
+    qkv_quads(p, off, h, plane, x0, x1);
     if (p.q_gain) head_rmsnorm<TPR, D>(x0, x1, p.q_gain, e, p.rms_eps);
     const float4* cs = (const float4*)(p.cs + (size_t)row * h + 4 * e);   // (cos, sin) of dims 4e .. 4e+3
     float4 y0, y1;
@@ -152,7 +181,8 @@ __global__ __launch_bounds__(256) void attn_qprep_kernel(AttnParams p) {
   const int r = is_k ? u - R : u - R - p.B;   // block position
   const int krow = b * p.B + r;
   const size_t off = (size_t)krow * ldq + (p.nq + (is_k ? 0 : p.nkv)) * D + m * D + 4 * e;
-  float4 x0 = qkv_quad(p, off, plane), x1 = qkv_quad(p, off + h, plane);
+  float4 x0, x1;
+  qkv_quads(p, off, h, plane, x0, x1);
   const size_t o = (((size_t)b * p.nkv + m) * p.B + r) * D + 4 * e;
   if (is_k) {   // rotated key (QK-normed first when asked)
     if (p.k_gain) head_rmsnorm<TPR, D>(x0, x1, p.k_gain, e, p.rms_eps);

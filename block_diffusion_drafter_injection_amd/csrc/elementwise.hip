@@ -196,9 +196,21 @@ __global__ __launch_bounds__(256) void lm_combine_kernel(const float4* part_f, c
   __shared__ int shi[4];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   LmAcc a{-INFINITY, -INFINITY, 0.f, -INFINITY, -1};
-  for (int t = tid; t < ntiles; t += 256) {
-    const float4 f = part_f[(size_t)r * ntiles + t];
-    lm_merge(a, f.x, f.y, f.z, f.w, part_i[(size_t)r * ntiles + t]);
+  // a thread's partials t = tid + 256 k, merged in k order; LMQ of them loaded
+  // per pass before the first merge, so their loads are in flight together
+  constexpr int LMQ = 8;
+  for (int t0 = tid; t0 < ntiles; t0 += 256 * LMQ) {
+    float4 f[LMQ];
+    int fi[LMQ];
+#pragma unroll
+    for (int q = 0; q < LMQ; ++q) {
+      const int t = t0 + 256 * q;
+      f[q] = t < ntiles ? part_f[(size_t)r * ntiles + t] : make_float4(0.f, 0.f, 0.f, 0.f);
+      fi[q] = t < ntiles ? part_i[(size_t)r * ntiles + t] : -1;
+    }
+#pragma unroll
+    for (int q = 0; q < LMQ; ++q)
+      if (t0 + 256 * q < ntiles) lm_merge(a, f[q].x, f[q].y, f[q].z, f[q].w, fi[q]);
   }
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1)
