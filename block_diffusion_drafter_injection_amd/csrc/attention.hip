@@ -14,6 +14,7 @@
 // (one 16-byte LDS read per fragment, no transpose).  P is split hi/lo too.
 // fp32 pool and the in-block split: a VALU kernel, four lanes per query row.
 #include <algorithm>
+#include <type_traits>
 
 #include "kernels.h"
 
@@ -456,8 +457,13 @@ __global__ __launch_bounds__(64 * NW) void attn_ctx_mfma_kernel(AttnParams p) {
       ATT_READ_V(0, vf);
     }
   }
-  for (int it = 0; it < ntiles; ++it) {
-    const bool more = it + 1 < ntiles;
+  // One iteration.  FAST: tiles it and it+1 are whole and every page of the
+  // split is mapped, so no score is masked and no tail is zeroed; the leading
+  // iterations of a split run so, the last ones (and every iteration of a split
+  // with an unmapped page) take the general path.
+  auto step = [&](int it, auto fast_c) __attribute__((always_inline)) {
+    constexpr bool FAST = decltype(fast_c)::value;
+    const bool more = FAST || it + 1 < ntiles;
     if (more) {
       wait_tile(it + 1);
       att_barrier();
@@ -465,7 +471,7 @@ __global__ __launch_bounds__(64 * NW) void attn_ctx_mfma_kernel(AttnParams p) {
         issue(page_of(issued), (it - 1) % STAGES);   // tile it+STAGES-1 into tile it-1's buffer
         ++issued;
       }
-      zero_tail(it + 1);
+      if constexpr (!FAST) zero_tail(it + 1);
     }
     if (wave_active) {
       // K of tile it+1 (stale and unused after the last tile)
@@ -493,10 +499,14 @@ __global__ __launch_bounds__(64 * NW) void attn_ctx_mfma_kernel(AttnParams p) {
       // lane owns query (lane & 15) and tokens tok0 + tl + 4t + e, all on page
       // lane >> 5 of the tile; scores in base-2 units (the queries carry
       // scale * log2 e)
-      const bool bad0 = unmapped(it, 0), bad1 = unmapped(it, 1);
+      bool bad0 = false, bad1 = false;
+      if constexpr (!FAST) {
+        bad0 = unmapped(it, 0);
+        bad1 = unmapped(it, 1);
+      }
       const bool page_ok = !((lane >> 5) ? bad1 : bad0);
       float s[8];
-      if (tok0 + 32 <= tok_end && !bad0 && !bad1) {
+      if (FAST || (tok0 + 32 <= tok_end && !bad0 && !bad1)) {
 #pragma unroll
         for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -543,7 +553,12 @@ __global__ __launch_bounds__(64 * NW) void attn_ctx_mfma_kernel(AttnParams p) {
       // tile it+1 landed (waited for above): its V fragments for the next P V
       if (more) ATT_READ_V(it + 1, vf);
     }
-  }
+  };
+  const int full = tok_end > pg0 * 16 ? min(ntiles, (tok_end - pg0 * 16) / 32) : 0;   // leading whole tiles
+  const int n_fast = any_bad ? 0 : max(0, full - 1);
+  int it = 0;
+  for (; it < n_fast; ++it) step(it, std::true_type{});
+  for (; it < ntiles; ++it) step(it, std::false_type{});
 #undef ATT_SCORES
 #undef ATT_READ_V
 
