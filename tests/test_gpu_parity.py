@@ -185,6 +185,24 @@ def test_draft_one_sequence_long_down_projection(inter, T):
     assert out["compared"] >= tok.size // 2
 
 
+@pytest.mark.parametrize("hidden,ctx", [
+    (512, [20, 5, 33, 12, 40, 8, 27, 16]),      # 128 rows of 512: 256 threads, one quad each
+    (1536, [40, 3, 17, 60, 9, 33, 25, 70]),     # 128 rows of 1536: two quads per thread
+    (6144, [12, 40, 7, 22, 31, 5, 18, 26]),     # 128 rows of 6144: 512 threads, four quads each
+    (6144, [30, 11]),                           # 32 rows of 6144: 1024 threads, two quads each
+])
+def test_draft_rmsnorm_row_widths(hidden, ctx):
+    """Every launch shape of the RMSNorm (threads per row and quads per thread follow the
+    row count and width), each folding the K-split partials of the O and down projections:
+    the draft against the oracle at hidden sizes and batches that select them."""
+    from dataclasses import replace
+    dims = replace(SMALL, hidden=hidden)
+    res, tok, lg, cf, _ = _draft_case(dims, ctx, 16, 2, 0.0, seed=170 + hidden % 11 + len(ctx))
+    out = compare_draft(dims, 2, res, tok, lg, cf)
+    print(f"draft hidden {hidden} ctx={ctx}: {out}")
+    assert out["compared"] >= tok.size // 2
+
+
 @pytest.mark.parametrize("name,ctx,B,S,T", [
     ("tiny", [64, 5], 4, 2, 0.0),
     ("small", [77], 8, 2, 0.0),           # one sequence: the skinny (at most 16 rows) GEMMs
